@@ -1,0 +1,137 @@
+/*
+ * libtgemm -- block-tiled dense matrix multiply for AMD Instinct MI355X (gfx950).
+ *
+ *   C[m,n] = sum_{k<K} A[m,k] * b(n,k),   A [M,K] row-major (K contiguous)
+ *     b_layout TGEMM_B_NK: B stored [N,K] row-major (K contiguous), b(n,k) = B[n*K+k],
+ *                          so C = A x B^T ("0. A Minimal Hopper Matmul", Tilus tutorial,
+ *                          section "Block Tiling": A (M,K), B (N,K), C (M,N), both K-major)
+ *     b_layout TGEMM_B_KN: B stored [K,N] row-major (N contiguous), b(n,k) = B[k*N+n],
+ *                          so C = A x B ("Tiling a matmul", section "Code"; "TileLang: a
+ *                          tile language one level below Triton", section "The first
+ *                          kernel: GEMM", where B is a (K,N) tensor)
+ *
+ * Inputs are IEEE binary16 (f16) or bfloat16 (bf16); products are summed in fp32 and the
+ * fp32 sum is rounded once, to nearest-even, to the same 16-bit type for C (the fp32
+ * accumulator and the single cast in the epilogue of the Tilus tutorial, sections "The
+ * Full Kernel" and "Epilogue").  The summation order is the kernel's own: results agree
+ * with an exact sum to within fp32 rounding, not bit for bit.
+ *
+ * Conventions shared by every entry point:
+ *   - Ownership: the caller allocates A, B and C in device memory (packed, no leading
+ *     dimensions) and keeps ownership.  The library allocates no device memory and keeps
+ *     no pointer after the call returns.  C is fully overwritten (no alpha/beta).
+ *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns at once.  Faults during execution surface at the caller's
+ *     next synchronisation with that stream, as for any HIP launch.
+ *   - Errors: a negative status; all argument checks run before anything is enqueued, and
+ *     a failed check enqueues nothing.  Nothing aborts or exits.
+ *   - Degenerate shapes: M == 0 or N == 0 is a no-op returning TGEMM_OK; K == 0 writes
+ *     +0.0 (the empty sum) to all of C.
+ *   - Alignment: any 2-byte-aligned pointers and any sizes are accepted.  The fast kernels
+ *     need A, B, C 16-byte aligned, K % 8 == 0 and N % 8 == 0; other calls run a slower
+ *     kernel with the same arithmetic.
+ *   - Limits: M, N, K < 2^31 and M*K, N*K, M*N < 2^31 elements (TGEMM_ERR_UNSUPPORTED).
+ *   - Aliasing: C may not overlap A or B (TGEMM_ERR_ALIASING).  A and B may overlap.
+ *   - Thread safety: the configuration table is read-only; calls from several host
+ *     threads are safe.  Calls on one stream execute in order.
+ */
+#ifndef TGEMM_H
+#define TGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TGEMM_F16 = 0, TGEMM_BF16 = 1 } tgemm_dtype;
+
+typedef enum {
+    TGEMM_B_NK = 0, /* B is [N,K], K contiguous: C = A x B^T */
+    TGEMM_B_KN = 1  /* B is [K,N], N contiguous: C = A x B   */
+} tgemm_b_layout;
+
+typedef enum {
+    TGEMM_OK = 0,
+    TGEMM_ERR_INVALID_VALUE = -1, /* negative size, unknown dtype or layout           */
+    TGEMM_ERR_NULL_POINTER = -2,  /* A, B or C NULL for a non-empty product            */
+    TGEMM_ERR_ALIGNMENT = -3,     /* a pointer not 2-byte aligned, or an explicit fast
+                                     configuration given operands it cannot take        */
+    TGEMM_ERR_ALIASING = -4,      /* C overlaps A or B                                  */
+    TGEMM_ERR_UNSUPPORTED = -5,   /* sizes past the limits, or a configuration that is
+                                     not compiled into the library                      */
+    TGEMM_ERR_LAUNCH = -6,        /* the HIP launch was refused (no gfx950 device...)   */
+    TGEMM_ERR_DEVICE = -7         /* the current device could not be queried            */
+} tgemm_status;
+
+/* Kernel families in the library. */
+typedef enum {
+    TGEMM_KERNEL_GENERIC = 0, /* any alignment and size: element loads, one LDS stage    */
+    TGEMM_KERNEL_TILED = 1,   /* 128-bit loads, register prefetch, two swizzled LDS
+                                 stages, MFMA 32x32x16, grouped XCD-aware tile order     */
+    TGEMM_KERNEL_SKINNY = 2   /* small M: the K range of a tile split over the waves of a
+                                 workgroup and summed in LDS                              */
+} tgemm_kernel;
+
+/* One tile configuration.  block_m x block_n is the C tile of one workgroup, block_k
+ * the K step, waves_m x waves_n the wavefront grid inside the workgroup (64 lanes each),
+ * stages the LDS buffers, group_m the tile rows of one launch-order group, and
+ * split_k the number of waves that share one C tile's K range (SKINNY only, else 1). */
+typedef struct {
+    int32_t kernel;
+    int32_t block_m, block_n, block_k;
+    int32_t waves_m, waves_n;
+    int32_t stages;
+    int32_t group_m;
+    int32_t split_k;
+} tgemm_config;
+
+/*
+ * C = A x B^T (TGEMM_B_NK) or A x B (TGEMM_B_KN) for fp16 inputs and output.
+ *   m, n, k   : sizes (>= 0)
+ *   A         : device pointer, m*k halves, row-major [m,k]
+ *   B         : device pointer, n*k halves, [n,k] or [k,n] per b_layout
+ *   C         : device pointer, m*n halves, row-major [m,n]; written, never read
+ *   b_layout  : tgemm_b_layout
+ *   stream    : hipStream_t to enqueue on (NULL = null stream)
+ * Returns a tgemm_status.  The configuration comes from the library's table.
+ */
+int gemm_f16(int64_t m, int64_t n, int64_t k, const void* A, const void* B, void* C,
+             int b_layout, void* stream);
+
+/* The same for bfloat16 inputs and output. */
+int gemm_bf16(int64_t m, int64_t n, int64_t k, const void* A, const void* B, void* C,
+              int b_layout, void* stream);
+
+/*
+ * The same product with an explicit dtype (tgemm_dtype) and, optionally, an explicit
+ * configuration (cfg == NULL: the table's choice).  A configuration must be one that
+ * tgemm_list_configs reports (else TGEMM_ERR_UNSUPPORTED); a fast-kernel configuration
+ * given operands that break its alignment rules fails with TGEMM_ERR_ALIGNMENT.  This is
+ * the entry point of the tile-configuration sweep.
+ */
+int gemm_ex(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const void* B,
+            void* C, int b_layout, const tgemm_config* cfg, void* stream);
+
+/* The configuration the table picks for this problem (written to *out).  Host-only: it
+ * touches no device.  Same argument checks as gemm_ex on the sizes, dtype and layout;
+ * `aligned` says whether the operands will meet the fast-kernel alignment rules. */
+int tgemm_query_config(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
+                       int aligned, tgemm_config* out);
+
+/* The configurations compiled into the library for (dtype, b_layout).  Writes up to
+ * `capacity` entries to `out` (which may be NULL when capacity is 0) and returns the
+ * total count, or a negative status.  Host-only. */
+int tgemm_list_configs(int dtype, int b_layout, tgemm_config* out, int capacity);
+
+/* A static, human-readable name for a status code. */
+const char* tgemm_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int tgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TGEMM_H */

@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the header
+declares, and rejects bad arguments before touching any device (no compute here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+tgemm = pytest.importorskip("tiled_dense_gemm_major_amd.tgemm")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tgemm.LIB_PATH):
+        from tiled_dense_gemm_major_amd import build
+        build.build()
+    return tgemm.load()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "tgemm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_function(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(tgemm.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert tgemm.version() >= 100
+    for code in range(0, -8, -1):
+        assert tgemm.status_string(code).startswith("TGEMM_")
+    assert "unknown" in tgemm.status_string(-99)
+
+
+FAKE = 1 << 40   # a 16-byte aligned address that is never dereferenced by these calls
+
+
+@pytest.mark.parametrize("fn", ["gemm_f16", "gemm_bf16"])
+def test_argument_errors(lib, fn):
+    f = getattr(lib, fn)
+    # negative sizes, bad layout
+    assert f(-1, 8, 8, FAKE, FAKE + 4096, FAKE + 8192, 0, None) == -1
+    assert f(8, -1, 8, FAKE, FAKE + 4096, FAKE + 8192, 0, None) == -1
+    assert f(8, 8, -1, FAKE, FAKE + 4096, FAKE + 8192, 0, None) == -1
+    assert f(8, 8, 8, FAKE, FAKE + 4096, FAKE + 8192, 2, None) == -1
+    # NULL operands of a non-empty product
+    assert f(8, 8, 8, None, FAKE + 4096, FAKE + 8192, 0, None) == -2
+    assert f(8, 8, 8, FAKE, None, FAKE + 8192, 0, None) == -2
+    assert f(8, 8, 8, FAKE, FAKE + 4096, None, 0, None) == -2
+    # odd addresses are not 16-bit element addresses
+    assert f(8, 8, 8, FAKE + 1, FAKE + 4096, FAKE + 8192, 0, None) == -3
+    # C overlapping A or B
+    assert f(8, 8, 8, FAKE, FAKE + 4096, FAKE + 64, 0, None) == -4
+    assert f(8, 8, 8, FAKE, FAKE + 4096, FAKE + 4096 + 126, 0, None) == -4
+    # sizes past the 2^31-element limits
+    assert f(1 << 31, 8, 8, FAKE, FAKE + 4096, FAKE + 8192, 0, None) == -5
+    assert f(1 << 20, 1 << 20, 8, FAKE, FAKE + (1 << 30), FAKE + (1 << 35), 0, None) == -5
+
+
+@pytest.mark.parametrize("fn", ["gemm_f16", "gemm_bf16"])
+def test_empty_products_are_no_ops(lib, fn):
+    f = getattr(lib, fn)
+    # M == 0 or N == 0 returns before any device work, even with NULL pointers
+    assert f(0, 8, 8, None, None, None, 0, None) == 0
+    assert f(8, 0, 8, None, None, None, 1, None) == 0
+
+
+def test_gemm_ex_rejects_unknown_config(lib):
+    bad = tgemm.Config(kernel=1, block_m=96, block_n=96, block_k=64, waves_m=2, waves_n=2,
+                       stages=2, group_m=4, split_k=1)
+    rc = lib.gemm_ex(1, 64, 64, 64, FAKE, FAKE + 65536, FAKE + 131072, 0, ctypes.byref(bad),
+                     None)
+    assert rc == -5
+    assert lib.gemm_ex(7, 64, 64, 64, FAKE, FAKE + 65536, FAKE + 131072, 0, None, None) == -1
+
+
+def test_fast_config_needs_alignment(lib):
+    tiled = [c for c in tgemm.list_configs(tgemm.BF16) if c.kernel == tgemm.KERNEL_TILED][0]
+    # K % 8 != 0 cannot take a 128-bit-load configuration
+    rc = lib.gemm_ex(1, 64, 64, 60, FAKE, FAKE + 65536, FAKE + 131072, 0,
+                     ctypes.byref(tiled), None)
+    assert rc == -3
+
+
+def test_query_config_table(lib):
+    big = tgemm.query_config(tgemm.BF16, 8192, 8192, 8192)
+    assert big.kernel == tgemm.KERNEL_TILED and big.block_m * big.block_n >= 128 * 128
+    odd = tgemm.query_config(tgemm.F16, 100, 100, 100, aligned=False)
+    assert odd.kernel == tgemm.KERNEL_GENERIC
+    listed = {tuple(sorted(c.as_dict().items())) for c in tgemm.list_configs(tgemm.BF16)}
+    for shape in [(512, 512, 512), (4096, 4096, 4096), (8192, 8192, 8192), (64, 8192, 8192),
+                  (4000, 3000, 1000)]:
+        c = tgemm.query_config(tgemm.BF16, *shape)
+        assert tuple(sorted(c.as_dict().items())) in listed, (shape, c)
+    with pytest.raises(tgemm.TGemmError):
+        tgemm.query_config(tgemm.BF16, -1, 8, 8)
+
+
+def test_list_configs(lib):
+    for dt in (tgemm.F16, tgemm.BF16):
+        for lay in (tgemm.B_NK, tgemm.B_KN):
+            cfgs = tgemm.list_configs(dt, lay)
+            kinds = {c.kernel for c in cfgs}
+            assert tgemm.KERNEL_GENERIC in kinds and tgemm.KERNEL_TILED in kinds
+            for c in cfgs:
+                if c.kernel == tgemm.KERNEL_TILED:
+                    # the LDS ring must fit the 160 KiB of one compute unit
+                    assert c.stages * (c.block_m + c.block_n) * c.block_k * 2 <= 160 * 1024
+    assert lib.tgemm_list_configs(5, 0, None, 0) == -1

@@ -1,0 +1,206 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the CPU oracle, element
+by element, with |gpu - oracle| <= 1e-3*sqrt(K) + one output ulp of |oracle|; bit for bit
+where every partial sum is exact."""
+import numpy as np
+import pytest
+
+from tests.gpu_util import (assert_parity, from_dev, require_gpu, run, sample_positions,
+                            say, to_dev, torch)
+from tiled_dense_gemm_major_amd.inputs import (BF16, B_KN, B_NK, F16, WORKLOADS, Stream,
+                                               Workload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _inputs(dtype, M, N, K, layout, seed, dist="uniform"):
+    s = Stream(seed)
+    A = s.matrix((M, K), dtype, dist)
+    B = s.matrix((N, K) if layout == B_NK else (K, N), dtype, dist)
+    return A, B
+
+
+def _configs(dtype, layout):
+    from tiled_dense_gemm_major_amd import tgemm
+    return tgemm.list_configs(dtype, layout)
+
+
+def _cfg_id(c):
+    return f"k{c.kernel}_{c.block_m}x{c.block_n}x{c.block_k}_w{c.waves_m}x{c.waves_n}"
+
+
+# ---------------------------------------------------------------------------------------
+# Every compiled configuration on ragged shapes spanning several tiles.
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("layout", [B_NK, B_KN])
+def test_every_config_ragged(dev, orc, dtype, layout):
+    M, N, K = 600, 536, 328          # ragged against 64/128/256 tiles; K tail of 8 past 64
+    A, B = _inputs(dtype, M, N, K, layout, 100 + dtype + 2 * layout)
+    want = orc.gemm(dtype, A, B, layout)
+    for cfg in _configs(dtype, layout):
+        say(f"config {_cfg_id(cfg)} dtype {dtype} layout {layout} {M}x{N}x{K}")
+        got = run(dtype, A, B, layout, cfg)
+        assert_parity(orc, dtype, K, got, want, _cfg_id(cfg))
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("layout", [B_NK, B_KN])
+@pytest.mark.parametrize("shape", [(1, 8, 8), (8, 8, 16), (33, 40, 72), (257, 264, 1000),
+                                   (64, 1024, 2048), (300, 8, 520)])
+def test_table_choice_shapes(dev, orc, dtype, layout, shape):
+    M, N, K = shape
+    A, B = _inputs(dtype, M, N, K, layout, 7 + M + N + K)
+    say(f"table choice {dtype} {layout} {shape}")
+    got = run(dtype, A, B, layout)
+    assert_parity(orc, dtype, K, got, orc.gemm(dtype, A, B, layout), str(shape))
+
+
+# ---------------------------------------------------------------------------------------
+# Exact arithmetic: small integers make every fp32 partial sum exact, so any summation
+# order gives the oracle's bits.  Index-coded and one-hot inputs catch mapping bugs.
+# ---------------------------------------------------------------------------------------
+def _int_bits(dtype, arr):
+    from tiled_dense_gemm_major_amd.inputs import round_to_bf16_bits, round_to_f16_bits
+    f = round_to_f16_bits if dtype == F16 else round_to_bf16_bits
+    return f(np.asarray(arr, dtype=np.float64))
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("layout", [B_NK, B_KN])
+def test_exact_small_integers_bitwise(dev, orc, dtype, layout):
+    rng = np.random.default_rng(17)
+    M, N, K = 520, 392, 264
+    A = _int_bits(dtype, rng.integers(-2, 3, (M, K)))
+    Bn = _int_bits(dtype, rng.integers(-2, 3, (N, K)))
+    B = Bn if layout == B_NK else np.ascontiguousarray(Bn.T)
+    want = orc.gemm(dtype, A, B, layout)
+    for cfg in _configs(dtype, layout):
+        say(f"exact ints {_cfg_id(cfg)}")
+        got = run(dtype, A, B, layout, cfg)
+        assert np.array_equal(got, want), _cfg_id(cfg)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_index_coded_and_one_hot_k(dev, orc, dtype):
+    # A[m,k] = 1 only at k = K-1 (catches K-tail bugs); B[n,k] = n/8 at k = K-1, so
+    # C[m,n] = n/8 exactly: column mapping is visible in every element.
+    M, N, K = 300, 272, 200
+    A = np.zeros((M, K)); A[:, K - 1] = 1.0
+    B = np.zeros((N, K)); B[:, K - 1] = np.arange(N) / 8.0
+    A, B = _int_bits(dtype, A), _int_bits(dtype, B)
+    want = orc.gemm(dtype, A, B, B_NK)
+    for cfg in _configs(dtype, B_NK):
+        say(f"one-hot k {_cfg_id(cfg)}")
+        assert np.array_equal(run(dtype, A, B, B_NK, cfg), want), _cfg_id(cfg)
+    # row-coded: A[m, k] = (m % 64) / 8 at k = 0 only, B = 1 at k = 0: C[m, n] = (m%64)/8
+    A = np.zeros((M, K)); A[:, 0] = (np.arange(M) % 64) / 8.0
+    B = np.zeros((N, K)); B[:, 0] = 1.0
+    A, B = _int_bits(dtype, A), _int_bits(dtype, B)
+    want = orc.gemm(dtype, A, B, B_NK)
+    for cfg in _configs(dtype, B_NK):
+        say(f"row-coded {_cfg_id(cfg)}")
+        assert np.array_equal(run(dtype, A, B, B_NK, cfg), want), _cfg_id(cfg)
+
+
+# ---------------------------------------------------------------------------------------
+# Degenerate and awkward arguments.
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_k_zero_writes_zeros(dev, orc, dtype):
+    A = np.zeros((70, 0), dtype=np.uint16)
+    B = np.zeros((0, 90), dtype=np.uint16)
+    say("k = 0")
+    got = run(dtype, A, B, B_KN)
+    assert got.shape == (70, 90) and np.all(got == 0)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("layout", [B_NK, B_KN])
+@pytest.mark.parametrize("shape,offsets", [((77, 51, 37), (0, 0, 0)),   # K, N not x8
+                                           ((128, 128, 128), (1, 0, 0)),  # A misaligned
+                                           ((128, 128, 128), (0, 3, 0)),  # B misaligned
+                                           ((128, 128, 128), (0, 0, 5)),  # C misaligned
+                                           ((5, 3, 1), (0, 0, 0))])
+def test_unaligned_and_odd_sizes(dev, orc, dtype, layout, shape, offsets):
+    M, N, K = shape
+    A, B = _inputs(dtype, M, N, K, layout, 55 + M)
+    say(f"odd sizes {shape} offsets {offsets}")
+    got = run(dtype, A, B, layout, a_offset=offsets[0], b_offset=offsets[1],
+              c_offset=offsets[2])
+    assert_parity(orc, dtype, K, got, orc.gemm(dtype, A, B, layout), str((shape, offsets)))
+
+
+def test_does_not_write_outside_c(dev, orc):
+    from tiled_dense_gemm_major_amd import tgemm
+    M, N, K = 200, 136, 96
+    A, B = _inputs(BF16, M, N, K, B_NK, 3)
+    guard = 4096
+    buf = torch.full((guard + M * N + guard,), 0x1234, dtype=torch.int16, device="cuda")
+    C = buf[guard:guard + M * N].view(torch.bfloat16).view(M, N)
+    say("guard bands")
+    tgemm.gemm_bf16(M, N, K, to_dev(A, BF16), to_dev(B, BF16), C)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    assert np.all(host[:guard] == 0x1234) and np.all(host[guard + M * N:] == 0x1234)
+
+
+def test_repeat_launches_bitwise_identical(dev, orc):
+    """Stage-reuse races show up as rare differences between launches (the tutorial's
+    corrupted-barrier lesson): the kernels have a fixed order and no atomics, so every
+    launch must give the same bits, with no NaN."""
+    from tiled_dense_gemm_major_amd import tgemm
+    w = WORKLOADS["bf16_4096"]
+    M, N, K = 2048, 2048, 4096
+    A, B = _inputs(BF16, M, N, K, B_NK, 77)
+    Ad, Bd = to_dev(A, BF16), to_dev(B, BF16)
+    C0 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    tgemm.gemm_bf16(M, N, K, Ad, Bd, C0)
+    ref = from_dev(C0)
+    assert not np.any(np.isnan(ref.view(np.uint16).astype(np.uint32) << 16)
+                      .view(np.float32))
+    say(f"repeat launches {w.name}-like {M}x{N}x{K}")
+    C = torch.empty_like(C0)
+    for _ in range(30):
+        tgemm.gemm_bf16(M, N, K, Ad, Bd, C)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(C), ref)
+
+
+def test_stream_argument(dev, orc):
+    from tiled_dense_gemm_major_amd import tgemm
+    M, N, K = 256, 256, 256
+    A, B = _inputs(F16, M, N, K, B_NK, 9)
+    s = torch.cuda.Stream()
+    Ad, Bd = to_dev(A, F16), to_dev(B, F16)
+    C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        tgemm.gemm_f16(M, N, K, Ad, Bd, C, stream=s)
+    s.synchronize()
+    assert_parity(orc, F16, K, from_dev(C), orc.gemm(F16, A, B, B_NK), "stream")
+
+
+# ---------------------------------------------------------------------------------------
+# The five workloads at their full sizes, in the configuration the table picks (the one
+# the benchmark times): whole-matrix comparison where the oracle is quick, sampled
+# entries (each summed on its own by the oracle) elsewhere.
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_full_size(dev, orc, name):
+    w = WORKLOADS[name]
+    A, B = w.generate()
+    say(f"workload {w.name}: {w.describe()}")
+    got = run(w.dtype, A, B, w.b_layout)
+    assert not np.any(got == 0x7E00)     # every element written
+    if w.M * w.N * w.K <= 2 ** 34:
+        want = orc.gemm(w.dtype, A, B, w.b_layout)
+        assert_parity(orc, w.dtype, w.K, got, want, name)
+    else:
+        rows, cols = sample_positions(w.M, w.N, 3000, w.seed)
+        want, _ = orc.gemm_entries(w.dtype, A, B, w.b_layout, rows, cols)
+        assert_parity(orc, w.dtype, w.K, got[rows, cols], want, name)

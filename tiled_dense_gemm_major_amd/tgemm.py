@@ -1,0 +1,170 @@
+"""Thin ctypes binding of libtgemm (include/tgemm.h): argument marshalling only.
+
+Every step of the product runs in the library's HIP kernels; PyTorch, when used, only
+supplies device memory (``data_ptr()``) and streams (``cuda_stream``).  There is no CPU
+fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+F16, BF16 = 0, 1
+B_NK, B_KN = 0, 1
+KERNEL_GENERIC, KERNEL_TILED, KERNEL_SKINNY = 0, 1, 2
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtgemm.so")
+
+EXPORTS = ("gemm_f16", "gemm_bf16", "gemm_ex", "tgemm_query_config", "tgemm_list_configs",
+           "tgemm_status_string", "tgemm_version")
+
+
+class TGemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class Config(ctypes.Structure):
+    """tgemm_config."""
+    _fields_ = [("kernel", ctypes.c_int32), ("block_m", ctypes.c_int32),
+                ("block_n", ctypes.c_int32), ("block_k", ctypes.c_int32),
+                ("waves_m", ctypes.c_int32), ("waves_n", ctypes.c_int32),
+                ("stages", ctypes.c_int32), ("group_m", ctypes.c_int32),
+                ("split_k", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        return {name: int(getattr(self, name)) for name, _ in self._fields_}
+
+    @classmethod
+    def from_dict(cls, d: dict) -> "Config":
+        return cls(**{name: int(d[name]) for name, _ in cls._fields_})
+
+    def __repr__(self):
+        return f"Config({self.as_dict()})"
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libtgemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it first (python -m tiled_dense_gemm_major_amd.build)")
+    lib = ctypes.CDLL(path)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    cfgp = ctypes.POINTER(Config)
+    lib.gemm_f16.argtypes = [i64, i64, i64, vp, vp, vp, i32, vp]
+    lib.gemm_bf16.argtypes = [i64, i64, i64, vp, vp, vp, i32, vp]
+    lib.gemm_ex.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, cfgp, vp]
+    lib.tgemm_query_config.argtypes = [i32, i64, i64, i64, i32, i32, cfgp]
+    lib.tgemm_list_configs.argtypes = [i32, i32, cfgp, i32]
+    lib.tgemm_status_string.argtypes = [i32]
+    lib.tgemm_status_string.restype = ctypes.c_char_p
+    for name in ("gemm_f16", "gemm_bf16", "gemm_ex", "tgemm_query_config",
+                 "tgemm_list_configs", "tgemm_version"):
+        getattr(lib, name).restype = i32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().tgemm_status_string(status).decode()
+
+
+def _addr(x) -> int:
+    """A device address from a torch tensor, an int, or None (NULL)."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        try:
+            import torch
+            if torch.cuda.is_available():
+                return int(torch.cuda.current_stream().cuda_stream)
+        except ImportError:
+            pass
+        return 0
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise TGemmError(rc, what)
+
+
+def gemm_f16(m, n, k, A, B, C, b_layout=B_NK, stream=None):
+    """C = A x B^T (B_NK) or A x B (B_KN), fp16.  A, B, C: device tensors or addresses."""
+    _check(load().gemm_f16(m, n, k, _addr(A), _addr(B), _addr(C), b_layout, _stream(stream)),
+           "gemm_f16")
+
+
+def gemm_bf16(m, n, k, A, B, C, b_layout=B_NK, stream=None):
+    """C = A x B^T (B_NK) or A x B (B_KN), bf16.  A, B, C: device tensors or addresses."""
+    _check(load().gemm_bf16(m, n, k, _addr(A), _addr(B), _addr(C), b_layout, _stream(stream)),
+           "gemm_bf16")
+
+
+def gemm_ex(dtype, m, n, k, A, B, C, b_layout=B_NK, config: Config | None = None,
+            stream=None):
+    """The product with an explicit dtype and, optionally, an explicit configuration."""
+    cfg = ctypes.byref(config) if config is not None else None
+    _check(load().gemm_ex(dtype, m, n, k, _addr(A), _addr(B), _addr(C), b_layout, cfg,
+                          _stream(stream)), "gemm_ex")
+
+
+def query_config(dtype, m, n, k, b_layout=B_NK, aligned=True) -> Config:
+    out = Config()
+    _check(load().tgemm_query_config(dtype, m, n, k, b_layout, int(bool(aligned)),
+                                     ctypes.byref(out)), "tgemm_query_config")
+    return out
+
+
+def list_configs(dtype, b_layout=B_NK) -> list:
+    lib = load()
+    count = lib.tgemm_list_configs(dtype, b_layout, None, 0)
+    if count < 0:
+        raise TGemmError(count, "tgemm_list_configs")
+    arr = (Config * count)()
+    lib.tgemm_list_configs(dtype, b_layout, arr, count)
+    return [arr[i] for i in range(count)]
+
+
+def version() -> int:
+    return int(load().tgemm_version())
+
+
+def gemm(A, B, C=None, b_layout=B_NK, config: Config | None = None, stream=None):
+    """Torch convenience: A [M,K], B [N,K] (B_NK) or [K,N] (B_KN), same 16-bit dtype on
+    one device; C [M,N] allocated by torch when not given.  Returns C."""
+    import torch
+    if A.dtype not in (torch.float16, torch.bfloat16) or B.dtype != A.dtype:
+        raise TypeError("A and B must share dtype float16 or bfloat16")
+    if not (A.is_contiguous() and B.is_contiguous()):
+        raise ValueError("A and B must be contiguous (packed row-major)")
+    M, K = A.shape
+    if b_layout == B_NK:
+        N, Kb = B.shape
+    else:
+        Kb, N = B.shape
+    if Kb != K:
+        raise ValueError(f"K mismatch: {K} vs {Kb}")
+    if C is None:
+        C = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    elif C.shape != (M, N) or C.dtype != A.dtype or not C.is_contiguous():
+        raise ValueError("C must be a contiguous [M,N] tensor of the input dtype")
+    dtype = F16 if A.dtype == torch.float16 else BF16
+    gemm_ex(dtype, M, N, K, A, B, C, b_layout, config, stream)
+    return C
