@@ -63,13 +63,13 @@ def cpu_baseline(A, B, w, budget_s: float):
     """The oracle (as it is) on the leading rows of C, sized to ~budget_s seconds."""
     import oracle
     cores = oracle.max_threads()
-    rows = 2
+    probe_rows = 64
     t0 = time.perf_counter()
-    oracle.gemm_rows(w.dtype, A, B, w.b_layout, 0, rows)
+    oracle.gemm_rows(w.dtype, A, B, w.b_layout, 0, probe_rows)
     t_probe = time.perf_counter() - t0
-    per_row = max(t_probe / rows, 1e-4)
-    rows = int(max(2, min(w.M, budget_s / per_row)))
-    log(f"cpu baseline: probe {t_probe:.2f}s for 2 rows; timing {rows} rows on {cores} threads")
+    rows = int(max(probe_rows, min(w.M, probe_rows * budget_s / max(t_probe, 1e-3))))
+    log(f"cpu baseline: {probe_rows} rows took {t_probe:.2f}s; timing {rows} rows on "
+        f"{cores} threads")
     t0 = time.perf_counter()
     oracle.gemm_rows(w.dtype, A, B, w.b_layout, 0, rows)
     dt = time.perf_counter() - t0

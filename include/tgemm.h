@@ -69,8 +69,10 @@ typedef enum {
     TGEMM_KERNEL_GENERIC = 0, /* any alignment and size: element loads, one LDS stage    */
     TGEMM_KERNEL_TILED = 1,   /* 128-bit loads, register prefetch, two swizzled LDS
                                  stages, MFMA 32x32x16, grouped XCD-aware tile order     */
-    TGEMM_KERNEL_SKINNY = 2   /* small M: the K range of a tile split over the waves of a
+    TGEMM_KERNEL_SKINNY = 2,  /* small M: the K range of a tile split over the waves of a
                                  workgroup and summed in LDS                              */
+    TGEMM_KERNEL_DMA = 3      /* B [N,K] only: global loads written straight into a deep
+                                 ring of swizzled LDS stages (no register staging)        */
 } tgemm_kernel;
 
 /* One tile configuration.  block_m x block_n is the C tile of one workgroup, block_k

@@ -92,7 +92,7 @@ def test_fast_config_needs_alignment(lib):
 
 def test_query_config_table(lib):
     big = tgemm.query_config(tgemm.BF16, 8192, 8192, 8192)
-    assert big.kernel == tgemm.KERNEL_TILED and big.block_m * big.block_n >= 128 * 128
+    assert big.kernel != tgemm.KERNEL_GENERIC and big.block_m * big.block_n >= 128 * 128
     odd = tgemm.query_config(tgemm.F16, 100, 100, 100, aligned=False)
     assert odd.kernel == tgemm.KERNEL_GENERIC
     listed = {tuple(sorted(c.as_dict().items())) for c in tgemm.list_configs(tgemm.BF16)}
@@ -111,7 +111,7 @@ def test_list_configs(lib):
             kinds = {c.kernel for c in cfgs}
             assert tgemm.KERNEL_GENERIC in kinds and tgemm.KERNEL_TILED in kinds
             for c in cfgs:
-                if c.kernel == tgemm.KERNEL_TILED:
+                if c.kernel != tgemm.KERNEL_GENERIC:
                     # the LDS ring must fit the 160 KiB of one compute unit
                     assert c.stages * (c.block_m + c.block_n) * c.block_k * 2 <= 160 * 1024
     assert lib.tgemm_list_configs(5, 0, None, 0) == -1

@@ -16,7 +16,7 @@ ARCH = "gfx950"
 # No packed-fp32 VALU instructions anywhere (-packed-fp32-ops): the host pass does not
 # know the feature and warns, which is harmless.
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]

@@ -15,6 +15,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace tgemm {
 
 typedef uint16_t u16;
@@ -86,15 +89,25 @@ __device__ __forceinline__ void tile_of(int wg, int grid_m, int grid_n, int grou
     tn = within / rows;
 }
 
-// LDS swizzle.  A tile row holds KC 16-byte chunks.  Chunk c of row r is stored at chunk
-// c ^ swz(r), so the 8 rows read by 8 neighbouring lanes (one 128-byte bank sweep) land
-// in 8 different 16-byte bank groups, for both the 128-bit writes and the 128-bit reads.
+// LDS swizzle.  A tile row holds KC 16-byte chunks.  The LDS serves a 128-bit access 16
+// lanes at a time from a 256-byte window of banks, and neighbouring lanes read or write
+// neighbouring tile rows at the same logical chunk.  Chunk c of row r is stored at chunk
+// c ^ swz(r), where swz changes every R = 16/KC rows (the rows sharing one 256-byte
+// window), so the 16 rows touched by 16 neighbouring lanes land in 16 different 16-byte
+// bank groups: conflict-free 128-bit writes (row-major loads) and fragment reads.
 template <int KC>
 __device__ __forceinline__ int swz(int row) {
-    if constexpr (KC >= 8)
-        return row & 7;
-    else
-        return (row / (8 / KC)) & (KC - 1);
+    constexpr int R = KC >= 16 ? 1 : 16 / KC;
+    return (row / R) & (KC - 1);
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
 }
 
 __device__ __forceinline__ void block_sync_lds() {
@@ -127,13 +140,23 @@ __device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t voff, uint32_t soff) 
 //   Template: DT (fp16/bf16), LAYOUT (B as [N,K] or [K,N]), BM x BN x BK tile, WM x WN
 //   waves (each owns a (BM/WM) x (BN/WN) block of the tile, in 32 x 32 MFMA blocks).
 //   Host-checked requirements: K % 8 == 0, N % 8 == 0, 16-byte aligned A, B, C, and
-//   A and B each at most 2^31 bytes (so an offset with the top bit set is out of range).
-//   Edges: rows of A past M and of B past N read as zero through the buffer range check
-//   (their results fall outside C and are not stored anyway); chunks with k >= K get an
-//   out-of-range offset and read as zero; stores outside [M,N] are skipped.
-// Pipeline: two LDS stages plus one register stage.  While the MFMAs run on the tile in
-// stage t%2, tile t+1 (already in registers) is written to the other stage and the
-// global loads of tile t+2 are issued, so every global load has a whole step to arrive.
+//   A and B each at most 2^31 bytes.
+//   Edges: a load that must not happen (a row of A past M, of B past N, a chunk with
+//   k >= K, a tile past the last) gets the offset kOutOfRange, which the buffer range
+//   check turns into zeros without a memory access; stores outside [M,N] are skipped.
+//
+// Pipeline (two LDS stages, one register stage, double-buffered MFMA operands).  Step t
+// computes tile t from LDS stage t%2 in KS k-substeps of 16.  Alongside its MFMAs:
+//   substep 0      : tile t+1 (A part) from registers to the other stage, then the
+//                    global loads of tile t+2 (A part) into the freed registers;
+//   substep 1      : the same for the B part;
+// so every global load has a whole step to arrive; and in every substep the operands of
+// the next substep are read from LDS.  The one
+// barrier per step sits before the last substep: by then every wave has written tile
+// t+1 and has read its last operands of tile t, so the last substep can read the first
+// operands of tile t+1 while its MFMAs run, and the next step begins with them in hand.
+// Steps past the last tile run with out-of-range loads (zeros), so the loop body has
+// no branches.
 // ------------------------------------------------------------------------------------
 template <int DT, int LAYOUT, int BM, int BN, int BK, int WM, int WN>
 __global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64),
@@ -144,19 +167,18 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
     constexpr int KC = BK / 8;              // 16-byte chunks in one tile row
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
-    constexpr int KS = BK / 16;             // MFMA k-steps per tile
+    constexpr int KS = BK / 16;             // MFMA k-substeps per tile
     constexpr int A_ELEMS = BM * BK;
     constexpr int STAGE = (BM + BN) * BK;   // elements of one LDS stage (A then B)
     constexpr int RS = NT / KC;             // rows between the chunks one thread loads
     constexpr int A_LD = BM / RS;           // A chunks per thread
-    constexpr int B_LD = (LAYOUT == LAYOUT_NK) ? BN / RS : 1;
-    // [K,N] B: a thread loads 8x8 blocks (8 k-rows of 8 n); KN_BLK blocks per tile.
-    constexpr int KN_BLK = KC * (BN / 8);
-    constexpr int KN_LD = (KN_BLK + NT - 1) / NT;
-    constexpr int B_REGS = (LAYOUT == LAYOUT_NK) ? B_LD : 8 * KN_LD;
+    constexpr int B_LD = (LAYOUT == LAYOUT_NK) ? BN / RS : 8;
+    constexpr int KN_BLK = KC * (BN / 8);   // [K,N] B: 8x8 blocks per tile (one per thread)
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(BK % 16 == 0 && NT % KC == 0 && RS % 8 == 0, "bad BK");
+    static_assert(BK % 32 == 0 && NT % KC == 0, "BK must give an even number of substeps");
+    static_assert((NT / 16) % KC == 0, "a thread's rows must share one swizzle");
     static_assert(BM % RS == 0 && (LAYOUT == LAYOUT_KN || BN % RS == 0), "bad load split");
+    static_assert(LAYOUT == LAYOUT_NK || KN_BLK <= NT, "one 8x8 [K,N] block per thread");
 
     __shared__ __attribute__((aligned(16))) u16 lds[2 * STAGE];
 
@@ -165,26 +187,26 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
     const int m0 = tm * BM, n0 = tn * BN;
     const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
+    const int nk = (K + BK - 1) / BK;
 
     const rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
     const rsrc_t rb = make_rsrc(B, (uint32_t)N * (uint32_t)K * 2u);
 
-    // ---- global -> register addressing (byte offsets; K position goes in soffset) ----
+    // ---- global -> register addressing (byte offsets; the K position goes in soffset) --
     const int lc = tid % KC;                 // this thread's chunk column (row-major loads)
     const int lr = tid / KC;                 // its first row; the others follow every RS
-    // Every offset that must not be read carries kOutOfRange, OR-ed in after all
-    // additions, so the range check rejects it whatever the SGPR offset adds.
     uint32_t a_off[A_LD];
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
         const int r = m0 + lr + i * RS;
         a_off[i] = r < M ? (uint32_t)(r * K + lc * 8) * 2u : kOutOfRange;
     }
-    // The LDS slot of chunk (row, lc): rows lr + i*RS share one swizzle (RS % 8 == 0).
     const int a_lds = lr * BK + ((lc ^ swz<KC>(lr)) * 8);
 
-    uint32_t b_off[LAYOUT == LAYOUT_NK ? B_LD : KN_LD];
-    int b_lds = 0, kn_kb = 0, kn_nb = 0;
+    uint32_t b_off[LAYOUT == LAYOUT_NK ? B_LD : 1];
+    int b_lds;
+    const int kn_kb = tid % KC, kn_nb = tid / KC;
+    bool kn_live = true;
     if constexpr (LAYOUT == LAYOUT_NK) {
 #pragma unroll
         for (int i = 0; i < B_LD; ++i) {
@@ -193,71 +215,86 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
         }
         b_lds = A_ELEMS + lr * BK + ((lc ^ swz<KC>(lr)) * 8);
     } else {
-        static_assert(LAYOUT == LAYOUT_NK || KN_LD == 1, "one 8x8 block per thread");
-        kn_kb = tid % KC;
-        kn_nb = tid / KC;
-        // Offset of row k = 8*kb (the K position goes in soffset); only meaningful for
-        // a live block whose 8 columns are inside [0, N) (N % 8 == 0).
+        // Thread tid loads the 8x8 block (k = 8*kn_kb .. +7, n = n0 + 8*kn_nb .. +7);
+        // its 8 columns lie inside [0, N) or outside it together (N % 8 == 0).
+        kn_live = (tid < KN_BLK) && (n0 + kn_nb * 8 < N);
         b_off[0] = ((uint32_t)(kn_kb * 8) * (uint32_t)N + (uint32_t)(n0 + kn_nb * 8)) * 2u;
         b_lds = A_ELEMS + (kn_nb * 8) * BK;
     }
-    const bool kn_live = ((KN_BLK % NT == 0) || (tid < KN_BLK)) && (n0 + kn_nb * 8 < N);
 
     u32x4 a_reg[A_LD];
-    u32x4 b_reg[B_REGS];
+    u32x4 b_reg[B_LD];
 
-    auto gload = [&](int kt) {
-        const int k0 = kt * BK;
-        const uint32_t kbad = (k0 + lc * 8 < K) ? 0u : kOutOfRange;
+    auto gload_a = [&](int kt) {
+        const bool live = kt < nk;
+        const int k0 = live ? kt * BK : 0;
+        const bool ok = live && (k0 + lc * 8 < K);
 #pragma unroll
         for (int i = 0; i < A_LD; ++i)
-            a_reg[i] = load16(ra, a_off[i] | kbad, (uint32_t)k0 * 2u);
+            a_reg[i] = load16(ra, ok ? a_off[i] : kOutOfRange, (uint32_t)k0 * 2u);
+    };
+    // One part of the B loads of tile kt: chunk i (NK) or k-row i of the 8x8 block (KN).
+    auto gload_b_part = [&](int kt, auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const bool live = kt < nk;
+        const int k0 = live ? kt * BK : 0;
         if constexpr (LAYOUT == LAYOUT_NK) {
-#pragma unroll
-            for (int i = 0; i < B_LD; ++i)
-                b_reg[i] = load16(rb, b_off[i] | kbad, (uint32_t)k0 * 2u);
+            const bool ok = live && (k0 + lc * 8 < K);
+            b_reg[i] = load16(rb, ok ? b_off[i] : kOutOfRange, (uint32_t)k0 * 2u);
         } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const bool ok = kn_live && (k0 + kn_kb * 8 + j < K);
-                b_reg[j] = load16(rb, (b_off[0] + (uint32_t)j * (uint32_t)N * 2u) | (ok ? 0u : kOutOfRange),
-                                  (uint32_t)k0 * (uint32_t)N * 2u);
-            }
+            const bool ok = live && kn_live && (k0 + kn_kb * 8 + i < K);
+            b_reg[i] = load16(rb, ok ? b_off[0] + (uint32_t)i * (uint32_t)N * 2u : kOutOfRange,
+                              (uint32_t)k0 * (uint32_t)N * 2u);
         }
     };
-
-    auto swrite = [&](u16* st) {
+    auto gload_b = [&](int kt) {
+        static_for<0, B_LD>([&](auto i) { gload_b_part(kt, i); });
+    };
+    auto swrite_a = [&](u16* st) {
 #pragma unroll
         for (int i = 0; i < A_LD; ++i)
             *reinterpret_cast<u32x4*>(st + a_lds + i * RS * BK) = a_reg[i];
+    };
+    // One part of the B tile's LDS write: chunk i (NK), or row n = i of the transposed
+    // 8x8 block (KN: b_reg[j] holds n = 0..7 at k = j; row n receives k = 0..7).
+    auto swrite_b_part = [&](u16* st, auto ic) {
+        constexpr int i = decltype(ic)::value;
         if constexpr (LAYOUT == LAYOUT_NK) {
-#pragma unroll
-            for (int i = 0; i < B_LD; ++i)
-                *reinterpret_cast<u32x4*>(st + b_lds + i * RS * BK) = b_reg[i];
+            *reinterpret_cast<u32x4*>(st + b_lds + i * RS * BK) = b_reg[i];
         } else {
-            {
-                // 8x8 transpose (a dead block holds zeros and lands in rows never stored): b_reg[j] holds n = 0..7 at k = j; row n gets k = 0..7.
-#pragma unroll
-                for (int n = 0; n < 8; ++n) {
-                    const int p = n >> 1;
-                    const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
-                    u32x4 o;
-                    o[0] = __builtin_amdgcn_perm(b_reg[1][p], b_reg[0][p], sel);
-                    o[1] = __builtin_amdgcn_perm(b_reg[3][p], b_reg[2][p], sel);
-                    o[2] = __builtin_amdgcn_perm(b_reg[5][p], b_reg[4][p], sel);
-                    o[3] = __builtin_amdgcn_perm(b_reg[7][p], b_reg[6][p], sel);
-                    *reinterpret_cast<u32x4*>(st + b_lds + n * BK +
-                                              ((kn_kb ^ swz<KC>(kn_nb * 8 + n)) * 8)) = o;
-                }
+            if (tid < KN_BLK) {
+                constexpr int p = i >> 1;
+                constexpr uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+                u32x4 o;
+                o[0] = __builtin_amdgcn_perm(b_reg[1][p], b_reg[0][p], sel);
+                o[1] = __builtin_amdgcn_perm(b_reg[3][p], b_reg[2][p], sel);
+                o[2] = __builtin_amdgcn_perm(b_reg[5][p], b_reg[4][p], sel);
+                o[3] = __builtin_amdgcn_perm(b_reg[7][p], b_reg[6][p], sel);
+                *reinterpret_cast<u32x4*>(st + b_lds + i * BK +
+                                          ((kn_kb ^ swz<KC>(kn_nb * 8 + i)) * 8)) = o;
             }
         }
     };
+    auto swrite_b = [&](u16* st) {
+        static_for<0, B_LD>([&](auto i) { swrite_b_part(st, i); });
+    };
 
     // ---- LDS -> MFMA operands ---------------------------------------------------------
-    const int xr = swz<KC>(lane & 31);       // swizzle of this lane's rows (bases are x8)
+    const int xr = swz<KC>(lane & 31);       // swizzle of this lane's rows (bases are x32)
     const int half = lane >> 5;               // which 8 of the 16 k of an MFMA step
     const int a_row0 = (wm * WTM + (lane & 31)) * BK;
     const int b_row0 = A_ELEMS + (wn * WTN + (lane & 31)) * BK;
+
+    u32x4 fa[2][TM], fb[2][TN];
+    auto read_frag = [&](const u16* st, int s, int buf, auto idx) {
+        constexpr int I = decltype(idx)::value;
+        const int koff = (((2 * s) | half) ^ xr) * 8;
+        if constexpr (I < TM)
+            fa[buf][I] = *reinterpret_cast<const u32x4*>(st + a_row0 + I * 32 * BK + koff);
+        else
+            fb[buf][I - TM] =
+                *reinterpret_cast<const u32x4*>(st + b_row0 + (I - TM) * 32 * BK + koff);
+    };
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -266,48 +303,257 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
         for (int j = 0; j < TN; ++j)
             acc[i][j] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
-    auto compute = [&](const u16* st) {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const int koff = (((2 * s) | half) ^ xr) * 8;
-            u32x4 af[TM], bf[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const u32x4*>(st + a_row0 + i * 32 * BK + koff);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                bf[j] = *reinterpret_cast<const u32x4*>(st + b_row0 + j * 32 * BK + koff);
-            // S0 = B rows (n), S1 = A rows (m): lane l then holds C row m = l % 32 and
-            // four consecutive columns n per group of four results.
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = mfma_32x32x16<DT>(bf[j], af[i], acc[i][j]);
-        }
-    };
-
-    const int nk = (K + BK - 1) / BK;
     if (nk > 0) {
-        gload(0);
-        swrite(lds);
-        if (nk > 1)
-            gload(1);
+        gload_a(0);
+        gload_b(0);
+        swrite_a(lds);
+        swrite_b(lds);
+        gload_a(1);
+        gload_b(1);
         block_sync_lds();
+        static_for<0, TM + TN>([&](auto i) { read_frag(lds, 0, 0, i); });
+
+        // Memory operations of substep S, in issue order: the TM + TN operand reads of
+        // the next substep, then (substep 0) the A part of tile t+1 to LDS and the A
+        // loads of tile t+2, then (substep WB) the same for B.  They are dealt out over
+        // the substep's TM*TN MFMA slots, front-loaded, one MFMA per slot.
+        constexpr int WB = KS > 2 ? 1 : 0;
+        constexpr int NR = TM + TN;
         for (int kt = 0; kt < nk; ++kt) {
             u16* cur = lds + (kt & 1) * STAGE;
             u16* nxt = lds + ((kt & 1) ^ 1) * STAGE;
-            compute(cur);
-            if (kt + 1 < nk) {
-                swrite(nxt);
-                if (kt + 2 < nk)
-                    gload(kt + 2);
-            }
-            block_sync_lds();
+            const int kt2 = kt + 2;
+            static_for<0, KS>([&](auto sc) {
+                constexpr int S = decltype(sc)::value;
+                constexpr int NWA = (S == 0) ? A_LD : 0;
+                constexpr int NWB = (S == WB) ? B_LD : 0;
+                constexpr int NOPS = NR + 2 * NWA + 2 * NWB;
+                constexpr int SLOTS = TM * TN;
+                auto mem_op = [&](auto oc) {
+                    constexpr int O = decltype(oc)::value;
+                    if constexpr (O < NR) {
+                        if constexpr (S + 1 < KS)
+                            read_frag(cur, S + 1, (S + 1) & 1, std::integral_constant<int, O>{});
+                        else
+                            read_frag(nxt, 0, 0, std::integral_constant<int, O>{});
+                    } else if constexpr (O < NR + NWA) {
+                        constexpr int i = O - NR;
+                        *reinterpret_cast<u32x4*>(nxt + a_lds + i * RS * BK) = a_reg[i];
+                    } else if constexpr (O < NR + 2 * NWA) {
+                        constexpr int i = O - NR - NWA;
+                        const bool live = kt2 < nk;
+                        const int k0 = live ? kt2 * BK : 0;
+                        const bool ok = live && (k0 + lc * 8 < K);
+                        a_reg[i] = load16(ra, ok ? a_off[i] : kOutOfRange, (uint32_t)k0 * 2u);
+                    } else if constexpr (O < NR + 2 * NWA + NWB) {
+                        constexpr int i = O - NR - 2 * NWA;
+                        swrite_b_part(nxt, std::integral_constant<int, i>{});
+                    } else {
+                        constexpr int i = O - NR - 2 * NWA - NWB;
+                        gload_b_part(kt2, std::integral_constant<int, i>{});
+                    }
+                };
+                static_for<0, SLOTS>([&](auto jc) {
+                    constexpr int J = decltype(jc)::value;
+                    constexpr int i = J / TN, j = J % TN;
+                    // S0 = B rows (n), S1 = A rows (m): lane l then holds C row m = l % 32
+                    // and four consecutive columns n per group of four results.
+                    acc[i][j] = mfma_32x32x16<DT>(fb[S & 1][j], fa[S & 1][i], acc[i][j]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (S == KS - 1 && J == 0) {
+                        block_sync_lds();
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    constexpr int lo = (J * NOPS + SLOTS - 1) / SLOTS;
+                    constexpr int hi = ((J + 1) * NOPS + SLOTS - 1) / SLOTS;
+                    static_for<lo, hi>([&](auto oc) {
+                        mem_op(oc);
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                });
+            });
         }
     }
 
     // ---- epilogue: cast once, store 4 consecutive columns (8 bytes) per group ----------
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int m = m0 + wm * WTM + i * 32 + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * half;
+                u32x2 v;
+                v[0] = pack2<DT>(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+                v[1] = pack2<DT>(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                if (m < M && n < N)
+                    *reinterpret_cast<u32x2*>(C + (size_t)m * N + n) = v;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Direct-to-LDS kernel (B as [N,K] only).
+//   The global loads write LDS themselves (buffer_load_dwordx4 ... lds): one instruction
+//   moves 64 lanes x 16 bytes into 1 KiB of consecutive LDS bytes starting at an address
+//   held in M0, lane l filling bytes [16l, 16l+16).  No register staging and no LDS-write
+//   instructions, so the tile ring can be deep: STAGES buffers of BK = 32 (two MFMA
+//   k-substeps each), the loads of tile t+STAGES-1 issued while tile t is computed.
+//   Swizzle: a 1 KiB block holds R = 64/KC consecutive tile rows; lane l lands in row
+//   l / KC at physical chunk l % KC, so it loads the logical chunk (l % KC) ^ swz(row)
+//   -- the same placement the fragment reads expect.
+//   Requirements as for gemm_tiled.  A chunk past K or a row past M/N is read out of
+//   range, which the hardware turns into zeros written to LDS.
+// Per step t (compute tile t from stage t % STAGES):
+//   substep 0: MFMAs; read the operands of substep 1; issue tile t+STAGES-1's loads into
+//              the stage tile t-1 used (free since the previous step's barrier);
+//   substep 1: one MFMA; wait until this wave's loads of tile t+1 have landed and meet the
+//              other waves (tile t+1 complete, tile t no longer read); the remaining
+//              MFMAs with the reads of tile t+1's first operands.
+// ------------------------------------------------------------------------------------
+template <int STAGE_BYTES>
+__device__ __forceinline__ void dma16(rsrc_t r, u16* lds_dst, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, soff, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_then_sync() {
+    // This wave's global->LDS loads down to N outstanding, its LDS traffic drained, then
+    // the workgroup barrier.
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int DT, int BM, int BN, int BK, int WM, int WN, int STAGES>
+__global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64),
+                               amdgpu_waves_per_eu(1, 1)))
+gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
+         int N, int K, int grid_m, int grid_n, int group_m) {
+    constexpr int NW = WM * WN;
+    constexpr int KC = BK / 8;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int KS = BK / 16;
+    constexpr int A_ELEMS = BM * BK;
+    constexpr int STAGE = (BM + BN) * BK;
+    constexpr int ROWS = 64 / KC;                 // tile rows per 1 KiB load
+    constexpr int A_LD = BM / ROWS / NW;          // A loads per wave per tile
+    constexpr int B_LD = BN / ROWS / NW;
+    constexpr int LD = A_LD + B_LD;
+    static_assert(KS == 2, "two k-substeps per tile");
+    static_assert((BM / ROWS) % NW == 0 && (BN / ROWS) % NW == 0, "bad load split");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(STAGES >= 3 && LD * (STAGES - 2) <= 63, "vmcnt range");
+    static_assert(STAGES * STAGE * 2 <= 160 * 1024, "LDS");
+
+    __shared__ __attribute__((aligned(1024))) u16 lds[STAGES * STAGE];
+
+    int tm, tn;
+    tile_of((int)blockIdx.x, grid_m, grid_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int nk = (K + BK - 1) / BK;
+
+    const rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
+    const rsrc_t rb = make_rsrc(B, (uint32_t)N * (uint32_t)K * 2u);
+
+    // This lane's row inside a 1 KiB block and the logical chunk it fetches.
+    const int prow = lane / KC;
+    const int lch = (lane % KC) ^ swz<KC>(prow);
+    uint32_t a_off[A_LD], b_off[B_LD];
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+        const int r = m0 + (wave * A_LD + i) * ROWS + prow;
+        a_off[i] = r < M ? (uint32_t)(r * K + lch * 8) * 2u : kOutOfRange;
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+        const int r = n0 + (wave * B_LD + i) * ROWS + prow;
+        b_off[i] = r < N ? (uint32_t)(r * K + lch * 8) * 2u : kOutOfRange;
+    }
+    auto stage_ptr = [&](int t) { return lds + (t % STAGES) * STAGE; };
+    // Load i (< LD) of tile kt into its stage.
+    auto dma = [&](int kt, auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const bool live = kt < nk;
+        const int k0 = live ? kt * BK : 0;
+        const bool ok = live && (k0 + lch * 8 < K);
+        u16* st = stage_ptr(kt);
+        if constexpr (i < A_LD)
+            dma16<0>(ra, st + (wave * A_LD + i) * ROWS * BK, ok ? a_off[i] : kOutOfRange,
+                     (uint32_t)k0 * 2u);
+        else
+            dma16<0>(rb, st + A_ELEMS + (wave * B_LD + (i - A_LD)) * ROWS * BK,
+                     ok ? b_off[i - A_LD] : kOutOfRange, (uint32_t)k0 * 2u);
+    };
+
+    const int xr = swz<KC>(lane & 31);
+    const int half = lane >> 5;
+    const int a_row0 = (wm * WTM + (lane & 31)) * BK;
+    const int b_row0 = A_ELEMS + (wn * WTN + (lane & 31)) * BK;
+    u32x4 fa[2][TM], fb[2][TN];
+    auto read_frag = [&](const u16* st, int s, int buf, auto idx) {
+        constexpr int I = decltype(idx)::value;
+        const int koff = (((2 * s) | half) ^ xr) * 8;
+        if constexpr (I < TM)
+            fa[buf][I] = *reinterpret_cast<const u32x4*>(st + a_row0 + I * 32 * BK + koff);
+        else
+            fb[buf][I - TM] =
+                *reinterpret_cast<const u32x4*>(st + b_row0 + (I - TM) * 32 * BK + koff);
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+
+    if (nk > 0) {
+        for (int p = 0; p < STAGES - 1; ++p)
+            static_for<0, LD>([&](auto i) { dma(p, i); });
+        wait_vm_then_sync<LD * (STAGES - 2)>();
+        static_for<0, TM + TN>([&](auto i) { read_frag(lds, 0, 0, i); });
+        constexpr int NR = TM + TN;
+        constexpr int SLOTS = TM * TN;
+        for (int kt = 0; kt < nk; ++kt) {
+            const u16* cur = stage_ptr(kt);
+            const u16* nxt = stage_ptr(kt + 1);
+            const int kl = kt + STAGES - 1;
+            static_for<0, KS>([&](auto sc) {
+                constexpr int S = decltype(sc)::value;
+                constexpr int NOPS = NR + (S == 0 ? LD : 0);
+                static_for<0, SLOTS>([&](auto jc) {
+                    constexpr int J = decltype(jc)::value;
+                    constexpr int i = J / TN, j = J % TN;
+                    acc[i][j] = mfma_32x32x16<DT>(fb[S][j], fa[S][i], acc[i][j]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (S == 1 && J == 0) {
+                        wait_vm_then_sync<LD * (STAGES - 2)>();
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    constexpr int lo = (J * NOPS + SLOTS - 1) / SLOTS;
+                    constexpr int hi = ((J + 1) * NOPS + SLOTS - 1) / SLOTS;
+                    static_for<lo, hi>([&](auto oc) {
+                        constexpr int O = decltype(oc)::value;
+                        if constexpr (O < NR) {
+                            if constexpr (S == 0)
+                                read_frag(cur, 1, 1, std::integral_constant<int, O>{});
+                            else
+                                read_frag(nxt, 0, 0, std::integral_constant<int, O>{});
+                        } else {
+                            dma(kl, std::integral_constant<int, O - NR>{});
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                });
+            });
+        }
+    }
+
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int m = m0 + wm * WTM + i * 32 + (lane & 31);

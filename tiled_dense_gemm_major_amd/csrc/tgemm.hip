@@ -39,6 +39,17 @@ hipError_t launch_tiled(const void* A, const void* B, void* C, int M, int N, int
     return hipGetLastError();
 }
 
+template <int DT, int BM, int BN, int BK, int WM, int WN, int STAGES>
+hipError_t launch_dma(const void* A, const void* B, void* C, int M, int N, int K, int group_m,
+                      hipStream_t s) {
+    const int gm = cdiv(M, BM), gn = cdiv(N, BN);
+    hipLaunchKernelGGL((tgemm::gemm_dma<DT, BM, BN, BK, WM, WN, STAGES>),
+                       dim3((unsigned)(gm * gn)), dim3(WM * WN * 64), 0, s,
+                       static_cast<const u16*>(A), static_cast<const u16*>(B),
+                       static_cast<u16*>(C), M, N, K, gm, gn, group_m);
+    return hipGetLastError();
+}
+
 template <int DT, int LAYOUT>
 hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, int K,
                           int group_m, hipStream_t s) {
@@ -59,11 +70,20 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
         DT, L, tgemm_config{TGEMM_KERNEL_GENERIC, 64, 64, 16, 2, 2, 1, 8, 1},              \
             &launch_generic<DT, L>                                                         \
     }
+#define DMA(DT, BM, BN, BK, WM, WN, ST, G)                                                 \
+    Variant {                                                                              \
+        DT, 0, tgemm_config{TGEMM_KERNEL_DMA, BM, BN, BK, WM, WN, ST, G, 1},               \
+            &launch_dma<DT, BM, BN, BK, WM, WN, ST>                                        \
+    }
+#define ALL_DMA(DT)                                                                        \
+    DMA(DT, 256, 256, 32, 2, 2, 4, 4), DMA(DT, 256, 256, 32, 2, 2, 5, 4)
 #define ALL_SHAPES(DT, L)                                                                  \
     GENERIC(DT, L), TILED(DT, L, 256, 256, 64, 2, 2, 4), TILED(DT, L, 128, 128, 64, 2, 2, 8), \
         TILED(DT, L, 64, 64, 64, 2, 2, 8)
 
 const Variant kVariants[] = {
+    ALL_DMA(0),
+    ALL_DMA(1),
     ALL_SHAPES(0, 0),
     ALL_SHAPES(0, 1),
     ALL_SHAPES(1, 0),
