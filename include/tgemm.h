@@ -71,8 +71,10 @@ typedef enum {
                                  stages, MFMA 32x32x16, grouped XCD-aware tile order     */
     TGEMM_KERNEL_SKINNY = 2,  /* small M: the K range of a tile split over the waves of a
                                  workgroup and summed in LDS                              */
-    TGEMM_KERNEL_DMA = 3      /* B [N,K] only: global loads written straight into a deep
+    TGEMM_KERNEL_DMA = 3,     /* B [N,K] only: global loads written straight into a deep
                                  ring of swizzled LDS stages (no register staging)        */
+    TGEMM_KERNEL_PINGPONG = 4 /* B [N,K] only: 8 waves, two per SIMD, alternating between
+                                 operand fetch and back-to-back MFMAs half a period apart */
 } tgemm_kernel;
 
 /* One tile configuration.  block_m x block_n is the C tile of one workgroup, block_k

@@ -8,7 +8,8 @@ from __future__ import annotations
 
 _BINDING = ("gemm_f16", "gemm_bf16", "gemm_ex", "gemm", "query_config", "list_configs",
             "status_string", "version", "Config", "TGemmError", "F16", "BF16", "B_NK",
-            "B_KN", "KERNEL_GENERIC", "KERNEL_TILED", "KERNEL_SKINNY", "KERNEL_DMA")
+            "B_KN", "KERNEL_GENERIC", "KERNEL_TILED", "KERNEL_SKINNY", "KERNEL_DMA",
+            "KERNEL_PINGPONG")
 
 
 def __getattr__(name):

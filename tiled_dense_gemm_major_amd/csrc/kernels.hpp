@@ -401,9 +401,9 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
 //   held in M0, lane l filling bytes [16l, 16l+16).  No register staging and no LDS-write
 //   instructions, so the tile ring can be deep: STAGES buffers of BK = 32 (two MFMA
 //   k-substeps each), the loads of tile t+STAGES-1 issued while tile t is computed.
-//   Swizzle: a 1 KiB block holds R = 64/KC consecutive tile rows; lane l lands in row
-//   l / KC at physical chunk l % KC, so it loads the logical chunk (l % KC) ^ swz(row)
-//   -- the same placement the fragment reads expect.
+//   Swizzle: a 1 KiB block holds 64/KC consecutive tile rows; lane l lands in row
+//   l / KC of the block at physical chunk l % KC, so it loads the logical chunk
+//   (l % KC) ^ swz(row) of that row -- the placement the fragment reads expect.
 //   Requirements as for gemm_tiled.  A chunk past K or a row past M/N is read out of
 //   range, which the hardware turns into zeros written to LDS.
 // Per step t (compute tile t from stage t % STAGES):
@@ -460,19 +460,22 @@ gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__
     const rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
     const rsrc_t rb = make_rsrc(B, (uint32_t)N * (uint32_t)K * 2u);
 
-    // This lane's row inside a 1 KiB block and the logical chunk it fetches.
+    // Lane l lands in row l / KC of a 1 KiB block at physical chunk l % KC; it fetches
+    // the logical chunk that the swizzle of that row (block base + l / KC) puts there.
     const int prow = lane / KC;
-    const int lch = (lane % KC) ^ swz<KC>(prow);
     uint32_t a_off[A_LD], b_off[B_LD];
+    int a_kc[A_LD], b_kc[B_LD];
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
-        const int r = m0 + (wave * A_LD + i) * ROWS + prow;
-        a_off[i] = r < M ? (uint32_t)(r * K + lch * 8) * 2u : kOutOfRange;
+        const int row = (wave * A_LD + i) * ROWS + prow;
+        a_kc[i] = ((lane % KC) ^ swz<KC>(row)) * 8;
+        a_off[i] = m0 + row < M ? (uint32_t)((m0 + row) * K + a_kc[i]) * 2u : kOutOfRange;
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-        const int r = n0 + (wave * B_LD + i) * ROWS + prow;
-        b_off[i] = r < N ? (uint32_t)(r * K + lch * 8) * 2u : kOutOfRange;
+        const int row = (wave * B_LD + i) * ROWS + prow;
+        b_kc[i] = ((lane % KC) ^ swz<KC>(row)) * 8;
+        b_off[i] = n0 + row < N ? (uint32_t)((n0 + row) * K + b_kc[i]) * 2u : kOutOfRange;
     }
     auto stage_ptr = [&](int t) { return lds + (t % STAGES) * STAGE; };
     // Load i (< LD) of tile kt into its stage.
@@ -480,14 +483,14 @@ gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__
         constexpr int i = decltype(ic)::value;
         const bool live = kt < nk;
         const int k0 = live ? kt * BK : 0;
-        const bool ok = live && (k0 + lch * 8 < K);
         u16* st = stage_ptr(kt);
         if constexpr (i < A_LD)
-            dma16<0>(ra, st + (wave * A_LD + i) * ROWS * BK, ok ? a_off[i] : kOutOfRange,
-                     (uint32_t)k0 * 2u);
+            dma16<0>(ra, st + (wave * A_LD + i) * ROWS * BK,
+                     live && k0 + a_kc[i] < K ? a_off[i] : kOutOfRange, (uint32_t)k0 * 2u);
         else
             dma16<0>(rb, st + A_ELEMS + (wave * B_LD + (i - A_LD)) * ROWS * BK,
-                     ok ? b_off[i - A_LD] : kOutOfRange, (uint32_t)k0 * 2u);
+                     live && k0 + b_kc[i - A_LD] < K ? b_off[i - A_LD] : kOutOfRange,
+                     (uint32_t)k0 * 2u);
     };
 
     const int xr = swz<KC>(lane & 31);
@@ -562,6 +565,189 @@ gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * half;
+                u32x2 v;
+                v[0] = pack2<DT>(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+                v[1] = pack2<DT>(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                if (m < M && n < N)
+                    *reinterpret_cast<u32x2*>(C + (size_t)m * N + n) = v;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Ping-pong kernel (B as [N,K] only).
+//   8 waves, two per SIMD, in two groups: group 0 (waves 0-3) owns C rows [0, BM/2) of the
+//   tile, group 1 (waves 4-7) rows [BM/2, BM); inside a group wave c owns a BN/4-wide
+//   column block, so each wave holds a (BM/2) x (BN/4) block of accumulators.  Waves w
+//   and w+4 share a SIMD.  Each wave alternates a memory phase (read all MFMA operands of
+//   one K step from LDS; issue direct-to-LDS loads) and a compute phase (the K step's
+//   MFMAs back to back, at raised issue priority), and the two groups run half a period
+//   apart, so on every SIMD one wave feeds the matrix core while the other fetches.
+//   Phases end at workgroup barriers:
+//     phase 2t   : group 0 reads tile t,   group 1 computes tile t-1
+//     phase 2t+1 : group 0 computes tile t, group 1 reads tile t
+//   Tiles alternate between two LDS stages.  A rows [0, BM/2) of a tile are read only by
+//   group 0 (in phase 2t), so they are free one phase earlier than the rest: group 1
+//   loads them for tile t+2 in its memory phase 2t+1; group 0 loads A rows [BM/2, BM)
+//   and B of tile t+2 in its memory phase 2t+2.  No loads are issued in compute phases.
+//   Tile t+2 must have landed by the end of phase 2t+3, where every wave waits for its
+//   own loads of it before the barrier.
+// ------------------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm_sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int DT, int BM, int BN, int BK>
+__global__ void __attribute__((amdgpu_flat_work_group_size(512, 512),
+                               amdgpu_waves_per_eu(2, 2)))
+gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
+              int N, int K, int grid_m, int grid_n, int group_m) {
+    constexpr int KC = BK / 8;
+    constexpr int WTM = BM / 2, WTN = BN / 4;     // one wave's block of C
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int KS = BK / 16;
+    constexpr int A_ELEMS = BM * BK;
+    constexpr int STAGE = (BM + BN) * BK;
+    constexpr int ROWS = 64 / KC;                  // tile rows per 1 KiB load
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave block must be whole 32x32 tiles");
+    static_assert((BM / 8) % ROWS == 0 && (BN / 4) % ROWS == 0, "bad load split");
+    static_assert(2 * STAGE * 2 <= 160 * 1024, "LDS");
+
+    __shared__ __attribute__((aligned(1024))) u16 lds[2 * STAGE];
+
+    int tm, tn;
+    tile_of((int)blockIdx.x, grid_m, grid_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = (int)threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, wc = wave & 3;
+    const int nk = (K + BK - 1) / BK;
+
+    const rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
+    const rsrc_t rb = make_rsrc(B, (uint32_t)N * (uint32_t)K * 2u);
+
+    // The rows this wave loads: group 1 wave c the A rows [c*BM/8, (c+1)*BM/8); group 0
+    // wave c the A rows [BM/2 + c*BM/8, ...) and the B rows [c*BN/4, (c+1)*BN/4).  They
+    // come in 1 KiB blocks of ROWS consecutive rows; lane l lands in row l / KC of a
+    // block at physical chunk l % KC and fetches the logical chunk the swizzle puts there,
+    // which (blocks start at multiples of ROWS) depends only on the block's parity.
+    constexpr int A_BLK = (BM / 8) / ROWS;         // A blocks per wave
+    constexpr int B_BLK = (BN / 4) / ROWS;         // B blocks per group-0 wave
+    static_assert(KC == 8 && ROWS == 8, "block parity swizzle assumes 8 chunks per row");
+    const int prow = lane / KC;
+    const int a_row = (grp ? 0 : BM / 2) + wc * (BM / 8);   // first A row of this wave
+    const int b_row = wc * (BN / 4);                          // first B row (group 0)
+    const int kc_even = ((lane % KC) ^ swz<KC>(prow)) * 8;
+    const int kc_odd = ((lane % KC) ^ swz<KC>(ROWS + prow)) * 8;
+    auto dma_tile = [&](int kt) {
+        const bool live = kt < nk;
+        const int k0 = live ? kt * BK : 0;
+        u16* st = lds + (kt & 1) * STAGE;
+        static_for<0, A_BLK>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            const int kc = (i & 1) ? kc_odd : kc_even;
+            const int r = m0 + a_row + i * ROWS + prow;
+            const bool ok = live && r < M && k0 + kc < K;
+            dma16<0>(ra, st + (a_row + i * ROWS) * BK,
+                     ok ? (uint32_t)(r * K + kc) * 2u : kOutOfRange, (uint32_t)k0 * 2u);
+        });
+        if (grp == 0) {
+            static_for<0, B_BLK>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                const int kc = (i & 1) ? kc_odd : kc_even;
+                const int r = n0 + b_row + i * ROWS + prow;
+                const bool ok = live && r < N && k0 + kc < K;
+                dma16<0>(rb, st + A_ELEMS + (b_row + i * ROWS) * BK,
+                         ok ? (uint32_t)(r * K + kc) * 2u : kOutOfRange, (uint32_t)k0 * 2u);
+            });
+        }
+    };
+    constexpr int LD0 = A_BLK + B_BLK, LD1 = A_BLK;
+
+    const int xr = swz<KC>(lane & 31);
+    const int half = lane >> 5;
+    const int a_row0 = (grp * WTM + (lane & 31)) * BK;
+    const int b_row0 = A_ELEMS + (wc * WTN + (lane & 31)) * BK;
+    u32x4 fa[KS][TM], fb[KS][TN];
+    auto read_tile = [&](const u16* st) {
+        static_for<0, KS>([&](auto sc) {
+            constexpr int S = decltype(sc)::value;
+            const int koff = (((2 * S) | half) ^ xr) * 8;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                fa[S][i] = *reinterpret_cast<const u32x4*>(st + a_row0 + i * 32 * BK + koff);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                fb[S][j] = *reinterpret_cast<const u32x4*>(st + b_row0 + j * 32 * BK + koff);
+        });
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+
+    if (nk > 0) {
+        dma_tile(0);
+        dma_tile(1);
+        if (grp == 0)
+            wait_vm<LD0>();                        // tile 0 landed (this wave's part)
+        else
+            wait_vm<LD1>();
+        wait_lgkm_sync();                          // end of phase -1
+        if (grp == 1)
+            wait_lgkm_sync();                      // group 1 sits out phase 0
+        for (int kt = 0; kt < nk; ++kt) {
+            // memory phase (2kt for group 0, 2kt+1 for group 1): this group's loads of
+            // the next tile whose stage part is free, and the operands of tile kt
+            // (loads first: they have the longest way to go)
+            if (grp == 0) {
+                if (kt >= 1 && kt + 1 < nk)
+                    dma_tile(kt + 1);
+                read_tile(lds + (kt & 1) * STAGE);
+                wait_lgkm_sync();                  // end of phase 2kt
+            } else {
+                if (kt + 2 < nk)
+                    dma_tile(kt + 2);
+                read_tile(lds + (kt & 1) * STAGE);
+                if (kt + 2 < nk)
+                    wait_vm<LD1>();                // tile kt+1 landed (this wave's part)
+                else
+                    wait_vm<0>();
+                wait_lgkm_sync();                  // end of phase 2kt+1
+            }
+            // compute phase: the K step's MFMAs back to back
+            __builtin_amdgcn_s_setprio(1);
+            static_for<0, KS * TM * TN>([&](auto qc) {
+                constexpr int Q = decltype(qc)::value;
+                constexpr int S = Q / (TM * TN), i = (Q / TN) % TM, j = Q % TN;
+                acc[i][j] = mfma_32x32x16<DT>(fb[S][j], fa[S][i], acc[i][j]);
+            });
+            __builtin_amdgcn_s_setprio(0);
+            if (grp == 0) {
+                wait_vm<0>();                      // tile kt+1 landed (this wave's part)
+                wait_lgkm_sync();                  // end of phase 2kt+1
+            } else if (kt + 1 < nk) {
+                wait_lgkm_sync();                  // end of phase 2kt+2
+            }
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int m = m0 + grp * WTM + i * 32 + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wc * WTN + j * 32 + 8 * g + 4 * half;
                 u32x2 v;
                 v[0] = pack2<DT>(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
                 v[1] = pack2<DT>(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);

@@ -11,7 +11,7 @@ import os
 
 F16, BF16 = 0, 1
 B_NK, B_KN = 0, 1
-KERNEL_GENERIC, KERNEL_TILED, KERNEL_SKINNY, KERNEL_DMA = 0, 1, 2, 3
+KERNEL_GENERIC, KERNEL_TILED, KERNEL_SKINNY, KERNEL_DMA, KERNEL_PINGPONG = 0, 1, 2, 3, 4
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtgemm.so")
