@@ -51,7 +51,8 @@ def test_every_config_ragged(dev, orc, dtype, layout):
 @pytest.mark.parametrize("dtype", [F16, BF16])
 @pytest.mark.parametrize("layout", [B_NK, B_KN])
 @pytest.mark.parametrize("shape", [(1, 8, 8), (8, 8, 16), (33, 40, 72), (257, 264, 1000),
-                                   (64, 1024, 2048), (300, 8, 520)])
+                                   (64, 1024, 2048), (300, 8, 520), (1, 264, 1032),
+                                   (50, 200, 4104), (100, 96, 1024), (128, 40, 3000)])
 def test_table_choice_shapes(dev, orc, dtype, layout, shape):
     M, N, K = shape
     A, B = _inputs(dtype, M, N, K, layout, 7 + M + N + K)

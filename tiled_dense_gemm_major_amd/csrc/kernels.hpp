@@ -759,6 +759,148 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
 }
 
 // ------------------------------------------------------------------------------------
+// Skinny kernel (small M, B as [N,K]): the product is a stream of B with little reuse
+// ("Tiling a matmul", section "Where it breaks": small or skinny shapes stay
+// memory-bound whatever the tiling; split-K keeps all the compute units busy).
+//   One workgroup per 32 columns of C (all MT*32 rows of a row block); its 8 waves split
+//   the K range into 8 contiguous parts (split-K inside the workgroup), each wave
+//   accumulating a full (MT*32) x 32 partial product.  Per 64-wide k chunk a wave loads
+//   whole 128-byte row segments (8 lanes per row: full cache lines), D chunks ahead into
+//   registers, writes the chunk to its own swizzled LDS buffer and reads it back in MFMA
+//   operand layout (a wave's LDS accesses complete in order, so no barrier is needed).
+//   At the end the 8 partial products are summed through LDS in a fixed order
+//   (deterministic), cast once and stored.  Requirements as for gemm_tiled; rows past
+//   M, columns past N and k past K read as zero through the buffer range check.
+// ------------------------------------------------------------------------------------
+template <int DT, int MT, int D>
+__global__ void __attribute__((amdgpu_flat_work_group_size(512, 512),
+                               amdgpu_waves_per_eu(2, 2)))
+gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
+            int N, int K) {
+    constexpr int NW = 8, BN = 32, CK = 64, KC = CK / 8;
+    constexpr int BM = MT * 32;
+    constexpr int ROWS = BM + BN;                  // rows of one chunk: A rows, then B rows
+    constexpr int LD = ROWS / 8;                   // 1 KiB loads per chunk per wave
+    constexpr int WBUF = ROWS * CK;                // elements of one wave's LDS buffer
+    constexpr int RED = NW * BN * BM;              // floats of the final reduction
+    constexpr int LDS_ELEMS = (NW * WBUF * 2 > RED * 4) ? NW * WBUF : RED * 2;
+    __shared__ __attribute__((aligned(16))) u16 lds[LDS_ELEMS];
+
+    const int n0 = (int)blockIdx.x * BN, m0 = (int)blockIdx.y * BM;
+    const int tid = (int)threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5;
+
+    const rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
+    const rsrc_t rb = make_rsrc(B, (uint32_t)N * (uint32_t)K * 2u);
+    // load i covers chunk rows 8i .. 8i+7: lane l takes row 8i + l/8, 16-byte piece l%8
+    const int lrow = lane >> 3, lpc = lane & 7;
+    uint32_t off[LD];
+#pragma unroll
+    for (int i = 0; i < LD; ++i) {
+        const int r = 8 * i + lrow;
+        if (r < BM)
+            off[i] = m0 + r < M ? (uint32_t)((m0 + r) * K + lpc * 8) * 2u : kOutOfRange;
+        else
+            off[i] = n0 + r - BM < N ? (uint32_t)((n0 + r - BM) * K + lpc * 8) * 2u
+                                     : kOutOfRange;
+    }
+    u16* wb = lds + wave * WBUF;
+    // LDS slot of load i's piece: chunk row 8i + lrow, swizzled by that row
+    auto wr_off = [&](int i) { return (8 * i + lrow) * CK + ((lpc ^ swz<KC>(8 * i + lrow)) * 8); };
+
+    const int nch = (K + CK - 1) / CK;
+    const int c_lo = wave * nch / NW, c_hi = (wave + 1) * nch / NW;
+
+    u32x4 buf[D][LD];
+    auto load_chunk = [&](int c, auto slot) {
+        constexpr int S = decltype(slot)::value;
+        const bool live = c < c_hi;
+        const int k0 = live ? c * CK : 0;
+        const bool ok = live && k0 + lpc * 8 < K;
+#pragma unroll
+        for (int i = 0; i < LD; ++i)
+            buf[S][i] = load16(i * 8 < BM ? ra : rb, ok ? off[i] : kOutOfRange,
+                               (uint32_t)k0 * 2u);
+    };
+
+    const int xr = swz<KC>(lane & 31);
+    f32x16 acc[MT];
+#pragma unroll
+    for (int h = 0; h < MT; ++h)
+        acc[h] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+
+    static_for<0, D>([&](auto d) { load_chunk(c_lo + decltype(d)::value, d); });
+    for (int c = c_lo; c < c_hi; c += D) {
+        static_for<0, D>([&](auto dc) {
+            constexpr int d = decltype(dc)::value;
+#pragma unroll
+            for (int i = 0; i < LD; ++i)
+                *reinterpret_cast<u32x4*>(wb + wr_off(i)) = buf[d][i];
+            u32x4 fa[4][MT], fb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int koff = (((2 * j) | half) ^ xr) * 8;
+#pragma unroll
+                for (int h = 0; h < MT; ++h)
+                    fa[j][h] = *reinterpret_cast<const u32x4*>(
+                        wb + (32 * h + (lane & 31)) * CK + koff);
+                fb[j] = *reinterpret_cast<const u32x4*>(wb + (BM + (lane & 31)) * CK + koff);
+            }
+            load_chunk(c + d + D, dc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int h = 0; h < MT; ++h)
+                    acc[h] = mfma_32x32x16<DT>(fb[j], fa[j][h], acc[h]);
+        });
+    }
+
+    // partial products to LDS as red[wave][n][m] (m contiguous), then a fixed-order sum
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int h = 0; h < MT; ++h)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int n = 8 * (v >> 2) + 4 * half + (v & 3);
+            red[(wave * BN + n) * BM + 32 * h + (lane & 31)] = acc[h][v];
+        }
+    __syncthreads();
+    constexpr int OUT_PER_T = BM * BN / (NW * 64);   // consecutive n per thread
+    static_assert(OUT_PER_T % 4 == 0 || OUT_PER_T == 2, "store groups");
+    const int m = tid % BM;
+    const int nb = (tid / BM) * OUT_PER_T;
+    float sum[OUT_PER_T];
+#pragma unroll
+    for (int q = 0; q < OUT_PER_T; ++q) {
+        float t = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            t += red[(w * BN + nb + q) * BM + m];
+        sum[q] = t;
+    }
+    const int gm = m0 + m;
+    if (gm < M) {
+        if constexpr (OUT_PER_T >= 4) {
+#pragma unroll
+            for (int q = 0; q < OUT_PER_T; q += 4) {
+                if (n0 + nb + q < N) {
+                    u32x2 v;
+                    v[0] = pack2<DT>(sum[q], sum[q + 1]);
+                    v[1] = pack2<DT>(sum[q + 2], sum[q + 3]);
+                    *reinterpret_cast<u32x2*>(C + (size_t)gm * N + n0 + nb + q) = v;
+                }
+            }
+        } else {
+            if (n0 + nb < N)
+                *reinterpret_cast<uint32_t*>(C + (size_t)gm * N + n0 + nb) =
+                    pack2<DT>(sum[0], sum[1]);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------
 // The generic kernel: any alignment, any M, N, K.  64 x 64 tile, K step 16, 4 waves each
 // owning one 32 x 32 MFMA block; element-by-element masked loads into one LDS stage.
 // ------------------------------------------------------------------------------------

@@ -60,6 +60,16 @@ hipError_t launch_pingpong(const void* A, const void* B, void* C, int M, int N, 
     return hipGetLastError();
 }
 
+template <int DT, int MT, int D>
+hipError_t launch_skinny(const void* A, const void* B, void* C, int M, int N, int K, int,
+                         hipStream_t s) {
+    hipLaunchKernelGGL((tgemm::gemm_skinny<DT, MT, D>),
+                       dim3((unsigned)cdiv(N, 32), (unsigned)cdiv(M, MT * 32)), dim3(512), 0, s,
+                       static_cast<const u16*>(A), static_cast<const u16*>(B),
+                       static_cast<u16*>(C), M, N, K);
+    return hipGetLastError();
+}
+
 template <int DT, int LAYOUT>
 hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, int K,
                           int group_m, hipStream_t s) {
@@ -90,9 +100,14 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
         DT, 0, tgemm_config{TGEMM_KERNEL_PINGPONG, BM, BN, BK, 2, 4, 2, G, 1},             \
             &launch_pingpong<DT, BM, BN, BK>                                               \
     }
+#define SKINNY(DT, MT, D)                                                                  \
+    Variant {                                                                              \
+        DT, 0, tgemm_config{TGEMM_KERNEL_SKINNY, MT * 32, 32, 64, 1, 8, D, 1, 8},          \
+            &launch_skinny<DT, MT, D>                                                      \
+    }
 #define ALL_DMA(DT)                                                                        \
     DMA(DT, 256, 256, 32, 2, 2, 4, 4), DMA(DT, 256, 256, 32, 2, 2, 5, 4),                  \
-        PINGPONG(DT, 256, 256, 64, 4)
+        PINGPONG(DT, 256, 256, 64, 4), SKINNY(DT, 1, 4), SKINNY(DT, 2, 3), SKINNY(DT, 4, 1)
 #define ALL_SHAPES(DT, L)                                                                  \
     GENERIC(DT, L), TILED(DT, L, 256, 256, 64, 2, 2, 4), TILED(DT, L, 128, 128, 64, 2, 2, 8), \
         TILED(DT, L, 64, 64, 64, 2, 2, 8)
@@ -126,11 +141,15 @@ const Variant* find_variant(int dtype, int layout, const tgemm_config& cfg) {
 // (256 compute units) is filled with the largest tile that still fills it.
 tgemm_config choose(int dtype, int layout, int64_t m, int64_t n, int64_t k, bool aligned) {
     (void)dtype;
-    (void)k;
     tgemm_config c;
     if (!aligned) {
         c = tgemm_config{TGEMM_KERNEL_GENERIC, 64, 64, 16, 2, 2, 1, 8, 1};
         return c;
+    }
+    if (layout == TGEMM_B_NK && m <= 128 && k >= 1024) {
+        const int mt = m <= 32 ? 1 : (m <= 64 ? 2 : 4);
+        const int depth = mt == 1 ? 4 : (mt == 2 ? 3 : 1);
+        return tgemm_config{TGEMM_KERNEL_SKINNY, mt * 32, 32, 64, 1, 8, depth, 1, 8};
     }
     const int64_t t256 = ((m + 255) / 256) * ((n + 255) / 256);
     const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
