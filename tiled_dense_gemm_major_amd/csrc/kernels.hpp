@@ -576,7 +576,7 @@ gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__
 }
 
 // ------------------------------------------------------------------------------------
-// Ping-pong kernel (B as [N,K] only).
+// Ping-pong kernel.
 //   8 waves, two per SIMD, in two groups: group 0 (waves 0-3) owns C rows [0, BM/2) of the
 //   tile, group 1 (waves 4-7) rows [BM/2, BM); inside a group wave c owns a BN/4-wide
 //   column block, so each wave holds a (BM/2) x (BN/4) block of accumulators.  Waves w
@@ -602,7 +602,7 @@ __device__ __forceinline__ void wait_lgkm_sync() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int DT, int BM, int BN, int BK>
+template <int DT, int LAYOUT, int BM, int BN, int BK>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512),
                                amdgpu_waves_per_eu(2, 2)))
 gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
@@ -617,6 +617,7 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave block must be whole 32x32 tiles");
     static_assert((BM / 8) % ROWS == 0 && (BN / 4) % ROWS == 0, "bad load split");
     static_assert(2 * STAGE * 2 <= 160 * 1024, "LDS");
+    static_assert(LAYOUT == LAYOUT_NK || (BN == 256 && BK == 64), "B [K,N] path: 256 x 64");
 
     __shared__ __attribute__((aligned(1024))) u16 lds[2 * STAGE];
 
@@ -637,7 +638,7 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
     // block at physical chunk l % KC and fetches the logical chunk the swizzle puts there,
     // which (blocks start at multiples of ROWS) depends only on the block's parity.
     constexpr int A_BLK = (BM / 8) / ROWS;         // A blocks per wave
-    constexpr int B_BLK = (BN / 4) / ROWS;         // B blocks per group-0 wave
+    constexpr int B_BLK = (BN * BK / 512) / 4;     // B blocks (1 KiB) per group-0 wave
     static_assert(KC == 8 && ROWS == 8, "block parity swizzle assumes 8 chunks per row");
     const int prow = lane / KC;
     const int a_row = (grp ? 0 : BM / 2) + wc * (BM / 8);   // first A row of this wave
@@ -657,14 +658,31 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
                      ok ? (uint32_t)(r * K + kc) * 2u : kOutOfRange, (uint32_t)k0 * 2u);
         });
         if (grp == 0) {
-            static_for<0, B_BLK>([&](auto ic) {
-                constexpr int i = decltype(ic)::value;
-                const int kc = (i & 1) ? kc_odd : kc_even;
-                const int r = n0 + b_row + i * ROWS + prow;
-                const bool ok = live && r < N && k0 + kc < K;
-                dma16<0>(rb, st + A_ELEMS + (b_row + i * ROWS) * BK,
-                         ok ? (uint32_t)(r * K + kc) * 2u : kOutOfRange, (uint32_t)k0 * 2u);
-            });
+            if constexpr (LAYOUT == LAYOUT_NK) {
+                static_for<0, B_BLK>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    const int kc = (i & 1) ? kc_odd : kc_even;
+                    const int r = n0 + b_row + i * ROWS + prow;
+                    const bool ok = live && r < N && k0 + kc < K;
+                    dma16<0>(rb, st + A_ELEMS + (b_row + i * ROWS) * BK,
+                             ok ? (uint32_t)(r * K + kc) * 2u : kOutOfRange,
+                             (uint32_t)k0 * 2u);
+                });
+            } else {
+                // B [K,N]: the stage holds k rows of BN columns; a 1 KiB load fills two
+                // rows, lane l row l / 32 at physical chunk l % 32, fetching the logical
+                // chunk that the row's swizzle (chunk ^ 4*(k % 4)) puts there.
+                static_for<0, B_BLK>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    const int kr = wc * (BK / 4) + 2 * i + (lane >> 5);
+                    const int cl = (lane & 31) ^ (4 * (kr & 3));
+                    const int n = n0 + 8 * cl;
+                    const bool ok = live && n < N && k0 + kr < K;
+                    dma16<0>(rb, st + A_ELEMS + (wc * (BK / 4) + 2 * i) * BN,
+                             ok ? (uint32_t)(kr * N + n) * 2u : kOutOfRange,
+                             (uint32_t)k0 * (uint32_t)N * 2u);
+                });
+            }
         }
     };
     constexpr int LD0 = A_BLK + B_BLK, LD1 = A_BLK;
@@ -673,6 +691,21 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
     const int half = lane >> 5;
     const int a_row0 = (grp * WTM + (lane & 31)) * BK;
     const int b_row0 = A_ELEMS + (wc * WTN + (lane & 31)) * BK;
+    // B [K,N] operands come from two transposing reads (ds_read_b64_tr_b16): in each
+    // 16-lane group, lane s points at the 4 columns [4(s%4), 4(s%4)+4) of k row s/4 of a
+    // 4 x 16 block, and lane i receives column i of those 4 rows; lane groups 0/1 cover
+    // columns 0-15/16-31 and groups 2/3 the same for the upper 8 k, so two reads (k and
+    // k+4) give each lane its column's 8 consecutive k in MFMA operand order.
+    int kn_base[TN];
+    if constexpr (LAYOUT == LAYOUT_KN) {
+        const int g = lane >> 4, sl = lane & 15;
+        const int kl = 8 * (g >> 1) + (sl >> 2);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = wc * WTN + 32 * j + 16 * (g & 1) + 4 * (sl & 3);
+            kn_base[j] = A_ELEMS + kl * BN + (((n >> 3) ^ (4 * (kl & 3))) << 3) + (n & 7);
+        }
+    }
     u32x4 fa[KS][TM], fb[KS][TN];
     auto read_tile = [&](const u16* st) {
         static_for<0, KS>([&](auto sc) {
@@ -682,8 +715,22 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
             for (int i = 0; i < TM; ++i)
                 fa[S][i] = *reinterpret_cast<const u32x4*>(st + a_row0 + i * 32 * BK + koff);
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                fb[S][j] = *reinterpret_cast<const u32x4*>(st + b_row0 + j * 32 * BK + koff);
+            for (int j = 0; j < TN; ++j) {
+                if constexpr (LAYOUT == LAYOUT_NK) {
+                    fb[S][j] = *reinterpret_cast<const u32x4*>(st + b_row0 + j * 32 * BK + koff);
+                } else {
+                    typedef short s16x4 __attribute__((ext_vector_type(4)));
+                    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+                    const u16* p0 = st + kn_base[j] + (16 * S) * BN;
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4*)(p0));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4*)(p0 + 4 * BN));
+                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+                    const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+                    fb[S][j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+                }
+            }
         });
     };
 
