@@ -29,7 +29,7 @@ from tiled_dense_gemm_major_amd.inputs import BF16, WORKLOADS  # noqa: E402
 
 HEADLINE = "bf16_8192"
 METRIC = "GEMM TFLOP/s at 8192^3 bf16 K-major (1 MI355X) and % of MFMA peak"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_tiled_bf16_8192.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_pingpong_bf16_8192.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_dense_gemm_major_amd", "csrc", f)
                   for f in ("kernels.hpp", "tgemm.hip")]
 
