@@ -587,22 +587,28 @@ gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__
 //   Phases end at workgroup barriers:
 //     phase 2t   : group 0 reads tile t,   group 1 computes tile t-1
 //     phase 2t+1 : group 0 computes tile t, group 1 reads tile t
-//   Tiles alternate between two LDS stages.  A rows [0, BM/2) of a tile are read only by
+//   Tiles rotate through STAGES LDS stages.  A rows [0, BM/2) of a tile are read only by
 //   group 0 (in phase 2t), so they are free one phase earlier than the rest: group 1
-//   loads them for tile t+2 in its memory phase 2t+1; group 0 loads A rows [BM/2, BM)
-//   and B of tile t+2 in its memory phase 2t+2.  No loads are issued in compute phases.
-//   Tile t+2 must have landed by the end of phase 2t+3, where every wave waits for its
-//   own loads of it before the barrier.
+//   loads them for tile t+STAGES in its memory phase 2t+1; group 0 loads A rows
+//   [BM/2, BM) and B of tile t+STAGES in its memory phase 2t+2.  No loads are issued in
+//   compute phases.  Each wave waits for its own part of tile t+1 before the barrier
+//   that ends phase 2t+1, so a load has 2*STAGES-2 phases to land; with BK = 32 the
+//   phases are half as long and the ring twice as deep (4-5 stages in 160 KiB), which
+//   hides a longer memory latency at the cost of twice as many barriers.
 // ------------------------------------------------------------------------------------
 template <int N>
 __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
 __device__ __forceinline__ void wait_lgkm_sync() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int DT, int LAYOUT, int BM, int BN, int BK>
+template <int DT, int LAYOUT, int BM, int BN, int BK, int STAGES>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512),
                                amdgpu_waves_per_eu(2, 2)))
 gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
@@ -616,10 +622,10 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
     constexpr int ROWS = 64 / KC;                  // tile rows per 1 KiB load
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave block must be whole 32x32 tiles");
     static_assert((BM / 8) % ROWS == 0 && (BN / 4) % ROWS == 0, "bad load split");
-    static_assert(2 * STAGE * 2 <= 160 * 1024, "LDS");
-    static_assert(LAYOUT == LAYOUT_NK || (BN == 256 && BK == 64), "B [K,N] path: 256 x 64");
+    static_assert(STAGES >= 2 && STAGES * STAGE * 2 <= 160 * 1024, "LDS");
+    static_assert(LAYOUT == LAYOUT_NK || BN == 256, "B [K,N] path: 256 columns");
 
-    __shared__ __attribute__((aligned(1024))) u16 lds[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) u16 lds[STAGES * STAGE];
 
     int tm, tn;
     tile_of((int)blockIdx.x, grid_m, grid_n, group_m, tm, tn);
@@ -639,53 +645,69 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
     // which (blocks start at multiples of ROWS) depends only on the block's parity.
     constexpr int A_BLK = (BM / 8) / ROWS;         // A blocks per wave
     constexpr int B_BLK = (BN * BK / 512) / 4;     // B blocks (1 KiB) per group-0 wave
-    static_assert(KC == 8 && ROWS == 8, "block parity swizzle assumes 8 chunks per row");
+    static_assert(KC == 4 || KC == 8, "the swizzle repeats every two blocks for 4 or 8 chunks");
     const int prow = lane / KC;
     const int a_row = (grp ? 0 : BM / 2) + wc * (BM / 8);   // first A row of this wave
     const int b_row = wc * (BN / 4);                          // first B row (group 0)
     const int kc_even = ((lane % KC) ^ swz<KC>(prow)) * 8;
     const int kc_odd = ((lane % KC) ^ swz<KC>(ROWS + prow)) * 8;
-    auto dma_tile = [&](int kt) {
+    // A tile past the end is loaded as zeros (every lane out of range) into a stage no
+    // one reads again, which keeps the number of loads in flight static.
+    auto dma_a = [&](int kt, auto ic) {            // block i of this wave's A rows
+        constexpr int i = decltype(ic)::value;
         const bool live = kt < nk;
         const int k0 = live ? kt * BK : 0;
-        u16* st = lds + (kt & 1) * STAGE;
-        static_for<0, A_BLK>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
+        u16* st = lds + (kt % STAGES) * STAGE;
+        const int kc = (i & 1) ? kc_odd : kc_even;
+        const int r = m0 + a_row + i * ROWS + prow;
+        const bool ok = live && r < M && k0 + kc < K;
+        dma16<0>(ra, st + (a_row + i * ROWS) * BK,
+                 ok ? (uint32_t)(r * K + kc) * 2u : kOutOfRange, (uint32_t)k0 * 2u);
+    };
+    // B [N,K]: the BN/4 rows of wave c's columns are read only by wave c of each group,
+    // so each of the two waves loads half of them: group 0 the upper half in its memory
+    // phase, group 1 the lower half in its own memory phase, once its reads of the stage
+    // have completed.  B [K,N]: every k row holds all waves' columns, so group 0 loads
+    // all of B.
+    auto dma_b = [&](int kt, auto ic) {            // block i of this wave's B share
+        constexpr int i = decltype(ic)::value;
+        const bool live = kt < nk;
+        const int k0 = live ? kt * BK : 0;
+        u16* st = lds + (kt % STAGES) * STAGE;
+        if constexpr (LAYOUT == LAYOUT_NK) {
+            const int r0 = b_row + (grp == 0 ? B_BLK / 2 : 0) * ROWS;
             const int kc = (i & 1) ? kc_odd : kc_even;
-            const int r = m0 + a_row + i * ROWS + prow;
-            const bool ok = live && r < M && k0 + kc < K;
-            dma16<0>(ra, st + (a_row + i * ROWS) * BK,
+            const int r = n0 + r0 + i * ROWS + prow;
+            const bool ok = live && r < N && k0 + kc < K;
+            dma16<0>(rb, st + A_ELEMS + (r0 + i * ROWS) * BK,
                      ok ? (uint32_t)(r * K + kc) * 2u : kOutOfRange, (uint32_t)k0 * 2u);
-        });
-        if (grp == 0) {
-            if constexpr (LAYOUT == LAYOUT_NK) {
-                static_for<0, B_BLK>([&](auto ic) {
-                    constexpr int i = decltype(ic)::value;
-                    const int kc = (i & 1) ? kc_odd : kc_even;
-                    const int r = n0 + b_row + i * ROWS + prow;
-                    const bool ok = live && r < N && k0 + kc < K;
-                    dma16<0>(rb, st + A_ELEMS + (b_row + i * ROWS) * BK,
-                             ok ? (uint32_t)(r * K + kc) * 2u : kOutOfRange,
-                             (uint32_t)k0 * 2u);
-                });
-            } else {
-                // B [K,N]: the stage holds k rows of BN columns; a 1 KiB load fills two
-                // rows, lane l row l / 32 at physical chunk l % 32, fetching the logical
-                // chunk that the row's swizzle (chunk ^ 4*(k % 4)) puts there.
-                static_for<0, B_BLK>([&](auto ic) {
-                    constexpr int i = decltype(ic)::value;
-                    const int kr = wc * (BK / 4) + 2 * i + (lane >> 5);
-                    const int cl = (lane & 31) ^ (4 * (kr & 3));
-                    const int n = n0 + 8 * cl;
-                    const bool ok = live && n < N && k0 + kr < K;
-                    dma16<0>(rb, st + A_ELEMS + (wc * (BK / 4) + 2 * i) * BN,
-                             ok ? (uint32_t)(kr * N + n) * 2u : kOutOfRange,
-                             (uint32_t)k0 * (uint32_t)N * 2u);
-                });
-            }
+        } else {
+            // the stage holds k rows of BN columns; a 1 KiB load fills two rows, lane l
+            // row l / 32 at physical chunk l % 32, fetching the logical chunk that the
+            // row's swizzle (chunk ^ 4*(k % 4)) puts there.
+            const int kr = wc * (BK / 4) + 2 * i + (lane >> 5);
+            const int cl = (lane & 31) ^ (4 * (kr & 3));
+            const int n = n0 + 8 * cl;
+            const bool ok = live && n < N && k0 + kr < K;
+            dma16<0>(rb, st + A_ELEMS + (wc * (BK / 4) + 2 * i) * BN,
+                     ok ? (uint32_t)(kr * N + n) * 2u : kOutOfRange,
+                     (uint32_t)k0 * (uint32_t)N * 2u);
         }
     };
-    constexpr int LD0 = A_BLK + B_BLK, LD1 = A_BLK;
+    static_assert(B_BLK % 2 == 0 && (B_BLK / 2) % 2 == 0, "B halves keep the block parity");
+    constexpr bool SPLIT_B = LAYOUT == LAYOUT_NK;
+    constexpr int B0 = SPLIT_B ? B_BLK / 2 : B_BLK;   // B blocks per group-0 wave
+    constexpr int B1 = SPLIT_B ? B_BLK / 2 : 0;       // B blocks per group-1 wave
+    constexpr int LD0 = A_BLK + B0, LD1 = A_BLK + B1; // loads per wave per tile
+    // load q of a group's share of tile kt: its A blocks, then its B blocks
+    auto load_q = [&](int kt, auto qc) {
+        constexpr int q = decltype(qc)::value;
+        if constexpr (q < A_BLK)
+            dma_a(kt, std::integral_constant<int, q>{});
+        else
+            dma_b(kt, std::integral_constant<int, q - A_BLK>{});
+    };
+
 
     const int xr = swz<KC>(lane & 31);
     const int half = lane >> 5;
@@ -707,32 +729,56 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
         }
     }
     u32x4 fa[KS][TM], fb[KS][TN];
-    auto read_tile = [&](const u16* st) {
-        static_for<0, KS>([&](auto sc) {
-            constexpr int S = decltype(sc)::value;
+    // Operand read r of tile kt: the B operands first (group 1 frees its B rows as soon
+    // as they are read), then A.
+    constexpr int NRB = KS * TN, NR = KS * (TN + TM);
+    auto read_r = [&](int kt, auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const u16* st = lds + (kt % STAGES) * STAGE;
+        if constexpr (r < NRB) {
+            constexpr int S = r / TN, j = r % TN;
             const int koff = (((2 * S) | half) ^ xr) * 8;
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                fa[S][i] = *reinterpret_cast<const u32x4*>(st + a_row0 + i * 32 * BK + koff);
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                if constexpr (LAYOUT == LAYOUT_NK) {
-                    fb[S][j] = *reinterpret_cast<const u32x4*>(st + b_row0 + j * 32 * BK + koff);
-                } else {
-                    typedef short s16x4 __attribute__((ext_vector_type(4)));
-                    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-                    const u16* p0 = st + kn_base[j] + (16 * S) * BN;
-                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_s16x4*)(p0));
-                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_s16x4*)(p0 + 4 * BN));
-                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-                    const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-                    fb[S][j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
-                }
+            if constexpr (LAYOUT == LAYOUT_NK) {
+                fb[S][j] = *reinterpret_cast<const u32x4*>(st + b_row0 + j * 32 * BK + koff);
+            } else {
+                typedef short s16x4 __attribute__((ext_vector_type(4)));
+                typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+                const u16* p0 = st + kn_base[j] + (16 * S) * BN;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+                const s16x4 hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * BN));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+                const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+                fb[S][j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
             }
-        });
+        } else {
+            constexpr int S = (r - NRB) / TM, i = (r - NRB) % TM;
+            const int koff = (((2 * S) | half) ^ xr) * 8;
+            fa[S][i] = *reinterpret_cast<const u32x4*>(st + a_row0 + i * 32 * BK + koff);
+        }
     };
+    // A memory phase: the operand reads of tile kt with the first NL loads of this
+    // group's share of tile lt spread evenly among them (load q goes before read
+    // q * NR / NL), so the load path and the LDS work side by side.
+    auto mem_phase = [&](int kt, int lt, auto nlc) {
+        constexpr int NL = decltype(nlc)::value;
+        static_for<0, NR>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            static_for<0, NL>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                if constexpr (q * NR / NL == r) {
+                    load_q(lt, qc);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            });
+            read_r(kt, rc);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // LDS reads a wave issues per tile for the A operands, capped at the 15 the counter
+    // can name: LDS instructions complete in order, so once at most this many are
+    // outstanding the B reads (issued first) are done
+    constexpr int A_READS = KS * TM < 15 ? KS * TM : 15;
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -742,32 +788,41 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
             acc[i][j] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
     if (nk > 0) {
-        dma_tile(0);
-        dma_tile(1);
+        // Group 1 loads the A rows [0, BM/2) of tile kt + STAGES in its memory phase
+        // 2kt+1 (group 0 finished reading them in phase 2kt); group 0 loads the rest of
+        // tile kt + STAGES - 1 in its memory phase 2kt (group 1 finished reading that
+        // stage in phase 2kt-1).  Before the loop: the first STAGES (group 1) or
+        // STAGES - 1 (group 0) tiles.
+        for (int u = 0; u < STAGES - (grp == 0 ? 1 : 0); ++u) {
+            if (grp == 0) {
+                static_for<0, LD0>([&](auto qc) { load_q(u, qc); });
+            } else {
+                static_for<0, LD1>([&](auto qc) { load_q(u, qc); });
+            }
+        }
         if (grp == 0)
-            wait_vm<LD0>();                        // tile 0 landed (this wave's part)
+            wait_vm<(STAGES - 2) * LD0>();         // tile 0 landed (this wave's part)
         else
-            wait_vm<LD1>();
+            wait_vm<(STAGES - 1) * LD1>();
         wait_lgkm_sync();                          // end of phase -1
         if (grp == 1)
             wait_lgkm_sync();                      // group 1 sits out phase 0
         for (int kt = 0; kt < nk; ++kt) {
             // memory phase (2kt for group 0, 2kt+1 for group 1): this group's loads of
-            // the next tile whose stage part is free, and the operands of tile kt
-            // (loads first: they have the longest way to go)
+            // the next free stage part (loads first: they have the longest way to go),
+            // then the operands of tile kt
             if (grp == 0) {
-                if (kt >= 1 && kt + 1 < nk)
-                    dma_tile(kt + 1);
-                read_tile(lds + (kt & 1) * STAGE);
+                mem_phase(kt, kt + STAGES - 1, std::integral_constant<int, LD0>{});
                 wait_lgkm_sync();                  // end of phase 2kt
             } else {
-                if (kt + 2 < nk)
-                    dma_tile(kt + 2);
-                read_tile(lds + (kt & 1) * STAGE);
-                if (kt + 2 < nk)
-                    wait_vm<LD1>();                // tile kt+1 landed (this wave's part)
-                else
-                    wait_vm<0>();
+                mem_phase(kt, kt + STAGES, std::integral_constant<int, A_BLK>{});
+                if constexpr (SPLIT_B) {
+                    wait_lgkm<A_READS>();          // this wave's B reads of tile kt done
+                    static_for<0, B1>([&](auto qc) {
+                        dma_b(kt + STAGES, qc);
+                    });
+                }
+                wait_vm<(STAGES - 1) * LD1>();     // tile kt+1 landed (this wave's part)
                 wait_lgkm_sync();                  // end of phase 2kt+1
             }
             // compute phase: the K step's MFMAs back to back
@@ -779,12 +834,13 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
             });
             __builtin_amdgcn_s_setprio(0);
             if (grp == 0) {
-                wait_vm<0>();                      // tile kt+1 landed (this wave's part)
+                wait_vm<(STAGES - 2) * LD0>();     // tile kt+1 landed (this wave's part)
                 wait_lgkm_sync();                  // end of phase 2kt+1
             } else if (kt + 1 < nk) {
                 wait_lgkm_sync();                  // end of phase 2kt+2
             }
         }
+        wait_vm<0>();                              // the trailing zero loads
     }
 
 #pragma unroll

@@ -50,11 +50,11 @@ hipError_t launch_dma(const void* A, const void* B, void* C, int M, int N, int K
     return hipGetLastError();
 }
 
-template <int DT, int LAYOUT, int BM, int BN, int BK>
+template <int DT, int LAYOUT, int BM, int BN, int BK, int S>
 hipError_t launch_pingpong(const void* A, const void* B, void* C, int M, int N, int K,
                            int group_m, hipStream_t s) {
     const int gm = cdiv(M, BM), gn = cdiv(N, BN);
-    hipLaunchKernelGGL((tgemm::gemm_pingpong<DT, LAYOUT, BM, BN, BK>), dim3((unsigned)(gm * gn)),
+    hipLaunchKernelGGL((tgemm::gemm_pingpong<DT, LAYOUT, BM, BN, BK, S>), dim3((unsigned)(gm * gn)),
                        dim3(512), 0, s, static_cast<const u16*>(A), static_cast<const u16*>(B),
                        static_cast<u16*>(C), M, N, K, gm, gn, group_m);
     return hipGetLastError();
@@ -95,10 +95,10 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
         DT, 0, tgemm_config{TGEMM_KERNEL_DMA, BM, BN, BK, WM, WN, ST, G, 1},               \
             &launch_dma<DT, BM, BN, BK, WM, WN, ST>                                        \
     }
-#define PINGPONG(DT, L, BM, BN, BK, G)                                                     \
+#define PINGPONG(DT, L, BM, BN, BK, S, G)                                                  \
     Variant {                                                                              \
-        DT, L, tgemm_config{TGEMM_KERNEL_PINGPONG, BM, BN, BK, 2, 4, 2, G, 1},             \
-            &launch_pingpong<DT, L, BM, BN, BK>                                            \
+        DT, L, tgemm_config{TGEMM_KERNEL_PINGPONG, BM, BN, BK, 2, 4, S, G, 1},             \
+            &launch_pingpong<DT, L, BM, BN, BK, S>                                         \
     }
 #define SKINNY(DT, MT, D)                                                                  \
     Variant {                                                                              \
@@ -107,7 +107,8 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
     }
 #define ALL_DMA(DT)                                                                        \
     DMA(DT, 256, 256, 32, 2, 2, 4, 4), DMA(DT, 256, 256, 32, 2, 2, 5, 4),                  \
-        PINGPONG(DT, 0, 256, 256, 64, 4), SKINNY(DT, 1, 4), SKINNY(DT, 2, 3), SKINNY(DT, 4, 1)
+        PINGPONG(DT, 0, 256, 256, 64, 2, 4), PINGPONG(DT, 0, 256, 256, 32, 4, 4), \
+        PINGPONG(DT, 0, 256, 256, 32, 5, 4), SKINNY(DT, 1, 4), SKINNY(DT, 2, 3), SKINNY(DT, 4, 1)
 #define ALL_SHAPES(DT, L)                                                                  \
     GENERIC(DT, L), TILED(DT, L, 256, 256, 64, 2, 2, 4), TILED(DT, L, 128, 128, 64, 2, 2, 8), \
         TILED(DT, L, 64, 64, 64, 2, 2, 8)
@@ -117,8 +118,10 @@ const Variant kVariants[] = {
     ALL_DMA(1),
     ALL_SHAPES(0, 0),
     ALL_SHAPES(0, 1),
-    PINGPONG(0, 1, 256, 256, 64, 4),
-    PINGPONG(1, 1, 256, 256, 64, 4),
+    PINGPONG(0, 1, 256, 256, 64, 2, 4),
+    PINGPONG(1, 1, 256, 256, 64, 2, 4),
+    PINGPONG(0, 1, 256, 256, 32, 5, 4),
+    PINGPONG(1, 1, 256, 256, 32, 5, 4),
     ALL_SHAPES(1, 0),
     ALL_SHAPES(1, 1),
 };
