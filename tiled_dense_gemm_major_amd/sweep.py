@@ -48,6 +48,8 @@ def main(argv=None):
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--torch-ref", action="store_true",
                     help="also time torch.matmul (the vendor library) as context")
+    ap.add_argument("--kernels", default="",
+                    help="comma-separated kernel ids to time (default: every compiled one)")
     args = ap.parse_args(argv)
 
     import numpy as np
@@ -77,7 +79,10 @@ def main(argv=None):
         flops = roofline.gemm_flops(w.M, w.N, w.K)
         nbytes = roofline.compulsory_bytes(w.M, w.N, w.K)
         table = tgemm.query_config(w.dtype, w.M, w.N, w.K, w.b_layout).as_dict()
+        kernels = {int(x) for x in args.kernels.split(",") if x}
         for cfg in tgemm.list_configs(w.dtype, w.b_layout):
+            if kernels and cfg.kernel not in kernels:
+                continue
             med, p10, p90 = time_config(tgemm, torch, w, A, B, C, cfg, args.warmup,
                                         args.repeat, stream)
             rec = {
