@@ -1,14 +1,20 @@
 /*
  * libtgemm -- block-tiled dense matrix multiply for AMD Instinct MI355X (gfx950).
  *
- *   C[m,n] = sum_{k<K} A[m,k] * b(n,k),   A [M,K] row-major (K contiguous)
- *     b_layout TGEMM_B_NK: B stored [N,K] row-major (K contiguous), b(n,k) = B[n*K+k],
+ *   C[m,n] = sum_{k<K} a(m,k) * b(n,k)
+ *     a(m,k) = A[m*lda + k]  (A stored [M,K], K contiguous; the packed entry points)
+ *     a(m,k) = A[k*lda + m]  (A stored [K,M], M contiguous; gemm_strided, TGEMM_A_KM)
+ *     b_layout TGEMM_B_NK: B stored [N,K] row-major (K contiguous), b(n,k) = B[n*ldb+k],
  *                          so C = A x B^T ("0. A Minimal Hopper Matmul", Tilus tutorial,
  *                          section "Block Tiling": A (M,K), B (N,K), C (M,N), both K-major)
- *     b_layout TGEMM_B_KN: B stored [K,N] row-major (N contiguous), b(n,k) = B[k*N+n],
+ *     b_layout TGEMM_B_KN: B stored [K,N] row-major (N contiguous), b(n,k) = B[k*ldb+n],
  *                          so C = A x B ("Tiling a matmul", section "Code"; "TileLang: a
  *                          tile language one level below Triton", section "The first
  *                          kernel: GEMM", where B is a (K,N) tensor)
+ *   and C[m,n] is stored at C[m*ldc + n].  gemm_f16, gemm_bf16 and gemm_ex take packed
+ *   operands (lda = K, ldb = K or N, ldc = N); gemm_strided takes leading dimensions
+ *   and either storage of A (operands may be K- or MN-contiguous: Tilus tutorial,
+ *   section "Block Tiling").
  *
  * Inputs are IEEE binary16 (f16) or bfloat16 (bf16); products are summed in fp32 and the
  * fp32 sum is rounded once, to nearest-even, to the same 16-bit type for C (the fp32
@@ -17,8 +23,7 @@
  * with an exact sum to within fp32 rounding, not bit for bit.
  *
  * Conventions shared by every entry point:
- *   - Ownership: the caller allocates A, B and C in device memory (packed, no leading
- *     dimensions) and keeps ownership.  The library allocates no device memory and keeps
+ *   - Ownership: the caller allocates A, B and C in device memory and keeps ownership.  The library allocates no device memory and keeps
  *     no pointer after the call returns.  C is fully overwritten (no alpha/beta).
  *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and the call returns at once.  Faults during execution surface at the caller's
@@ -27,11 +32,14 @@
  *     a failed check enqueues nothing.  Nothing aborts or exits.
  *   - Degenerate shapes: M == 0 or N == 0 is a no-op returning TGEMM_OK; K == 0 writes
  *     +0.0 (the empty sum) to all of C.
- *   - Alignment: any 2-byte-aligned pointers and any sizes are accepted.  The fast kernels
- *     need A, B, C 16-byte aligned, K % 8 == 0 and N % 8 == 0; other calls run a slower
- *     kernel with the same arithmetic.
- *   - Limits: M, N, K < 2^31 and M*K, N*K, M*N < 2^31 elements (TGEMM_ERR_UNSUPPORTED).
- *   - Aliasing: C may not overlap A or B (TGEMM_ERR_ALIASING).  A and B may overlap.
+ *   - Alignment: any 2-byte-aligned pointers, sizes and leading dimensions are accepted.
+ *     The fast kernels need A, B, C 16-byte aligned, K, N, lda, ldb and ldc multiples of
+ *     8, M a multiple of 8 when A is [K,M], and A and B each spanning at most 2^31 bytes;
+ *     other calls run a slower kernel with the same arithmetic.
+ *   - Limits: M, N, K < 2^31, M*K, N*K, M*N < 2^31, and the element span of each operand
+ *     ((rows - 1) * ld + row length) < 2^31 (TGEMM_ERR_UNSUPPORTED).
+ *   - Aliasing: the span of C may not overlap the span of A or B (TGEMM_ERR_ALIASING).
+ *     A and B may overlap.
  *   - Thread safety: the configuration table is read-only; calls from several host
  *     threads are safe.  Calls on one stream execute in order.
  */
@@ -52,12 +60,18 @@ typedef enum {
 } tgemm_b_layout;
 
 typedef enum {
+    TGEMM_A_MK = 0, /* A is [M,K], K contiguous (the packed entry points) */
+    TGEMM_A_KM = 1  /* A is [K,M], M contiguous                           */
+} tgemm_a_layout;
+
+typedef enum {
     TGEMM_OK = 0,
-    TGEMM_ERR_INVALID_VALUE = -1, /* negative size, unknown dtype or layout           */
+    TGEMM_ERR_INVALID_VALUE = -1, /* negative size, unknown dtype or layout, or a
+                                     leading dimension below its row length (or < 1)    */
     TGEMM_ERR_NULL_POINTER = -2,  /* A, B or C NULL for a non-empty product            */
     TGEMM_ERR_ALIGNMENT = -3,     /* a pointer not 2-byte aligned, or an explicit fast
                                      configuration given operands it cannot take        */
-    TGEMM_ERR_ALIASING = -4,      /* C overlaps A or B                                  */
+    TGEMM_ERR_ALIASING = -4,      /* C's span overlaps A's or B's                       */
     TGEMM_ERR_UNSUPPORTED = -5,   /* sizes past the limits, or a configuration that is
                                      not compiled into the library                      */
     TGEMM_ERR_LAUNCH = -6,        /* the HIP launch was refused (no gfx950 device...)   */
@@ -71,10 +85,11 @@ typedef enum {
                                  stages, MFMA 32x32x16, grouped XCD-aware tile order     */
     TGEMM_KERNEL_SKINNY = 2,  /* small M: the K range of a tile split over the waves of a
                                  workgroup and summed in LDS                              */
-    TGEMM_KERNEL_DMA = 3,     /* B [N,K] only: global loads written straight into a deep
-                                 ring of swizzled LDS stages (no register staging)        */
-    TGEMM_KERNEL_PINGPONG = 4 /* B [N,K] only: 8 waves, two per SIMD, alternating between
-                                 operand fetch and back-to-back MFMAs half a period apart */
+    TGEMM_KERNEL_DMA = 3,     /* A [M,K], B [N,K] only: global loads written straight into
+                                 a deep ring of swizzled LDS stages (no register staging) */
+    TGEMM_KERNEL_PINGPONG = 4 /* 8 waves, two per SIMD, alternating between operand fetch
+                                 and back-to-back MFMAs half a period apart; direct-to-LDS
+                                 loads; [K,N] B and [K,M] A through transposing reads    */
 } tgemm_kernel;
 
 /* One tile configuration.  block_m x block_n is the C tile of one workgroup, block_k
@@ -117,6 +132,22 @@ int gemm_bf16(int64_t m, int64_t n, int64_t k, const void* A, const void* B, voi
 int gemm_ex(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const void* B,
             void* C, int b_layout, const tgemm_config* cfg, void* stream);
 
+/*
+ * The general product: either storage of A, either storage of B, leading dimensions.
+ *   A        : device pointer; a_layout TGEMM_A_MK: a(m,k) = A[m*lda + k] (lda >= k);
+ *              TGEMM_A_KM: a(m,k) = A[k*lda + m] (lda >= m)
+ *   B        : device pointer; TGEMM_B_NK: b(n,k) = B[n*ldb + k] (ldb >= k);
+ *              TGEMM_B_KN: b(n,k) = B[k*ldb + n] (ldb >= n)
+ *   C        : device pointer; C[m*ldc + n] (ldc >= n); elements between rows are left
+ *              untouched
+ *   lda, ldb, ldc are in elements and at least 1.  cfg as for gemm_ex (NULL = table);
+ *   the configurations are those tgemm_list_configs_ex reports for the two layouts.
+ * Returns a tgemm_status.
+ */
+int gemm_strided(int dtype, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
+                 int a_layout, const void* B, int64_t ldb, int b_layout, void* C,
+                 int64_t ldc, const tgemm_config* cfg, void* stream);
+
 /* The configuration the table picks for this problem (written to *out).  Host-only: it
  * touches no device.  Same argument checks as gemm_ex on the sizes, dtype and layout;
  * `aligned` says whether the operands will meet the fast-kernel alignment rules. */
@@ -127,6 +158,13 @@ int tgemm_query_config(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
  * `capacity` entries to `out` (which may be NULL when capacity is 0) and returns the
  * total count, or a negative status.  Host-only. */
 int tgemm_list_configs(int dtype, int b_layout, tgemm_config* out, int capacity);
+
+/* tgemm_query_config and tgemm_list_configs for either storage of A (tgemm_a_layout);
+ * the functions above answer for TGEMM_A_MK. */
+int tgemm_query_config_ex(int dtype, int64_t m, int64_t n, int64_t k, int a_layout,
+                          int b_layout, int aligned, tgemm_config* out);
+int tgemm_list_configs_ex(int dtype, int a_layout, int b_layout, tgemm_config* out,
+                          int capacity);
 
 /* A static, human-readable name for a status code. */
 const char* tgemm_status_string(int status);

@@ -115,3 +115,42 @@ def test_list_configs(lib):
                     # the LDS ring must fit the 160 KiB of one compute unit
                     assert c.stages * (c.block_m + c.block_n) * c.block_k * 2 <= 160 * 1024
     assert lib.tgemm_list_configs(5, 0, None, 0) == -1
+
+
+def test_strided_argument_errors(lib):
+    f = lib.gemm_strided
+    A, B, C = FAKE, FAKE + (1 << 20), FAKE + (1 << 21)
+    ok = dict(lda=64, ldb=64, ldc=64)
+
+    def call(m=32, n=32, k=32, lda=64, a_layout=0, ldb=64, b_layout=0, ldc=64, a=A, b=B, c=C):
+        return f(1, m, n, k, a, lda, a_layout, b, ldb, b_layout, c, ldc, None, None)
+
+    # leading dimensions below the row length, or below 1
+    assert call(lda=31) == -1 and call(ldb=31) == -1 and call(ldc=31) == -1
+    assert call(a_layout=1, m=48, lda=40) == -1           # [K,M]: lda >= m
+    assert call(b_layout=1, n=48, ldb=40) == -1           # [K,N]: ldb >= n
+    assert call(m=0, lda=0) == -1                         # >= 1 even when empty
+    # unknown layouts
+    assert call(a_layout=2) == -1 and call(b_layout=7) == -1
+    # C's span overlapping A's: rows 64 apart reach into A
+    assert call(c=A + 2 * 64 * 31) == -4
+    # spans past 2^31 elements
+    assert call(m=1 << 16, lda=1 << 16) == -5
+    # empty products are no-ops
+    assert call(m=0, a=0, b=0, c=0) == 0
+
+
+def test_strided_query_and_list(lib):
+    for a_layout in (tgemm.A_MK, tgemm.A_KM):
+        for b_layout in (tgemm.B_NK, tgemm.B_KN):
+            cfgs = tgemm.list_configs(tgemm.BF16, b_layout, a_layout)
+            kinds = {c.kernel for c in cfgs}
+            assert {tgemm.KERNEL_GENERIC, tgemm.KERNEL_TILED, tgemm.KERNEL_PINGPONG} <= kinds
+            big = tgemm.query_config(tgemm.BF16, 8192, 8192, 8192, b_layout, True, a_layout)
+            assert big.kernel == tgemm.KERNEL_PINGPONG
+            listed = {tuple(sorted(c.as_dict().items())) for c in cfgs}
+            assert tuple(sorted(big.as_dict().items())) in listed
+    # the skinny kernel reads A [M,K] and B [N,K] only
+    assert tgemm.query_config(tgemm.BF16, 64, 8192, 8192, tgemm.B_NK, True,
+                              tgemm.A_KM).kernel != tgemm.KERNEL_SKINNY
+    assert lib.tgemm_list_configs_ex(1, 2, 0, None, 0) == -1

@@ -1,0 +1,135 @@
+"""GPU parity of the general product (gemm_strided): A stored [M,K] or [K,M], B stored
+[N,K] or [K,N], each operand and C with a leading dimension larger than its row.  The
+padding between rows holds NaN patterns, so a kernel that read it would poison C, and C's
+own padding must come back untouched.  The oracle sees the same logical operands."""
+import numpy as np
+import pytest
+
+from tests.gpu_util import assert_parity, from_dev, require_gpu, say, tdtype, torch
+from tiled_dense_gemm_major_amd.inputs import BF16, B_KN, B_NK, F16, Stream
+
+pytestmark = pytest.mark.gpu
+
+A_MK, A_KM = 0, 1
+POISON = 0x7E00          # a NaN in both fp16 and bf16 (and the C sentinel)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _store(logical, transposed, pad):
+    """The storage of a logical [R, K] operand: [R, K + pad] (row-major, K contiguous) or
+    [K, R + pad] (transposed), padding filled with POISON.  Returns (storage, ld)."""
+    R, K = logical.shape
+    if transposed:
+        st = np.full((K, R + pad), POISON, dtype=np.uint16)
+        st[:, :R] = logical.T
+        return st, R + pad
+    st = np.full((R, K + pad), POISON, dtype=np.uint16)
+    st[:, :K] = logical
+    return st, K + pad
+
+
+def run_strided(dtype, A, Bn, a_layout, b_layout, pads=(8, 16, 24), config=None):
+    """C = A x Bn^T (logical A [M,K], Bn [N,K]) through gemm_strided with the given
+    storages; returns C's bits and checks that its padding was not written."""
+    from tiled_dense_gemm_major_amd import tgemm
+    M, K = A.shape
+    N = Bn.shape[0]
+    a_st, lda = _store(A, a_layout == A_KM, pads[0])
+    b_st, ldb = _store(Bn, b_layout == B_KN, pads[1])
+    ldc = N + pads[2]
+    Ad = torch.from_numpy(a_st.view(np.int16)).cuda().view(tdtype(dtype))
+    Bd = torch.from_numpy(b_st.view(np.int16)).cuda().view(tdtype(dtype))
+    Cd = torch.full((max(M, 1), ldc), POISON, dtype=torch.int16, device="cuda")
+    tgemm.gemm_strided(dtype, M, N, K, Ad, lda, a_layout, Bd, ldb, b_layout,
+                       Cd.view(tdtype(dtype)), ldc, config)
+    torch.cuda.synchronize()
+    c = from_dev(Cd)
+    assert np.all(c[:, N:] == POISON), "C padding was written"
+    return c[:M, :N]
+
+
+def _inputs(dtype, M, N, K, seed):
+    s = Stream(seed)
+    return s.matrix((M, K), dtype, "uniform"), s.matrix((N, K), dtype, "uniform")
+
+
+def _int_bits(dtype, arr):
+    from tiled_dense_gemm_major_amd.inputs import round_to_bf16_bits, round_to_f16_bits
+    f = round_to_f16_bits if dtype == F16 else round_to_bf16_bits
+    return f(np.asarray(arr, dtype=np.float64))
+
+
+LAYOUTS = [(A_MK, B_NK), (A_MK, B_KN), (A_KM, B_NK), (A_KM, B_KN)]
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("a_layout,b_layout", LAYOUTS)
+def test_strided_every_config(dev, orc, dtype, a_layout, b_layout):
+    from tiled_dense_gemm_major_amd import tgemm
+    M, N, K = 600, 536, 328         # ragged against every tile; multiples of 8
+    A, Bn = _inputs(dtype, M, N, K, 300 + 4 * dtype + 2 * a_layout + b_layout)
+    want = orc.gemm(dtype, A, Bn, B_NK)
+    for cfg in tgemm.list_configs(dtype, b_layout, a_layout):
+        say(f"strided {dtype} A{a_layout} B{b_layout} {cfg.as_dict()}")
+        got = run_strided(dtype, A, Bn, a_layout, b_layout, config=cfg)
+        assert_parity(orc, dtype, K, got, want, str(cfg.as_dict()))
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("a_layout,b_layout", LAYOUTS)
+def test_strided_exact_ints_bitwise(dev, orc, dtype, a_layout, b_layout):
+    from tiled_dense_gemm_major_amd import tgemm
+    rng = np.random.default_rng(23 + a_layout + 2 * b_layout)
+    M, N, K = 520, 392, 264
+    A = _int_bits(dtype, rng.integers(-2, 3, (M, K)))
+    Bn = _int_bits(dtype, rng.integers(-2, 3, (N, K)))
+    want = orc.gemm(dtype, A, Bn, B_NK)
+    for cfg in tgemm.list_configs(dtype, b_layout, a_layout):
+        say(f"strided exact {dtype} A{a_layout} B{b_layout} {cfg.as_dict()}")
+        got = run_strided(dtype, A, Bn, a_layout, b_layout, pads=(16, 8, 8), config=cfg)
+        assert np.array_equal(got, want), str(cfg.as_dict())
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("a_layout,b_layout", LAYOUTS)
+@pytest.mark.parametrize("shape,pads", [((77, 51, 37), (3, 5, 7)),      # nothing x8
+                                        ((128, 128, 128), (1, 0, 0)),   # lda odd
+                                        ((128, 128, 128), (0, 0, 3)),   # ldc odd
+                                        ((100, 64, 64), (0, 0, 0)),     # M % 8 != 0
+                                        ((1, 1, 1), (0, 0, 0))])
+def test_strided_table_choice_any_alignment(dev, orc, dtype, a_layout, b_layout, shape,
+                                            pads):
+    M, N, K = shape
+    A, Bn = _inputs(dtype, M, N, K, 77 + M + sum(pads))
+    say(f"strided table {dtype} A{a_layout} B{b_layout} {shape} pads {pads}")
+    got = run_strided(dtype, A, Bn, a_layout, b_layout, pads=pads)
+    assert_parity(orc, dtype, K, got, orc.gemm(dtype, A, Bn, B_NK), str((shape, pads)))
+
+
+@pytest.mark.parametrize("a_layout,b_layout", LAYOUTS)
+def test_strided_large_table_choice(dev, orc, a_layout, b_layout):
+    """A shape the ping-pong kernel takes, checked on sampled entries."""
+    from tests.gpu_util import sample_positions
+    from tiled_dense_gemm_major_amd import tgemm
+    dtype = BF16
+    M, N, K = 3584, 4096, 1000
+    assert tgemm.query_config(dtype, M, N, K, b_layout, True, a_layout).kernel == \
+        tgemm.KERNEL_PINGPONG
+    A, Bn = _inputs(dtype, M, N, K, 900 + a_layout + 2 * b_layout)
+    say(f"strided large A{a_layout} B{b_layout} {M}x{N}x{K}")
+    got = run_strided(dtype, A, Bn, a_layout, b_layout, pads=(64, 8, 256))
+    rows, cols = sample_positions(M, N, 2000, 5)
+    want, _ = orc.gemm_entries(dtype, A, Bn, B_NK, rows, cols)
+    assert_parity(orc, dtype, K, got[rows, cols], want, "large")
+
+
+def test_strided_packed_matches_gemm_ex(dev, orc):
+    """With leading dimensions equal to the row lengths, gemm_strided is gemm_ex."""
+    from tests.gpu_util import run
+    A, Bn = _inputs(BF16, 300, 264, 200, 5)
+    got = run_strided(BF16, A, Bn, A_MK, B_NK, pads=(0, 0, 0))
+    assert np.array_equal(got, run(BF16, A, Bn, B_NK))

@@ -6,9 +6,9 @@ package loads nothing: the library is opened on first use and a missing library 
 """
 from __future__ import annotations
 
-_BINDING = ("gemm_f16", "gemm_bf16", "gemm_ex", "gemm", "query_config", "list_configs",
-            "status_string", "version", "Config", "TGemmError", "F16", "BF16", "B_NK",
-            "B_KN", "KERNEL_GENERIC", "KERNEL_TILED", "KERNEL_SKINNY", "KERNEL_DMA",
+_BINDING = ("gemm_f16", "gemm_bf16", "gemm_ex", "gemm_strided", "gemm", "query_config",
+            "list_configs", "status_string", "version", "Config", "TGemmError", "F16", "BF16",
+            "B_NK", "B_KN", "A_MK", "A_KM", "KERNEL_GENERIC", "KERNEL_TILED", "KERNEL_SKINNY", "KERNEL_DMA",
             "KERNEL_PINGPONG")
 
 

@@ -28,7 +28,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 enum { DT_F16 = 0, DT_BF16 = 1 };
-enum { LAYOUT_NK = 0, LAYOUT_KN = 1 };
+enum { LAYOUT_NK = 0, LAYOUT_KN = 1 };   // B stored [N,K] (K contiguous) or [K,N]
+enum { LAYOUT_MK = 0, LAYOUT_KM = 1 };   // A stored [M,K] (K contiguous) or [K,M]
 
 // ------------------------------------------------------------------------------------
 // Matrix-core step: D(32x32, fp32) += S0(32 x 16) * S1(16 x 32).  Lane l supplies, for
@@ -131,6 +132,13 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
                                              (int)kRsrcWord3);
 }
 
+// Bytes spanned by an operand stored as `rows` rows of `cols` elements, `ld` elements
+// apart (the host keeps this within 2^31).
+__device__ __forceinline__ uint32_t span_bytes(int rows, int cols, int ld) {
+    return rows > 0 && cols > 0 ? ((uint32_t)(rows - 1) * (uint32_t)ld + (uint32_t)cols) * 2u
+                                : 0u;
+}
+
 __device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
@@ -158,11 +166,11 @@ __device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t voff, uint32_t soff) 
 // Steps past the last tile run with out-of-range loads (zeros), so the loop body has
 // no branches.
 // ------------------------------------------------------------------------------------
-template <int DT, int LAYOUT, int BM, int BN, int BK, int WM, int WN>
+template <int DT, int ALAYOUT, int LAYOUT, int BM, int BN, int BK, int WM, int WN>
 __global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64),
                                amdgpu_waves_per_eu(1, 1)))
 gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
-           int N, int K, int grid_m, int grid_n, int group_m) {
+           int N, int K, int lda, int ldb, int ldc, int grid_m, int grid_n, int group_m) {
     constexpr int NT = WM * WN * 64;
     constexpr int KC = BK / 8;              // 16-byte chunks in one tile row
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -171,13 +179,18 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
     constexpr int A_ELEMS = BM * BK;
     constexpr int STAGE = (BM + BN) * BK;   // elements of one LDS stage (A then B)
     constexpr int RS = NT / KC;             // rows between the chunks one thread loads
-    constexpr int A_LD = BM / RS;           // A chunks per thread
+    // Per thread: A_LD / B_LD 16-byte chunks of a K-contiguous operand, or the 8 rows of
+    // one 8x8 block of an operand stored with K as its row index ([K,M] A, [K,N] B).
+    constexpr int A_LD = (ALAYOUT == LAYOUT_MK) ? BM / RS : 8;
     constexpr int B_LD = (LAYOUT == LAYOUT_NK) ? BN / RS : 8;
-    constexpr int KN_BLK = KC * (BN / 8);   // [K,N] B: 8x8 blocks per tile (one per thread)
+    constexpr int KM_BLK = KC * (BM / 8);   // 8x8 blocks of a [K,M] A tile
+    constexpr int KN_BLK = KC * (BN / 8);   // 8x8 blocks of a [K,N] B tile
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(BK % 32 == 0 && NT % KC == 0, "BK must give an even number of substeps");
     static_assert((NT / 16) % KC == 0, "a thread's rows must share one swizzle");
-    static_assert(BM % RS == 0 && (LAYOUT == LAYOUT_KN || BN % RS == 0), "bad load split");
+    static_assert((ALAYOUT == LAYOUT_KM || BM % RS == 0) &&
+                  (LAYOUT == LAYOUT_KN || BN % RS == 0), "bad load split");
+    static_assert(ALAYOUT == LAYOUT_MK || KM_BLK <= NT, "one 8x8 [K,M] block per thread");
     static_assert(LAYOUT == LAYOUT_NK || KN_BLK <= NT, "one 8x8 [K,N] block per thread");
 
     __shared__ __attribute__((aligned(16))) u16 lds[2 * STAGE];
@@ -189,91 +202,110 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
     const int wm = wave / WN, wn = wave % WN;
     const int nk = (K + BK - 1) / BK;
 
-    const rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
-    const rsrc_t rb = make_rsrc(B, (uint32_t)N * (uint32_t)K * 2u);
+    const rsrc_t ra = ALAYOUT == LAYOUT_MK ? make_rsrc(A, span_bytes(M, K, lda))
+                                           : make_rsrc(A, span_bytes(K, M, lda));
+    const rsrc_t rb = LAYOUT == LAYOUT_NK ? make_rsrc(B, span_bytes(N, K, ldb))
+                                          : make_rsrc(B, span_bytes(K, N, ldb));
 
     // ---- global -> register addressing (byte offsets; the K position goes in soffset) --
     const int lc = tid % KC;                 // this thread's chunk column (row-major loads)
     const int lr = tid / KC;                 // its first row; the others follow every RS
-    uint32_t a_off[A_LD];
+    // For an operand stored with K as its row index, thread tid loads the 8x8 block
+    // (k = 8*kb .. +7, row r0 + 8*rb .. +7); its 8 rows of the tile lie inside the
+    // operand or outside it together (the row count is a multiple of 8).
+    const int t_kb = tid % KC, t_rb = tid / KC;
+
+    uint32_t a_off[ALAYOUT == LAYOUT_MK ? A_LD : 1];
+    int a_lds;
+    bool km_live = true;
+    if constexpr (ALAYOUT == LAYOUT_MK) {
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-        const int r = m0 + lr + i * RS;
-        a_off[i] = r < M ? (uint32_t)(r * K + lc * 8) * 2u : kOutOfRange;
+        for (int i = 0; i < A_LD; ++i) {
+            const int r = m0 + lr + i * RS;
+            a_off[i] = r < M ? (uint32_t)(r * lda + lc * 8) * 2u : kOutOfRange;
+        }
+        a_lds = lr * BK + ((lc ^ swz<KC>(lr)) * 8);
+    } else {
+        km_live = (tid < KM_BLK) && (m0 + t_rb * 8 < M);
+        a_off[0] = ((uint32_t)(t_kb * 8) * (uint32_t)lda + (uint32_t)(m0 + t_rb * 8)) * 2u;
+        a_lds = (t_rb * 8) * BK;
     }
-    const int a_lds = lr * BK + ((lc ^ swz<KC>(lr)) * 8);
 
     uint32_t b_off[LAYOUT == LAYOUT_NK ? B_LD : 1];
     int b_lds;
-    const int kn_kb = tid % KC, kn_nb = tid / KC;
     bool kn_live = true;
     if constexpr (LAYOUT == LAYOUT_NK) {
 #pragma unroll
         for (int i = 0; i < B_LD; ++i) {
             const int r = n0 + lr + i * RS;
-            b_off[i] = r < N ? (uint32_t)(r * K + lc * 8) * 2u : kOutOfRange;
+            b_off[i] = r < N ? (uint32_t)(r * ldb + lc * 8) * 2u : kOutOfRange;
         }
         b_lds = A_ELEMS + lr * BK + ((lc ^ swz<KC>(lr)) * 8);
     } else {
-        // Thread tid loads the 8x8 block (k = 8*kn_kb .. +7, n = n0 + 8*kn_nb .. +7);
-        // its 8 columns lie inside [0, N) or outside it together (N % 8 == 0).
-        kn_live = (tid < KN_BLK) && (n0 + kn_nb * 8 < N);
-        b_off[0] = ((uint32_t)(kn_kb * 8) * (uint32_t)N + (uint32_t)(n0 + kn_nb * 8)) * 2u;
-        b_lds = A_ELEMS + (kn_nb * 8) * BK;
+        kn_live = (tid < KN_BLK) && (n0 + t_rb * 8 < N);
+        b_off[0] = ((uint32_t)(t_kb * 8) * (uint32_t)ldb + (uint32_t)(n0 + t_rb * 8)) * 2u;
+        b_lds = A_ELEMS + (t_rb * 8) * BK;
     }
 
     u32x4 a_reg[A_LD];
     u32x4 b_reg[B_LD];
 
-    auto gload_a = [&](int kt) {
-        const bool live = kt < nk;
-        const int k0 = live ? kt * BK : 0;
-        const bool ok = live && (k0 + lc * 8 < K);
-#pragma unroll
-        for (int i = 0; i < A_LD; ++i)
-            a_reg[i] = load16(ra, ok ? a_off[i] : kOutOfRange, (uint32_t)k0 * 2u);
-    };
-    // One part of the B loads of tile kt: chunk i (NK) or k-row i of the 8x8 block (KN).
-    auto gload_b_part = [&](int kt, auto ic) {
+    // One part of an operand's loads of tile kt: chunk i (K contiguous) or k row i of the
+    // thread's 8x8 block (K as the row index).
+    auto gload_part = [&](u32x4* reg, rsrc_t rs, const uint32_t* off, bool kmajor,
+                          bool t_live, int ld, int kt, auto ic) {
         constexpr int i = decltype(ic)::value;
         const bool live = kt < nk;
         const int k0 = live ? kt * BK : 0;
-        if constexpr (LAYOUT == LAYOUT_NK) {
+        if (kmajor) {
             const bool ok = live && (k0 + lc * 8 < K);
-            b_reg[i] = load16(rb, ok ? b_off[i] : kOutOfRange, (uint32_t)k0 * 2u);
+            reg[i] = load16(rs, ok ? off[i] : kOutOfRange, (uint32_t)k0 * 2u);
         } else {
-            const bool ok = live && kn_live && (k0 + kn_kb * 8 + i < K);
-            b_reg[i] = load16(rb, ok ? b_off[0] + (uint32_t)i * (uint32_t)N * 2u : kOutOfRange,
-                              (uint32_t)k0 * (uint32_t)N * 2u);
+            const bool ok = live && t_live && (k0 + t_kb * 8 + i < K);
+            reg[i] = load16(rs, ok ? off[0] + (uint32_t)i * (uint32_t)ld * 2u : kOutOfRange,
+                            (uint32_t)k0 * (uint32_t)ld * 2u);
         }
+    };
+    auto gload_a_part = [&](int kt, auto ic) {
+        gload_part(a_reg, ra, a_off, ALAYOUT == LAYOUT_MK, km_live, lda, kt, ic);
+    };
+    auto gload_b_part = [&](int kt, auto ic) {
+        gload_part(b_reg, rb, b_off, LAYOUT == LAYOUT_NK, kn_live, ldb, kt, ic);
+    };
+    auto gload_a = [&](int kt) {
+        static_for<0, A_LD>([&](auto i) { gload_a_part(kt, i); });
     };
     auto gload_b = [&](int kt) {
         static_for<0, B_LD>([&](auto i) { gload_b_part(kt, i); });
     };
-    auto swrite_a = [&](u16* st) {
-#pragma unroll
-        for (int i = 0; i < A_LD; ++i)
-            *reinterpret_cast<u32x4*>(st + a_lds + i * RS * BK) = a_reg[i];
-    };
-    // One part of the B tile's LDS write: chunk i (NK), or row n = i of the transposed
-    // 8x8 block (KN: b_reg[j] holds n = 0..7 at k = j; row n receives k = 0..7).
-    auto swrite_b_part = [&](u16* st, auto ic) {
+    // One part of an operand tile's LDS write: chunk i (K contiguous), or tile row
+    // 8*rb + i of the transposed 8x8 block (reg[j] holds rows 0..7 at k = j; row i
+    // receives k = 0..7).
+    auto swrite_part = [&](u16* st, const u32x4* reg, int lds_at, bool kmajor, int blocks,
+                           auto ic) {
         constexpr int i = decltype(ic)::value;
-        if constexpr (LAYOUT == LAYOUT_NK) {
-            *reinterpret_cast<u32x4*>(st + b_lds + i * RS * BK) = b_reg[i];
-        } else {
-            if (tid < KN_BLK) {
-                constexpr int p = i >> 1;
-                constexpr uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-                u32x4 o;
-                o[0] = __builtin_amdgcn_perm(b_reg[1][p], b_reg[0][p], sel);
-                o[1] = __builtin_amdgcn_perm(b_reg[3][p], b_reg[2][p], sel);
-                o[2] = __builtin_amdgcn_perm(b_reg[5][p], b_reg[4][p], sel);
-                o[3] = __builtin_amdgcn_perm(b_reg[7][p], b_reg[6][p], sel);
-                *reinterpret_cast<u32x4*>(st + b_lds + i * BK +
-                                          ((kn_kb ^ swz<KC>(kn_nb * 8 + i)) * 8)) = o;
-            }
+        if (kmajor) {
+            *reinterpret_cast<u32x4*>(st + lds_at + i * RS * BK) = reg[i];
+        } else if (tid < blocks) {
+            constexpr int p = i >> 1;
+            constexpr uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+            u32x4 o;
+            o[0] = __builtin_amdgcn_perm(reg[1][p], reg[0][p], sel);
+            o[1] = __builtin_amdgcn_perm(reg[3][p], reg[2][p], sel);
+            o[2] = __builtin_amdgcn_perm(reg[5][p], reg[4][p], sel);
+            o[3] = __builtin_amdgcn_perm(reg[7][p], reg[6][p], sel);
+            *reinterpret_cast<u32x4*>(st + lds_at + i * BK +
+                                      ((t_kb ^ swz<KC>(t_rb * 8 + i)) * 8)) = o;
         }
+    };
+    auto swrite_a_part = [&](u16* st, auto ic) {
+        swrite_part(st, a_reg, a_lds, ALAYOUT == LAYOUT_MK, KM_BLK, ic);
+    };
+    auto swrite_b_part = [&](u16* st, auto ic) {
+        swrite_part(st, b_reg, b_lds, LAYOUT == LAYOUT_NK, KN_BLK, ic);
+    };
+    auto swrite_a = [&](u16* st) {
+        static_for<0, A_LD>([&](auto i) { swrite_a_part(st, i); });
     };
     auto swrite_b = [&](u16* st) {
         static_for<0, B_LD>([&](auto i) { swrite_b_part(st, i); });
@@ -338,13 +370,10 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
                             read_frag(nxt, 0, 0, std::integral_constant<int, O>{});
                     } else if constexpr (O < NR + NWA) {
                         constexpr int i = O - NR;
-                        *reinterpret_cast<u32x4*>(nxt + a_lds + i * RS * BK) = a_reg[i];
+                        swrite_a_part(nxt, std::integral_constant<int, i>{});
                     } else if constexpr (O < NR + 2 * NWA) {
                         constexpr int i = O - NR - NWA;
-                        const bool live = kt2 < nk;
-                        const int k0 = live ? kt2 * BK : 0;
-                        const bool ok = live && (k0 + lc * 8 < K);
-                        a_reg[i] = load16(ra, ok ? a_off[i] : kOutOfRange, (uint32_t)k0 * 2u);
+                        gload_a_part(kt2, std::integral_constant<int, i>{});
                     } else if constexpr (O < NR + 2 * NWA + NWB) {
                         constexpr int i = O - NR - 2 * NWA;
                         swrite_b_part(nxt, std::integral_constant<int, i>{});
@@ -388,7 +417,7 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
                 v[0] = pack2<DT>(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
                 v[1] = pack2<DT>(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
                 if (m < M && n < N)
-                    *reinterpret_cast<u32x2*>(C + (size_t)m * N + n) = v;
+                    *reinterpret_cast<u32x2*>(C + (size_t)m * ldc + n) = v;
             }
         }
     }
@@ -430,7 +459,7 @@ template <int DT, int BM, int BN, int BK, int WM, int WN, int STAGES>
 __global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64),
                                amdgpu_waves_per_eu(1, 1)))
 gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
-         int N, int K, int grid_m, int grid_n, int group_m) {
+         int N, int K, int lda, int ldb, int ldc, int grid_m, int grid_n, int group_m) {
     constexpr int NW = WM * WN;
     constexpr int KC = BK / 8;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -457,8 +486,8 @@ gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__
     const int wm = wave / WN, wn = wave % WN;
     const int nk = (K + BK - 1) / BK;
 
-    const rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
-    const rsrc_t rb = make_rsrc(B, (uint32_t)N * (uint32_t)K * 2u);
+    const rsrc_t ra = make_rsrc(A, span_bytes(M, K, lda));
+    const rsrc_t rb = make_rsrc(B, span_bytes(N, K, ldb));
 
     // Lane l lands in row l / KC of a 1 KiB block at physical chunk l % KC; it fetches
     // the logical chunk that the swizzle of that row (block base + l / KC) puts there.
@@ -469,13 +498,13 @@ gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__
     for (int i = 0; i < A_LD; ++i) {
         const int row = (wave * A_LD + i) * ROWS + prow;
         a_kc[i] = ((lane % KC) ^ swz<KC>(row)) * 8;
-        a_off[i] = m0 + row < M ? (uint32_t)((m0 + row) * K + a_kc[i]) * 2u : kOutOfRange;
+        a_off[i] = m0 + row < M ? (uint32_t)((m0 + row) * lda + a_kc[i]) * 2u : kOutOfRange;
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
         const int row = (wave * B_LD + i) * ROWS + prow;
         b_kc[i] = ((lane % KC) ^ swz<KC>(row)) * 8;
-        b_off[i] = n0 + row < N ? (uint32_t)((n0 + row) * K + b_kc[i]) * 2u : kOutOfRange;
+        b_off[i] = n0 + row < N ? (uint32_t)((n0 + row) * ldb + b_kc[i]) * 2u : kOutOfRange;
     }
     auto stage_ptr = [&](int t) { return lds + (t % STAGES) * STAGE; };
     // Load i (< LD) of tile kt into its stage.
@@ -569,7 +598,7 @@ gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__
                 v[0] = pack2<DT>(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
                 v[1] = pack2<DT>(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
                 if (m < M && n < N)
-                    *reinterpret_cast<u32x2*>(C + (size_t)m * N + n) = v;
+                    *reinterpret_cast<u32x2*>(C + (size_t)m * ldc + n) = v;
             }
         }
     }
@@ -608,11 +637,11 @@ __device__ __forceinline__ void wait_lgkm_sync() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int DT, int LAYOUT, int BM, int BN, int BK, int STAGES>
+template <int DT, int ALAYOUT, int LAYOUT, int BM, int BN, int BK, int STAGES>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512),
                                amdgpu_waves_per_eu(2, 2)))
 gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
-              int N, int K, int grid_m, int grid_n, int group_m) {
+              int N, int K, int lda, int ldb, int ldc, int grid_m, int grid_n, int group_m) {
     constexpr int KC = BK / 8;
     constexpr int WTM = BM / 2, WTN = BN / 4;     // one wave's block of C
     constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -624,6 +653,7 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
     static_assert((BM / 8) % ROWS == 0 && (BN / 4) % ROWS == 0, "bad load split");
     static_assert(STAGES >= 2 && STAGES * STAGE * 2 <= 160 * 1024, "LDS");
     static_assert(LAYOUT == LAYOUT_NK || BN == 256, "B [K,N] path: 256 columns");
+    static_assert(ALAYOUT == LAYOUT_MK || BM == 256, "A [K,M] path: 256 rows");
 
     __shared__ __attribute__((aligned(1024))) u16 lds[STAGES * STAGE];
 
@@ -635,8 +665,10 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
     const int grp = wave >> 2, wc = wave & 3;
     const int nk = (K + BK - 1) / BK;
 
-    const rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
-    const rsrc_t rb = make_rsrc(B, (uint32_t)N * (uint32_t)K * 2u);
+    const rsrc_t ra = ALAYOUT == LAYOUT_MK ? make_rsrc(A, span_bytes(M, K, lda))
+                                           : make_rsrc(A, span_bytes(K, M, lda));
+    const rsrc_t rb = LAYOUT == LAYOUT_NK ? make_rsrc(B, span_bytes(N, K, ldb))
+                                          : make_rsrc(B, span_bytes(K, N, ldb));
 
     // The rows this wave loads: group 1 wave c the A rows [c*BM/8, (c+1)*BM/8); group 0
     // wave c the A rows [BM/2 + c*BM/8, ...) and the B rows [c*BN/4, (c+1)*BN/4).  They
@@ -653,16 +685,31 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
     const int kc_odd = ((lane % KC) ^ swz<KC>(ROWS + prow)) * 8;
     // A tile past the end is loaded as zeros (every lane out of range) into a stage no
     // one reads again, which keeps the number of loads in flight static.
+    // A [K,M] tiles are kept as two halves, rows [0, BM/2) and [BM/2, BM) of the tile,
+    // each BK k rows of BM/2 columns (256-byte rows) with 16-byte chunks swizzled by
+    // 4*(k % 4); group 1 loads the first half, group 0 the second, 4 k rows per load.
+    constexpr int HALF = (BM / 2) * BK;
+    const int a_half = grp ? 0 : 1;
     auto dma_a = [&](int kt, auto ic) {            // block i of this wave's A rows
         constexpr int i = decltype(ic)::value;
         const bool live = kt < nk;
         const int k0 = live ? kt * BK : 0;
         u16* st = lds + (kt % STAGES) * STAGE;
-        const int kc = (i & 1) ? kc_odd : kc_even;
-        const int r = m0 + a_row + i * ROWS + prow;
-        const bool ok = live && r < M && k0 + kc < K;
-        dma16<0>(ra, st + (a_row + i * ROWS) * BK,
-                 ok ? (uint32_t)(r * K + kc) * 2u : kOutOfRange, (uint32_t)k0 * 2u);
+        if constexpr (ALAYOUT == LAYOUT_MK) {
+            const int kc = (i & 1) ? kc_odd : kc_even;
+            const int r = m0 + a_row + i * ROWS + prow;
+            const bool ok = live && r < M && k0 + kc < K;
+            dma16<0>(ra, st + (a_row + i * ROWS) * BK,
+                     ok ? (uint32_t)(r * lda + kc) * 2u : kOutOfRange, (uint32_t)k0 * 2u);
+        } else {
+            const int kr = wc * (BK / 4) + 4 * i + (lane >> 4);
+            const int cl = (lane & 15) ^ (4 * (kr & 3));
+            const int m = m0 + a_half * (BM / 2) + 8 * cl;
+            const bool ok = live && m < M && k0 + kr < K;
+            dma16<0>(ra, st + a_half * HALF + (wc * (BK / 4) + 4 * i) * (BM / 2),
+                     ok ? (uint32_t)(kr * lda + m) * 2u : kOutOfRange,
+                     (uint32_t)k0 * (uint32_t)lda * 2u);
+        }
     };
     // B [N,K]: the BN/4 rows of wave c's columns are read only by wave c of each group,
     // so each of the two waves loads half of them: group 0 the upper half in its memory
@@ -680,7 +727,7 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
             const int r = n0 + r0 + i * ROWS + prow;
             const bool ok = live && r < N && k0 + kc < K;
             dma16<0>(rb, st + A_ELEMS + (r0 + i * ROWS) * BK,
-                     ok ? (uint32_t)(r * K + kc) * 2u : kOutOfRange, (uint32_t)k0 * 2u);
+                     ok ? (uint32_t)(r * ldb + kc) * 2u : kOutOfRange, (uint32_t)k0 * 2u);
         } else {
             // the stage holds k rows of BN columns; a 1 KiB load fills two rows, lane l
             // row l / 32 at physical chunk l % 32, fetching the logical chunk that the
@@ -690,8 +737,8 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
             const int n = n0 + 8 * cl;
             const bool ok = live && n < N && k0 + kr < K;
             dma16<0>(rb, st + A_ELEMS + (wc * (BK / 4) + 2 * i) * BN,
-                     ok ? (uint32_t)(kr * N + n) * 2u : kOutOfRange,
-                     (uint32_t)k0 * (uint32_t)N * 2u);
+                     ok ? (uint32_t)(kr * ldb + n) * 2u : kOutOfRange,
+                     (uint32_t)k0 * (uint32_t)ldb * 2u);
         }
     };
     static_assert(B_BLK % 2 == 0 && (B_BLK / 2) % 2 == 0, "B halves keep the block parity");
@@ -718,16 +765,38 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
     // 4 x 16 block, and lane i receives column i of those 4 rows; lane groups 0/1 cover
     // columns 0-15/16-31 and groups 2/3 the same for the upper 8 k, so two reads (k and
     // k+4) give each lane its column's 8 consecutive k in MFMA operand order.
-    int kn_base[TN];
-    if constexpr (LAYOUT == LAYOUT_KN) {
+    // The same reads serve an A [K,M] half (rows of BM/2 columns).
+    int kn_base[TN], km_base[TM];
+    {
         const int g = lane >> 4, sl = lane & 15;
         const int kl = 8 * (g >> 1) + (sl >> 2);
+        if constexpr (LAYOUT == LAYOUT_KN) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = wc * WTN + 32 * j + 16 * (g & 1) + 4 * (sl & 3);
-            kn_base[j] = A_ELEMS + kl * BN + (((n >> 3) ^ (4 * (kl & 3))) << 3) + (n & 7);
+            for (int j = 0; j < TN; ++j) {
+                const int n = wc * WTN + 32 * j + 16 * (g & 1) + 4 * (sl & 3);
+                kn_base[j] = A_ELEMS + kl * BN + (((n >> 3) ^ (4 * (kl & 3))) << 3) + (n & 7);
+            }
+        }
+        if constexpr (ALAYOUT == LAYOUT_KM) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int m = 32 * i + 16 * (g & 1) + 4 * (sl & 3);   // inside the half
+                km_base[i] = grp * HALF + kl * (BM / 2) +
+                             (((m >> 3) ^ (4 * (kl & 3))) << 3) + (m & 7);
+            }
         }
     }
+    // two transposing reads, k rows kr and kr + 4 (row length RL), as one MFMA operand
+    auto read_tr = [&](const u16* p0, auto rlc) {
+        constexpr int RL = decltype(rlc)::value;
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * RL));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    };
     u32x4 fa[KS][TM], fb[KS][TN];
     // Operand read r of tile kt: the B operands first (group 1 frees its B rows as soon
     // as they are read), then A.
@@ -741,20 +810,18 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
             if constexpr (LAYOUT == LAYOUT_NK) {
                 fb[S][j] = *reinterpret_cast<const u32x4*>(st + b_row0 + j * 32 * BK + koff);
             } else {
-                typedef short s16x4 __attribute__((ext_vector_type(4)));
-                typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-                const u16* p0 = st + kn_base[j] + (16 * S) * BN;
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-                const s16x4 hi =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * BN));
-                const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-                const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-                fb[S][j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+                fb[S][j] = read_tr(st + kn_base[j] + (16 * S) * BN,
+                                   std::integral_constant<int, BN>{});
             }
         } else {
             constexpr int S = (r - NRB) / TM, i = (r - NRB) % TM;
-            const int koff = (((2 * S) | half) ^ xr) * 8;
-            fa[S][i] = *reinterpret_cast<const u32x4*>(st + a_row0 + i * 32 * BK + koff);
+            if constexpr (ALAYOUT == LAYOUT_MK) {
+                const int koff = (((2 * S) | half) ^ xr) * 8;
+                fa[S][i] = *reinterpret_cast<const u32x4*>(st + a_row0 + i * 32 * BK + koff);
+            } else {
+                fa[S][i] = read_tr(st + km_base[i] + (16 * S) * (BM / 2),
+                                   std::integral_constant<int, BM / 2>{});
+            }
         }
     };
     // A memory phase: the operand reads of tile kt with the first NL loads of this
@@ -855,7 +922,7 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
                 v[0] = pack2<DT>(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
                 v[1] = pack2<DT>(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
                 if (m < M && n < N)
-                    *reinterpret_cast<u32x2*>(C + (size_t)m * N + n) = v;
+                    *reinterpret_cast<u32x2*>(C + (size_t)m * ldc + n) = v;
             }
         }
     }
@@ -879,7 +946,7 @@ template <int DT, int MT, int D>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512),
                                amdgpu_waves_per_eu(2, 2)))
 gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
-            int N, int K) {
+            int N, int K, int lda, int ldb, int ldc) {
     constexpr int NW = 8, BN = 32, CK = 64, KC = CK / 8;
     constexpr int BM = MT * 32;
     constexpr int ROWS = BM + BN;                  // rows of one chunk: A rows, then B rows
@@ -894,8 +961,8 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5;
 
-    const rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
-    const rsrc_t rb = make_rsrc(B, (uint32_t)N * (uint32_t)K * 2u);
+    const rsrc_t ra = make_rsrc(A, span_bytes(M, K, lda));
+    const rsrc_t rb = make_rsrc(B, span_bytes(N, K, ldb));
     // load i covers chunk rows 8i .. 8i+7: lane l takes row 8i + l/8, 16-byte piece l%8
     const int lrow = lane >> 3, lpc = lane & 7;
     uint32_t off[LD];
@@ -903,9 +970,9 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
     for (int i = 0; i < LD; ++i) {
         const int r = 8 * i + lrow;
         if (r < BM)
-            off[i] = m0 + r < M ? (uint32_t)((m0 + r) * K + lpc * 8) * 2u : kOutOfRange;
+            off[i] = m0 + r < M ? (uint32_t)((m0 + r) * lda + lpc * 8) * 2u : kOutOfRange;
         else
-            off[i] = n0 + r - BM < N ? (uint32_t)((n0 + r - BM) * K + lpc * 8) * 2u
+            off[i] = n0 + r - BM < N ? (uint32_t)((n0 + r - BM) * ldb + lpc * 8) * 2u
                                      : kOutOfRange;
     }
     u16* wb = lds + wave * WBUF;
@@ -992,12 +1059,12 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
                     u32x2 v;
                     v[0] = pack2<DT>(sum[q], sum[q + 1]);
                     v[1] = pack2<DT>(sum[q + 2], sum[q + 3]);
-                    *reinterpret_cast<u32x2*>(C + (size_t)gm * N + n0 + nb + q) = v;
+                    *reinterpret_cast<u32x2*>(C + (size_t)gm * ldc + n0 + nb + q) = v;
                 }
             }
         } else {
             if (n0 + nb < N)
-                *reinterpret_cast<uint32_t*>(C + (size_t)gm * N + n0 + nb) =
+                *reinterpret_cast<uint32_t*>(C + (size_t)gm * ldc + n0 + nb) =
                     pack2<DT>(sum[0], sum[1]);
         }
     }
@@ -1007,10 +1074,10 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
 // The generic kernel: any alignment, any M, N, K.  64 x 64 tile, K step 16, 4 waves each
 // owning one 32 x 32 MFMA block; element-by-element masked loads into one LDS stage.
 // ------------------------------------------------------------------------------------
-template <int DT, int LAYOUT>
+template <int DT, int ALAYOUT, int LAYOUT>
 __global__ void __launch_bounds__(256)
 gemm_generic(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
-             int N, int K, int grid_m, int grid_n, int group_m) {
+             int N, int K, int lda, int ldb, int ldc, int grid_m, int grid_n, int group_m) {
     __shared__ __attribute__((aligned(16))) u16 As[64 * 16];
     __shared__ __attribute__((aligned(16))) u16 Bs[64 * 16];
     int tm, tn;
@@ -1023,19 +1090,24 @@ gemm_generic(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restri
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = tid + 256 * i;
-            {   // A: consecutive threads walk k (contiguous in memory)
+            // consecutive threads walk the contiguous index of each operand
+            if constexpr (ALAYOUT == LAYOUT_MK) {
                 const int r = e >> 4, kk = e & 15;
                 const int gm = m0 + r, gk = k0 + kk;
-                As[r * 16 + kk] = (gm < M && gk < K) ? A[(size_t)gm * K + gk] : (u16)0;
+                As[r * 16 + kk] = (gm < M && gk < K) ? A[(size_t)gm * lda + gk] : (u16)0;
+            } else {
+                const int r = e & 63, kk = e >> 6;
+                const int gm = m0 + r, gk = k0 + kk;
+                As[r * 16 + kk] = (gm < M && gk < K) ? A[(size_t)gk * lda + gm] : (u16)0;
             }
             if constexpr (LAYOUT == LAYOUT_NK) {
                 const int r = e >> 4, kk = e & 15;
                 const int gn = n0 + r, gk = k0 + kk;
-                Bs[r * 16 + kk] = (gn < N && gk < K) ? B[(size_t)gn * K + gk] : (u16)0;
-            } else {   // consecutive threads walk n (contiguous in memory)
+                Bs[r * 16 + kk] = (gn < N && gk < K) ? B[(size_t)gn * ldb + gk] : (u16)0;
+            } else {
                 const int r = e & 63, kk = e >> 6;
                 const int gn = n0 + r, gk = k0 + kk;
-                Bs[r * 16 + kk] = (gn < N && gk < K) ? B[(size_t)gk * N + gn] : (u16)0;
+                Bs[r * 16 + kk] = (gn < N && gk < K) ? B[(size_t)gk * ldb + gn] : (u16)0;
             }
         }
         __syncthreads();
@@ -1050,7 +1122,7 @@ gemm_generic(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restri
         for (int v = 0; v < 16; ++v) {
             const int n = n0 + wn * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
             if (n < N)
-                C[(size_t)m * N + n] = cvt1<DT>(acc[v]);
+                C[(size_t)m * ldc + n] = cvt1<DT>(acc[v]);
         }
     }
 }

@@ -14,13 +14,15 @@ namespace {
 using tgemm::u16;
 
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
-constexpr int kLdsBytes = 160 * 1024;
 
+// Leading dimensions are in elements: A[m*lda + k] ([M,K]) or A[k*lda + m] ([K,M]);
+// B[n*ldb + k] ([N,K]) or B[k*ldb + n] ([K,N]); C[m*ldc + n].
 typedef hipError_t (*launch_fn)(const void* A, const void* B, void* C, int M, int N, int K,
-                                int group_m, hipStream_t s);
+                                int lda, int ldb, int ldc, int group_m, hipStream_t s);
 
 struct Variant {
     int dtype;
+    int a_layout;
     int layout;
     tgemm_config cfg;
     launch_fn launch;
@@ -28,102 +30,103 @@ struct Variant {
 
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-template <int DT, int LAYOUT, int BM, int BN, int BK, int WM, int WN>
-hipError_t launch_tiled(const void* A, const void* B, void* C, int M, int N, int K,
-                        int group_m, hipStream_t s) {
+#define KARGS                                                                              \
+    static_cast<const u16*>(A), static_cast<const u16*>(B), static_cast<u16*>(C), M, N, K, \
+        lda, ldb, ldc
+
+template <int DT, int AL, int LAYOUT, int BM, int BN, int BK, int WM, int WN>
+hipError_t launch_tiled(const void* A, const void* B, void* C, int M, int N, int K, int lda,
+                        int ldb, int ldc, int group_m, hipStream_t s) {
     const int gm = cdiv(M, BM), gn = cdiv(N, BN);
-    hipLaunchKernelGGL((tgemm::gemm_tiled<DT, LAYOUT, BM, BN, BK, WM, WN>),
-                       dim3((unsigned)(gm * gn)), dim3(WM * WN * 64), 0, s,
-                       static_cast<const u16*>(A), static_cast<const u16*>(B),
-                       static_cast<u16*>(C), M, N, K, gm, gn, group_m);
+    hipLaunchKernelGGL((tgemm::gemm_tiled<DT, AL, LAYOUT, BM, BN, BK, WM, WN>),
+                       dim3((unsigned)(gm * gn)), dim3(WM * WN * 64), 0, s, KARGS, gm, gn,
+                       group_m);
     return hipGetLastError();
 }
 
 template <int DT, int BM, int BN, int BK, int WM, int WN, int STAGES>
-hipError_t launch_dma(const void* A, const void* B, void* C, int M, int N, int K, int group_m,
-                      hipStream_t s) {
+hipError_t launch_dma(const void* A, const void* B, void* C, int M, int N, int K, int lda,
+                      int ldb, int ldc, int group_m, hipStream_t s) {
     const int gm = cdiv(M, BM), gn = cdiv(N, BN);
     hipLaunchKernelGGL((tgemm::gemm_dma<DT, BM, BN, BK, WM, WN, STAGES>),
-                       dim3((unsigned)(gm * gn)), dim3(WM * WN * 64), 0, s,
-                       static_cast<const u16*>(A), static_cast<const u16*>(B),
-                       static_cast<u16*>(C), M, N, K, gm, gn, group_m);
+                       dim3((unsigned)(gm * gn)), dim3(WM * WN * 64), 0, s, KARGS, gm, gn,
+                       group_m);
     return hipGetLastError();
 }
 
-template <int DT, int LAYOUT, int BM, int BN, int BK, int S>
-hipError_t launch_pingpong(const void* A, const void* B, void* C, int M, int N, int K,
-                           int group_m, hipStream_t s) {
+template <int DT, int AL, int LAYOUT, int BM, int BN, int BK, int S>
+hipError_t launch_pingpong(const void* A, const void* B, void* C, int M, int N, int K, int lda,
+                           int ldb, int ldc, int group_m, hipStream_t s) {
     const int gm = cdiv(M, BM), gn = cdiv(N, BN);
-    hipLaunchKernelGGL((tgemm::gemm_pingpong<DT, LAYOUT, BM, BN, BK, S>), dim3((unsigned)(gm * gn)),
-                       dim3(512), 0, s, static_cast<const u16*>(A), static_cast<const u16*>(B),
-                       static_cast<u16*>(C), M, N, K, gm, gn, group_m);
+    hipLaunchKernelGGL((tgemm::gemm_pingpong<DT, AL, LAYOUT, BM, BN, BK, S>),
+                       dim3((unsigned)(gm * gn)), dim3(512), 0, s, KARGS, gm, gn, group_m);
     return hipGetLastError();
 }
 
 template <int DT, int MT, int D>
-hipError_t launch_skinny(const void* A, const void* B, void* C, int M, int N, int K, int,
-                         hipStream_t s) {
+hipError_t launch_skinny(const void* A, const void* B, void* C, int M, int N, int K, int lda,
+                         int ldb, int ldc, int, hipStream_t s) {
     hipLaunchKernelGGL((tgemm::gemm_skinny<DT, MT, D>),
                        dim3((unsigned)cdiv(N, 32), (unsigned)cdiv(M, MT * 32)), dim3(512), 0, s,
-                       static_cast<const u16*>(A), static_cast<const u16*>(B),
-                       static_cast<u16*>(C), M, N, K);
+                       KARGS);
     return hipGetLastError();
 }
 
-template <int DT, int LAYOUT>
-hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, int K,
-                          int group_m, hipStream_t s) {
+template <int DT, int AL, int LAYOUT>
+hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, int K, int lda,
+                          int ldb, int ldc, int group_m, hipStream_t s) {
     const int gm = cdiv(M, 64), gn = cdiv(N, 64);
-    hipLaunchKernelGGL((tgemm::gemm_generic<DT, LAYOUT>), dim3((unsigned)(gm * gn)), dim3(256),
-                       0, s, static_cast<const u16*>(A), static_cast<const u16*>(B),
-                       static_cast<u16*>(C), M, N, K, gm, gn, group_m);
+    hipLaunchKernelGGL((tgemm::gemm_generic<DT, AL, LAYOUT>), dim3((unsigned)(gm * gn)),
+                       dim3(256), 0, s, KARGS, gm, gn, group_m);
     return hipGetLastError();
 }
 
-#define TILED(DT, L, BM, BN, BK, WM, WN, G)                                               \
+#define TILED(DT, AL, L, BM, BN, BK, WM, WN, G)                                           \
     Variant {                                                                              \
-        DT, L, tgemm_config{TGEMM_KERNEL_TILED, BM, BN, BK, WM, WN, 2, G, 1},              \
-            &launch_tiled<DT, L, BM, BN, BK, WM, WN>                                       \
+        DT, AL, L, tgemm_config{TGEMM_KERNEL_TILED, BM, BN, BK, WM, WN, 2, G, 1},          \
+            &launch_tiled<DT, AL, L, BM, BN, BK, WM, WN>                                   \
     }
-#define GENERIC(DT, L)                                                                     \
+#define GENERIC(DT, AL, L)                                                                 \
     Variant {                                                                              \
-        DT, L, tgemm_config{TGEMM_KERNEL_GENERIC, 64, 64, 16, 2, 2, 1, 8, 1},              \
-            &launch_generic<DT, L>                                                         \
+        DT, AL, L, tgemm_config{TGEMM_KERNEL_GENERIC, 64, 64, 16, 2, 2, 1, 8, 1},          \
+            &launch_generic<DT, AL, L>                                                     \
     }
 #define DMA(DT, BM, BN, BK, WM, WN, ST, G)                                                 \
     Variant {                                                                              \
-        DT, 0, tgemm_config{TGEMM_KERNEL_DMA, BM, BN, BK, WM, WN, ST, G, 1},               \
+        DT, 0, 0, tgemm_config{TGEMM_KERNEL_DMA, BM, BN, BK, WM, WN, ST, G, 1},            \
             &launch_dma<DT, BM, BN, BK, WM, WN, ST>                                        \
     }
-#define PINGPONG(DT, L, BM, BN, BK, S, G)                                                  \
+#define PINGPONG(DT, AL, L, BM, BN, BK, S, G)                                              \
     Variant {                                                                              \
-        DT, L, tgemm_config{TGEMM_KERNEL_PINGPONG, BM, BN, BK, 2, 4, S, G, 1},             \
-            &launch_pingpong<DT, L, BM, BN, BK, S>                                         \
+        DT, AL, L, tgemm_config{TGEMM_KERNEL_PINGPONG, BM, BN, BK, 2, 4, S, G, 1},         \
+            &launch_pingpong<DT, AL, L, BM, BN, BK, S>                                     \
     }
 #define SKINNY(DT, MT, D)                                                                  \
     Variant {                                                                              \
-        DT, 0, tgemm_config{TGEMM_KERNEL_SKINNY, MT * 32, 32, 64, 1, 8, D, 1, 8},          \
+        DT, 0, 0, tgemm_config{TGEMM_KERNEL_SKINNY, MT * 32, 32, 64, 1, 8, D, 1, 8},       \
             &launch_skinny<DT, MT, D>                                                      \
     }
-#define ALL_DMA(DT)                                                                        \
-    DMA(DT, 256, 256, 32, 2, 2, 4, 4), DMA(DT, 256, 256, 32, 2, 2, 5, 4),                  \
-        PINGPONG(DT, 0, 256, 256, 64, 2, 4), PINGPONG(DT, 0, 256, 256, 32, 4, 4), \
-        PINGPONG(DT, 0, 256, 256, 32, 5, 4), SKINNY(DT, 1, 4), SKINNY(DT, 2, 3), SKINNY(DT, 4, 1)
-#define ALL_SHAPES(DT, L)                                                                  \
-    GENERIC(DT, L), TILED(DT, L, 256, 256, 64, 2, 2, 4), TILED(DT, L, 128, 128, 64, 2, 2, 8), \
-        TILED(DT, L, 64, 64, 64, 2, 2, 8)
+// A [M,K], B [N,K]: every kernel
+#define ALL_MK_NK(DT)                                                                      \
+    GENERIC(DT, 0, 0), TILED(DT, 0, 0, 256, 256, 64, 2, 2, 4),                             \
+        TILED(DT, 0, 0, 128, 128, 64, 2, 2, 8), TILED(DT, 0, 0, 64, 64, 64, 2, 2, 8),      \
+        DMA(DT, 256, 256, 32, 2, 2, 4, 4), DMA(DT, 256, 256, 32, 2, 2, 5, 4),              \
+        PINGPONG(DT, 0, 0, 256, 256, 64, 2, 4), PINGPONG(DT, 0, 0, 256, 256, 32, 4, 4),    \
+        PINGPONG(DT, 0, 0, 256, 256, 32, 5, 4), SKINNY(DT, 1, 4), SKINNY(DT, 2, 3),        \
+        SKINNY(DT, 4, 1)
+// A [M,K], B [K,N]
+#define ALL_MK_KN(DT)                                                                      \
+    GENERIC(DT, 0, 1), TILED(DT, 0, 1, 256, 256, 64, 2, 2, 4),                             \
+        TILED(DT, 0, 1, 128, 128, 64, 2, 2, 8), TILED(DT, 0, 1, 64, 64, 64, 2, 2, 8),      \
+        PINGPONG(DT, 0, 1, 256, 256, 64, 2, 4), PINGPONG(DT, 0, 1, 256, 256, 32, 5, 4)
+// A [K,M], either B
+#define ALL_KM(DT, L)                                                                      \
+    GENERIC(DT, 1, L), TILED(DT, 1, L, 128, 128, 64, 2, 2, 8),                             \
+        TILED(DT, 1, L, 64, 64, 64, 2, 2, 8), PINGPONG(DT, 1, L, 256, 256, 32, 4, 4)
 
 const Variant kVariants[] = {
-    ALL_DMA(0),
-    ALL_DMA(1),
-    ALL_SHAPES(0, 0),
-    ALL_SHAPES(0, 1),
-    PINGPONG(0, 1, 256, 256, 64, 2, 4),
-    PINGPONG(1, 1, 256, 256, 64, 2, 4),
-    PINGPONG(0, 1, 256, 256, 32, 5, 4),
-    PINGPONG(1, 1, 256, 256, 32, 5, 4),
-    ALL_SHAPES(1, 0),
-    ALL_SHAPES(1, 1),
+    ALL_MK_NK(0), ALL_MK_NK(1), ALL_MK_KN(0), ALL_MK_KN(1),
+    ALL_KM(0, 0), ALL_KM(1, 0), ALL_KM(0, 1), ALL_KM(1, 1),
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -133,31 +136,33 @@ bool same_shape(const tgemm_config& a, const tgemm_config& b) {
            a.stages == b.stages && a.split_k == b.split_k;
 }
 
-const Variant* find_variant(int dtype, int layout, const tgemm_config& cfg) {
+const Variant* find_variant(int dtype, int a_layout, int layout, const tgemm_config& cfg) {
     for (int i = 0; i < kNumVariants; ++i) {
         const Variant& v = kVariants[i];
-        if (v.dtype == dtype && v.layout == layout && same_shape(v.cfg, cfg))
+        if (v.dtype == dtype && v.a_layout == a_layout && v.layout == layout &&
+            same_shape(v.cfg, cfg))
             return &v;
     }
     return nullptr;
 }
 
 // The table: fast configurations by how many workgroups they give, so that the chip
-// (256 compute units) is filled with the largest tile that still fills it.
-tgemm_config choose(int dtype, int layout, int64_t m, int64_t n, int64_t k, bool aligned) {
+// (256 compute units) is filled with the largest tile that still fills it; small M with
+// long K goes to the split-K skinny kernel.
+tgemm_config choose(int dtype, int a_layout, int layout, int64_t m, int64_t n, int64_t k,
+                    bool aligned) {
     (void)dtype;
-    tgemm_config c;
-    if (!aligned) {
-        c = tgemm_config{TGEMM_KERNEL_GENERIC, 64, 64, 16, 2, 2, 1, 8, 1};
-        return c;
-    }
-    if (layout == TGEMM_B_NK && m <= 128 && k >= 1024) {
+    if (!aligned)
+        return tgemm_config{TGEMM_KERNEL_GENERIC, 64, 64, 16, 2, 2, 1, 8, 1};
+    if (a_layout == TGEMM_A_MK && layout == TGEMM_B_NK && m <= 128 && k >= 1024) {
         const int mt = m <= 32 ? 1 : (m <= 64 ? 2 : 4);
         const int depth = mt == 1 ? 4 : (mt == 2 ? 3 : 1);
         return tgemm_config{TGEMM_KERNEL_SKINNY, mt * 32, 32, 64, 1, 8, depth, 1, 8};
     }
     const int64_t t256 = ((m + 255) / 256) * ((n + 255) / 256);
     const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
+    if (t256 >= 192 && a_layout == TGEMM_A_KM)   // the BK 32 ring needs fewer registers
+        return tgemm_config{TGEMM_KERNEL_PINGPONG, 256, 256, 32, 2, 4, 4, 4, 1};
     if (t256 >= 192)
         return tgemm_config{TGEMM_KERNEL_PINGPONG, 256, 256, 64, 2, 4, 2, 4, 1};
     if (t128 >= 128)
@@ -165,8 +170,36 @@ tgemm_config choose(int dtype, int layout, int64_t m, int64_t n, int64_t k, bool
     return tgemm_config{TGEMM_KERNEL_TILED, 64, 64, 64, 2, 2, 2, 8, 1};
 }
 
-int check_problem(int dtype, int64_t m, int64_t n, int64_t k, int b_layout) {
+// One product as the caller described it.
+struct Problem {
+    int dtype;
+    int64_t m, n, k;
+    const void* A;
+    int64_t lda;
+    int a_layout;
+    const void* B;
+    int64_t ldb;
+    int b_layout;
+    void* C;
+    int64_t ldc;
+};
+
+// Elements spanned by `rows` rows of `cols` elements, `ld` apart.
+int64_t span(int64_t rows, int64_t cols, int64_t ld) {
+    return rows > 0 && cols > 0 ? (rows - 1) * ld + cols : 0;
+}
+int64_t span_a(const Problem& p) {
+    return p.a_layout == TGEMM_A_MK ? span(p.m, p.k, p.lda) : span(p.k, p.m, p.lda);
+}
+int64_t span_b(const Problem& p) {
+    return p.b_layout == TGEMM_B_NK ? span(p.n, p.k, p.ldb) : span(p.k, p.n, p.ldb);
+}
+int64_t span_c(const Problem& p) { return span(p.m, p.n, p.ldc); }
+
+int check_sizes(int dtype, int64_t m, int64_t n, int64_t k, int a_layout, int b_layout) {
     if (dtype != TGEMM_F16 && dtype != TGEMM_BF16)
+        return TGEMM_ERR_INVALID_VALUE;
+    if (a_layout != TGEMM_A_MK && a_layout != TGEMM_A_KM)
         return TGEMM_ERR_INVALID_VALUE;
     if (b_layout != TGEMM_B_NK && b_layout != TGEMM_B_KN)
         return TGEMM_ERR_INVALID_VALUE;
@@ -179,84 +212,98 @@ int check_problem(int dtype, int64_t m, int64_t n, int64_t k, int b_layout) {
     return TGEMM_OK;
 }
 
+int check_problem(const Problem& p) {
+    int rc = check_sizes(p.dtype, p.m, p.n, p.k, p.a_layout, p.b_layout);
+    if (rc != TGEMM_OK)
+        return rc;
+    // a leading dimension covers at least the contiguous extent of a row (and is >= 1)
+    const int64_t a_min = p.a_layout == TGEMM_A_MK ? p.k : p.m;
+    const int64_t b_min = p.b_layout == TGEMM_B_NK ? p.k : p.n;
+    if (p.lda < 1 || p.lda < a_min || p.ldb < 1 || p.ldb < b_min || p.ldc < 1 || p.ldc < p.n)
+        return TGEMM_ERR_INVALID_VALUE;
+    if (p.lda > kMaxElems || p.ldb > kMaxElems || p.ldc > kMaxElems)
+        return TGEMM_ERR_UNSUPPORTED;
+    // spans, computed only once every factor is known to fit (no int64 overflow)
+    if (span_a(p) > kMaxElems || span_b(p) > kMaxElems || span_c(p) > kMaxElems)
+        return TGEMM_ERR_UNSUPPORTED;
+    return TGEMM_OK;
+}
+
 bool overlaps(const void* p, int64_t pbytes, const void* q, int64_t qbytes) {
     const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
     return pbytes > 0 && qbytes > 0 && a < b + (uintptr_t)qbytes && b < a + (uintptr_t)pbytes;
 }
 
 // The fast kernels read A and B through buffer resources whose range check rejects any
-// offset with bit 31 set, which holds only for operands of at most 2^31 bytes.
+// offset with bit 31 set, which holds only for operands spanning at most 2^31 bytes; they
+// move 16-byte pieces, so every contiguous extent and leading dimension is a multiple of
+// 8 elements and every base address 16-byte aligned.
 constexpr int64_t kMaxFastOperandBytes = int64_t(1) << 31;
 
-bool fast_aligned(int64_t m, int64_t n, int64_t k, const void* A, const void* B,
-                  const void* C) {
-    return k % 8 == 0 && n % 8 == 0 && ((uintptr_t)A % 16) == 0 && ((uintptr_t)B % 16) == 0 &&
-           ((uintptr_t)C % 16) == 0 && 2 * m * k <= kMaxFastOperandBytes &&
-           2 * n * k <= kMaxFastOperandBytes;
+bool fast_aligned(const Problem& p) {
+    const auto al16 = [](const void* q) { return ((uintptr_t)q % 16) == 0; };
+    return p.k % 8 == 0 && p.n % 8 == 0 && (p.a_layout == TGEMM_A_MK || p.m % 8 == 0) &&
+           p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % 8 == 0 && al16(p.A) && al16(p.B) &&
+           al16(p.C) && 2 * span_a(p) <= kMaxFastOperandBytes &&
+           2 * span_b(p) <= kMaxFastOperandBytes;
 }
 
-int run(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const void* B, void* C,
-        int b_layout, const tgemm_config* cfg, void* stream) {
-    int rc = check_problem(dtype, m, n, k, b_layout);
+int run(const Problem& p, const tgemm_config* cfg, void* stream) {
+    int rc = check_problem(p);
     if (rc != TGEMM_OK)
         return rc;
-    if (m == 0 || n == 0)
+    if (p.m == 0 || p.n == 0)
         return TGEMM_OK;
-    if (!C || (k > 0 && (!A || !B)))
+    if (!p.C || (p.k > 0 && (!p.A || !p.B)))
         return TGEMM_ERR_NULL_POINTER;
-    if (((uintptr_t)C & 1) || ((uintptr_t)A & 1) || ((uintptr_t)B & 1))
+    if (((uintptr_t)p.C & 1) || ((uintptr_t)p.A & 1) || ((uintptr_t)p.B & 1))
         return TGEMM_ERR_ALIGNMENT;
-    if (overlaps(C, 2 * m * n, A, 2 * m * k) || overlaps(C, 2 * m * n, B, 2 * n * k))
+    if (overlaps(p.C, 2 * span_c(p), p.A, 2 * span_a(p)) ||
+        overlaps(p.C, 2 * span_c(p), p.B, 2 * span_b(p)))
         return TGEMM_ERR_ALIASING;
-    const bool aligned = fast_aligned(m, n, k, A, B, C);
-    tgemm_config use = cfg ? *cfg : choose(dtype, b_layout, m, n, k, aligned);
-    const Variant* v = find_variant(dtype, b_layout, use);
+    const bool aligned = fast_aligned(p);
+    tgemm_config use =
+        cfg ? *cfg : choose(p.dtype, p.a_layout, p.b_layout, p.m, p.n, p.k, aligned);
+    const Variant* v = find_variant(p.dtype, p.a_layout, p.b_layout, use);
     if (!v)
         return TGEMM_ERR_UNSUPPORTED;
     if (use.kernel != TGEMM_KERNEL_GENERIC && !aligned)
         return TGEMM_ERR_ALIGNMENT;
     const int group_m = use.group_m > 0 ? use.group_m : v->cfg.group_m;
     (void)hipGetLastError();   // start from a clean error state for this launch
-    const hipError_t e = v->launch(A, B, C, (int)m, (int)n, (int)k, group_m,
-                                   static_cast<hipStream_t>(stream));
+    const hipError_t e =
+        v->launch(p.A, p.B, p.C, (int)p.m, (int)p.n, (int)p.k, (int)p.lda, (int)p.ldb,
+                  (int)p.ldc, group_m, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
 }
 
-}  // namespace
-
-extern "C" {
-
-int gemm_f16(int64_t m, int64_t n, int64_t k, const void* A, const void* B, void* C,
-             int b_layout, void* stream) {
-    return run(TGEMM_F16, m, n, k, A, B, C, b_layout, nullptr, stream);
+// A packed product: A [M,K], B [N,K] or [K,N], C [M,N], no padding between rows (an
+// empty row length still gives a leading dimension of 1).
+Problem packed(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const void* B,
+               void* C, int b_layout) {
+    const auto ld = [](int64_t x) { return x > 1 ? x : int64_t(1); };
+    return Problem{dtype,     m, n, k, A, ld(k), TGEMM_A_MK, B, ld(b_layout == TGEMM_B_KN ? n : k),
+                   b_layout, C, ld(n)};
 }
 
-int gemm_bf16(int64_t m, int64_t n, int64_t k, const void* A, const void* B, void* C,
-              int b_layout, void* stream) {
-    return run(TGEMM_BF16, m, n, k, A, B, C, b_layout, nullptr, stream);
-}
-
-int gemm_ex(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const void* B, void* C,
-            int b_layout, const tgemm_config* cfg, void* stream) {
-    return run(dtype, m, n, k, A, B, C, b_layout, cfg, stream);
-}
-
-int tgemm_query_config(int dtype, int64_t m, int64_t n, int64_t k, int b_layout, int aligned,
-                       tgemm_config* out) {
-    int rc = check_problem(dtype, m, n, k, b_layout);
+int query(int dtype, int64_t m, int64_t n, int64_t k, int a_layout, int b_layout, int aligned,
+          tgemm_config* out) {
+    int rc = check_sizes(dtype, m, n, k, a_layout, b_layout);
     if (rc != TGEMM_OK)
         return rc;
     if (!out)
         return TGEMM_ERR_NULL_POINTER;
-    *out = choose(dtype, b_layout, m, n, k, aligned != 0);
-    const Variant* v = find_variant(dtype, b_layout, *out);
+    *out = choose(dtype, a_layout, b_layout, m, n, k, aligned != 0);
+    const Variant* v = find_variant(dtype, a_layout, b_layout, *out);
     if (v)
         out->group_m = v->cfg.group_m;
     return TGEMM_OK;
 }
 
-int tgemm_list_configs(int dtype, int b_layout, tgemm_config* out, int capacity) {
+int list(int dtype, int a_layout, int b_layout, tgemm_config* out, int capacity) {
     if (dtype != TGEMM_F16 && dtype != TGEMM_BF16)
+        return TGEMM_ERR_INVALID_VALUE;
+    if (a_layout != TGEMM_A_MK && a_layout != TGEMM_A_KM)
         return TGEMM_ERR_INVALID_VALUE;
     if (b_layout != TGEMM_B_NK && b_layout != TGEMM_B_KN)
         return TGEMM_ERR_INVALID_VALUE;
@@ -265,7 +312,7 @@ int tgemm_list_configs(int dtype, int b_layout, tgemm_config* out, int capacity)
     int count = 0;
     for (int i = 0; i < kNumVariants; ++i) {
         const Variant& v = kVariants[i];
-        if (v.dtype != dtype || v.layout != b_layout)
+        if (v.dtype != dtype || v.a_layout != a_layout || v.layout != b_layout)
             continue;
         if (count < capacity)
             out[count] = v.cfg;
@@ -274,10 +321,56 @@ int tgemm_list_configs(int dtype, int b_layout, tgemm_config* out, int capacity)
     return count;
 }
 
+}  // namespace
+
+extern "C" {
+
+int gemm_f16(int64_t m, int64_t n, int64_t k, const void* A, const void* B, void* C,
+             int b_layout, void* stream) {
+    return run(packed(TGEMM_F16, m, n, k, A, B, C, b_layout), nullptr, stream);
+}
+
+int gemm_bf16(int64_t m, int64_t n, int64_t k, const void* A, const void* B, void* C,
+              int b_layout, void* stream) {
+    return run(packed(TGEMM_BF16, m, n, k, A, B, C, b_layout), nullptr, stream);
+}
+
+int gemm_ex(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const void* B, void* C,
+            int b_layout, const tgemm_config* cfg, void* stream) {
+    return run(packed(dtype, m, n, k, A, B, C, b_layout), cfg, stream);
+}
+
+int gemm_strided(int dtype, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
+                 int a_layout, const void* B, int64_t ldb, int b_layout, void* C, int64_t ldc,
+                 const tgemm_config* cfg, void* stream) {
+    return run(Problem{dtype, m, n, k, A, lda, a_layout, B, ldb, b_layout, C, ldc}, cfg,
+               stream);
+}
+
+int tgemm_query_config(int dtype, int64_t m, int64_t n, int64_t k, int b_layout, int aligned,
+                       tgemm_config* out) {
+    return query(dtype, m, n, k, TGEMM_A_MK, b_layout, aligned, out);
+}
+
+int tgemm_query_config_ex(int dtype, int64_t m, int64_t n, int64_t k, int a_layout,
+                          int b_layout, int aligned, tgemm_config* out) {
+    return query(dtype, m, n, k, a_layout, b_layout, aligned, out);
+}
+
+int tgemm_list_configs(int dtype, int b_layout, tgemm_config* out, int capacity) {
+    return list(dtype, TGEMM_A_MK, b_layout, out, capacity);
+}
+
+int tgemm_list_configs_ex(int dtype, int a_layout, int b_layout, tgemm_config* out,
+                          int capacity) {
+    return list(dtype, a_layout, b_layout, out, capacity);
+}
+
 const char* tgemm_status_string(int status) {
     switch (status) {
     case TGEMM_OK: return "TGEMM_OK";
-    case TGEMM_ERR_INVALID_VALUE: return "TGEMM_ERR_INVALID_VALUE: bad size, dtype or layout";
+    case TGEMM_ERR_INVALID_VALUE:
+        return "TGEMM_ERR_INVALID_VALUE: bad size, leading dimension, dtype or layout";
     case TGEMM_ERR_NULL_POINTER: return "TGEMM_ERR_NULL_POINTER: NULL operand";
     case TGEMM_ERR_ALIGNMENT: return "TGEMM_ERR_ALIGNMENT: operand alignment not supported";
     case TGEMM_ERR_ALIASING: return "TGEMM_ERR_ALIASING: C overlaps A or B";
@@ -288,6 +381,6 @@ const char* tgemm_status_string(int status) {
     }
 }
 
-int tgemm_version(void) { return 100; }
+int tgemm_version(void) { return 200; }
 
 }  // extern "C"

@@ -11,12 +11,14 @@ import os
 
 F16, BF16 = 0, 1
 B_NK, B_KN = 0, 1
+A_MK, A_KM = 0, 1
 KERNEL_GENERIC, KERNEL_TILED, KERNEL_SKINNY, KERNEL_DMA, KERNEL_PINGPONG = 0, 1, 2, 3, 4
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtgemm.so")
 
-EXPORTS = ("gemm_f16", "gemm_bf16", "gemm_ex", "tgemm_query_config", "tgemm_list_configs",
+EXPORTS = ("gemm_f16", "gemm_bf16", "gemm_ex", "gemm_strided", "tgemm_query_config",
+           "tgemm_query_config_ex", "tgemm_list_configs", "tgemm_list_configs_ex",
            "tgemm_status_string", "tgemm_version")
 
 
@@ -62,12 +64,17 @@ def load(path: str = LIB_PATH):
     lib.gemm_f16.argtypes = [i64, i64, i64, vp, vp, vp, i32, vp]
     lib.gemm_bf16.argtypes = [i64, i64, i64, vp, vp, vp, i32, vp]
     lib.gemm_ex.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, cfgp, vp]
+    lib.gemm_strided.argtypes = [i32, i64, i64, i64, vp, i64, i32, vp, i64, i32, vp, i64,
+                                 cfgp, vp]
     lib.tgemm_query_config.argtypes = [i32, i64, i64, i64, i32, i32, cfgp]
+    lib.tgemm_query_config_ex.argtypes = [i32, i64, i64, i64, i32, i32, i32, cfgp]
     lib.tgemm_list_configs.argtypes = [i32, i32, cfgp, i32]
+    lib.tgemm_list_configs_ex.argtypes = [i32, i32, i32, cfgp, i32]
     lib.tgemm_status_string.argtypes = [i32]
     lib.tgemm_status_string.restype = ctypes.c_char_p
-    for name in ("gemm_f16", "gemm_bf16", "gemm_ex", "tgemm_query_config",
-                 "tgemm_list_configs", "tgemm_version"):
+    for name in ("gemm_f16", "gemm_bf16", "gemm_ex", "gemm_strided", "tgemm_query_config",
+                 "tgemm_query_config_ex", "tgemm_list_configs", "tgemm_list_configs_ex",
+                 "tgemm_version"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -125,20 +132,30 @@ def gemm_ex(dtype, m, n, k, A, B, C, b_layout=B_NK, config: Config | None = None
                           _stream(stream)), "gemm_ex")
 
 
-def query_config(dtype, m, n, k, b_layout=B_NK, aligned=True) -> Config:
+def gemm_strided(dtype, m, n, k, A, lda, a_layout, B, ldb, b_layout, C, ldc,
+                 config: Config | None = None, stream=None):
+    """The general product: A [M,K] (A_MK) or [K,M] (A_KM), B [N,K] (B_NK) or [K,N] (B_KN),
+    C [M,N], each with a leading dimension in elements."""
+    cfg = ctypes.byref(config) if config is not None else None
+    _check(load().gemm_strided(dtype, m, n, k, _addr(A), lda, a_layout, _addr(B), ldb,
+                               b_layout, _addr(C), ldc, cfg, _stream(stream)), "gemm_strided")
+
+
+def query_config(dtype, m, n, k, b_layout=B_NK, aligned=True, a_layout=A_MK) -> Config:
     out = Config()
-    _check(load().tgemm_query_config(dtype, m, n, k, b_layout, int(bool(aligned)),
-                                     ctypes.byref(out)), "tgemm_query_config")
+    _check(load().tgemm_query_config_ex(dtype, m, n, k, a_layout, b_layout,
+                                        int(bool(aligned)), ctypes.byref(out)),
+           "tgemm_query_config_ex")
     return out
 
 
-def list_configs(dtype, b_layout=B_NK) -> list:
+def list_configs(dtype, b_layout=B_NK, a_layout=A_MK) -> list:
     lib = load()
-    count = lib.tgemm_list_configs(dtype, b_layout, None, 0)
+    count = lib.tgemm_list_configs_ex(dtype, a_layout, b_layout, None, 0)
     if count < 0:
-        raise TGemmError(count, "tgemm_list_configs")
+        raise TGemmError(count, "tgemm_list_configs_ex")
     arr = (Config * count)()
-    lib.tgemm_list_configs(dtype, b_layout, arr, count)
+    lib.tgemm_list_configs_ex(dtype, a_layout, b_layout, arr, count)
     return [arr[i] for i in range(count)]
 
 
