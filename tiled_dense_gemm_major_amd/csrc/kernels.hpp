@@ -442,10 +442,27 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
 //              other waves (tile t+1 complete, tile t no longer read); the remaining
 //              MFMAs with the reads of tile t+1's first operands.
 // ------------------------------------------------------------------------------------
-template <int STAGE_BYTES>
-__device__ __forceinline__ void dma16(rsrc_t r, u16* lds_dst, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, soff, 0, 0);
+// The same buffer resource as four dwords (base address low/high, size, format), for the
+// direct-to-LDS loads below.
+typedef u32x4 rsrc4_t;
+__device__ __forceinline__ rsrc4_t make_rsrc4(const void* base, uint32_t bytes) {
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    return rsrc4_t{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, kRsrcWord3};
+}
+
+// One direct-to-LDS load: 64 lanes x 16 bytes to lds_dst (M0) + 16 * lane.  Issued from
+// inline assembly so that the compiler does not track it: it would otherwise wait for
+// every such load in flight before each transposing LDS read (it cannot tell that they
+// touch different stages).  The kernels order these loads themselves, with explicit
+// vmcnt waits and barriers, and never read a stage before their own waits say it landed.
+__device__ __forceinline__ void dma16(rsrc4_t r, u16* lds_dst, uint32_t voff, uint32_t soff) {
+    // the destination and the K offset are the same for every lane of the wave
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_dst);
+    const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 ::"v"(voff), "s"(r), "s"(so), "s"(m0v)
+                 : "memory", "m0");
 }
 
 template <int N>
@@ -486,8 +503,8 @@ gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__
     const int wm = wave / WN, wn = wave % WN;
     const int nk = (K + BK - 1) / BK;
 
-    const rsrc_t ra = make_rsrc(A, span_bytes(M, K, lda));
-    const rsrc_t rb = make_rsrc(B, span_bytes(N, K, ldb));
+    const rsrc4_t ra = make_rsrc4(A, span_bytes(M, K, lda));
+    const rsrc4_t rb = make_rsrc4(B, span_bytes(N, K, ldb));
 
     // Lane l lands in row l / KC of a 1 KiB block at physical chunk l % KC; it fetches
     // the logical chunk that the swizzle of that row (block base + l / KC) puts there.
@@ -514,10 +531,10 @@ gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__
         const int k0 = live ? kt * BK : 0;
         u16* st = stage_ptr(kt);
         if constexpr (i < A_LD)
-            dma16<0>(ra, st + (wave * A_LD + i) * ROWS * BK,
+            dma16(ra, st + (wave * A_LD + i) * ROWS * BK,
                      live && k0 + a_kc[i] < K ? a_off[i] : kOutOfRange, (uint32_t)k0 * 2u);
         else
-            dma16<0>(rb, st + A_ELEMS + (wave * B_LD + (i - A_LD)) * ROWS * BK,
+            dma16(rb, st + A_ELEMS + (wave * B_LD + (i - A_LD)) * ROWS * BK,
                      live && k0 + b_kc[i - A_LD] < K ? b_off[i - A_LD] : kOutOfRange,
                      (uint32_t)k0 * 2u);
     };
@@ -665,10 +682,10 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
     const int grp = wave >> 2, wc = wave & 3;
     const int nk = (K + BK - 1) / BK;
 
-    const rsrc_t ra = ALAYOUT == LAYOUT_MK ? make_rsrc(A, span_bytes(M, K, lda))
-                                           : make_rsrc(A, span_bytes(K, M, lda));
-    const rsrc_t rb = LAYOUT == LAYOUT_NK ? make_rsrc(B, span_bytes(N, K, ldb))
-                                          : make_rsrc(B, span_bytes(K, N, ldb));
+    const rsrc4_t ra = ALAYOUT == LAYOUT_MK ? make_rsrc4(A, span_bytes(M, K, lda))
+                                            : make_rsrc4(A, span_bytes(K, M, lda));
+    const rsrc4_t rb = LAYOUT == LAYOUT_NK ? make_rsrc4(B, span_bytes(N, K, ldb))
+                                           : make_rsrc4(B, span_bytes(K, N, ldb));
 
     // The rows this wave loads: group 1 wave c the A rows [c*BM/8, (c+1)*BM/8); group 0
     // wave c the A rows [BM/2 + c*BM/8, ...) and the B rows [c*BN/4, (c+1)*BN/4).  They
@@ -699,14 +716,14 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
             const int kc = (i & 1) ? kc_odd : kc_even;
             const int r = m0 + a_row + i * ROWS + prow;
             const bool ok = live && r < M && k0 + kc < K;
-            dma16<0>(ra, st + (a_row + i * ROWS) * BK,
+            dma16(ra, st + (a_row + i * ROWS) * BK,
                      ok ? (uint32_t)(r * lda + kc) * 2u : kOutOfRange, (uint32_t)k0 * 2u);
         } else {
             const int kr = wc * (BK / 4) + 4 * i + (lane >> 4);
             const int cl = (lane & 15) ^ (4 * (kr & 3));
             const int m = m0 + a_half * (BM / 2) + 8 * cl;
             const bool ok = live && m < M && k0 + kr < K;
-            dma16<0>(ra, st + a_half * HALF + (wc * (BK / 4) + 4 * i) * (BM / 2),
+            dma16(ra, st + a_half * HALF + (wc * (BK / 4) + 4 * i) * (BM / 2),
                      ok ? (uint32_t)(kr * lda + m) * 2u : kOutOfRange,
                      (uint32_t)k0 * (uint32_t)lda * 2u);
         }
@@ -726,7 +743,7 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
             const int kc = (i & 1) ? kc_odd : kc_even;
             const int r = n0 + r0 + i * ROWS + prow;
             const bool ok = live && r < N && k0 + kc < K;
-            dma16<0>(rb, st + A_ELEMS + (r0 + i * ROWS) * BK,
+            dma16(rb, st + A_ELEMS + (r0 + i * ROWS) * BK,
                      ok ? (uint32_t)(r * ldb + kc) * 2u : kOutOfRange, (uint32_t)k0 * 2u);
         } else {
             // the stage holds k rows of BN columns; a 1 KiB load fills two rows, lane l
@@ -736,7 +753,7 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
             const int cl = (lane & 31) ^ (4 * (kr & 3));
             const int n = n0 + 8 * cl;
             const bool ok = live && n < N && k0 + kr < K;
-            dma16<0>(rb, st + A_ELEMS + (wc * (BK / 4) + 2 * i) * BN,
+            dma16(rb, st + A_ELEMS + (wc * (BK / 4) + 2 * i) * BN,
                      ok ? (uint32_t)(kr * ldb + n) * 2u : kOutOfRange,
                      (uint32_t)k0 * (uint32_t)ldb * 2u);
         }
