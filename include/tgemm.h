@@ -87,15 +87,21 @@ typedef enum {
                                  workgroup and summed in LDS                              */
     TGEMM_KERNEL_DMA = 3,     /* A [M,K], B [N,K] only: global loads written straight into
                                  a deep ring of swizzled LDS stages (no register staging) */
-    TGEMM_KERNEL_PINGPONG = 4 /* 8 waves, two per SIMD, alternating between operand fetch
+    TGEMM_KERNEL_PINGPONG = 4,/* 8 waves, two per SIMD, alternating between operand fetch
                                  and back-to-back MFMAs half a period apart; direct-to-LDS
                                  loads; [K,N] B and [K,M] A through transposing reads    */
+    TGEMM_KERNEL_QUAD = 5     /* A [M,K], B [N,K] only: one wave per SIMD, each owning a
+                                 128x128 quadrant of a 256x256 tile; direct-to-LDS loads
+                                 into three A and two B slots, one barrier per K step;
+                                 lda, ldb <= 2^24 (else TGEMM_ERR_UNSUPPORTED)           */
 } tgemm_kernel;
 
 /* One tile configuration.  block_m x block_n is the C tile of one workgroup, block_k
  * the K step, waves_m x waves_n the wavefront grid inside the workgroup (64 lanes each),
- * stages the LDS buffers, group_m the tile rows of one launch-order group, and
- * split_k the number of waves that share one C tile's K range (SKINNY only, else 1). */
+ * stages the LDS buffers (QUAD: operand slots of block_m x block_k elements, three for
+ * A tiles and two for B tiles), group_m the tile rows of one launch-order group,
+ * split_k the number of waves that share one C tile's K range (SKINNY only, else 1),
+ * and mfma the matrix instruction's block size: 32 (32x32x16) or 16 (16x16x32). */
 typedef struct {
     int32_t kernel;
     int32_t block_m, block_n, block_k;
@@ -103,6 +109,7 @@ typedef struct {
     int32_t stages;
     int32_t group_m;
     int32_t split_k;
+    int32_t mfma;
 } tgemm_config;
 
 /*

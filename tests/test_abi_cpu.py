@@ -111,7 +111,10 @@ def test_list_configs(lib):
             kinds = {c.kernel for c in cfgs}
             assert tgemm.KERNEL_GENERIC in kinds and tgemm.KERNEL_TILED in kinds
             for c in cfgs:
-                if c.kernel != tgemm.KERNEL_GENERIC:
+                if c.kernel == tgemm.KERNEL_QUAD:
+                    # operand slots of block_m x block_k (three A, two B)
+                    assert c.stages * max(c.block_m, c.block_n) * c.block_k * 2 <= 160 * 1024
+                elif c.kernel != tgemm.KERNEL_GENERIC:
                     # the LDS ring must fit the 160 KiB of one compute unit
                     assert c.stages * (c.block_m + c.block_n) * c.block_k * 2 <= 160 * 1024
     assert lib.tgemm_list_configs(5, 0, None, 0) == -1
@@ -147,7 +150,8 @@ def test_strided_query_and_list(lib):
             kinds = {c.kernel for c in cfgs}
             assert {tgemm.KERNEL_GENERIC, tgemm.KERNEL_TILED, tgemm.KERNEL_PINGPONG} <= kinds
             big = tgemm.query_config(tgemm.BF16, 8192, 8192, 8192, b_layout, True, a_layout)
-            assert big.kernel == tgemm.KERNEL_PINGPONG
+            quad = a_layout == tgemm.A_MK and b_layout == tgemm.B_NK
+            assert big.kernel == (tgemm.KERNEL_QUAD if quad else tgemm.KERNEL_PINGPONG)
             listed = {tuple(sorted(c.as_dict().items())) for c in cfgs}
             assert tuple(sorted(big.as_dict().items())) in listed
     # the skinny kernel reads A [M,K] and B [N,K] only

@@ -30,7 +30,8 @@ def _configs(dtype, layout):
 
 
 def _cfg_id(c):
-    return f"k{c.kernel}_{c.block_m}x{c.block_n}x{c.block_k}_w{c.waves_m}x{c.waves_n}"
+    return (f"k{c.kernel}_{c.block_m}x{c.block_n}x{c.block_k}_w{c.waves_m}x{c.waves_n}"
+            f"_s{c.stages}_m{c.mfma}")
 
 
 # ---------------------------------------------------------------------------------------
@@ -205,3 +206,43 @@ def test_workload_full_size(dev, orc, name):
         rows, cols = sample_positions(w.M, w.N, 3000, w.seed)
         want, _ = orc.gemm_entries(w.dtype, A, B, w.b_layout, rows, cols)
         assert_parity(orc, w.dtype, w.K, got[rows, cols], want, name)
+
+
+# ---------------------------------------------------------------------------------------
+# Short K walks: fewer K tiles than pipeline slots (loads of tiles past the end must add
+# nothing), and K tails inside the last tile, for every compiled configuration.
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("K", [8, 64, 72, 128, 200])
+def test_every_config_short_k_exact(dev, orc, dtype, K):
+    rng = np.random.default_rng(K)
+    M, N = 264, 520
+    A = _int_bits(dtype, rng.integers(-2, 3, (M, K)))
+    B = _int_bits(dtype, rng.integers(-2, 3, (N, K)))
+    want = orc.gemm(dtype, A, B, B_NK)
+    for cfg in _configs(dtype, B_NK):
+        say(f"short k {K} {_cfg_id(cfg)}")
+        assert np.array_equal(run(dtype, A, B, B_NK, cfg), want), (K, _cfg_id(cfg))
+
+
+def test_quad_repeat_launches_bitwise_identical(dev, orc):
+    """Many workgroups per compute unit through the five-slot ring: a stage reused too
+    early shows up as launch-to-launch differences."""
+    from tiled_dense_gemm_major_amd import tgemm
+    M, N, K = 2048, 2304, 1536
+    A, B = _inputs(BF16, M, N, K, B_NK, 91)
+    Ad, Bd = to_dev(A, BF16), to_dev(B, BF16)
+    for cfg in [c for c in _configs(BF16, B_NK) if c.kernel == tgemm.KERNEL_QUAD]:
+        say(f"quad repeat launches {_cfg_id(cfg)} mfma {cfg.mfma}")
+        C0 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        tgemm.gemm_ex(BF16, M, N, K, Ad, Bd, C0, B_NK, cfg)
+        torch.cuda.synchronize()
+        ref = from_dev(C0)
+        rows, cols = sample_positions(M, N, 500, 91)
+        want, _ = orc.gemm_entries(BF16, A, B, B_NK, rows, cols)
+        assert_parity(orc, BF16, K, ref[rows, cols], want, "quad sampled")
+        C = torch.empty_like(C0)
+        for _ in range(20):
+            tgemm.gemm_ex(BF16, M, N, K, Ad, Bd, C, B_NK, cfg)
+            torch.cuda.synchronize()
+            assert np.array_equal(from_dev(C), ref)

@@ -24,6 +24,7 @@ typedef uint16_t u16;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -44,6 +45,20 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 s0, u32x4 s1, f32x16 acc) 
                                                       __builtin_bit_cast(f16x8, s1), acc, 0, 0, 0);
     else
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, s0),
+                                                       __builtin_bit_cast(bf16x8, s1), acc, 0, 0, 0);
+}
+
+// Matrix-core step: D(16x16, fp32) += S0(16 x 32) * S1(32 x 16).  Lane l supplies, for
+// both sources, 8 consecutive-k values k = 8*(l/16) .. 8*(l/16)+7 of row (l % 16) of S0
+// and of column (l % 16) of S1 (the same k for both, whatever order the unit sums them
+// in).  Lane l receives D column (l % 16), rows 4*(l/16) + v in element v of the result.
+template <int DT>
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 s0, u32x4 s1, f32x4 acc) {
+    if constexpr (DT == DT_F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, s0),
+                                                      __builtin_bit_cast(f16x8, s1), acc, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, s0),
                                                        __builtin_bit_cast(bf16x8, s1), acc, 0, 0, 0);
 }
 
@@ -463,6 +478,32 @@ __device__ __forceinline__ void dma16(rsrc4_t r, u16* lds_dst, uint32_t voff, ui
     asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                  ::"v"(voff), "s"(r), "s"(so), "s"(m0v)
                  : "memory", "m0");
+}
+
+// The same load with the destination given as an LDS byte address (wave-uniform), so
+// that the address arithmetic stays in scalar registers.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// POL selects the cache policy of the load (0: default, 1: nt, 2: sc0, 3: sc1,
+// 4: sc0 sc1, 5: sc0 nt, 6: sc1 nt).
+template <int POL = 0>
+__device__ __forceinline__ void dma16_at(rsrc4_t r, uint32_t lds_byte, uint32_t voff,
+                                         uint32_t soff) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_byte);
+    const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+#define TGEMM_DMA_ASM(SUFFIX)                                                              \
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen" SUFFIX " lds" \
+                 ::"v"(voff), "s"(r), "s"(so), "s"(m0v)                                      \
+                 : "memory", "m0")
+    if constexpr (POL == 0) TGEMM_DMA_ASM("");
+    else if constexpr (POL == 1) TGEMM_DMA_ASM(" nt");
+    else if constexpr (POL == 2) TGEMM_DMA_ASM(" sc0");
+    else if constexpr (POL == 3) TGEMM_DMA_ASM(" sc1");
+    else if constexpr (POL == 4) TGEMM_DMA_ASM(" sc0 sc1");
+    else if constexpr (POL == 5) TGEMM_DMA_ASM(" sc0 nt");
+    else TGEMM_DMA_ASM(" sc1 nt");
+#undef TGEMM_DMA_ASM
 }
 
 template <int N>
@@ -935,6 +976,262 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + wc * WTN + j * 32 + 8 * g + 4 * half;
+                u32x2 v;
+                v[0] = pack2<DT>(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+                v[1] = pack2<DT>(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                if (m < M && n < N)
+                    *reinterpret_cast<u32x2*>(C + (size_t)m * ldc + n) = v;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Quadrant kernel (A [M,K], B [N,K]).
+//   One wave per SIMD: 4 waves in 2 x 2, each owning a 128 x 128 quadrant of the
+//   256 x 256 tile with all of its accumulators in registers.  Per MFMA this reads a
+//   third fewer operand bytes from LDS than 8 waves of 128 x 64 (4 x 256 instead of
+//   8 x 192 tile rows per K step).  MF picks the matrix instruction: 16 (16x16x32,
+//   8 x 8 blocks per wave) or 32 (32x32x16, 4 x 4 blocks per wave).
+//   Tiles of BK = 64 k (128-byte row segments: every load request is a whole cache
+//   line) arrive by direct-to-LDS loads; wave w loads rows [64w, 64w + 64) of each
+//   operand tile, 8 loads per operand.  The 160 KiB of LDS hold three A slots and two B
+//   slots (32 KiB each), so the A part of a tile can be fetched a step earlier than
+//   the B part and the two halves of a tile's loads go out in different halves of a
+//   step: the load stream stays even instead of leaving each barrier in one burst.
+// Step t computes tile t in KS sub-steps (BK / k per MFMA).  Each sub-step's MFMAs run
+// back to back with its memory operations dealt out among them:
+//   sub-steps s < KS-1 : the operand reads of sub-step s+1 (registers double-buffered),
+//                        and the A loads of tile t+2 (its slot held tile t-1);
+//   sub-step KS-1      : after PRE MFMAs, each wave waits for its own loads of tile t+1
+//                        and meets the others at the step's one barrier (tile t+1 is
+//                        then in LDS and every wave has read all of tile t), then the
+//                        reads of tile t+1's first operands and the B loads of tile t+2
+//                        into the B slot tile t used.
+// An A load has a step and a half to land, a B load one step.  Loads past the last
+// tile are issued out of range (zeros into a slot no step reads), so every step has the
+// same number of loads in flight.  STAG starts the K walk of the workgroups of XCD x at
+// x/8 of K (wrapping), so that the eight XCDs do not stream the same addresses at once;
+// POL is the cache policy of the loads.
+// ------------------------------------------------------------------------------------
+template <int NOPS, int SLOTS, int J>
+struct deal {   // ops [lo, hi) follow slot J when NOPS ops are dealt over SLOTS slots
+    static constexpr int lo = J >= SLOTS ? NOPS : (J * NOPS + SLOTS - 1) / SLOTS;
+    static constexpr int hi = J >= SLOTS ? NOPS : ((J + 1) * NOPS + SLOTS - 1) / SLOTS;
+};
+// Op o of a sequence of NL loads and NR reads with the loads spaced evenly among the
+// reads: the load index, or -1 - (read index).
+template <int NL, int NR>
+constexpr int op_kind(int o) {
+    int loads = 0;
+    for (int p = 0; p <= o; ++p) {
+        const bool is_load = loads < NL && p == loads * (NL + NR) / NL;
+        if (p == o)
+            return is_load ? loads : -1 - (o - loads);
+        loads += is_load;
+    }
+    return 0;
+}
+
+template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
+                               amdgpu_waves_per_eu(1, 1)))
+gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
+          int N, int K, int lda, int ldb, int ldc, int grid_m, int grid_n, int group_m) {
+    constexpr int BM = 256, BN = 256, BK = 64;
+    constexpr int KC = BK / 8;                 // 16-byte chunks per tile row
+    constexpr int ROWS = 64 / KC;              // tile rows per 1 KiB load (8)
+    constexpr int SLOT = BM * BK;              // elements of one operand slot (32 KiB)
+    constexpr int SA = 3, SB = 2;              // A and B slots
+    constexpr int NB = 64 / ROWS;              // loads per wave per operand per tile (8)
+    constexpr int KM = MF == 16 ? 32 : 16;     // k per MFMA
+    constexpr int KS = BK / KM;                // sub-steps per tile
+    constexpr int CPS = KM / 8;                // 16-byte chunks per sub-step
+    constexpr int TM = 128 / MF, TN = 128 / MF;
+    constexpr int NR = TM + TN;                // operand reads per sub-step
+    constexpr int NM = TM * TN;                // MFMAs per sub-step
+    using acc_t = std::conditional_t<MF == 16, f32x4, f32x16>;
+    static_assert(MF == 16 || MF == 32, "MFMA 16x16x32 or 32x32x16");
+    static_assert(KS % 2 == 0, "every step starts from operand buffer 0");
+    static_assert((SA + SB) * SLOT * 2 <= 160 * 1024, "LDS");
+    static_assert(PRE >= 1 && PRE < NM && SPA >= 1 && SPB >= 1, "schedule");
+
+    __shared__ __attribute__((aligned(1024))) u16 lds[(SA + SB) * SLOT];
+
+    int tm, tn;
+    tile_of((int)blockIdx.x, grid_m, grid_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = (int)threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nk = (K + BK - 1) / BK;
+
+    const rsrc4_t ra = make_rsrc4(A, span_bytes(M, K, lda));
+    const rsrc4_t rb = make_rsrc4(B, span_bytes(N, K, ldb));
+
+    // Lane l lands in row r0 + b*ROWS (r0 = 64w + l/KC) of block b at physical chunk
+    // l % KC and fetches the logical chunk that the row's swizzle puts there; the
+    // swizzle repeats every 16 rows, i.e. every two blocks.  Blocks b and b % 2 differ by
+    // a whole number of 16-row strides, which go in the scalar offset; a block's rows lie
+    // inside the operand when b * ROWS < lim (per lane).
+    const int prow = lane / KC, pch = lane % KC;
+    const int r0 = 64 * wave + prow;
+    uint32_t a_off[2], b_off[2];
+    int kcol[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        kcol[p] = (pch ^ swz<KC>(p * ROWS + prow)) * 8;
+        a_off[p] = (uint32_t)((m0 + r0 + p * ROWS) * lda + kcol[p]) * 2u;
+        b_off[p] = (uint32_t)((n0 + r0 + p * ROWS) * ldb + kcol[p]) * 2u;
+    }
+    const int a_lim = M - m0 - r0, b_lim = N - n0 - r0;
+    const int kofs = STAG ? (((int)blockIdx.x & 7) * nk) >> 3 : 0;
+    const uint32_t lds0 = lds_addr(lds);
+    const uint32_t wave_at = (uint32_t)(64 * wave * BK * 2);
+    // load b (< NB) of operand A (IS_A) or B of tile kt into the slot at LDS byte
+    // address slot_at
+    auto load_b = [&](uint32_t slot_at, int kt, auto isac, auto bc) {
+        constexpr bool is_a = decltype(isac)::value;
+        constexpr int b = decltype(bc)::value, p = b & 1;
+        // a tile past the end: every offset gets the out-of-range bit (no branches)
+        const bool live = kt < nk;
+        const int kp = kt + kofs >= nk ? kt + kofs - nk : kt + kofs;
+        const int k0 = live ? kp * BK : 0;
+        const uint32_t dead = live ? 0u : kOutOfRange;
+        const bool ok = (k0 + kcol[p] < K) & (b * ROWS < (is_a ? a_lim : b_lim));
+        const uint32_t row_step = (uint32_t)((b >> 1) * 2 * ROWS) * (uint32_t)(is_a ? lda : ldb);
+        dma16_at<POL>(is_a ? ra : rb, slot_at + wave_at + (uint32_t)(b * ROWS * BK * 2),
+                      (ok ? (is_a ? a_off[p] : b_off[p]) : kOutOfRange) | dead,
+                      (row_step + (uint32_t)k0) * 2u);
+    };
+    auto a_slot = [&](int i) { return lds0 + (uint32_t)(i * SLOT * 2); };
+    auto b_slot = [&](int j) { return lds0 + (uint32_t)((SA + j) * SLOT * 2); };
+
+    // Operand reads: lane l takes row l % MF of an MFMA block, 16-byte chunk
+    // s * CPS + l / MF of the sub-step (the swizzle of its row depends on l % 16 only).
+    const int lr = lane % MF, kq = lane / MF;
+    const int xr = swz<KC>(lr);
+    const int a_row0 = (wm * 128 + lr) * BK;
+    const int b_row0 = (wn * 128 + lr) * BK;
+    u32x4 fa[2][TM], fb[2][TN];
+    auto read_r = [&](const u16* as, const u16* bs, auto sc, auto bufc, auto rc) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int bf = decltype(bufc)::value;
+        constexpr int r = decltype(rc)::value;
+        const int koff = ((s * CPS + kq) ^ xr) * 8;
+        if constexpr (r < TN)
+            fb[bf][r] = *reinterpret_cast<const u32x4*>(bs + b_row0 + r * MF * BK + koff);
+        else
+            fa[bf][r - TN] =
+                *reinterpret_cast<const u32x4*>(as + a_row0 + (r - TN) * MF * BK + koff);
+    };
+
+    acc_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = acc_t{};
+    // MFMA J of a sub-step from operand buffer bf.  S0 = B rows (n), S1 = A rows (m): a
+    // lane then holds one C row and groups of four consecutive columns.
+    auto mma = [&](auto bufc, auto jc) {
+        constexpr int bf = decltype(bufc)::value;
+        constexpr int J = decltype(jc)::value;
+        constexpr int i = J / TN, j = J % TN;
+        if constexpr (MF == 16)
+            acc[i][j] = mfma_16x16x32<DT>(fb[bf][j], fa[bf][i], acc[i][j]);
+        else
+            acc[i][j] = mfma_32x32x16<DT>(fb[bf][j], fa[bf][i], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // One step: tile t from A slot ia and B slot jb; tile t+1 lies in A slot ia1 and
+    // B slot jb1 (= the other B slot); A slot ia2 takes tile t+2.
+    auto step = [&](int t, int ia, int ia1, int ia2, int jb, int jb1) {
+        const u16* as = lds + ia * SLOT;
+        const u16* bs = lds + (SA + jb) * SLOT;
+        const u16* as1 = lds + ia1 * SLOT;
+        const u16* bs1 = lds + (SA + jb1) * SLOT;
+        const uint32_t a2_at = a_slot(ia2), b_at = b_slot(jb);
+        static_for<0, KS>([&](auto subc) {
+            constexpr int s = decltype(subc)::value;
+            constexpr int cb = s & 1, nb = cb ^ 1;
+            constexpr bool last = s + 1 == KS;
+            constexpr int J0 = last ? PRE : 0;
+            if constexpr (last) {
+                static_for<0, PRE>([&](auto jc) { mma(std::integral_constant<int, cb>{}, jc); });
+                wait_vm_then_sync<NB>();       // tile t+1 landed; the A loads of t+2 may fly
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // the A loads of tile t+2 are dealt over the first SPA MFMA slots of the
+            // sub-steps before the barrier, the reads (and, after the barrier, the B
+            // loads of tile t+2) over the first SPB slots of each sub-step
+            constexpr int PRE_SLOTS = (KS - 1) * NM;
+            constexpr int SA_ = SPA < PRE_SLOTS ? SPA : PRE_SLOTS;
+            constexpr int NL = last ? NB : 0;
+            constexpr int NOPS = NR + NL;
+            constexpr int SS = SPB < NM - J0 ? SPB : NM - J0;
+            static_for<J0, NM>([&](auto jc) {
+                constexpr int J = decltype(jc)::value;
+                mma(std::integral_constant<int, cb>{}, jc);
+                if constexpr (!last) {
+                    constexpr int G = s * NM + J;     // slot index over the pre-barrier sub-steps
+                    static_for<deal<NB, SA_, G>::lo, deal<NB, SA_, G>::hi>([&](auto bc) {
+                        load_b(a2_at, t + 2, std::true_type{}, bc);
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                }
+                static_for<deal<NOPS, SS, J - J0>::lo, deal<NOPS, SS, J - J0>::hi>(
+                    [&](auto oc) {
+                        constexpr int kind = op_kind<NL, NR>(decltype(oc)::value);
+                        if constexpr (kind >= 0)
+                            load_b(b_at, t + 2, std::false_type{},
+                                   std::integral_constant<int, kind>{});
+                        else if constexpr (!last)
+                            read_r(as, bs, std::integral_constant<int, s + 1>{},
+                                   std::integral_constant<int, nb>{},
+                                   std::integral_constant<int, -1 - kind>{});
+                        else
+                            read_r(as1, bs1, std::integral_constant<int, 0>{},
+                                   std::integral_constant<int, nb>{},
+                                   std::integral_constant<int, -1 - kind>{});
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+            });
+        });
+    };
+
+    if (nk > 0) {
+        // tiles 0 and 1 (A then B each); step 0 issues the A loads of tile 2
+        static_for<0, NB>([&](auto bc) { load_b(a_slot(0), 0, std::true_type{}, bc); });
+        static_for<0, NB>([&](auto bc) { load_b(b_slot(0), 0, std::false_type{}, bc); });
+        static_for<0, NB>([&](auto bc) { load_b(a_slot(1), 1, std::true_type{}, bc); });
+        static_for<0, NB>([&](auto bc) { load_b(b_slot(1), 1, std::false_type{}, bc); });
+        wait_vm_then_sync<2 * NB>();              // tile 0 complete
+        static_for<0, NR>([&](auto rc) {
+            read_r(lds, lds + SA * SLOT, std::integral_constant<int, 0>{},
+                   std::integral_constant<int, 0>{}, rc);
+        });
+        int ia = 0;                                // A slot of tile t (t % 3)
+        for (int t = 0; t < nk; ++t) {
+            const int ia1 = ia == SA - 1 ? 0 : ia + 1;
+            const int ia2 = ia1 == SA - 1 ? 0 : ia1 + 1;
+            const int jb = t & 1;
+            step(t, ia, ia1, ia2, jb, jb ^ 1);
+            ia = ia1;
+        }
+        wait_vm<0>();                              // the trailing zero loads
+    }
+
+    // epilogue: one cast, 4 consecutive columns (8 bytes) per store
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int m = m0 + wm * 128 + i * MF + lr;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int g = 0; g < (MF == 16 ? 1 : 4); ++g) {
+                const int n = n0 + wn * 128 + j * MF + (MF == 16 ? 4 * kq : 8 * g + 4 * kq);
                 u32x2 v;
                 v[0] = pack2<DT>(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
                 v[1] = pack2<DT>(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);

@@ -14,6 +14,9 @@ namespace {
 using tgemm::u16;
 
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
+// Leading-dimension bound of the quad kernel: a 64-row block step plus the K offset stays
+// below 2^31 bytes in its 32-bit scalar load offsets.
+constexpr int64_t kMaxQuadLd = int64_t(1) << 24;
 
 // Leading dimensions are in elements: A[m*lda + k] ([M,K]) or A[k*lda + m] ([K,M]);
 // B[n*ldb + k] ([N,K]) or B[k*ldb + n] ([K,N]); C[m*ldc + n].
@@ -63,6 +66,15 @@ hipError_t launch_pingpong(const void* A, const void* B, void* C, int M, int N, 
     return hipGetLastError();
 }
 
+template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL>
+hipError_t launch_quad(const void* A, const void* B, void* C, int M, int N, int K, int lda,
+                       int ldb, int ldc, int group_m, hipStream_t s) {
+    const int gm = cdiv(M, 256), gn = cdiv(N, 256);
+    hipLaunchKernelGGL((tgemm::gemm_quad<DT, MF, PRE, SPA, SPB, STAG, POL>),
+                       dim3((unsigned)(gm * gn)), dim3(256), 0, s, KARGS, gm, gn, group_m);
+    return hipGetLastError();
+}
+
 template <int DT, int MT, int D>
 hipError_t launch_skinny(const void* A, const void* B, void* C, int M, int N, int K, int lda,
                          int ldb, int ldc, int, hipStream_t s) {
@@ -83,27 +95,35 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
 
 #define TILED(DT, AL, L, BM, BN, BK, WM, WN, G)                                           \
     Variant {                                                                              \
-        DT, AL, L, tgemm_config{TGEMM_KERNEL_TILED, BM, BN, BK, WM, WN, 2, G, 1},          \
+        DT, AL, L, tgemm_config{TGEMM_KERNEL_TILED, BM, BN, BK, WM, WN, 2, G, 1, 32},          \
             &launch_tiled<DT, AL, L, BM, BN, BK, WM, WN>                                   \
     }
 #define GENERIC(DT, AL, L)                                                                 \
     Variant {                                                                              \
-        DT, AL, L, tgemm_config{TGEMM_KERNEL_GENERIC, 64, 64, 16, 2, 2, 1, 8, 1},          \
+        DT, AL, L, tgemm_config{TGEMM_KERNEL_GENERIC, 64, 64, 16, 2, 2, 1, 8, 1, 32},      \
             &launch_generic<DT, AL, L>                                                     \
     }
 #define DMA(DT, BM, BN, BK, WM, WN, ST, G)                                                 \
     Variant {                                                                              \
-        DT, 0, 0, tgemm_config{TGEMM_KERNEL_DMA, BM, BN, BK, WM, WN, ST, G, 1},            \
+        DT, 0, 0, tgemm_config{TGEMM_KERNEL_DMA, BM, BN, BK, WM, WN, ST, G, 1, 32},            \
             &launch_dma<DT, BM, BN, BK, WM, WN, ST>                                        \
     }
 #define PINGPONG(DT, AL, L, BM, BN, BK, S, G)                                              \
     Variant {                                                                              \
-        DT, AL, L, tgemm_config{TGEMM_KERNEL_PINGPONG, BM, BN, BK, 2, 4, S, G, 1},         \
+        DT, AL, L, tgemm_config{TGEMM_KERNEL_PINGPONG, BM, BN, BK, 2, 4, S, G, 1, 32},         \
             &launch_pingpong<DT, AL, L, BM, BN, BK, S>                                     \
+    }
+// Quad kernel schedules (pre-barrier MFMAs, A-load and read spreads), from the sweep;
+// K walks staggered per XCD, loads with the sc0 cache policy.
+#define QUAD(DT, MF, G)                                                                    \
+    Variant {                                                                              \
+        DT, 0, 0, tgemm_config{TGEMM_KERNEL_QUAD, 256, 256, 64, 2, 2, 5, G, 1, MF},        \
+            &launch_quad<DT, MF, (MF == 16 ? 2 : 1), (MF == 16 ? 56 : 40),                 \
+                         (MF == 16 ? 40 : 12), 1, 2>                                       \
     }
 #define SKINNY(DT, MT, D)                                                                  \
     Variant {                                                                              \
-        DT, 0, 0, tgemm_config{TGEMM_KERNEL_SKINNY, MT * 32, 32, 64, 1, 8, D, 1, 8},       \
+        DT, 0, 0, tgemm_config{TGEMM_KERNEL_SKINNY, MT * 32, 32, 64, 1, 8, D, 1, 8, 32},       \
             &launch_skinny<DT, MT, D>                                                      \
     }
 // A [M,K], B [N,K]: every kernel
@@ -112,8 +132,8 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
         TILED(DT, 0, 0, 128, 128, 64, 2, 2, 8), TILED(DT, 0, 0, 64, 64, 64, 2, 2, 8),      \
         DMA(DT, 256, 256, 32, 2, 2, 4, 4), DMA(DT, 256, 256, 32, 2, 2, 5, 4),              \
         PINGPONG(DT, 0, 0, 256, 256, 64, 2, 4), PINGPONG(DT, 0, 0, 256, 256, 32, 4, 4),    \
-        PINGPONG(DT, 0, 0, 256, 256, 32, 5, 4), SKINNY(DT, 1, 4), SKINNY(DT, 2, 3),        \
-        SKINNY(DT, 4, 1)
+        PINGPONG(DT, 0, 0, 256, 256, 32, 5, 4), QUAD(DT, 16, 4), QUAD(DT, 32, 4),          \
+        SKINNY(DT, 1, 4), SKINNY(DT, 2, 3), SKINNY(DT, 4, 1)
 // A [M,K], B [K,N]
 #define ALL_MK_KN(DT)                                                                      \
     GENERIC(DT, 0, 1), TILED(DT, 0, 1, 256, 256, 64, 2, 2, 4),                             \
@@ -133,7 +153,7 @@ constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 bool same_shape(const tgemm_config& a, const tgemm_config& b) {
     return a.kernel == b.kernel && a.block_m == b.block_m && a.block_n == b.block_n &&
            a.block_k == b.block_k && a.waves_m == b.waves_m && a.waves_n == b.waves_n &&
-           a.stages == b.stages && a.split_k == b.split_k;
+           a.stages == b.stages && a.split_k == b.split_k && a.mfma == b.mfma;
 }
 
 const Variant* find_variant(int dtype, int a_layout, int layout, const tgemm_config& cfg) {
@@ -153,21 +173,23 @@ tgemm_config choose(int dtype, int a_layout, int layout, int64_t m, int64_t n, i
                     bool aligned) {
     (void)dtype;
     if (!aligned)
-        return tgemm_config{TGEMM_KERNEL_GENERIC, 64, 64, 16, 2, 2, 1, 8, 1};
+        return tgemm_config{TGEMM_KERNEL_GENERIC, 64, 64, 16, 2, 2, 1, 8, 1, 32};
     if (a_layout == TGEMM_A_MK && layout == TGEMM_B_NK && m <= 128 && k >= 1024) {
         const int mt = m <= 32 ? 1 : (m <= 64 ? 2 : 4);
         const int depth = mt == 1 ? 4 : (mt == 2 ? 3 : 1);
-        return tgemm_config{TGEMM_KERNEL_SKINNY, mt * 32, 32, 64, 1, 8, depth, 1, 8};
+        return tgemm_config{TGEMM_KERNEL_SKINNY, mt * 32, 32, 64, 1, 8, depth, 1, 8, 32};
     }
     const int64_t t256 = ((m + 255) / 256) * ((n + 255) / 256);
     const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
+    if (t256 >= 192 && a_layout == TGEMM_A_MK && layout == TGEMM_B_NK)
+        return tgemm_config{TGEMM_KERNEL_QUAD, 256, 256, 64, 2, 2, 5, 4, 1, 16};
     if (t256 >= 192 && a_layout == TGEMM_A_KM)   // the BK 32 ring needs fewer registers
-        return tgemm_config{TGEMM_KERNEL_PINGPONG, 256, 256, 32, 2, 4, 4, 4, 1};
+        return tgemm_config{TGEMM_KERNEL_PINGPONG, 256, 256, 32, 2, 4, 4, 4, 1, 32};
     if (t256 >= 192)
-        return tgemm_config{TGEMM_KERNEL_PINGPONG, 256, 256, 64, 2, 4, 2, 4, 1};
+        return tgemm_config{TGEMM_KERNEL_PINGPONG, 256, 256, 64, 2, 4, 2, 4, 1, 32};
     if (t128 >= 128)
-        return tgemm_config{TGEMM_KERNEL_TILED, 128, 128, 64, 2, 2, 2, 8, 1};
-    return tgemm_config{TGEMM_KERNEL_TILED, 64, 64, 64, 2, 2, 2, 8, 1};
+        return tgemm_config{TGEMM_KERNEL_TILED, 128, 128, 64, 2, 2, 2, 8, 1, 32};
+    return tgemm_config{TGEMM_KERNEL_TILED, 64, 64, 64, 2, 2, 2, 8, 1, 32};
 }
 
 // One product as the caller described it.
@@ -269,6 +291,9 @@ int run(const Problem& p, const tgemm_config* cfg, void* stream) {
         return TGEMM_ERR_UNSUPPORTED;
     if (use.kernel != TGEMM_KERNEL_GENERIC && !aligned)
         return TGEMM_ERR_ALIGNMENT;
+    // the quad kernel steps over 16-row blocks in its scalar load offsets
+    if (use.kernel == TGEMM_KERNEL_QUAD && (p.lda > kMaxQuadLd || p.ldb > kMaxQuadLd))
+        return TGEMM_ERR_UNSUPPORTED;
     const int group_m = use.group_m > 0 ? use.group_m : v->cfg.group_m;
     (void)hipGetLastError();   // start from a clean error state for this launch
     const hipError_t e =

@@ -12,7 +12,7 @@ import os
 F16, BF16 = 0, 1
 B_NK, B_KN = 0, 1
 A_MK, A_KM = 0, 1
-KERNEL_GENERIC, KERNEL_TILED, KERNEL_SKINNY, KERNEL_DMA, KERNEL_PINGPONG = 0, 1, 2, 3, 4
+KERNEL_GENERIC, KERNEL_TILED, KERNEL_SKINNY, KERNEL_DMA, KERNEL_PINGPONG, KERNEL_QUAD = range(6)
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtgemm.so")
@@ -34,7 +34,7 @@ class Config(ctypes.Structure):
                 ("block_n", ctypes.c_int32), ("block_k", ctypes.c_int32),
                 ("waves_m", ctypes.c_int32), ("waves_n", ctypes.c_int32),
                 ("stages", ctypes.c_int32), ("group_m", ctypes.c_int32),
-                ("split_k", ctypes.c_int32)]
+                ("split_k", ctypes.c_int32), ("mfma", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {name: int(getattr(self, name)) for name, _ in self._fields_}
