@@ -92,8 +92,7 @@ typedef enum {
                                  loads; [K,N] B and [K,M] A through transposing reads    */
     TGEMM_KERNEL_QUAD = 5     /* A [M,K], B [N,K] only: one wave per SIMD, each owning a
                                  128x128 quadrant of a 256x256 tile; direct-to-LDS loads
-                                 into three A and two B slots, one barrier per K step;
-                                 lda, ldb <= 2^24 (else TGEMM_ERR_UNSUPPORTED)           */
+                                 into three A and two B slots, one barrier per K step  */
 } tgemm_kernel;
 
 /* One tile configuration.  block_m x block_n is the C tile of one workgroup, block_k

@@ -506,6 +506,33 @@ __device__ __forceinline__ void dma16_at(rsrc4_t r, uint32_t lds_byte, uint32_t 
 #undef TGEMM_DMA_ASM
 }
 
+// Direct-to-LDS loads that walk M0 themselves: set_m0 points M0 at the first 1 KiB
+// destination, and each dma16_next writes the next 1 KiB block and advances M0 by 1 KiB,
+// so consecutive blocks need no M0 set-up of their own.  An M0 write needs one
+// instruction before the next LDS-DMA load: NOP emits it where nothing else intervenes.
+__device__ __forceinline__ void set_m0(uint32_t lds_byte) {
+    asm volatile("s_mov_b32 m0, %0" ::"s"(__builtin_amdgcn_readfirstlane(lds_byte)) : "m0");
+}
+template <int POL, bool NOP>
+__device__ __forceinline__ void dma16_next(rsrc4_t r, uint32_t voff, uint32_t soff) {
+    const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+    if constexpr (NOP) {
+        if constexpr (POL == 2)
+            asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen sc0 lds\n\ts_add_u32 m0, m0, 0x400"
+                         ::"v"(voff), "s"(r), "s"(so) : "memory", "m0");
+        else
+            asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds\n\ts_add_u32 m0, m0, 0x400"
+                         ::"v"(voff), "s"(r), "s"(so) : "memory", "m0");
+    } else {
+        if constexpr (POL == 2)
+            asm volatile("buffer_load_dwordx4 %0, %1, %2 offen sc0 lds\n\ts_add_u32 m0, m0, 0x400"
+                         ::"v"(voff), "s"(r), "s"(so) : "memory", "m0");
+        else
+            asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds\n\ts_add_u32 m0, m0, 0x400"
+                         ::"v"(voff), "s"(r), "s"(so) : "memory", "m0");
+    }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm_then_sync() {
     // This wave's global->LDS loads down to N outstanding, its LDS traffic drained, then
@@ -1009,8 +1036,8 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
 //                        reads of tile t+1's first operands and the B loads of tile t+2
 //                        into the B slot tile t used.
 // An A load has a step and a half to land, a B load one step.  Loads past the last
-// tile are issued out of range (zeros into a slot no step reads), so every step has the
-// same number of loads in flight.  STAG starts the K walk of the workgroups of XCD x at
+// tile fetch tile 0 into a slot no step reads, so every step has the same number of
+// loads in flight.  STAG starts the K walk of the workgroups of XCD x at
 // x/8 of K (wrapping), so that the eight XCDs do not stream the same addresses at once;
 // POL is the cache policy of the loads.
 // ------------------------------------------------------------------------------------
@@ -1070,39 +1097,59 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     const rsrc4_t rb = make_rsrc4(B, span_bytes(N, K, ldb));
 
     // Lane l lands in row r0 + b*ROWS (r0 = 64w + l/KC) of block b at physical chunk
-    // l % KC and fetches the logical chunk that the row's swizzle puts there; the
-    // swizzle repeats every 16 rows, i.e. every two blocks.  Blocks b and b % 2 differ by
-    // a whole number of 16-row strides, which go in the scalar offset; a block's rows lie
-    // inside the operand when b * ROWS < lim (per lane).
+    // l % KC and fetches the logical chunk that the row's swizzle puts there (the swizzle
+    // repeats every 16 rows, i.e. every two blocks).  The byte offset of each block's row
+    // and chunk is computed once, out-of-range for rows past M (A) or N (B); a load adds
+    // the K position of its tile as the scalar offset.
     const int prow = lane / KC, pch = lane % KC;
     const int r0 = 64 * wave + prow;
-    uint32_t a_off[2], b_off[2];
     int kcol[2];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < 2; ++p)
         kcol[p] = (pch ^ swz<KC>(p * ROWS + prow)) * 8;
-        a_off[p] = (uint32_t)((m0 + r0 + p * ROWS) * lda + kcol[p]) * 2u;
-        b_off[p] = (uint32_t)((n0 + r0 + p * ROWS) * ldb + kcol[p]) * 2u;
+    uint32_t a_vo[NB], b_vo[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int ra = m0 + r0 + b * ROWS, rbn = n0 + r0 + b * ROWS;
+        a_vo[b] = ra < M ? (uint32_t)(ra * lda + kcol[b & 1]) * 2u : kOutOfRange;
+        b_vo[b] = rbn < N ? (uint32_t)(rbn * ldb + kcol[b & 1]) * 2u : kOutOfRange;
     }
-    const int a_lim = M - m0 - r0, b_lim = N - n0 - r0;
-    const int kofs = STAG ? (((int)blockIdx.x & 7) * nk) >> 3 : 0;
+    // The K walk: the whole tiles first, starting kofs tiles in (XCD x starts x/8 of the
+    // way along) and wrapping, then the tail tile holding the last K % BK columns, if any.
+    const int nfull = K / BK;
+    const bool tail = nfull < nk;
+    const int kofs = STAG ? (((int)blockIdx.x & 7) * nfull) >> 3 : 0;
     const uint32_t lds0 = lds_addr(lds);
     const uint32_t wave_at = (uint32_t)(64 * wave * BK * 2);
-    // load b (< NB) of operand A (IS_A) or B of tile kt into the slot at LDS byte
-    // address slot_at
-    auto load_b = [&](uint32_t slot_at, int kt, auto isac, auto bc) {
+    // K position of the tile loaded at walk step kt; a step past the end is never read,
+    // so its loads fetch tile 0 (any valid tile would do)
+    auto k_base = [&](int kt) {
+        if (kt >= nk)
+            return 0;
+        if (kt >= nfull)
+            return nfull * BK;
+        return (kt + kofs >= nfull ? kt + kofs - nfull : kt + kofs) * BK;
+    };
+    // Before the tail tile's loads (the last real loads of the walk): chunks past K get
+    // out-of-range offsets (zeros), in place, since every later load is never read.
+    auto mask_tail = [&]() {
+        const int rem = K - nfull * BK;
+        const bool ok0 = kcol[0] < rem, ok1 = kcol[1] < rem;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const bool ok = (b & 1) ? ok1 : ok0;
+            a_vo[b] = ok ? a_vo[b] : kOutOfRange;
+            b_vo[b] = ok ? b_vo[b] : kOutOfRange;
+        }
+    };
+    // Load b (< NB) of operand A (is_a) or B of the tile at K position k0, into the 1 KiB
+    // block M0 points at (the loads of one operand's tile go out in block order, M0 set to
+    // the wave's first block beforehand).
+    auto load_b = [&](int k0, auto isac, auto bc, auto nopc) {
         constexpr bool is_a = decltype(isac)::value;
-        constexpr int b = decltype(bc)::value, p = b & 1;
-        // a tile past the end: every offset gets the out-of-range bit (no branches)
-        const bool live = kt < nk;
-        const int kp = kt + kofs >= nk ? kt + kofs - nk : kt + kofs;
-        const int k0 = live ? kp * BK : 0;
-        const uint32_t dead = live ? 0u : kOutOfRange;
-        const bool ok = (k0 + kcol[p] < K) & (b * ROWS < (is_a ? a_lim : b_lim));
-        const uint32_t row_step = (uint32_t)((b >> 1) * 2 * ROWS) * (uint32_t)(is_a ? lda : ldb);
-        dma16_at<POL>(is_a ? ra : rb, slot_at + wave_at + (uint32_t)(b * ROWS * BK * 2),
-                      (ok ? (is_a ? a_off[p] : b_off[p]) : kOutOfRange) | dead,
-                      (row_step + (uint32_t)k0) * 2u);
+        constexpr int b = decltype(bc)::value;
+        dma16_next<POL, decltype(nopc)::value>(is_a ? ra : rb, is_a ? a_vo[b] : b_vo[b],
+                                               (uint32_t)k0 * 2u);
     };
     auto a_slot = [&](int i) { return lds0 + (uint32_t)(i * SLOT * 2); };
     auto b_slot = [&](int j) { return lds0 + (uint32_t)((SA + j) * SLOT * 2); };
@@ -1153,14 +1200,23 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
         const u16* as1 = lds + ia1 * SLOT;
         const u16* bs1 = lds + (SA + jb1) * SLOT;
         const uint32_t a2_at = a_slot(ia2), b_at = b_slot(jb);
+        const int k2 = k_base(t + 2);                 // this step loads tile t+2
+        if (tail && t + 2 == nfull)
+            mask_tail();
         static_for<0, KS>([&](auto subc) {
             constexpr int s = decltype(subc)::value;
             constexpr int cb = s & 1, nb = cb ^ 1;
             constexpr bool last = s + 1 == KS;
             constexpr int J0 = last ? PRE : 0;
+            if constexpr (s == 0) {
+                set_m0(a2_at + wave_at);               // the A loads of tile t+2
+                __builtin_amdgcn_sched_barrier(0);
+            }
             if constexpr (last) {
                 static_for<0, PRE>([&](auto jc) { mma(std::integral_constant<int, cb>{}, jc); });
                 wait_vm_then_sync<NB>();       // tile t+1 landed; the A loads of t+2 may fly
+                __builtin_amdgcn_sched_barrier(0);
+                set_m0(b_at + wave_at);                // the B loads of tile t+2
                 __builtin_amdgcn_sched_barrier(0);
             }
             // the A loads of tile t+2 are dealt over the first SPA MFMA slots of the
@@ -1177,7 +1233,7 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
                 if constexpr (!last) {
                     constexpr int G = s * NM + J;     // slot index over the pre-barrier sub-steps
                     static_for<deal<NB, SA_, G>::lo, deal<NB, SA_, G>::hi>([&](auto bc) {
-                        load_b(a2_at, t + 2, std::true_type{}, bc);
+                        load_b(k2, std::true_type{}, bc, std::false_type{});
                         __builtin_amdgcn_sched_barrier(0);
                     });
                 }
@@ -1185,8 +1241,8 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
                     [&](auto oc) {
                         constexpr int kind = op_kind<NL, NR>(decltype(oc)::value);
                         if constexpr (kind >= 0)
-                            load_b(b_at, t + 2, std::false_type{},
-                                   std::integral_constant<int, kind>{});
+                            load_b(k2, std::false_type{}, std::integral_constant<int, kind>{},
+                                   std::false_type{});
                         else if constexpr (!last)
                             read_r(as, bs, std::integral_constant<int, s + 1>{},
                                    std::integral_constant<int, nb>{},
@@ -1203,10 +1259,19 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
 
     if (nk > 0) {
         // tiles 0 and 1 (A then B each); step 0 issues the A loads of tile 2
-        static_for<0, NB>([&](auto bc) { load_b(a_slot(0), 0, std::true_type{}, bc); });
-        static_for<0, NB>([&](auto bc) { load_b(b_slot(0), 0, std::false_type{}, bc); });
-        static_for<0, NB>([&](auto bc) { load_b(a_slot(1), 1, std::true_type{}, bc); });
-        static_for<0, NB>([&](auto bc) { load_b(b_slot(1), 1, std::false_type{}, bc); });
+        for (int u = 0; u < 2; ++u) {
+            if (tail && u == nfull)
+                mask_tail();
+            const int ku = k_base(u);
+            set_m0(a_slot(u) + wave_at);
+            static_for<0, NB>([&](auto bc) {
+                load_b(ku, std::true_type{}, bc, std::true_type{});
+            });
+            set_m0(b_slot(u) + wave_at);
+            static_for<0, NB>([&](auto bc) {
+                load_b(ku, std::false_type{}, bc, std::true_type{});
+            });
+        }
         wait_vm_then_sync<2 * NB>();              // tile 0 complete
         static_for<0, NR>([&](auto rc) {
             read_r(lds, lds + SA * SLOT, std::integral_constant<int, 0>{},
@@ -1223,22 +1288,41 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
         wait_vm<0>();                              // the trailing zero loads
     }
 
-    // epilogue: one cast, 4 consecutive columns (8 bytes) per store
+    // Epilogue: one cast per value.  A lane holds groups of four consecutive columns of a
+    // row, which would leave each store as 16 scattered 32-byte pieces; instead each wave
+    // stages its 128 x 128 block in LDS (the ring is free once every wave's loads have
+    // landed and its reads are done; rows padded to 272 bytes so the 8-byte writes of 16
+    // rows fall in distinct banks) and stores it back as 256-byte row segments, 16 bytes
+    // per lane.
+    constexpr int RSE = 128 + 8;                   // staged row stride in elements
+    static_assert(4 * 128 * RSE <= (SA + SB) * SLOT, "C staging fits the LDS ring");
+    wait_vm_then_sync<0>();
+    u16* stage = lds + wave * 128 * RSE;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-        const int m = m0 + wm * 128 + i * MF + lr;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
 #pragma unroll
             for (int g = 0; g < (MF == 16 ? 1 : 4); ++g) {
-                const int n = n0 + wn * 128 + j * MF + (MF == 16 ? 4 * kq : 8 * g + 4 * kq);
+                const int r = i * MF + lr;
+                const int c = j * MF + (MF == 16 ? 4 * kq : 8 * g + 4 * kq);
                 u32x2 v;
                 v[0] = pack2<DT>(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
                 v[1] = pack2<DT>(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-                if (m < M && n < N)
-                    *reinterpret_cast<u32x2*>(C + (size_t)m * ldc + n) = v;
+                *reinterpret_cast<u32x2*>(stage + r * RSE + c) = v;
             }
         }
+    }
+    // a wave's LDS accesses complete in order: its reads below see its writes above
+    const int sr = lane >> 4, sc = (lane & 15) * 8;
+    const int n = n0 + wn * 128 + sc;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+        const int r = 4 * q + sr;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * RSE + sc);
+        const int m = m0 + wm * 128 + r;
+        if (m < M && n < N)
+            *reinterpret_cast<u32x4*>(C + (size_t)m * ldc + n) = v;
     }
 }
 

@@ -14,9 +14,6 @@ namespace {
 using tgemm::u16;
 
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
-// Leading-dimension bound of the quad kernel: a 64-row block step plus the K offset stays
-// below 2^31 bytes in its 32-bit scalar load offsets.
-constexpr int64_t kMaxQuadLd = int64_t(1) << 24;
 
 // Leading dimensions are in elements: A[m*lda + k] ([M,K]) or A[k*lda + m] ([K,M]);
 // B[n*ldb + k] ([N,K]) or B[k*ldb + n] ([K,N]); C[m*ldc + n].
@@ -291,9 +288,6 @@ int run(const Problem& p, const tgemm_config* cfg, void* stream) {
         return TGEMM_ERR_UNSUPPORTED;
     if (use.kernel != TGEMM_KERNEL_GENERIC && !aligned)
         return TGEMM_ERR_ALIGNMENT;
-    // the quad kernel steps over 16-row blocks in its scalar load offsets
-    if (use.kernel == TGEMM_KERNEL_QUAD && (p.lda > kMaxQuadLd || p.ldb > kMaxQuadLd))
-        return TGEMM_ERR_UNSUPPORTED;
     const int group_m = use.group_m > 0 ? use.group_m : v->cfg.group_m;
     (void)hipGetLastError();   // start from a clean error state for this launch
     const hipError_t e =
