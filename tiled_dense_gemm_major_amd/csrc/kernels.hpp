@@ -510,6 +510,8 @@ __device__ __forceinline__ void dma16_at(rsrc4_t r, uint32_t lds_byte, uint32_t 
 // destination, and each dma16_next writes the next 1 KiB block and advances M0 by 1 KiB,
 // so consecutive blocks need no M0 set-up of their own.  An M0 write needs one
 // instruction before the next LDS-DMA load: NOP emits it where nothing else intervenes.
+// The M0 increment also writes SCC, which the asm declares (a condition the compiler
+// keeps in SCC across the load would otherwise be lost).
 __device__ __forceinline__ void set_m0(uint32_t lds_byte) {
     asm volatile("s_mov_b32 m0, %0" ::"s"(__builtin_amdgcn_readfirstlane(lds_byte)) : "m0");
 }
@@ -519,17 +521,17 @@ __device__ __forceinline__ void dma16_next(rsrc4_t r, uint32_t voff, uint32_t so
     if constexpr (NOP) {
         if constexpr (POL == 2)
             asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen sc0 lds\n\ts_add_u32 m0, m0, 0x400"
-                         ::"v"(voff), "s"(r), "s"(so) : "memory", "m0");
+                         ::"v"(voff), "s"(r), "s"(so) : "memory", "m0", "scc");
         else
             asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds\n\ts_add_u32 m0, m0, 0x400"
-                         ::"v"(voff), "s"(r), "s"(so) : "memory", "m0");
+                         ::"v"(voff), "s"(r), "s"(so) : "memory", "m0", "scc");
     } else {
         if constexpr (POL == 2)
             asm volatile("buffer_load_dwordx4 %0, %1, %2 offen sc0 lds\n\ts_add_u32 m0, m0, 0x400"
-                         ::"v"(voff), "s"(r), "s"(so) : "memory", "m0");
+                         ::"v"(voff), "s"(r), "s"(so) : "memory", "m0", "scc");
         else
             asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds\n\ts_add_u32 m0, m0, 0x400"
-                         ::"v"(voff), "s"(r), "s"(so) : "memory", "m0");
+                         ::"v"(voff), "s"(r), "s"(so) : "memory", "m0", "scc");
     }
 }
 
