@@ -23,8 +23,9 @@
  * with an exact sum to within fp32 rounding, not bit for bit.
  *
  * Conventions shared by every entry point:
- *   - Ownership: the caller allocates A, B and C in device memory and keeps ownership.  The library allocates no device memory and keeps
- *     no pointer after the call returns.  C is fully overwritten (no alpha/beta).
+ *   - Ownership: the caller allocates A, B and C (and the workspace of gemm_ex_ws) in
+ *     device memory and keeps ownership.  The library allocates no device memory and
+ *     keeps no pointer after the call returns.  C is fully overwritten (no alpha/beta).
  *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and the call returns at once.  Faults during execution surface at the caller's
  *     next synchronisation with that stream, as for any HIP launch.
@@ -75,7 +76,9 @@ typedef enum {
     TGEMM_ERR_UNSUPPORTED = -5,   /* sizes past the limits, or a configuration that is
                                      not compiled into the library                      */
     TGEMM_ERR_LAUNCH = -6,        /* the HIP launch was refused (no gfx950 device...)   */
-    TGEMM_ERR_DEVICE = -7         /* the current device could not be queried            */
+    TGEMM_ERR_DEVICE = -7,        /* the current device could not be queried            */
+    TGEMM_ERR_WORKSPACE = -8      /* the configuration needs a workspace and none, or
+                                     too small a one, was given                         */
 } tgemm_status;
 
 /* Kernel families in the library. */
@@ -90,17 +93,22 @@ typedef enum {
     TGEMM_KERNEL_PINGPONG = 4,/* 8 waves, two per SIMD, alternating between operand fetch
                                  and back-to-back MFMAs half a period apart; direct-to-LDS
                                  loads; [K,N] B and [K,M] A through transposing reads    */
-    TGEMM_KERNEL_QUAD = 5     /* A [M,K], B [N,K] only: one wave per SIMD, each owning a
+    TGEMM_KERNEL_QUAD = 5,    /* A [M,K], B [N,K] only: one wave per SIMD, each owning a
                                  128x128 quadrant of a 256x256 tile; direct-to-LDS loads
                                  into three A and two B slots, one barrier per K step  */
+    TGEMM_KERNEL_SPLITK = 6   /* A [M,K], B [N,K] only, with a workspace: the K range of
+                                 each C tile split over split_k workgroups (direct-to-LDS
+                                 ring), fp32 partial tiles in the workspace, summed in
+                                 split order and cast by a second kernel               */
 } tgemm_kernel;
 
 /* One tile configuration.  block_m x block_n is the C tile of one workgroup, block_k
  * the K step, waves_m x waves_n the wavefront grid inside the workgroup (64 lanes each),
  * stages the LDS buffers (QUAD: operand slots of block_m x block_k elements, three for
  * A tiles and two for B tiles), group_m the tile rows of one launch-order group,
- * split_k the number of waves that share one C tile's K range (SKINNY only, else 1),
- * and mfma the matrix instruction's block size: 32 (32x32x16) or 16 (16x16x32). */
+ * split_k the number of waves (SKINNY) or workgroups (SPLITK, 2..64, chosen per call)
+ * that share one C tile's K range (else 1), and mfma the matrix instruction's block
+ * size: 32 (32x32x16) or 16 (16x16x32). */
 typedef struct {
     int32_t kernel;
     int32_t block_m, block_n, block_k;
@@ -139,6 +147,28 @@ int gemm_ex(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const voi
             void* C, int b_layout, const tgemm_config* cfg, void* stream);
 
 /*
+ * gemm_ex with a workspace lent by the caller, for configurations that need one
+ * (TGEMM_KERNEL_SPLITK: split_k * m * n * 4 bytes of fp32 partial tiles).  Split-K over
+ * workgroups follows "Tiling a matmul", section "Where it breaks": a product with few
+ * output tiles (small or skinny) leaves compute units idle unless K is split.
+ *   workspace       : device pointer, 16-byte aligned, not overlapping A, B or C; its
+ *                     contents on entry do not matter and are overwritten; the caller
+ *                     keeps ownership and must not reuse it until the stream has run
+ *                     this call (two calls in flight on one workspace race)
+ *   workspace_bytes : its size in bytes (>= 0)
+ *   cfg             : NULL = the table's choice given a workspace (see
+ *                     tgemm_query_config_ws), else as for gemm_ex; a SPLITK configuration
+ *                     names its split count in split_k
+ * Errors as gemm_ex, plus TGEMM_ERR_WORKSPACE (workspace NULL or smaller than the
+ * configuration needs), TGEMM_ERR_ALIGNMENT (workspace not 16-byte aligned) and
+ * TGEMM_ERR_ALIASING (workspace overlapping an operand).  A configuration that needs no
+ * workspace ignores it.
+ */
+int gemm_ex_ws(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const void* B,
+               void* C, int b_layout, const tgemm_config* cfg, void* workspace,
+               int64_t workspace_bytes, void* stream);
+
+/*
  * The general product: either storage of A, either storage of B, leading dimensions.
  *   A        : device pointer; a_layout TGEMM_A_MK: a(m,k) = A[m*lda + k] (lda >= k);
  *              TGEMM_A_KM: a(m,k) = A[k*lda + m] (lda >= m)
@@ -171,6 +201,15 @@ int tgemm_query_config_ex(int dtype, int64_t m, int64_t n, int64_t k, int a_layo
                           int b_layout, int aligned, tgemm_config* out);
 int tgemm_list_configs_ex(int dtype, int a_layout, int b_layout, tgemm_config* out,
                           int capacity);
+
+/* The configuration the table picks when the caller can lend a workspace (A [M,K]), and
+ * the workspace bytes it needs (0 when it needs none).  Host-only. */
+int tgemm_query_config_ws(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
+                          int aligned, tgemm_config* out, int64_t* workspace_bytes);
+
+/* Workspace bytes a configuration needs for an m x n product (0 for all but SPLITK).
+ * Host-only. */
+int tgemm_workspace_size(int64_t m, int64_t n, const tgemm_config* cfg, int64_t* bytes);
 
 /* A static, human-readable name for a status code. */
 const char* tgemm_status_string(int status);

@@ -55,7 +55,14 @@ def run(dtype, A_bits, B_bits, b_layout=B_NK, config=None, c_offset=0, a_offset=
     B = to_dev(B_bits, dtype, b_offset)
     cbuf = torch.full((M * N + c_offset,), fill, dtype=torch.int16, device="cuda")
     C = cbuf[c_offset:].view(tdtype(dtype)).view(M, N)
-    tgemm.gemm_ex(dtype, M, N, K, A, B, C, b_layout, config)
+    ws_bytes = tgemm.workspace_size(M, N, config) if config is not None else 0
+    if ws_bytes:
+        # a split-K configuration: lend it a workspace filled with NaN patterns (its
+        # contents on entry must not matter)
+        ws = torch.full((ws_bytes // 4,), -1, dtype=torch.int32, device="cuda")
+        tgemm.gemm_ex_ws(dtype, M, N, K, A, B, C, ws, ws_bytes, b_layout, config)
+    else:
+        tgemm.gemm_ex(dtype, M, N, K, A, B, C, b_layout, config)
     torch.cuda.synchronize()
     return from_dev(C)
 

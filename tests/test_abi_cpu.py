@@ -35,7 +35,7 @@ def test_exports_every_declared_function(lib):
 
 def test_version_and_status_strings(lib):
     assert tgemm.version() >= 100
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         assert tgemm.status_string(code).startswith("TGEMM_")
     assert "unknown" in tgemm.status_string(-99)
 
@@ -158,3 +158,58 @@ def test_strided_query_and_list(lib):
     assert tgemm.query_config(tgemm.BF16, 64, 8192, 8192, tgemm.B_NK, True,
                               tgemm.A_KM).kernel != tgemm.KERNEL_SKINNY
     assert lib.tgemm_list_configs_ex(1, 2, 0, None, 0) == -1
+
+
+def _splitk(splits):
+    return tgemm.Config(kernel=tgemm.KERNEL_SPLITK, block_m=64, block_n=256, block_k=32,
+                        waves_m=1, waves_n=4, stages=5, group_m=1, split_k=splits, mfma=32)
+
+
+def test_query_config_ws_and_workspace_size(lib):
+    # a skinny product with a long K: split over K, one workgroup per compute unit
+    cfg, nbytes = tgemm.query_config_ws(tgemm.BF16, 64, 8192, 8192)
+    assert cfg.kernel == tgemm.KERNEL_SPLITK and cfg.split_k == 8
+    assert nbytes == 8 * 64 * 8192 * 4 == tgemm.workspace_size(64, 8192, cfg)
+    # enough tiles already, or a short K: the workspace-free choice, no workspace
+    for shape in [(8192, 8192, 8192), (64, 8192, 512), (4000, 3000, 1000)]:
+        cfg, nbytes = tgemm.query_config_ws(tgemm.BF16, *shape)
+        assert cfg.as_dict() == tgemm.query_config(tgemm.BF16, *shape).as_dict()
+        assert nbytes == 0
+    # B [K,N] is not split
+    cfg, nbytes = tgemm.query_config_ws(tgemm.BF16, 64, 8192, 8192, tgemm.B_KN)
+    assert cfg.kernel != tgemm.KERNEL_SPLITK and nbytes == 0
+    # splits between 2 and 64
+    assert tgemm.workspace_size(10, 24, _splitk(64)) == 64 * 10 * 24 * 4
+    for bad in (1, 65):
+        with pytest.raises(tgemm.TGemmError):
+            tgemm.workspace_size(10, 24, _splitk(bad))
+    tiled = [c for c in tgemm.list_configs(tgemm.BF16) if c.kernel == tgemm.KERNEL_TILED][0]
+    assert tgemm.workspace_size(4096, 4096, tiled) == 0
+
+
+def test_workspace_entry_point_errors(lib):
+    f = lib.gemm_ex_ws
+    M, N, K = 64, 1024, 2048
+    A, B, C = FAKE, FAKE + (1 << 24), FAKE + (1 << 25)
+    ws = FAKE + (1 << 26)
+    cfg = _splitk(8)
+    need = 8 * M * N * 4
+
+    def call(c=cfg, w=ws, nbytes=need, a=A, b=B, out=C, layout=0):
+        return f(1, M, N, K, a, b, out, layout, ctypes.byref(c) if c is not None else None,
+                 w, nbytes, None)
+
+    assert call(w=None) == -8                 # no workspace
+    assert call(nbytes=need - 1) == -8        # too small
+    assert call(nbytes=-1) == -1              # negative size
+    assert call(w=ws + 8) == -3               # not 16-byte aligned
+    assert call(w=C + 64) == -4               # overlapping C
+    assert call(w=A) == -4                    # overlapping A
+    assert call(c=_splitk(1)) == -5           # split counts 2..64 only
+    assert call(c=_splitk(65)) == -5
+    assert call(layout=1) == -5               # B [K,N] has no split-K kernel
+    # operands that break the fast-kernel rules
+    assert f(1, M, N, K - 4, A, B, C, 0, ctypes.byref(cfg), ws, need, None) == -3
+    # without a workspace, the table's choice needs none, and empty products stay no-ops
+    assert f(1, 0, N, K, None, None, None, 0, None, None, 0, None) == 0
+    assert lib.gemm_ex(1, M, N, K, A, B, C, 0, ctypes.byref(cfg), None) == -8

@@ -1,0 +1,175 @@
+"""GPU parity of split-K over workgroups (gemm_ex_ws with a lent workspace): the K range
+of each C tile summed by several workgroups into fp32 partial tiles, then added in split
+order and cast once.  Held to the oracle's rule element by element; bit for bit where
+every partial sum is exact; the same bits on every launch (fixed order, no atomics)."""
+import numpy as np
+import pytest
+
+from tests.gpu_util import (assert_parity, from_dev, require_gpu, sample_positions, say,
+                            tdtype, to_dev, torch)
+from tiled_dense_gemm_major_amd.inputs import BF16, B_NK, F16, WORKLOADS, Stream
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _splitk(splits, block_n=256):
+    from tiled_dense_gemm_major_amd import tgemm
+    return tgemm.Config(kernel=tgemm.KERNEL_SPLITK, block_m=64, block_n=block_n, block_k=32,
+                        waves_m=1, waves_n=4, stages=5, group_m=1, split_k=splits, mfma=32)
+
+
+def _run_ws(dtype, A, B, cfg, ws_fill=-1, guard=1024):
+    """C from gemm_ex_ws; the workspace (pre-filled with ws_fill) has a guard band after
+    the bytes the configuration needs, which must stay untouched."""
+    from tiled_dense_gemm_major_amd import tgemm
+    M, K = A.shape
+    N = B.shape[0]
+    need = tgemm.workspace_size(M, N, cfg) if cfg is not None else \
+        tgemm.query_config_ws(dtype, M, N, K)[1]
+    ws = torch.full(((need + guard) // 4,), ws_fill, dtype=torch.int32, device="cuda")
+    C = torch.full((M, N), 0x7E00, dtype=torch.int16, device="cuda").view(tdtype(dtype))
+    tgemm.gemm_ex_ws(dtype, M, N, K, to_dev(A, dtype), to_dev(B, dtype), C, ws, need, B_NK,
+                     cfg)
+    torch.cuda.synchronize()
+    host = ws.cpu().numpy()
+    assert np.all(host[need // 4:] == ws_fill), "workspace written past its size"
+    return from_dev(C)
+
+
+def _inputs(dtype, M, N, K, seed):
+    s = Stream(seed)
+    return s.matrix((M, K), dtype, "uniform"), s.matrix((N, K), dtype, "uniform")
+
+
+def _int_bits(dtype, vals):
+    from tiled_dense_gemm_major_amd.inputs import round_to_bf16_bits, round_to_f16_bits
+    f = round_to_f16_bits if dtype == F16 else round_to_bf16_bits
+    return f(np.asarray(vals, dtype=np.float64))
+
+
+_WANT = {}
+
+
+def _case(orc, dtype, M, N, K):
+    """Seeded inputs and the oracle's product for one (dtype, shape), computed once."""
+    key = (dtype, M, N, K)
+    if key not in _WANT:
+        A, B = _inputs(dtype, M, N, K, 11 + M + N + K)
+        _WANT[key] = (A, B, orc.gemm(dtype, A, B, B_NK))
+    return _WANT[key]
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("shape", [(64, 1024, 2048), (50, 1000, 3000), (1, 264, 1032),
+                                   (128, 520, 4104), (200, 536, 328)])
+@pytest.mark.parametrize("splits", [2, 3, 8, 13, 64])
+@pytest.mark.parametrize("block_n", [256, 128])
+def test_splitk_ragged(dev, orc, dtype, shape, splits, block_n):
+    M, N, K = shape
+    A, B, want = _case(orc, dtype, M, N, K)
+    say(f"split-K {dtype} {shape} splits {splits} block_n {block_n}")
+    got = _run_ws(dtype, A, B, _splitk(splits, block_n))
+    assert_parity(orc, dtype, K, got, want, f"split-K {shape} x{splits}")
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("K", [0, 8, 72, 200, 1000, 2056])
+def test_splitk_exact_small_integers(dev, orc, dtype, K):
+    """Small-integer inputs make every partial sum exact: any split must give the oracle's
+    bits, including splits with nothing to sum (K shorter than the splits)."""
+    rng = np.random.default_rng(K + 5)
+    M, N = 72, 520
+    A = _int_bits(dtype, rng.integers(-2, 3, (M, K)))
+    B = _int_bits(dtype, rng.integers(-2, 3, (N, K)))
+    want = orc.gemm(dtype, A, B, B_NK)
+    if K == 0:
+        # packed operands with K = 0 have lda = 1, which no fast configuration takes: the
+        # table's choice (the generic kernel) writes the empty sums, with a workspace lent
+        say(f"split-K entry point K=0 {dtype}")
+        assert np.array_equal(_run_ws(dtype, A, B, None), want)
+        return
+    for splits in (2, 5, 8, 32):
+        say(f"split-K exact {dtype} K={K} splits {splits}")
+        assert np.array_equal(_run_ws(dtype, A, B, _splitk(splits)), want), (K, splits)
+
+
+def test_splitk_table_choice_skinny_workload(dev, orc):
+    """The skinny workload at full size through the table's choice with a workspace
+    (the split-K kernel), on sampled entries summed one by one by the oracle."""
+    from tiled_dense_gemm_major_amd import tgemm
+    w = WORKLOADS["bf16_skinny_64x8192x8192"]
+    cfg, need = tgemm.query_config_ws(w.dtype, w.M, w.N, w.K)
+    assert cfg.kernel == tgemm.KERNEL_SPLITK and need > 0
+    A, B = w.generate()
+    say(f"split-K table choice {w.describe()} splits {cfg.split_k}")
+    got = _run_ws(w.dtype, A, B, None)
+    assert not np.any(got == 0x7E00)
+    rows, cols = sample_positions(w.M, w.N, 3000, w.seed)
+    want, _ = orc.gemm_entries(w.dtype, A, B, w.b_layout, rows, cols)
+    assert_parity(orc, w.dtype, w.K, got[rows, cols], want, "skinny split-K")
+
+
+def test_splitk_repeat_launches_bitwise_identical(dev, orc):
+    from tiled_dense_gemm_major_amd import tgemm
+    M, N, K = 96, 4096, 8192
+    A, B = _inputs(BF16, M, N, K, 23)
+    Ad, Bd = to_dev(A, BF16), to_dev(B, BF16)
+    cfg = _splitk(16)
+    need = tgemm.workspace_size(M, N, cfg)
+    ws = torch.empty((need // 4,), dtype=torch.int32, device="cuda")
+    C0 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    tgemm.gemm_ex_ws(BF16, M, N, K, Ad, Bd, C0, ws, need, B_NK, cfg)
+    torch.cuda.synchronize()
+    ref = from_dev(C0)
+    rows, cols = sample_positions(M, N, 500, 23)
+    want, _ = orc.gemm_entries(BF16, A, B, B_NK, rows, cols)
+    assert_parity(orc, BF16, K, ref[rows, cols], want, "split-K sampled")
+    say("split-K repeat launches")
+    C = torch.empty_like(C0)
+    for _ in range(20):
+        tgemm.gemm_ex_ws(BF16, M, N, K, Ad, Bd, C, ws, need, B_NK, cfg)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(C), ref)
+
+
+def test_splitk_does_not_write_outside_c(dev, orc):
+    from tiled_dense_gemm_major_amd import tgemm
+    M, N, K = 70, 264, 1032
+    A, B = _inputs(F16, M, N, K, 4)
+    guard = 4096
+    buf = torch.full((guard + M * N + guard,), 0x1234, dtype=torch.int16, device="cuda")
+    C = buf[guard:guard + M * N].view(torch.float16).view(M, N)
+    cfg = _splitk(8)
+    need = tgemm.workspace_size(M, N, cfg)
+    ws = torch.empty((need // 4,), dtype=torch.int32, device="cuda")
+    say("split-K guard bands")
+    tgemm.gemm_ex_ws(F16, M, N, K, to_dev(A, F16), to_dev(B, F16), C, ws, need, B_NK, cfg)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    assert np.all(host[:guard] == 0x1234) and np.all(host[guard + M * N:] == 0x1234)
+    assert_parity(orc, F16, K, host[guard:guard + M * N].view(np.uint16).reshape(M, N),
+                  orc.gemm(F16, A, B, B_NK), "split-K guard")
+
+
+def test_splitk_one_workspace_many_shapes(dev, orc):
+    """One workspace through a sequence of different shapes and split counts: what a call
+    leaves behind must not leak into the next."""
+    from tiled_dense_gemm_major_amd import tgemm
+    shapes = [(64, 1024, 2048, 8), (128, 2048, 1032, 4), (8, 264, 4104, 16), (64, 1024, 2048, 3),
+              (200, 536, 328, 64)]
+    need = max(tgemm.workspace_size(M, N, _splitk(sk)) for M, N, K, sk in shapes)
+    ws = torch.empty((need // 4,), dtype=torch.int32, device="cuda")
+    for rep in range(2):
+        for M, N, K, sk in shapes:
+            A, B, want = _case(orc, BF16, M, N, K)
+            C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            say(f"one workspace {M}x{N}x{K} splits {sk} pass {rep}")
+            tgemm.gemm_ex_ws(BF16, M, N, K, to_dev(A, BF16), to_dev(B, BF16), C, ws, need,
+                             B_NK, _splitk(sk))
+            torch.cuda.synchronize()
+            assert_parity(orc, BF16, K, from_dev(C), want, f"{M}x{N}x{K} x{sk}")

@@ -450,12 +450,22 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
 //   (l % KC) ^ swz(row) of that row -- the placement the fragment reads expect.
 //   Requirements as for gemm_tiled.  A chunk past K or a row past M/N is read out of
 //   range, which the hardware turns into zeros written to LDS.
-// Per step t (compute tile t from stage t % STAGES):
-//   substep 0: MFMAs; read the operands of substep 1; issue tile t+STAGES-1's loads into
-//              the stage tile t-1 used (free since the previous step's barrier);
-//   substep 1: one MFMA; wait until this wave's loads of tile t+1 have landed and meet the
-//              other waves (tile t+1 complete, tile t no longer read); the remaining
-//              MFMAs with the reads of tile t+1's first operands.
+// Per step t (compute tile t from stage t % STAGES, BK / 16 substeps, an even number):
+//   substep 0     : MFMAs; read the operands of substep 1; issue tile t+STAGES-1's loads
+//                   into the stage tile t-1 used (free since the previous step's barrier);
+//   substep s     : MFMAs; read the operands of substep s+1;
+//   last substep  : one MFMA; wait until this wave's loads of tile t+1 have landed and
+//                   meet the other waves (tile t+1 complete, tile t no longer read); the
+//                   remaining MFMAs with the reads of tile t+1's first operands.
+// BK = 64 makes every row segment a whole 128-byte line (one request per line).
+// SPLIT: split-K over workgroups ("Tiling a matmul", section "Where it breaks": a grid of
+// few output tiles leaves compute units idle; splitting K gives each of them work).
+// Workgroup (tile, z) sums k in [z*kc, min(K, (z+1)*kc)) (kc a multiple of BK) and
+// writes its fp32 partial tile to W[z][m][n] (packed [M,N] per split) instead of C;
+// splitk_reduce, the next kernel on the stream, adds the partials in split order, casts
+// once and stores C.  (Summing in the last workgroup of each tile instead, behind a
+// device-scope arrival counter, measured slower on gfx950: the partials then have to be
+// made coherent across the XCDs inside the kernel.)
 // ------------------------------------------------------------------------------------
 // The same buffer resource as four dwords (base address low/high, size, format), for the
 // direct-to-LDS loads below.
@@ -536,17 +546,30 @@ __device__ __forceinline__ void dma16_next(rsrc4_t r, uint32_t voff, uint32_t so
 }
 
 template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm_sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int N>
 __device__ __forceinline__ void wait_vm_then_sync() {
     // This wave's global->LDS loads down to N outstanding, its LDS traffic drained, then
     // the workgroup barrier.
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int DT, int BM, int BN, int BK, int WM, int WN, int STAGES>
+template <int DT, int BM, int BN, int BK, int WM, int WN, int STAGES, bool SPLIT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64),
                                amdgpu_waves_per_eu(1, 1)))
 gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
-         int N, int K, int lda, int ldb, int ldc, int grid_m, int grid_n, int group_m) {
+         int N, int K, int lda, int ldb, int ldc, int grid_m, int grid_n, int group_m,
+         float* __restrict__ W, int kc) {
     constexpr int NW = WM * WN;
     constexpr int KC = BK / 8;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -558,7 +581,7 @@ gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__
     constexpr int A_LD = BM / ROWS / NW;          // A loads per wave per tile
     constexpr int B_LD = BN / ROWS / NW;
     constexpr int LD = A_LD + B_LD;
-    static_assert(KS == 2, "two k-substeps per tile");
+    static_assert(KS % 2 == 0, "an even number of k-substeps per tile");
     static_assert((BM / ROWS) % NW == 0 && (BN / ROWS) % NW == 0, "bad load split");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(STAGES >= 3 && LD * (STAGES - 2) <= 63, "vmcnt range");
@@ -571,7 +594,10 @@ gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__
     const int m0 = tm * BM, n0 = tn * BN;
     const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const int nk = (K + BK - 1) / BK;
+    // this workgroup's K range [kb, ke)
+    const int kb = SPLIT ? (int)blockIdx.y * kc : 0;
+    const int ke = SPLIT ? (K - kb < kc ? K : kb + kc) : K;
+    const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
 
     const rsrc4_t ra = make_rsrc4(A, span_bytes(M, K, lda));
     const rsrc4_t rb = make_rsrc4(B, span_bytes(N, K, ldb));
@@ -598,14 +624,14 @@ gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__
     auto dma = [&](int kt, auto ic) {
         constexpr int i = decltype(ic)::value;
         const bool live = kt < nk;
-        const int k0 = live ? kt * BK : 0;
+        const int k0 = live ? kb + kt * BK : 0;
         u16* st = stage_ptr(kt);
         if constexpr (i < A_LD)
             dma16(ra, st + (wave * A_LD + i) * ROWS * BK,
-                     live && k0 + a_kc[i] < K ? a_off[i] : kOutOfRange, (uint32_t)k0 * 2u);
+                     live && k0 + a_kc[i] < ke ? a_off[i] : kOutOfRange, (uint32_t)k0 * 2u);
         else
             dma16(rb, st + A_ELEMS + (wave * B_LD + (i - A_LD)) * ROWS * BK,
-                     live && k0 + b_kc[i - A_LD] < K ? b_off[i - A_LD] : kOutOfRange,
+                     live && k0 + b_kc[i - A_LD] < ke ? b_off[i - A_LD] : kOutOfRange,
                      (uint32_t)k0 * 2u);
     };
 
@@ -648,9 +674,9 @@ gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__
                 static_for<0, SLOTS>([&](auto jc) {
                     constexpr int J = decltype(jc)::value;
                     constexpr int i = J / TN, j = J % TN;
-                    acc[i][j] = mfma_32x32x16<DT>(fb[S][j], fa[S][i], acc[i][j]);
+                    acc[i][j] = mfma_32x32x16<DT>(fb[S & 1][j], fa[S & 1][i], acc[i][j]);
                     __builtin_amdgcn_sched_barrier(0);
-                    if constexpr (S == 1 && J == 0) {
+                    if constexpr (S == KS - 1 && J == 0) {
                         wait_vm_then_sync<LD * (STAGES - 2)>();
                         __builtin_amdgcn_sched_barrier(0);
                     }
@@ -659,8 +685,9 @@ gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__
                     static_for<lo, hi>([&](auto oc) {
                         constexpr int O = decltype(oc)::value;
                         if constexpr (O < NR) {
-                            if constexpr (S == 0)
-                                read_frag(cur, 1, 1, std::integral_constant<int, O>{});
+                            if constexpr (S + 1 < KS)
+                                read_frag(cur, S + 1, (S + 1) & 1,
+                                          std::integral_constant<int, O>{});
                             else
                                 read_frag(nxt, 0, 0, std::integral_constant<int, O>{});
                         } else {
@@ -673,23 +700,88 @@ gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__
         }
     }
 
+    wait_vm<0>();                                  // the trailing loads into LDS
+
+    // a lane's C elements: row m(i), four consecutive columns n(j, g)
+    auto m_of = [&](int i) { return m0 + wm * WTM + i * 32 + (lane & 31); };
+    auto n_of = [&](int j, int g) { return n0 + wn * WTN + j * 32 + 8 * g + 4 * half; };
+    auto quad = [&](int i, int j, int g) {
+        return f32x4{acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                     acc[i][j][4 * g + 3]};
+    };
+    auto store_c = [&](int m, int n, f32x4 v) {
+        u32x2 p;
+        p[0] = pack2<DT>(v[0], v[1]);
+        p[1] = pack2<DT>(v[2], v[3]);
+        if (m < M && n < N)
+            *reinterpret_cast<u32x2*>(C + (size_t)m * ldc + n) = p;
+    };
+    if constexpr (!SPLIT) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int m = m0 + wm * WTM + i * 32 + (lane & 31);
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * half;
-                u32x2 v;
-                v[0] = pack2<DT>(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-                v[1] = pack2<DT>(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-                if (m < M && n < N)
-                    *reinterpret_cast<u32x2*>(C + (size_t)m * ldc + n) = v;
+                for (int g = 0; g < 4; ++g)
+                    store_c(m_of(i), n_of(j, g), quad(i, j, g));
+    } else {
+        const size_t plane = (size_t)M * (size_t)N;
+        float* wz = W + (size_t)blockIdx.y * plane;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int m = m_of(i), n = n_of(j, g);
+                    if (m < M && n < N)
+                        *reinterpret_cast<f32x4*>(wz + (size_t)m * N + n) = quad(i, j, g);
+                }
+    }
+}
+
+// C = cast(sum over z of W[z]), the partial tiles of a split-K product summed in split
+// order (a fixed order: repeated calls give the same bits).  One thread per 8
+// consecutive columns of a row of C (N is a multiple of 8).  The partials are fetched
+// eight splits at a time, all loads in flight before the first add.
+template <int DT>
+__global__ void __launch_bounds__(256)
+splitk_reduce(const float* __restrict__ W, u16* __restrict__ C, int M, int N, int ldc,
+              int S) {
+    constexpr int U = 8;
+    const int per_row = N >> 3;
+    const int idx = (int)blockIdx.x * 256 + (int)threadIdx.x;
+    if (idx >= M * per_row)
+        return;
+    const int m = idx / per_row, n = (idx - m * per_row) * 8;
+    const size_t plane = (size_t)M * (size_t)N;
+    const float* p = W + (size_t)m * (size_t)N + n;
+    f32x4 lo = {0.0f, 0.0f, 0.0f, 0.0f}, hi = lo;
+    for (int z0 = 0; z0 < S; z0 += U) {
+        f32x4 a[U], b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (z0 + u < S) {
+                a[u] = *reinterpret_cast<const f32x4*>(p + (size_t)(z0 + u) * plane);
+                b[u] = *reinterpret_cast<const f32x4*>(p + (size_t)(z0 + u) * plane + 4);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (z0 + u < S) {
+                lo += a[u];
+                hi += b[u];
             }
         }
     }
+    u32x4 v;
+    v[0] = pack2<DT>(lo[0], lo[1]);
+    v[1] = pack2<DT>(lo[2], lo[3]);
+    v[2] = pack2<DT>(hi[0], hi[1]);
+    v[3] = pack2<DT>(hi[2], hi[3]);
+    *reinterpret_cast<u32x4*>(C + (size_t)m * ldc + n) = v;
 }
+
 
 // ------------------------------------------------------------------------------------
 // Ping-pong kernel.
@@ -712,18 +804,6 @@ gemm_dma(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__
 //   phases are half as long and the ring twice as deep (4-5 stages in 160 KiB), which
 //   hides a longer memory latency at the cost of twice as many barriers.
 // ------------------------------------------------------------------------------------
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_lgkm() {
-    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void wait_lgkm_sync() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 template <int DT, int ALAYOUT, int LAYOUT, int BM, int BN, int BK, int STAGES>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512),
                                amdgpu_waves_per_eu(2, 2)))

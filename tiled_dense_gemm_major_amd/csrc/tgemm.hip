@@ -19,14 +19,22 @@ constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
 // B[n*ldb + k] ([N,K]) or B[k*ldb + n] ([K,N]); C[m*ldc + n].
 typedef hipError_t (*launch_fn)(const void* A, const void* B, void* C, int M, int N, int K,
                                 int lda, int ldb, int ldc, int group_m, hipStream_t s);
+// Split-K launches also take the number of K splits and the caller's workspace.
+typedef hipError_t (*splitk_fn)(const void* A, const void* B, void* C, int M, int N, int K,
+                                int lda, int ldb, int ldc, int group_m, int splits, void* ws,
+                                hipStream_t s);
 
 struct Variant {
     int dtype;
     int a_layout;
     int layout;
     tgemm_config cfg;
-    launch_fn launch;
+    launch_fn launch;              // every kernel but SPLITK
+    splitk_fn split_launch;        // SPLITK only
 };
+
+// Split-K bounds: at least 2 and at most kMaxSplits workgroups per C tile.
+constexpr int kMaxSplits = 64;
 
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -48,9 +56,30 @@ template <int DT, int BM, int BN, int BK, int WM, int WN, int STAGES>
 hipError_t launch_dma(const void* A, const void* B, void* C, int M, int N, int K, int lda,
                       int ldb, int ldc, int group_m, hipStream_t s) {
     const int gm = cdiv(M, BM), gn = cdiv(N, BN);
-    hipLaunchKernelGGL((tgemm::gemm_dma<DT, BM, BN, BK, WM, WN, STAGES>),
+    hipLaunchKernelGGL((tgemm::gemm_dma<DT, BM, BN, BK, WM, WN, STAGES, false>),
                        dim3((unsigned)(gm * gn)), dim3(WM * WN * 64), 0, s, KARGS, gm, gn,
-                       group_m);
+                       group_m, static_cast<float*>(nullptr), 0);
+    return hipGetLastError();
+}
+
+// Split-K: splits workgroups per C tile, each over a whole number of K steps, write fp32
+// partial tiles to the workspace ([splits][M][N]); a second kernel sums them in split
+// order and writes C.
+template <int DT, int BM, int BN, int BK, int WM, int WN, int STAGES>
+hipError_t launch_splitk(const void* A, const void* B, void* C, int M, int N, int K, int lda,
+                         int ldb, int ldc, int group_m, int splits, void* ws, hipStream_t s) {
+    const int gm = cdiv(M, BM), gn = cdiv(N, BN);
+    const int kc = cdiv(cdiv(K, splits), BK) * BK;
+    float* W = static_cast<float*>(ws);
+    hipLaunchKernelGGL((tgemm::gemm_dma<DT, BM, BN, BK, WM, WN, STAGES, true>),
+                       dim3((unsigned)(gm * gn), (unsigned)splits), dim3(WM * WN * 64), 0, s,
+                       KARGS, gm, gn, group_m, W, kc);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((tgemm::splitk_reduce<DT>), dim3((unsigned)cdiv(M * (N / 8), 256)),
+                       dim3(256), 0, s, static_cast<const float*>(W), static_cast<u16*>(C), M,
+                       N, ldc, splits);
     return hipGetLastError();
 }
 
@@ -118,6 +147,12 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
             &launch_quad<DT, MF, (MF == 16 ? 2 : 1), (MF == 16 ? 56 : 40),                 \
                          (MF == 16 ? 40 : 12), 1, 2>                                       \
     }
+// Split-K over workgroups (registry entries carry split_k = 2; a call gives its own count).
+#define SPLITK(DT, BM, BN, BK, WM, WN, ST, G)                                              \
+    Variant {                                                                              \
+        DT, 0, 0, tgemm_config{TGEMM_KERNEL_SPLITK, BM, BN, BK, WM, WN, ST, G, 2, 32},         \
+            nullptr, &launch_splitk<DT, BM, BN, BK, WM, WN, ST>                            \
+    }
 #define SKINNY(DT, MT, D)                                                                  \
     Variant {                                                                              \
         DT, 0, 0, tgemm_config{TGEMM_KERNEL_SKINNY, MT * 32, 32, 64, 1, 8, D, 1, 8, 32},       \
@@ -130,7 +165,10 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
         DMA(DT, 256, 256, 32, 2, 2, 4, 4), DMA(DT, 256, 256, 32, 2, 2, 5, 4),              \
         PINGPONG(DT, 0, 0, 256, 256, 64, 2, 4), PINGPONG(DT, 0, 0, 256, 256, 32, 4, 4),    \
         PINGPONG(DT, 0, 0, 256, 256, 32, 5, 4), QUAD(DT, 16, 4), QUAD(DT, 32, 4),          \
-        SKINNY(DT, 1, 4), SKINNY(DT, 2, 3), SKINNY(DT, 4, 1)
+        SKINNY(DT, 1, 4), SKINNY(DT, 2, 3), SKINNY(DT, 4, 1),                              \
+        SPLITK(DT, 64, 256, 32, 1, 4, 5, 1), SPLITK(DT, 64, 128, 32, 1, 4, 5, 1),          \
+        SPLITK(DT, 64, 256, 64, 1, 4, 4, 1), SPLITK(DT, 64, 128, 64, 1, 4, 4, 1),          \
+        SPLITK(DT, 64, 128, 64, 1, 4, 6, 1)
 // A [M,K], B [K,N]
 #define ALL_MK_KN(DT)                                                                      \
     GENERIC(DT, 0, 1), TILED(DT, 0, 1, 256, 256, 64, 2, 2, 4),                             \
@@ -148,9 +186,13 @@ const Variant kVariants[] = {
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
 bool same_shape(const tgemm_config& a, const tgemm_config& b) {
+    // a split-K configuration's split count is a per-call choice
+    const bool split_ok = a.kernel == TGEMM_KERNEL_SPLITK
+                              ? b.split_k >= 2 && b.split_k <= kMaxSplits
+                              : a.split_k == b.split_k;
     return a.kernel == b.kernel && a.block_m == b.block_m && a.block_n == b.block_n &&
            a.block_k == b.block_k && a.waves_m == b.waves_m && a.waves_n == b.waves_n &&
-           a.stages == b.stages && a.split_k == b.split_k && a.mfma == b.mfma;
+           a.stages == b.stages && split_ok && a.mfma == b.mfma;
 }
 
 const Variant* find_variant(int dtype, int a_layout, int layout, const tgemm_config& cfg) {
@@ -187,6 +229,32 @@ tgemm_config choose(int dtype, int a_layout, int layout, int64_t m, int64_t n, i
     if (t128 >= 128)
         return tgemm_config{TGEMM_KERNEL_TILED, 128, 128, 64, 2, 2, 2, 8, 1, 32};
     return tgemm_config{TGEMM_KERNEL_TILED, 64, 64, 64, 2, 2, 2, 8, 1, 32};
+}
+
+// The table when the caller lends a workspace: a grid of few output tiles with a long K
+// ("Tiling a matmul", section "Where it breaks": skinny products leave compute units
+// idle) is split over K so that about one workgroup per compute unit runs, each split
+// at least 256 deep; everything else as without a workspace.
+tgemm_config choose_ws(int dtype, int a_layout, int layout, int64_t m, int64_t n, int64_t k,
+                       bool aligned) {
+    const tgemm_config plain = choose(dtype, a_layout, layout, m, n, k, aligned);
+    if (!aligned || a_layout != TGEMM_A_MK || layout != TGEMM_B_NK || m > 128 || k < 1024)
+        return plain;
+    const int64_t tiles = ((m + 63) / 64) * ((n + 255) / 256);
+    int64_t splits = 256 / (tiles > 0 ? tiles : 1);
+    if (splits > k / 256)
+        splits = k / 256;
+    if (splits > kMaxSplits)
+        splits = kMaxSplits;
+    if (splits < 2)
+        return plain;
+    return tgemm_config{TGEMM_KERNEL_SPLITK, 64, 256, 64, 1, 4, 4, 1, (int32_t)splits, 32};
+}
+
+// Workspace bytes of a configuration for an m x n product: the fp32 partial tiles of a
+// split-K configuration, nothing for the others.
+int64_t workspace_bytes(const tgemm_config& cfg, int64_t m, int64_t n) {
+    return cfg.kernel == TGEMM_KERNEL_SPLITK ? (int64_t)cfg.split_k * m * n * 4 : 0;
 }
 
 // One product as the caller described it.
@@ -267,7 +335,7 @@ bool fast_aligned(const Problem& p) {
            2 * span_b(p) <= kMaxFastOperandBytes;
 }
 
-int run(const Problem& p, const tgemm_config* cfg, void* stream) {
+int run(const Problem& p, const tgemm_config* cfg, void* ws, int64_t ws_bytes, void* stream) {
     int rc = check_problem(p);
     if (rc != TGEMM_OK)
         return rc;
@@ -282,17 +350,33 @@ int run(const Problem& p, const tgemm_config* cfg, void* stream) {
         return TGEMM_ERR_ALIASING;
     const bool aligned = fast_aligned(p);
     tgemm_config use =
-        cfg ? *cfg : choose(p.dtype, p.a_layout, p.b_layout, p.m, p.n, p.k, aligned);
+        cfg ? *cfg
+            : (ws ? choose_ws(p.dtype, p.a_layout, p.b_layout, p.m, p.n, p.k, aligned)
+                  : choose(p.dtype, p.a_layout, p.b_layout, p.m, p.n, p.k, aligned));
     const Variant* v = find_variant(p.dtype, p.a_layout, p.b_layout, use);
     if (!v)
         return TGEMM_ERR_UNSUPPORTED;
     if (use.kernel != TGEMM_KERNEL_GENERIC && !aligned)
         return TGEMM_ERR_ALIGNMENT;
+    const int64_t need = workspace_bytes(use, p.m, p.n);
+    if (need > 0) {
+        if (!ws || ws_bytes < need)
+            return TGEMM_ERR_WORKSPACE;
+        if ((uintptr_t)ws % 16 != 0)
+            return TGEMM_ERR_ALIGNMENT;
+        if (overlaps(ws, need, p.A, 2 * span_a(p)) || overlaps(ws, need, p.B, 2 * span_b(p)) ||
+            overlaps(ws, need, p.C, 2 * span_c(p)))
+            return TGEMM_ERR_ALIASING;
+    }
     const int group_m = use.group_m > 0 ? use.group_m : v->cfg.group_m;
     (void)hipGetLastError();   // start from a clean error state for this launch
     const hipError_t e =
-        v->launch(p.A, p.B, p.C, (int)p.m, (int)p.n, (int)p.k, (int)p.lda, (int)p.ldb,
-                  (int)p.ldc, group_m, static_cast<hipStream_t>(stream));
+        v->split_launch
+            ? v->split_launch(p.A, p.B, p.C, (int)p.m, (int)p.n, (int)p.k, (int)p.lda,
+                              (int)p.ldb, (int)p.ldc, group_m, use.split_k, ws,
+                              static_cast<hipStream_t>(stream))
+            : v->launch(p.A, p.B, p.C, (int)p.m, (int)p.n, (int)p.k, (int)p.lda, (int)p.ldb,
+                        (int)p.ldc, group_m, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
 }
 
@@ -306,13 +390,14 @@ Problem packed(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const 
 }
 
 int query(int dtype, int64_t m, int64_t n, int64_t k, int a_layout, int b_layout, int aligned,
-          tgemm_config* out) {
+          tgemm_config* out, bool with_ws = false) {
     int rc = check_sizes(dtype, m, n, k, a_layout, b_layout);
     if (rc != TGEMM_OK)
         return rc;
     if (!out)
         return TGEMM_ERR_NULL_POINTER;
-    *out = choose(dtype, a_layout, b_layout, m, n, k, aligned != 0);
+    *out = with_ws ? choose_ws(dtype, a_layout, b_layout, m, n, k, aligned != 0)
+                   : choose(dtype, a_layout, b_layout, m, n, k, aligned != 0);
     const Variant* v = find_variant(dtype, a_layout, b_layout, *out);
     if (v)
         out->group_m = v->cfg.group_m;
@@ -346,24 +431,33 @@ extern "C" {
 
 int gemm_f16(int64_t m, int64_t n, int64_t k, const void* A, const void* B, void* C,
              int b_layout, void* stream) {
-    return run(packed(TGEMM_F16, m, n, k, A, B, C, b_layout), nullptr, stream);
+    return run(packed(TGEMM_F16, m, n, k, A, B, C, b_layout), nullptr, nullptr, 0, stream);
 }
 
 int gemm_bf16(int64_t m, int64_t n, int64_t k, const void* A, const void* B, void* C,
               int b_layout, void* stream) {
-    return run(packed(TGEMM_BF16, m, n, k, A, B, C, b_layout), nullptr, stream);
+    return run(packed(TGEMM_BF16, m, n, k, A, B, C, b_layout), nullptr, nullptr, 0, stream);
 }
 
 int gemm_ex(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const void* B, void* C,
             int b_layout, const tgemm_config* cfg, void* stream) {
-    return run(packed(dtype, m, n, k, A, B, C, b_layout), cfg, stream);
+    return run(packed(dtype, m, n, k, A, B, C, b_layout), cfg, nullptr, 0, stream);
+}
+
+int gemm_ex_ws(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const void* B,
+               void* C, int b_layout, const tgemm_config* cfg, void* workspace,
+               int64_t workspace_bytes, void* stream) {
+    if (workspace_bytes < 0)
+        return TGEMM_ERR_INVALID_VALUE;
+    return run(packed(dtype, m, n, k, A, B, C, b_layout), cfg, workspace, workspace_bytes,
+               stream);
 }
 
 int gemm_strided(int dtype, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
                  int a_layout, const void* B, int64_t ldb, int b_layout, void* C, int64_t ldc,
                  const tgemm_config* cfg, void* stream) {
     return run(Problem{dtype, m, n, k, A, lda, a_layout, B, ldb, b_layout, C, ldc}, cfg,
-               stream);
+               nullptr, 0, stream);
 }
 
 int tgemm_query_config(int dtype, int64_t m, int64_t n, int64_t k, int b_layout, int aligned,
@@ -374,6 +468,30 @@ int tgemm_query_config(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
 int tgemm_query_config_ex(int dtype, int64_t m, int64_t n, int64_t k, int a_layout,
                           int b_layout, int aligned, tgemm_config* out) {
     return query(dtype, m, n, k, a_layout, b_layout, aligned, out);
+}
+
+int tgemm_query_config_ws(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
+                          int aligned, tgemm_config* out, int64_t* workspace_bytes_out) {
+    if (!workspace_bytes_out)
+        return TGEMM_ERR_NULL_POINTER;
+    const int rc = query(dtype, m, n, k, TGEMM_A_MK, b_layout, aligned, out, true);
+    if (rc != TGEMM_OK)
+        return rc;
+    *workspace_bytes_out = workspace_bytes(*out, m, n);
+    return TGEMM_OK;
+}
+
+int tgemm_workspace_size(int64_t m, int64_t n, const tgemm_config* cfg, int64_t* bytes) {
+    if (!cfg || !bytes)
+        return TGEMM_ERR_NULL_POINTER;
+    if (m < 0 || n < 0)
+        return TGEMM_ERR_INVALID_VALUE;
+    if (cfg->kernel == TGEMM_KERNEL_SPLITK && (cfg->split_k < 2 || cfg->split_k > kMaxSplits))
+        return TGEMM_ERR_UNSUPPORTED;
+    if (m > kMaxElems || n > kMaxElems || (n > 0 && m > kMaxElems / n))
+        return TGEMM_ERR_UNSUPPORTED;
+    *bytes = workspace_bytes(*cfg, m, n);
+    return TGEMM_OK;
 }
 
 int tgemm_list_configs(int dtype, int b_layout, tgemm_config* out, int capacity) {
@@ -396,10 +514,12 @@ const char* tgemm_status_string(int status) {
     case TGEMM_ERR_UNSUPPORTED: return "TGEMM_ERR_UNSUPPORTED: size or configuration not supported";
     case TGEMM_ERR_LAUNCH: return "TGEMM_ERR_LAUNCH: kernel launch failed";
     case TGEMM_ERR_DEVICE: return "TGEMM_ERR_DEVICE: device query failed";
+    case TGEMM_ERR_WORKSPACE:
+        return "TGEMM_ERR_WORKSPACE: the configuration needs a larger workspace";
     default: return "unknown tgemm status";
     }
 }
 
-int tgemm_version(void) { return 200; }
+int tgemm_version(void) { return 300; }
 
 }  // extern "C"

@@ -12,6 +12,13 @@ against which hardware byte counters (FETCH_SIZE, WRITE_SIZE) are scaled.
 
 Prints one JSON line per (workload, configuration): median/p10/p90 microseconds from HIP
 events on the launch stream, TFLOP/s, fraction of the MFMA peak and of the HBM roofline.
+
+  --cold N     rotate over N separately allocated copies of A and B, one per launch, so
+               that (with N copies larger than the 256 MB last-level cache) every launch
+               reads its operands from HBM;
+  --rounds R   time the configurations (and the vendor library) in R interleaved rounds
+               of --repeat launches each, so that slow drifts of the clock (the chip is
+               power-limited) fall on every configuration alike.
 """
 from __future__ import annotations
 
@@ -23,20 +30,20 @@ from . import roofline
 from .inputs import BF16, WORKLOADS
 
 
-def time_config(tgemm, torch, w, A, B, C, cfg, warmup, repeat, stream):
-    def go():
-        tgemm.gemm_ex(w.dtype, w.M, w.N, w.K, A, B, C, w.b_layout, cfg, stream)
-    for _ in range(warmup):
-        go()
-    torch.cuda.synchronize()
+def time_launches(torch, fn, n, stream):
+    """Durations (us) of n launches of fn, each bracketed by HIP events on the stream."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(repeat)]
-    for a, b in evs:
+           for _ in range(n)]
+    for i, (a, b) in enumerate(evs):
         a.record(stream)
-        go()
+        fn(i)
         b.record(stream)
     torch.cuda.synchronize()
-    t = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    return [a.elapsed_time(b) * 1e3 for a, b in evs]
+
+
+def summary(t):
+    t = sorted(t)
     return t[len(t) // 2], t[len(t) // 10], t[(9 * len(t)) // 10]
 
 
@@ -46,6 +53,10 @@ def main(argv=None):
     ap.add_argument("--repeat", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--cold", type=int, default=0,
+                    help="rotate over this many copies of A and B (HBM-resident operands)")
+    ap.add_argument("--rounds", type=int, default=1,
+                    help="interleaved timing rounds of --repeat launches per configuration")
     ap.add_argument("--torch-ref", action="store_true",
                     help="also time torch.matmul (the vendor library) as context")
     ap.add_argument("--kernels", default="",
@@ -72,49 +83,71 @@ def main(argv=None):
         w = WORKLOADS[name]
         A_bits, B_bits = w.generate()
         tdt = torch.bfloat16 if w.dtype == BF16 else torch.float16
-        A = torch.from_numpy(A_bits.view(np.int16)).cuda().view(tdt)
-        B = torch.from_numpy(B_bits.view(np.int16)).cuda().view(tdt)
+        copies = max(1, args.cold)
+        As = [torch.from_numpy(A_bits.view(np.int16)).cuda().view(tdt) for _ in range(copies)]
+        Bs = [torch.from_numpy(B_bits.view(np.int16)).cuda().view(tdt) for _ in range(copies)]
         C = torch.empty((w.M, w.N), dtype=tdt, device="cuda")
         dname = "bf16" if w.dtype == BF16 else "f16"
         flops = roofline.gemm_flops(w.M, w.N, w.K)
         nbytes = roofline.compulsory_bytes(w.M, w.N, w.K)
         table = tgemm.query_config(w.dtype, w.M, w.N, w.K, w.b_layout).as_dict()
+        table_ws = tgemm.query_config_ws(w.dtype, w.M, w.N, w.K, w.b_layout)[0].as_dict()
         kernels = {int(x) for x in args.kernels.split(",") if x}
+
+        runners = []
+        ws_cfg, _ = tgemm.query_config_ws(w.dtype, w.M, w.N, w.K, w.b_layout)
         for cfg in tgemm.list_configs(w.dtype, w.b_layout):
             if kernels and cfg.kernel not in kernels:
                 continue
-            med, p10, p90 = time_config(tgemm, torch, w, A, B, C, cfg, args.warmup,
-                                        args.repeat, stream)
+            if cfg.kernel == tgemm.KERNEL_SPLITK:
+                # split counts: the table's (with a workspace) and its neighbours
+                base = ws_cfg.split_k if ws_cfg.kernel == tgemm.KERNEL_SPLITK else 8
+                variants = []
+                for sk in sorted({max(2, base // 2), base, min(64, base * 2)}):
+                    c = tgemm.Config.from_dict({**cfg.as_dict(), "split_k": sk})
+                    variants.append(c)
+            else:
+                variants = [cfg]
+            for c in variants:
+                nbytes = tgemm.workspace_size(w.M, w.N, c)
+                ws = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device="cuda")
+                def go(i, c=c, ws=ws, nbytes=nbytes):
+                    tgemm.gemm_ex_ws(w.dtype, w.M, w.N, w.K, As[i % copies],
+                                     Bs[i % copies], C, ws, nbytes, w.b_layout, c, stream)
+                runners.append((c, go))
+        if args.torch_ref:
+            # the [K, N] operand either way
+            Bts = [B.t() if w.b_layout == 0 else B for B in Bs]
+            def ref(i):
+                torch.matmul(As[i % copies], Bts[i % copies], out=C)
+            runners.append((None, ref))
+
+        times = [[] for _ in runners]
+        for _, fn in runners:
+            for i in range(args.warmup):
+                fn(i)
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.rounds)):
+            for r, (_, fn) in enumerate(runners):
+                times[r] += time_launches(torch, fn, args.repeat, stream)
+        for (cfg, _), t in zip(runners, times):
+            med, p10, p90 = summary(t)
             rec = {
-                "workload": name, "config": cfg.as_dict(), "table_choice":
-                cfg.as_dict() == table, "median_us": med, "p10_us": p10, "p90_us": p90,
+                "workload": name,
+                "config": cfg.as_dict() if cfg is not None else "torch.matmul (vendor library)",
+                "table_choice": cfg is not None and cfg.as_dict() == table,
+                "table_choice_ws": cfg is not None and cfg.as_dict() == table_ws,
+                "median_us": med, "p10_us": p10, "p90_us": p90,
                 "tflops": flops / med / 1e6,
                 "frac_mfma_peak": flops / med / 1e6 / (roofline.PEAK_FLOPS[dname] / 1e12),
                 "gbps": nbytes / med / 1e3,
                 "frac_hbm": nbytes / med / 1e3 / (roofline.HBM_BYTES_PER_S / 1e9),
+                "cold_copies": args.cold, "launches": len(t),
             }
             print(json.dumps(rec), flush=True)
-            if name not in best or med < best[name]["median_us"]:
+            if cfg is not None and (name not in best or med < best[name]["median_us"]):
                 best[name] = rec
-        if args.torch_ref:
-            Bt = B.t() if w.b_layout == 0 else B     # the [K, N] operand either way
-            def ref():
-                torch.matmul(A, Bt, out=C)
-            for _ in range(args.warmup):
-                ref()
-            torch.cuda.synchronize()
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(args.repeat)]
-            for a, b in evs:
-                a.record(stream)
-                ref()
-                b.record(stream)
-            torch.cuda.synchronize()
-            t = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
-            med = t[len(t) // 2]
-            print(json.dumps({"workload": name, "config": "torch.matmul (vendor library)",
-                              "median_us": med, "tflops": flops / med / 1e6}), flush=True)
-        del A, B, C
+        del As, Bs, C
         torch.cuda.empty_cache()
     for name, rec in best.items():
         print(f"best {name}: {rec['config']} {rec['median_us']:.1f} us "

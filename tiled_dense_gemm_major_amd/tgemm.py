@@ -12,13 +12,15 @@ import os
 F16, BF16 = 0, 1
 B_NK, B_KN = 0, 1
 A_MK, A_KM = 0, 1
-KERNEL_GENERIC, KERNEL_TILED, KERNEL_SKINNY, KERNEL_DMA, KERNEL_PINGPONG, KERNEL_QUAD = range(6)
+(KERNEL_GENERIC, KERNEL_TILED, KERNEL_SKINNY, KERNEL_DMA, KERNEL_PINGPONG, KERNEL_QUAD,
+ KERNEL_SPLITK) = range(7)
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtgemm.so")
 
-EXPORTS = ("gemm_f16", "gemm_bf16", "gemm_ex", "gemm_strided", "tgemm_query_config",
-           "tgemm_query_config_ex", "tgemm_list_configs", "tgemm_list_configs_ex",
+EXPORTS = ("gemm_f16", "gemm_bf16", "gemm_ex", "gemm_ex_ws", "gemm_strided",
+           "tgemm_query_config", "tgemm_query_config_ex", "tgemm_query_config_ws",
+           "tgemm_workspace_size", "tgemm_list_configs", "tgemm_list_configs_ex",
            "tgemm_status_string", "tgemm_version")
 
 
@@ -64,10 +66,14 @@ def load(path: str = LIB_PATH):
     lib.gemm_f16.argtypes = [i64, i64, i64, vp, vp, vp, i32, vp]
     lib.gemm_bf16.argtypes = [i64, i64, i64, vp, vp, vp, i32, vp]
     lib.gemm_ex.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, cfgp, vp]
+    lib.gemm_ex_ws.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, cfgp, vp, i64, vp]
     lib.gemm_strided.argtypes = [i32, i64, i64, i64, vp, i64, i32, vp, i64, i32, vp, i64,
                                  cfgp, vp]
     lib.tgemm_query_config.argtypes = [i32, i64, i64, i64, i32, i32, cfgp]
     lib.tgemm_query_config_ex.argtypes = [i32, i64, i64, i64, i32, i32, i32, cfgp]
+    lib.tgemm_query_config_ws.argtypes = [i32, i64, i64, i64, i32, i32, cfgp,
+                                          ctypes.POINTER(ctypes.c_int64)]
+    lib.tgemm_workspace_size.argtypes = [i64, i64, cfgp, ctypes.POINTER(ctypes.c_int64)]
     lib.tgemm_list_configs.argtypes = [i32, i32, cfgp, i32]
     lib.tgemm_list_configs_ex.argtypes = [i32, i32, i32, cfgp, i32]
     lib.tgemm_status_string.argtypes = [i32]
@@ -130,6 +136,32 @@ def gemm_ex(dtype, m, n, k, A, B, C, b_layout=B_NK, config: Config | None = None
     cfg = ctypes.byref(config) if config is not None else None
     _check(load().gemm_ex(dtype, m, n, k, _addr(A), _addr(B), _addr(C), b_layout, cfg,
                           _stream(stream)), "gemm_ex")
+
+
+def gemm_ex_ws(dtype, m, n, k, A, B, C, workspace, workspace_bytes, b_layout=B_NK,
+               config: Config | None = None, stream=None):
+    """gemm_ex with a caller-lent device workspace (split-K configurations need one)."""
+    cfg = ctypes.byref(config) if config is not None else None
+    _check(load().gemm_ex_ws(dtype, m, n, k, _addr(A), _addr(B), _addr(C), b_layout, cfg,
+                             _addr(workspace) if workspace is not None else None,
+                             int(workspace_bytes), _stream(stream)), "gemm_ex_ws")
+
+
+def query_config_ws(dtype, m, n, k, b_layout=B_NK, aligned=True):
+    """(configuration, workspace bytes) the table picks when a workspace can be lent."""
+    out = Config()
+    nbytes = ctypes.c_int64(0)
+    _check(load().tgemm_query_config_ws(dtype, m, n, k, b_layout, int(bool(aligned)),
+                                        ctypes.byref(out), ctypes.byref(nbytes)),
+           "tgemm_query_config_ws")
+    return out, int(nbytes.value)
+
+
+def workspace_size(m, n, config: Config) -> int:
+    nbytes = ctypes.c_int64(0)
+    _check(load().tgemm_workspace_size(m, n, ctypes.byref(config), ctypes.byref(nbytes)),
+           "tgemm_workspace_size")
+    return int(nbytes.value)
 
 
 def gemm_strided(dtype, m, n, k, A, lda, a_layout, B, ldb, b_layout, C, ldc,
