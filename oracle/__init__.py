@@ -13,6 +13,11 @@ below Triton", section "The first kernel: GEMM" (B as a (K,N) tensor).
 
 The acceptance test that the GPU results are held to (``tolerance`` below) allows, per
 element, 1e-3 * sqrt(K) plus one step ("ulp") of the output format at the oracle's value.
+
+``attention`` is the plain definition of the attention forward pass of "TileLang: a tile
+language one level below Triton", section "FlashAttention: online softmax as tile code"
+(softmax over the keys of Q K^T / sqrt(dim), causal or not, times V; fp64, one rounding to
+fp16); ``attention_tolerance`` states the bound its GPU results are held to.
 """
 from __future__ import annotations
 
@@ -59,8 +64,10 @@ def _load():
                                         i32]
     lib.oracle_gemm_f64.argtypes = [i64, i64, i64, vp, vp, i32, vp, i32]
     lib.oracle_tiled_f64.argtypes = [i64, i64, vp, vp, vp, vp]
+    lib.oracle_attention.argtypes = [i64, i64, i64, i64, vp, vp, vp, i32, vp, vp, i32]
     for name in ("oracle_decode", "oracle_encode", "oracle_gemm", "oracle_gemm_rows",
-                 "oracle_gemm_entries", "oracle_gemm_f64", "oracle_tiled_f64"):
+                 "oracle_gemm_entries", "oracle_gemm_f64", "oracle_tiled_f64",
+                 "oracle_attention"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -176,6 +183,50 @@ def tiled_f64(A, B, t: int):
     _check(_load().oracle_tiled_f64(n, t, _ptr(A), _ptr(B), _ptr(C), ctypes.byref(loads)),
            "tiled_f64")
     return C, int(loads.value)
+
+
+def attention(Q, K, V, causal: bool, nthreads: int = 0, want_f64: bool = False):
+    """Attention forward on fp16 bit patterns [B, S, H, D] (the definition in oracle.c:
+    softmax over the keys of Q K^T / sqrt(D), causal or not, times V; one rounding).
+    Returns O's bits (and the unrounded fp64 values if ``want_f64``)."""
+    Q, K, V = _u16(Q), _u16(K), _u16(V)
+    if Q.ndim != 4 or Q.shape != K.shape or Q.shape != V.shape:
+        raise ValueError("Q, K, V must share one [B, S, H, D] shape")
+    Bn, S, H, D = Q.shape
+    O = np.empty(Q.shape, dtype=np.uint16)
+    O64 = np.empty(Q.shape, dtype=np.float64) if want_f64 else None
+    _check(_load().oracle_attention(Bn, S, H, D, _ptr(Q), _ptr(K), _ptr(V), int(bool(causal)),
+                                    _ptr(O), _ptr(O64), nthreads), "attention")
+    return (O, O64) if want_f64 else O
+
+
+def attention_tolerance(V, causal: bool, orc_values) -> np.ndarray:
+    """Per-element bound for a kernel that rounds the softmax weights to fp16 before the
+    product with V (as the page's kernel does) and sums those rounded weights for the
+    normalizer: each weight is off by at most 2^-11 relative, so the normalized average
+    moves by at most 2 * 2^-11 * max_j |v(j,d)| over the keys it averages; doubled for
+    the fp32 score, exponential and sum errors, plus one fp16 ulp of |oracle| for the two
+    final roundings.  max_j |v(j,d)| is taken over all keys of the (batch, head) (a
+    superset of the keys a causal row sees)."""
+    v = np.abs(decode(F16, V))                              # [B, S, H, D]
+    vmax = v.max(axis=1, keepdims=True)                     # [B, 1, H, D]
+    return 4.0 * 2.0 ** -11 * np.broadcast_to(vmax, v.shape) + ulp_out(F16, orc_values)
+
+
+def compare_attention(V, causal: bool, got_bits, want_bits) -> dict:
+    got = decode(F16, got_bits)
+    want = decode(F16, want_bits)
+    tol = attention_tolerance(V, causal, want)
+    err = np.abs(got - want)
+    bad = ~np.isfinite(got) | ~(err <= tol)
+    idx = np.flatnonzero(bad.ravel())
+    return {
+        "n": int(got.size),
+        "n_fail": int(idx.size),
+        "first_fail": int(idx[0]) if idx.size else -1,
+        "max_err": float(np.max(err)) if err.size else 0.0,
+        "max_err_over_tol": float(np.max(err / tol)) if err.size else 0.0,
+    }
 
 
 # ---------------------------------------------------------------------------------------

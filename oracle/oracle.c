@@ -1,5 +1,6 @@
 /*
- * CPU oracle for the block-tiled dense matrix multiply.  TEST INFRASTRUCTURE ONLY:
+ * CPU oracle for the block-tiled dense matrix multiply (and, at the end of this file, the
+ * attention forward pass built on the same tiles).  TEST INFRASTRUCTURE ONLY:
  * the test suite, the smoke check and the CPU-baseline leg of the benchmark are the
  * only callers.  It shares no code, header, table or helper with the GPU library.
  *
@@ -352,4 +353,97 @@ int oracle_tiled_f64(int64_t n, int64_t t, const double* A, const double* B, dou
     if (loads)
         *loads = count;
     return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Attention forward, the plain definition (no tiling and no online rescaling):          */
+/*                                                                                        */
+/*   s_j    = ( sum_{d<D} q(i,d) * k(j,d) ) / sqrt(D)      keys j < S (and j <= i if causal) */
+/*   O(i,d) = round_f16( sum_j e^{s_j - m} v(j,d) / sum_j e^{s_j - m} ),   m = max_j s_j  */
+/*                                                                                        */
+/* per batch b and head h, with Q, K, V, O stored [B, S, H, D] (D contiguous), fp16.     */
+/* Source: "TileLang: a tile language one level below Triton", section "FlashAttention:  */
+/* online softmax as tile code": the forward pass over (batch, seq, heads, dim) tensors  */
+/* in float16, scores Q K^T scaled by 1/sqrt(dim), the causal mask (a query sees the keys */
+/* at or before its own position), the softmax over the keys and the product with V.     */
+/* The page's kernel reaches the same result up to rounding by an online softmax with    */
+/* base-2 exponentials (log2(e) folded into the scale); the oracle uses e^x and one pass */
+/* over all scores.  Every sum runs in increasing index order in fp64; the result is     */
+/* rounded once to fp16 (nearest-even).  O64 (optional) receives the unrounded values.   */
+/* A query with no key (S == 0) does not exist; D == 0 gives +0.0.                       */
+/* ------------------------------------------------------------------------------------ */
+int oracle_attention(int64_t B, int64_t S, int64_t H, int64_t D, const uint16_t* Q,
+                     const uint16_t* K, const uint16_t* V, int causal, uint16_t* O,
+                     double* O64, int nthreads) {
+    if (B < 0 || S < 0 || H < 0 || D < 0 || (causal != 0 && causal != 1))
+        return ORC_EINVAL;
+    const int64_t n = B * S * H * D;
+    if (n == 0)
+        return ORC_OK;
+    set_threads(nthreads);
+    double* q = (double*)malloc(sizeof(double) * (size_t)n);
+    double* k = (double*)malloc(sizeof(double) * (size_t)n);
+    double* v = (double*)malloc(sizeof(double) * (size_t)n);
+    if (!q || !k || !v) {
+        free(q);
+        free(k);
+        free(v);
+        return ORC_ENOMEM;
+    }
+    for (int64_t i = 0; i < n; ++i) {
+        q[i] = decode_f16(Q[i]);
+        k[i] = decode_f16(K[i]);
+        v[i] = decode_f16(V[i]);
+    }
+    const double inv_sqrt_d = 1.0 / sqrt((double)D);
+    int rc = ORC_OK;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)S);
+        if (!s) {
+#pragma omp atomic write
+            rc = ORC_ENOMEM;
+        }
+#pragma omp for collapse(3) schedule(static)
+        for (int64_t b = 0; b < B; ++b) {
+            for (int64_t h = 0; h < H; ++h) {
+                for (int64_t i = 0; i < S; ++i) {
+                    if (!s)
+                        continue;
+                    const double* qi = q + ((b * S + i) * H + h) * D;
+                    const int64_t nkeys = causal ? i + 1 : S;
+                    double m = -INFINITY;
+                    for (int64_t j = 0; j < nkeys; ++j) {
+                        const double* kj = k + ((b * S + j) * H + h) * D;
+                        double dot = 0.0;
+                        for (int64_t d = 0; d < D; ++d)
+                            dot += qi[d] * kj[d];
+                        s[j] = dot * inv_sqrt_d;
+                        if (s[j] > m)
+                            m = s[j];
+                    }
+                    double denom = 0.0;
+                    for (int64_t j = 0; j < nkeys; ++j) {
+                        s[j] = exp(s[j] - m);
+                        denom += s[j];
+                    }
+                    for (int64_t d = 0; d < D; ++d) {
+                        double num = 0.0;
+                        for (int64_t j = 0; j < nkeys; ++j)
+                            num += s[j] * v[((b * S + j) * H + h) * D + d];
+                        const double o = num / denom;
+                        const int64_t at = ((b * S + i) * H + h) * D + d;
+                        O[at] = encode_f16(o);
+                        if (O64)
+                            O64[at] = o;
+                    }
+                }
+            }
+        }
+        free(s);
+    }
+    free(q);
+    free(k);
+    free(v);
+    return rc;
 }

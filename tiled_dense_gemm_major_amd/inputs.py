@@ -162,3 +162,43 @@ WORKLOADS = {
     "bf16_skinny_64x8192x8192": Workload("bf16_skinny_64x8192x8192", BF16, 64, 8192, 8192,
                                          B_NK, "uniform", 5),
 }
+
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    """One attention-forward workload: Q, K, V, O of shape [batch, seq, heads, dim], fp16
+    ("TileLang: a tile language one level below Triton", section "FlashAttention: online
+    softmax as tile code": (batch, seq, heads, dim) tensors in float16, causal mask)."""
+    name: str
+    batch: int
+    seq: int
+    heads: int
+    dim: int
+    causal: bool
+    seed: int
+    dist: str = "normal"
+    sigma: float = 1.0
+
+    @property
+    def shape(self):
+        return (self.batch, self.seq, self.heads, self.dim)
+
+    def describe(self) -> str:
+        return (f"fp16 attention B={self.batch} S={self.seq} H={self.heads} D={self.dim} "
+                f"{'causal' if self.causal else 'full'} N(0,{self.sigma:g}) seed {self.seed}")
+
+    def generate(self):
+        """(Q, K, V) bits, uint16 [B, S, H, D], filled in that order."""
+        s = Stream(self.seed)
+        return tuple(s.matrix(self.shape, F16, self.dist, self.sigma) for _ in range(3))
+
+
+ATTN_WORKLOADS = {
+    # the page's configuration: flash_attn(1, 8, 1024, 64), causal
+    "attn_f16_b1_s1024_h8_d64_causal": AttnWorkload("attn_f16_b1_s1024_h8_d64_causal",
+                                                    1, 1024, 8, 64, True, 6),
+    # a larger one of the same kind, for throughput
+    "attn_f16_b4_s4096_h16_d64_causal": AttnWorkload("attn_f16_b4_s4096_h16_d64_causal",
+                                                     4, 4096, 16, 64, True, 7),
+}
+

@@ -71,3 +71,18 @@ def bound(M: int, N: int, K: int, dtype: str = "bf16") -> str:
     """'mfma' when the compulsory intensity is above the ridge, else 'hbm'."""
     ai = gemm_flops(M, N, K) / compulsory_bytes(M, N, K)
     return "mfma" if ai >= PEAK_FLOPS[dtype] / HBM_BYTES_PER_S else "hbm"
+
+
+def attention_flops(batch: int, seq: int, heads: int, dim: int, causal: bool) -> int:
+    """Attention forward: the multiply-adds of Q K^T and of P V (two flops each) over the
+    (query, key) pairs the mask keeps -- seq*(seq+1)/2 per (batch, head) when causal
+    ("TileLang: a tile language one level below Triton", exercise 3: causal attention
+    does about half the work of full attention), seq*seq otherwise."""
+    pairs = seq * (seq + 1) // 2 if causal else seq * seq
+    return 4 * batch * heads * pairs * dim
+
+
+def attention_bytes(batch: int, seq: int, heads: int, dim: int, elem: int = 2) -> int:
+    """Compulsory traffic: Q, K, V read once, O written once."""
+    return 4 * batch * seq * heads * dim * elem
+
