@@ -211,6 +211,30 @@ int tgemm_query_config_ws(int dtype, int64_t m, int64_t n, int64_t k, int b_layo
  * Host-only. */
 int tgemm_workspace_size(int64_t m, int64_t n, const tgemm_config* cfg, int64_t* bytes);
 
+/*
+ * Attention forward, fp16 ("TileLang: a tile language one level below Triton", section
+ * "FlashAttention: online softmax as tile code"):
+ *   O[b,i,h,:] = sum_j softmax_j( Q[b,i,h,:] . K[b,j,h,:] / sqrt(dim) ) V[b,j,h,:]
+ * over the keys j < seq, or j <= i when causal is 1, per batch b and head h.
+ *   batch, seq, heads, dim : sizes (>= 0); dim must be 64; batch and heads at most 65535
+ *   Q, K, V                : device pointers, fp16, each [batch, seq, heads, dim]
+ *                            (dim contiguous), 16-byte aligned
+ *   O                      : device pointer, same shape and alignment; written, never
+ *                            read; may not overlap Q, K or V
+ *   causal                 : 0 (every key) or 1 (keys up to the query's own position)
+ *   stream                 : hipStream_t (NULL = null stream)
+ * The scores and the softmax run in fp32 (base-2 exponentials, log2(e) folded into the
+ * scale), the probabilities are cast to fp16 for the product with V (fp32 sums), and
+ * each output is divided by its row sum and rounded once to fp16.  Returns a
+ * tgemm_status: TGEMM_ERR_INVALID_VALUE (negative size, causal not 0 or 1),
+ * TGEMM_ERR_UNSUPPORTED (dim != 64, or a tensor over 2^31 bytes), TGEMM_ERR_NULL_POINTER,
+ * TGEMM_ERR_ALIGNMENT, TGEMM_ERR_ALIASING, TGEMM_ERR_LAUNCH.  An empty tensor (batch,
+ * seq or heads 0) is a no-op.  Same ownership, stream and thread-safety rules as the
+ * products; nothing is allocated.
+ */
+int attn_fwd_f16(int64_t batch, int64_t seq, int64_t heads, int64_t dim, const void* Q,
+                 const void* K, const void* V, void* O, int causal, void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* tgemm_status_string(int status);
 

@@ -213,3 +213,20 @@ def test_workspace_entry_point_errors(lib):
     # without a workspace, the table's choice needs none, and empty products stay no-ops
     assert f(1, 0, N, K, None, None, None, 0, None, None, 0, None) == 0
     assert lib.gemm_ex(1, M, N, K, A, B, C, 0, ctypes.byref(cfg), None) == -8
+
+
+def test_attention_argument_errors(lib):
+    f = lib.attn_fwd_f16
+    Q, K, V, O = FAKE, FAKE + (1 << 24), FAKE + (1 << 25), FAKE + (1 << 26)
+
+    def call(b=1, s=128, h=2, d=64, q=Q, k=K, v=V, o=O, causal=1):
+        return f(b, s, h, d, q, k, v, o, causal, None)
+
+    assert call(b=-1) == -1 and call(s=-1) == -1 and call(causal=2) == -1
+    assert call(b=0, q=None, k=None, v=None, o=None) == 0        # empty: a no-op
+    assert call(s=0) == 0 and call(h=0) == 0
+    assert call(d=128) == -5 and call(d=32) == -5               # dim 64 only
+    assert call(b=1 << 20, s=1 << 20) == -5                     # past 2^31 bytes
+    assert call(q=None) == -2 and call(o=None) == -2
+    assert call(q=Q + 8) == -3 and call(o=O + 2) == -3          # 16-byte alignment
+    assert call(o=Q + 64) == -4 and call(o=V) == -4             # O overlapping an input

@@ -8,7 +8,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "tgemm.hip")
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("tgemm.hip", "attention.hip")]
 LIB = os.path.join(PKG, "libtgemm.so")
 INCLUDE = os.path.join(ROOT, "include")
 ARCH = "gfx950"
@@ -31,7 +31,7 @@ def hipcc() -> str:
 def build(extra_flags=(), out: str = LIB, quiet: bool = True) -> str:
     """Compile every kernel and the C ABI into ``out`` (always recompiles)."""
     tmp = out + ".tmp"
-    cmd = [hipcc(), *FLAGS, *extra_flags, f"-I{INCLUDE}", SRC, "-o", tmp]
+    cmd = [hipcc(), *FLAGS, *extra_flags, f"-I{INCLUDE}", *SRCS, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]

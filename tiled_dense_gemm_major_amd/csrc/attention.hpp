@@ -1,0 +1,246 @@
+// Attention forward on the matrix cores of gfx950: the tile pipeline of the product kernels
+// (direct-to-LDS loads into a ring of swizzled LDS stages, MFMA operands read from LDS)
+// applied twice per key tile, with the softmax kept online in registers.
+//
+// "TileLang: a tile language one level below Triton", section "FlashAttention: online
+// softmax as tile code": each block takes block_M queries and walks the keys tile by tile;
+// it keeps a running row maximum and row sum, rescales what it has accumulated to each new
+// maximum, uses base-2 exponentials with log2(e) folded into the 1/sqrt(dim) scale, casts
+// the probabilities to float16 for the product with V, divides by the row sum once at the
+// end, and handles the causal mask at two levels (key tiles wholly above the diagonal are
+// not visited; inside the diagonal tile the masked scores become -infinity).
+#pragma once
+
+#include "kernels.hpp"
+
+namespace tgemm {
+
+// Q, K, V, O: fp16 [batch, seq, heads, D] (D contiguous).  One workgroup per 128 queries
+// of one (batch, head); 4 waves, wave w owning queries [32w, 32w+32) of the block.
+//   Scores:  S = Q K^T for 64 keys at a time with v_mfma_f32_32x32x16_f16, the key rows
+//            as the first source and the query rows as the second, so that lane l holds
+//            query row l % 32 and keys 8g + 4(l/32) + (0..3) of each 32-key block: a
+//            row's 64 scores sit in two lanes (l, l+32).
+//   Softmax: row maximum over the lane's 32 scores and its partner's (one lane swap),
+//            p = 2^(s*scale - max) in fp32, rescale of the running sum and of O by
+//            2^(old max - new max).  Each lane keeps its half of the row sum; the halves
+//            are added once at the end.
+//   P V:     the probabilities, cast to fp16, are the second source as they lie: for the
+//            16 keys of an MFMA step the lane supplies its own 8 (keys 0-3 and 8-11 of
+//            the step for l < 32, keys 4-7 and 12-15 for l >= 32), and the first source
+//            reads V^T in that same key order with two transposing LDS reads
+//            (ds_read_b64_tr_b16), keys base and base + 8.
+//   Loads:   K and V tiles (64 x D each) arrive by direct-to-LDS 16-byte loads into a
+//            3-stage ring; tile t+2's loads go out once every wave has met at the start of
+//            step t.  K rows are stored with 16-byte chunk c at c ^ ((row / 2) mod KC) (the
+//            row-wise reads of 32 rows hit distinct banks); V rows with chunk c at
+//            c ^ 2(row mod 4) (the 4 x 16 blocks of the transposing reads hit distinct
+//            banks).  Rows past seq read as zeros (buffer range check).
+//   The whole (b, h) slice spans at most 2^31 bytes (checked by the host).
+template <int D, bool CAUSAL>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
+                               amdgpu_waves_per_eu(2, 2)))
+attn_fwd(const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
+         u16* __restrict__ O, int S, int H, float scale_log2, int nqb) {
+    constexpr int BM = 128, BN = 64, ST = 3;
+    constexpr int KC = D / 8;                  // 16-byte chunks per row
+    constexpr int ROWS = 64 / KC;              // rows per 1 KiB load
+    constexpr int TILE = BN * D;               // elements of one K or V tile
+    constexpr int LW = BN / ROWS / 4;          // loads per wave per K (or V) tile
+    constexpr int NS = D / 16;                 // k-steps of Q K^T
+    constexpr int NDB = D / 32;                // 32-wide column blocks of O
+    // (the V swizzle and the load split are laid out for 128-byte rows)
+    static_assert(D == 64, "head dimension 64");
+    static_assert(LW >= 1 && (BN / ROWS) % 4 == 0, "load split");
+    __shared__ __attribute__((aligned(1024))) u16 lds[ST * 2 * TILE];   // [stage][K|V]
+
+    const int tid = (int)threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // the blocks with the most keys first (causal: the last queries)
+    const int qb = CAUSAL ? nqb - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    const int h = (int)blockIdx.y, b = (int)blockIdx.z;
+    const int q0 = qb * BM + 32 * wave;
+    const int r = lane & 31, hh = lane >> 5;
+    const uint32_t rs = (uint32_t)H * D;               // elements between sequence positions
+    const size_t base = ((size_t)b * S * H + h) * D;   // (b, 0, h, 0)
+    const uint32_t span = S > 0 ? ((uint32_t)(S - 1) * rs + D) * 2u : 0u;
+    const rsrc_t rq = make_rsrc(Q + base, span);
+    const rsrc4_t rk = make_rsrc4(K + base, span);
+    const rsrc4_t rv = make_rsrc4(V + base, span);
+
+    // key tiles this block visits: those holding a key at or before its last query
+    const int ntile_all = (S + BN - 1) / BN;
+    const int nkt = CAUSAL ? min(ntile_all, ((qb + 1) * BM + BN - 1) / BN) : ntile_all;
+
+    // Q fragments (second source of the score MFMAs): query row q0 + r, 8 dims per lane
+    u32x4 qf[NS];
+    {
+        const int q = q0 + r;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            qf[s] = load16(rq, q < S ? ((uint32_t)q * rs + 16 * s + 8 * hh) * 2u : kOutOfRange,
+                           0);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            asm volatile("" ::"v"(qf[s]));     // landed before the loop, not waited in it
+    }
+
+    // direct-to-LDS loads: wave w fills rows [BN/4 * w, BN/4 * (w+1)) of a tile, ROWS at a
+    // time; lane l lands in row l / KC at physical chunk l % KC
+    const int prow = lane / KC, pch = lane % KC;
+    int kchunk[LW], vchunk[LW], trow[LW];
+#pragma unroll
+    for (int i = 0; i < LW; ++i) {
+        trow[i] = (BN / 4) * wave + ROWS * i + prow;
+        kchunk[i] = pch ^ swz<KC>(trow[i]);
+        vchunk[i] = pch ^ (2 * (trow[i] & 3));
+    }
+    const uint32_t lds0 = lds_addr(lds);
+    auto issue = [&](int kt) {
+        const int st = kt % ST;
+#pragma unroll
+        for (int i = 0; i < LW; ++i) {
+            const int key = kt * BN + trow[i];
+            const uint32_t row = (uint32_t)key * rs;
+            const uint32_t ldsb = lds0 + (uint32_t)((st * 2 * TILE + (BN / 4 * wave + ROWS * i) * D) * 2);
+            dma16_at(rk, ldsb, key < S ? (row + kchunk[i] * 8) * 2u : kOutOfRange, 0);
+            dma16_at(rv, ldsb + TILE * 2, key < S ? (row + vchunk[i] * 8) * 2u : kOutOfRange,
+                     0);
+        }
+    };
+
+    // V^T reads: lane sl of 16-lane group g points at key row base + 4(g/2) + sl/4 and the
+    // 4 columns 16(g%2) + 4(sl%4) of a 32-column block
+    const int g = lane >> 4, sl = lane & 15;
+    const int vrow = 4 * (g >> 1) + (sl >> 2);       // plus 32 kb + 16 q (+ 8)
+    const int vcol = 16 * (g & 1) + 4 * (sl & 3);    // plus 32 db
+    auto read_vt = [&](const u16* vt, int kb, int step, int db) {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const int row = 32 * kb + 16 * step + vrow;
+        const int col = 32 * db + vcol;
+        const int off = ((col >> 3) ^ (2 * (row & 3))) * 8 + (col & 7);   // row & 3 same at +8
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + row * D + off));
+        const s16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + (row + 8) * D + off));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    };
+
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+        oacc[db] = f32x16{};
+    float m_run = -__builtin_huge_valf();      // running maximum (scaled scores, base 2)
+    float l_run = 0.0f;                        // this lane's half of the running row sum
+    const int q = q0 + r;
+
+    if (nkt > 0) {
+        issue(0);
+        if (nkt > 1)
+            issue(1);
+    }
+    for (int kt = 0; kt < nkt; ++kt) {
+        // tile kt has landed (tile kt+1 may fly) and every wave is done with tile kt-1
+        if (kt + 1 < nkt)
+            wait_vm_then_sync<2 * LW>();
+        else
+            wait_vm_then_sync<0>();
+        if (kt + 2 < nkt)
+            issue(kt + 2);
+        // keys of this tile all after this wave's last query: nothing to add
+        if (CAUSAL && kt * BN > q0 + 31)
+            continue;
+        const u16* kt_lds = lds + (kt % ST) * 2 * TILE;
+        const u16* vt_lds = kt_lds + TILE;
+
+        // S = Q K^T, two 32-key blocks
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            sacc[kb] = f32x16{};
+            const int krow = 32 * kb + r;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const u32x4 kf = *reinterpret_cast<const u32x4*>(
+                    kt_lds + krow * D + (((2 * s + hh) ^ swz<KC>(krow)) * 8));
+                sacc[kb] = mfma_32x32x16<DT_F16>(kf, qf[s], sacc[kb]);
+            }
+        }
+        // scale, mask, row maximum
+        const bool edge = kt * BN + BN > S || (CAUSAL && kt * BN + BN - 1 > q0);
+        float mx = -__builtin_huge_valf();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                float x = sacc[kb][v] * scale_log2;
+                if (edge) {
+                    const int key = kt * BN + 32 * kb + 8 * (v >> 2) + 4 * hh + (v & 3);
+                    if (key >= S || (CAUSAL && key > q))
+                        x = -__builtin_huge_valf();
+                }
+                sacc[kb][v] = x;
+                mx = fmaxf(mx, x);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        // a row with no key yet keeps an offset of 0 (its scores are all -infinity)
+        const float m_use = m_new == -__builtin_huge_valf() ? 0.0f : m_new;
+        const float rescale = __builtin_amdgcn_exp2f(m_run - m_use);
+        m_run = m_new;
+        float psum = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float p = __builtin_amdgcn_exp2f(sacc[kb][v] - m_use);
+                sacc[kb][v] = p;
+                psum += p;
+            }
+        }
+        l_run = l_run * rescale + psum;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                oacc[db][v] *= rescale;
+
+        // O += P V: four 16-key steps, the probabilities in fp16
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+                u32x4 pf;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    pf[e] = pack2<DT_F16>(sacc[kb][8 * qq + 2 * e], sacc[kb][8 * qq + 2 * e + 1]);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    oacc[db] = mfma_32x32x16<DT_F16>(read_vt(vt_lds, kb, qq, db), pf, oacc[db]);
+            }
+        }
+    }
+    wait_vm<0>();                               // no load left in flight
+
+    // divide by the row sum once, cast, store: lane holds row q, columns 8g' + 4hh + 0..3
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if (q < S) {
+        u16* orow = O + base + (size_t)q * rs;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                u32x2 v;
+                v[0] = pack2<DT_F16>(oacc[db][4 * gg + 0] * inv, oacc[db][4 * gg + 1] * inv);
+                v[1] = pack2<DT_F16>(oacc[db][4 * gg + 2] * inv, oacc[db][4 * gg + 3] * inv);
+                *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * gg + 4 * hh) = v;
+            }
+        }
+    }
+}
+
+}  // namespace tgemm

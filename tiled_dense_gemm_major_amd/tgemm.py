@@ -18,7 +18,7 @@ A_MK, A_KM = 0, 1
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtgemm.so")
 
-EXPORTS = ("gemm_f16", "gemm_bf16", "gemm_ex", "gemm_ex_ws", "gemm_strided",
+EXPORTS = ("attn_fwd_f16", "gemm_f16", "gemm_bf16", "gemm_ex", "gemm_ex_ws", "gemm_strided",
            "tgemm_query_config", "tgemm_query_config_ex", "tgemm_query_config_ws",
            "tgemm_workspace_size", "tgemm_list_configs", "tgemm_list_configs_ex",
            "tgemm_status_string", "tgemm_version")
@@ -67,6 +67,7 @@ def load(path: str = LIB_PATH):
     lib.gemm_bf16.argtypes = [i64, i64, i64, vp, vp, vp, i32, vp]
     lib.gemm_ex.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, cfgp, vp]
     lib.gemm_ex_ws.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, cfgp, vp, i64, vp]
+    lib.attn_fwd_f16.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, i32, vp]
     lib.gemm_strided.argtypes = [i32, i64, i64, i64, vp, i64, i32, vp, i64, i32, vp, i64,
                                  cfgp, vp]
     lib.tgemm_query_config.argtypes = [i32, i64, i64, i64, i32, i32, cfgp]
@@ -78,10 +79,9 @@ def load(path: str = LIB_PATH):
     lib.tgemm_list_configs_ex.argtypes = [i32, i32, i32, cfgp, i32]
     lib.tgemm_status_string.argtypes = [i32]
     lib.tgemm_status_string.restype = ctypes.c_char_p
-    for name in ("gemm_f16", "gemm_bf16", "gemm_ex", "gemm_strided", "tgemm_query_config",
-                 "tgemm_query_config_ex", "tgemm_list_configs", "tgemm_list_configs_ex",
-                 "tgemm_version"):
-        getattr(lib, name).restype = i32
+    for name in EXPORTS:
+        if name != "tgemm_status_string":
+            getattr(lib, name).restype = i32
     _lib = lib
     return lib
 
@@ -189,6 +189,14 @@ def list_configs(dtype, b_layout=B_NK, a_layout=A_MK) -> list:
     arr = (Config * count)()
     lib.tgemm_list_configs_ex(dtype, a_layout, b_layout, arr, count)
     return [arr[i] for i in range(count)]
+
+
+def attn_fwd_f16(batch, seq, heads, dim, Q, K, V, O, causal=True, stream=None):
+    """Attention forward, fp16 tensors [batch, seq, heads, dim]: O = softmax(Q K^T /
+    sqrt(dim)) V per (batch, head), causal or not.  Q, K, V, O: device tensors or
+    addresses."""
+    _check(load().attn_fwd_f16(batch, seq, heads, dim, _addr(Q), _addr(K), _addr(V), _addr(O),
+                               int(bool(causal)), _stream(stream)), "attn_fwd_f16")
 
 
 def version() -> int:
