@@ -110,29 +110,48 @@ attn_fwd(const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __rest
     };
 
     // V^T reads: lane sl of 16-lane group g points at key row base + 4(g/2) + sl/4 and the
-    // 4 columns 16(g%2) + 4(sl%4) of a 32-column block
+    // 4 columns 16(g%2) + 4(sl%4) of a 32-column block.  The lane's part of the address
+    // (row, swizzled column) is fixed; the tile rows of a step (32 kb + 16 step, + 8 for the
+    // second read, a multiple of 4: same swizzle) come in as constant offsets.
     const int g = lane >> 4, sl = lane & 15;
-    const int vrow = 4 * (g >> 1) + (sl >> 2);       // plus 32 kb + 16 q (+ 8)
-    const int vcol = 16 * (g & 1) + 4 * (sl & 3);    // plus 32 db
-    auto read_vt = [&](const u16* vt, int kb, int step, int db) {
-        typedef short s16x4 __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-        const int row = 32 * kb + 16 * step + vrow;
+    const int vrow = 4 * (g >> 1) + (sl >> 2);
+    const int vcol = 16 * (g & 1) + 4 * (sl & 3);
+    int vofs[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
         const int col = 32 * db + vcol;
-        const int off = ((col >> 3) ^ (2 * (row & 3))) * 8 + (col & 7);   // row & 3 same at +8
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + row * D + off));
-        const s16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + (row + 8) * D + off));
+        vofs[db] = vrow * D + ((col >> 3) ^ (2 * (vrow & 3))) * 8 + (col & 7);
+    }
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    typedef __attribute__((address_space(3))) u16 lds_u16;
+    auto read_vt = [&](const lds_u16* vt, int kb, int step, int db) {
+        const lds_u16* p = vt + vofs[db] + (32 * kb + 16 * step) * D;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * D));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
         const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
         return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    };
+    // K reads: lane's key row r of a 32-key block, chunk (2 s + l/32) swizzled by the row
+    // (the swizzle of rows r and 32 + r agree)
+    int kofs[NS];
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2)
+        kofs[s2] = r * D + (((2 * s2 + hh) ^ swz<KC>(r)) * 8);
+    // fp16 pair, nearest-even (one packed conversion)
+    auto pack_f16 = [](float a, float b) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, h2));
     };
 
     f32x16 oacc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
         oacc[db] = f32x16{};
-    float m_run = -__builtin_huge_valf();      // running maximum (scaled scores, base 2)
+    constexpr float kSlack = 8.0f;             // log2 of the largest weight allowed
+    float m_run = -__builtin_huge_valf();      // reference maximum (scaled scores, base 2)
     float l_run = 0.0f;                        // this lane's half of the running row sum
     const int q = q0 + r;
 
@@ -149,64 +168,75 @@ attn_fwd(const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __rest
             wait_vm_then_sync<0>();
         if (kt + 2 < nkt)
             issue(kt + 2);
-        // keys of this tile all after this wave's last query: nothing to add
-        if (CAUSAL && kt * BN > q0 + 31)
-            continue;
         const u16* kt_lds = lds + (kt % ST) * 2 * TILE;
-        const u16* vt_lds = kt_lds + TILE;
+        const lds_u16* vt_lds = (const lds_u16*)(kt_lds + TILE);
 
         // S = Q K^T, two 32-key blocks
         f32x16 sacc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             sacc[kb] = f32x16{};
-            const int krow = 32 * kb + r;
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const u32x4 kf = *reinterpret_cast<const u32x4*>(
-                    kt_lds + krow * D + (((2 * s + hh) ^ swz<KC>(krow)) * 8));
+                const u32x4 kf =
+                    *reinterpret_cast<const u32x4*>(kt_lds + kofs[s] + 32 * kb * D);
                 sacc[kb] = mfma_32x32x16<DT_F16>(kf, qf[s], sacc[kb]);
             }
         }
-        // scale, mask, row maximum
-        const bool edge = kt * BN + BN > S || (CAUSAL && kt * BN + BN - 1 > q0);
+        // mask (tiles on the diagonal or past the end only), row maximum of the raw scores
+        if (kt * BN + BN > S || (CAUSAL && kt * BN + BN - 1 > q0)) {
+            const int lim = CAUSAL ? min(S, q + 1) : S;   // keys below lim count
+            const int k0 = kt * BN + 4 * hh;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    sacc[kb][v] = k0 + 32 * kb + 8 * (v >> 2) + (v & 3) < lim
+                                      ? sacc[kb][v]
+                                      : -__builtin_huge_valf();
+        }
+        // row maximum of the raw scores: three-input maxima (the scores come straight
+        // from the matrix core, so no NaN needs quieting first)
         float mx = -__builtin_huge_valf();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                float x = sacc[kb][v] * scale_log2;
-                if (edge) {
-                    const int key = kt * BN + 32 * kb + 8 * (v >> 2) + 4 * hh + (v & 3);
-                    if (key >= S || (CAUSAL && key > q))
-                        x = -__builtin_huge_valf();
-                }
-                sacc[kb][v] = x;
-                mx = fmaxf(mx, x);
-            }
-        }
+            for (int v = 0; v < 16; v += 2)
+                asm("v_max3_f32 %0, %1, %2, %3" : "=v"(mx) : "v"(mx), "v"(sacc[kb][v]),
+                    "v"(sacc[kb][v + 1]));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        // a row with no key yet keeps an offset of 0 (its scores are all -infinity)
-        const float m_use = m_new == -__builtin_huge_valf() ? 0.0f : m_new;
-        const float rescale = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
+        // The exponentials are taken against a reference m_run that moves only when the
+        // row maximum (scaled) has risen more than kSlack above it, so most tiles skip the
+        // rescale of O: a weight is then at most 2^kSlack, which fp16 and the fp32 sums
+        // hold exactly as well (the softmax does not depend on the reference).
+        const float m_cand = fmaxf(m_run, mx * scale_log2);
+        const bool move = m_cand > m_run + kSlack;         // also the first finite maximum
+        {
+            const float m_new = move ? m_cand : m_run;
+            // a row with no key yet keeps an offset of 0 (its scores are all -infinity)
+            const float m_use = m_new == -__builtin_huge_valf() ? 0.0f : m_new;
+            const float rescale = __builtin_amdgcn_exp2f(m_run - m_use);   // 1 if not moved
+            m_run = m_new;
+            l_run *= rescale;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    oacc[db][v] *= rescale;
+        }
+        const float m_use = m_run == -__builtin_huge_valf() ? 0.0f : m_run;
         float psum = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const float p = __builtin_amdgcn_exp2f(sacc[kb][v] - m_use);
+                // p = 2^(s * scale - m_run), one fused multiply-add before the exponential
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], scale_log2, -m_use));
                 sacc[kb][v] = p;
                 psum += p;
             }
         }
-        l_run = l_run * rescale + psum;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                oacc[db][v] *= rescale;
+        l_run += psum;
 
         // O += P V: four 16-key steps, the probabilities in fp16
 #pragma unroll
@@ -216,7 +246,7 @@ attn_fwd(const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __rest
                 u32x4 pf;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    pf[e] = pack2<DT_F16>(sacc[kb][8 * qq + 2 * e], sacc[kb][8 * qq + 2 * e + 1]);
+                    pf[e] = pack_f16(sacc[kb][8 * qq + 2 * e], sacc[kb][8 * qq + 2 * e + 1]);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
                     oacc[db] = mfma_32x32x16<DT_F16>(read_vt(vt_lds, kb, qq, db), pf, oacc[db]);
@@ -235,8 +265,8 @@ attn_fwd(const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __rest
 #pragma unroll
             for (int gg = 0; gg < 4; ++gg) {
                 u32x2 v;
-                v[0] = pack2<DT_F16>(oacc[db][4 * gg + 0] * inv, oacc[db][4 * gg + 1] * inv);
-                v[1] = pack2<DT_F16>(oacc[db][4 * gg + 2] * inv, oacc[db][4 * gg + 3] * inv);
+                v[0] = pack_f16(oacc[db][4 * gg + 0] * inv, oacc[db][4 * gg + 1] * inv);
+                v[1] = pack_f16(oacc[db][4 * gg + 2] * inv, oacc[db][4 * gg + 3] * inv);
                 *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * gg + 4 * hh) = v;
             }
         }
