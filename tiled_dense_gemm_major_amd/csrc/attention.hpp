@@ -39,7 +39,7 @@ namespace tgemm {
 //   The whole (b, h) slice spans at most 2^31 bytes (checked by the host).
 template <int D, bool CAUSAL>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
-                               amdgpu_waves_per_eu(2, 2)))
+                               amdgpu_waves_per_eu(3, 3)))
 attn_fwd(const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
          u16* __restrict__ O, int S, int H, float scale_log2, int nqb) {
     constexpr int BM = 128, BN = 64, ST = 3;
