@@ -19,6 +19,12 @@ events on the launch stream, TFLOP/s, fraction of the MFMA peak and of the HBM r
   --rounds R   time the configurations (and the vendor library) in R interleaved rounds
                of --repeat launches each, so that slow drifts of the clock (the chip is
                power-limited) fall on every configuration alike.
+
+  python -m tiled_dense_gemm_major_amd.sweep --attention [--repeat 20]
+
+times the attention forward pass (attn_fwd_f16) on its workloads instead: median/p10/p90
+microseconds, TFLOP/s over the (query, key) pairs the mask keeps, and the fractions of the
+fp16 MFMA peak and of the HBM roofline (Q, K, V read once, O written once).
 """
 from __future__ import annotations
 
@@ -47,6 +53,36 @@ def summary(t):
     return t[len(t) // 2], t[len(t) // 10], t[(9 * len(t)) // 10]
 
 
+def time_attention(tgemm, torch, np, args, stream):
+    from .inputs import ATTN_WORKLOADS
+    for name, w in ATTN_WORKLOADS.items():
+        Q, K, V = (torch.from_numpy(x.view(np.int16)).cuda().view(torch.float16)
+                   for x in w.generate())
+        O = torch.empty_like(Q)
+        B, S, H, D = w.shape
+
+        def go(i):
+            tgemm.attn_fwd_f16(B, S, H, D, Q, K, V, O, w.causal, stream)
+        for i in range(args.warmup):
+            go(i)
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(max(1, args.rounds)):
+            t += time_launches(torch, go, args.repeat, stream)
+        med, p10, p90 = summary(t)
+        flops = roofline.attention_flops(B, S, H, D, w.causal)
+        nbytes = roofline.attention_bytes(B, S, H, D)
+        print(json.dumps({
+            "workload": name, "kernel": "attn_fwd_f16", "median_us": med, "p10_us": p10,
+            "p90_us": p90, "tflops": flops / med / 1e6,
+            "frac_mfma_peak": flops / med / 1e6 / (roofline.PEAK_FLOPS["f16"] / 1e12),
+            "gbps": nbytes / med / 1e3,
+            "frac_hbm": nbytes / med / 1e3 / (roofline.HBM_BYTES_PER_S / 1e9),
+            "launches": len(t)}), flush=True)
+        del Q, K, V, O
+        torch.cuda.empty_cache()
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--workloads", default=",".join(WORKLOADS))
@@ -55,6 +91,8 @@ def main(argv=None):
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--cold", type=int, default=0,
                     help="rotate over this many copies of A and B (HBM-resident operands)")
+    ap.add_argument("--attention", action="store_true",
+                    help="time the attention forward pass on its workloads instead")
     ap.add_argument("--rounds", type=int, default=1,
                     help="interleaved timing rounds of --repeat launches per configuration")
     ap.add_argument("--torch-ref", action="store_true",
@@ -78,6 +116,9 @@ def main(argv=None):
     from . import tgemm
     tgemm.load()
     stream = torch.cuda.current_stream()
+    if args.attention:
+        time_attention(tgemm, torch, np, args, stream)
+        return
     best = {}
     for name in args.workloads.split(","):
         w = WORKLOADS[name]
