@@ -230,3 +230,33 @@ def test_attention_argument_errors(lib):
     assert call(q=None) == -2 and call(o=None) == -2
     assert call(q=Q + 8) == -3 and call(o=O + 2) == -3          # 16-byte alignment
     assert call(o=Q + 64) == -4 and call(o=V) == -4             # O overlapping an input
+
+
+def _frozen_table():
+    """Entries of the frozen per-device table (csrc/tile_table.inc)."""
+    text = open(os.path.join(ROOT, "tiled_dense_gemm_major_amd", "csrc", "tile_table.inc")).read()
+    grid = {ax: [int(v) for v in re.search(r"kTable%s\[\] = \{([^}]*)\}" % ax, text).group(1)
+                 .split(",")] for ax in "MNK"}
+    entries = []
+    for m in re.finditer(r"\{(-?\d+), (\d+), (\d+), (\d+), \{([-\d, ]+)\}\}", text):
+        layout, mi, ni, ki = (int(m.group(i)) for i in range(1, 5))
+        if layout < 0:
+            continue
+        cfg = [int(v) for v in m.group(5).split(",")]
+        entries.append((layout, mi, ni, ki, cfg))
+    return grid, entries
+
+
+def test_frozen_table_entries_are_compiled_and_chosen(lib):
+    """Every entry of the frozen table names a compiled configuration of its layout, and
+    the table's own grid points get exactly that entry from the table lookup."""
+    grid, entries = _frozen_table()
+    names = [n for n, _ in tgemm.Config._fields_]
+    for layout, mi, ni, ki, cfg in entries:
+        want = dict(zip(names, cfg))
+        listed = [c.as_dict() for c in tgemm.list_configs(tgemm.BF16, layout)]
+        assert want in listed, (layout, mi, ni, ki, want)
+        M, N, K = grid["M"][mi], grid["N"][ni], grid["K"][ki]
+        for dt in (tgemm.BF16, tgemm.F16):
+            got = tgemm.query_config(dt, M, N, K, layout).as_dict()
+            assert got == want, (layout, M, N, K, got, want)

@@ -4,6 +4,7 @@
 #include "tgemm.h"
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -208,11 +209,48 @@ const Variant* find_variant(int dtype, int a_layout, int layout, const tgemm_con
 // The table: fast configurations by how many workgroups they give, so that the chip
 // (256 compute units) is filled with the largest tile that still fills it; small M with
 // long K goes to the split-K skinny kernel.
+// The frozen per-device table (tile_table.inc, written by the sweep's --emit-table from
+// timings of every fast configuration on a grid of shapes): for A [M,K], the entry at
+// the grid point nearest in log2 of M, N and K, if the table has one.
+struct TableEntry {
+    int8_t layout, mi, ni, ki;
+    tgemm_config cfg;
+};
+#include "tile_table.inc"
+
+template <int N>
+int nearest_point(const int64_t (&grid)[N], int64_t x) {
+    const double lx = log2((double)(x > 1 ? x : 1));
+    int best = 0;
+    double bd = 1e300;
+    for (int i = 0; i < N; ++i) {
+        const double d = fabs(log2((double)grid[i]) - lx);
+        if (d < bd) {
+            bd = d;
+            best = i;
+        }
+    }
+    return best;
+}
+
+const tgemm_config* table_lookup(int layout, int64_t m, int64_t n, int64_t k) {
+    const int mi = nearest_point(kTableM, m), ni = nearest_point(kTableN, n),
+              ki = nearest_point(kTableK, k);
+    for (const TableEntry& e : kTable)
+        if (e.layout == layout && e.mi == mi && e.ni == ni && e.ki == ki)
+            return &e.cfg;
+    return nullptr;
+}
+
 tgemm_config choose(int dtype, int a_layout, int layout, int64_t m, int64_t n, int64_t k,
                     bool aligned) {
     (void)dtype;
     if (!aligned)
         return tgemm_config{TGEMM_KERNEL_GENERIC, 64, 64, 16, 2, 2, 1, 8, 1, 32};
+    if (a_layout == TGEMM_A_MK) {
+        if (const tgemm_config* c = table_lookup(layout, m, n, k))
+            return *c;
+    }
     if (a_layout == TGEMM_A_MK && layout == TGEMM_B_NK && m <= 128 && k >= 1024) {
         const int mt = m <= 32 ? 1 : (m <= 64 ? 2 : 4);
         const int depth = mt == 1 ? 4 : (mt == 2 ? 3 : 1);

@@ -20,6 +20,13 @@ events on the launch stream, TFLOP/s, fraction of the MFMA peak and of the HBM r
                of --repeat launches each, so that slow drifts of the clock (the chip is
                power-limited) fall on every configuration alike.
 
+  python -m tiled_dense_gemm_major_amd.sweep --emit-table tiled_dense_gemm_major_amd/csrc/tile_table.inc
+
+refreshes the library's frozen per-device table: every fast configuration is timed on a
+grid of shapes (A [M,K], B [N,K] and [K,N]; bf16, whose kernels are fp16's too), and the
+fastest per grid point is written as a C++ table that `choose` consults (the nearest grid
+point in log2 of M, N and K) before its fallback rules.  Rebuild the library afterwards.
+
   python -m tiled_dense_gemm_major_amd.sweep --attention [--repeat 20]
 
 times the attention forward pass (attn_fwd_f16) on its workloads instead: median/p10/p90
@@ -51,6 +58,76 @@ def time_launches(torch, fn, n, stream):
 def summary(t):
     t = sorted(t)
     return t[len(t) // 2], t[len(t) // 10], t[(9 * len(t)) // 10]
+
+
+# The table's grid (powers of two, plus the small M of decode-like products).
+TABLE_M = (16, 64, 128, 512, 1024, 2048, 4096, 8192)
+TABLE_N = (512, 2048, 8192)
+TABLE_K = (512, 2048, 8192)
+
+
+def emit_table(tgemm, torch, np, args, stream, path):
+    """Time every fast configuration on the grid and write the fastest per point."""
+    import datetime
+    from .inputs import B_KN, B_NK, Stream
+    rows = []
+    for layout in (B_NK, B_KN):
+        cfgs = [c for c in tgemm.list_configs(BF16, layout)
+                if c.kernel not in (tgemm.KERNEL_GENERIC, tgemm.KERNEL_SPLITK)]
+        for mi, M in enumerate(TABLE_M):
+            for ni, N in enumerate(TABLE_N):
+                for ki, K in enumerate(TABLE_K):
+                    st = Stream(1000 + M + N + K)
+                    A = torch.from_numpy(st.matrix((M, K), BF16, "uniform").view(np.int16)
+                                         ).cuda().view(torch.bfloat16)
+                    shape_b = (N, K) if layout == B_NK else (K, N)
+                    B = torch.from_numpy(st.matrix(shape_b, BF16, "uniform").view(np.int16)
+                                         ).cuda().view(torch.bfloat16)
+                    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+                    runs = []
+                    for c in cfgs:
+                        def go(i, c=c):
+                            tgemm.gemm_ex(BF16, M, N, K, A, B, C, layout, c, stream)
+                        runs.append((c, go))
+                    times = [[] for _ in runs]
+                    for _, fn in runs:
+                        for i in range(args.warmup):
+                            fn(i)
+                    torch.cuda.synchronize()
+                    for _ in range(max(1, args.rounds)):
+                        for r, (_, fn) in enumerate(runs):
+                            times[r] += time_launches(torch, fn, args.repeat, stream)
+                    meds = [summary(t)[0] for t in times]
+                    best = int(np.argmin(meds))
+                    c = runs[best][0]
+                    rows.append((layout, mi, ni, ki, c, meds[best]))
+                    print(json.dumps({"layout": layout, "M": M, "N": N, "K": K,
+                                      "best": c.as_dict(), "median_us": meds[best]}),
+                          flush=True)
+                    del A, B, C
+    dev = torch.cuda.get_device_properties(0)
+    lines = [
+        "// Frozen per-device configuration table (generated; do not edit by hand).",
+        f"// Device: {dev.name} ({getattr(dev, 'gcnArchName', 'gfx950')}), "
+        f"{datetime.date.today().isoformat()}; bf16, warmup {args.warmup}, "
+        f"{max(1, args.rounds)} x {args.repeat} launches per configuration, medians.",
+        "// Regenerate: python -m tiled_dense_gemm_major_amd.sweep --emit-table <this file>",
+        "static const int64_t kTableM[] = {" + ", ".join(map(str, TABLE_M)) + "};",
+        "static const int64_t kTableN[] = {" + ", ".join(map(str, TABLE_N)) + "};",
+        "static const int64_t kTableK[] = {" + ", ".join(map(str, TABLE_K)) + "};",
+        "// {b_layout, m index, n index, k index, {config}}  (median us when measured)",
+        "static const TableEntry kTable[] = {",
+    ]
+    for layout, mi, ni, ki, c, us in rows:
+        d = c.as_dict()
+        lines.append(
+            f"    {{{layout}, {mi}, {ni}, {ki}, {{{d['kernel']}, {d['block_m']}, {d['block_n']}, "
+            f"{d['block_k']}, {d['waves_m']}, {d['waves_n']}, {d['stages']}, {d['group_m']}, "
+            f"{d['split_k']}, {d['mfma']}}}}},  // {us:.1f}")
+    lines.append("};")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {path}: {len(rows)} entries", file=sys.stderr)
 
 
 def time_attention(tgemm, torch, np, args, stream):
@@ -91,6 +168,8 @@ def main(argv=None):
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--cold", type=int, default=0,
                     help="rotate over this many copies of A and B (HBM-resident operands)")
+    ap.add_argument("--emit-table", default="",
+                    help="time the grid and write the frozen configuration table here")
     ap.add_argument("--attention", action="store_true",
                     help="time the attention forward pass on its workloads instead")
     ap.add_argument("--rounds", type=int, default=1,
@@ -118,6 +197,9 @@ def main(argv=None):
     stream = torch.cuda.current_stream()
     if args.attention:
         time_attention(tgemm, torch, np, args, stream)
+        return
+    if args.emit_table:
+        emit_table(tgemm, torch, np, args, stream, args.emit_table)
         return
     best = {}
     for name in args.workloads.split(","):
