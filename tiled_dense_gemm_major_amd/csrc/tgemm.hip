@@ -162,6 +162,7 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
 // A [M,K], B [N,K]: every kernel
 #define ALL_MK_NK(DT)                                                                      \
     GENERIC(DT, 0, 0), TILED(DT, 0, 0, 256, 256, 64, 2, 2, 4),                             \
+        TILED(DT, 0, 0, 256, 128, 64, 2, 2, 8), TILED(DT, 0, 0, 128, 256, 64, 2, 2, 8),    \
         TILED(DT, 0, 0, 128, 128, 64, 2, 2, 8), TILED(DT, 0, 0, 64, 64, 64, 2, 2, 8),      \
         DMA(DT, 256, 256, 32, 2, 2, 4, 4), DMA(DT, 256, 256, 32, 2, 2, 5, 4),              \
         PINGPONG(DT, 0, 0, 256, 256, 64, 2, 4), PINGPONG(DT, 0, 0, 256, 256, 32, 4, 4),    \
@@ -173,6 +174,7 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
 // A [M,K], B [K,N]
 #define ALL_MK_KN(DT)                                                                      \
     GENERIC(DT, 0, 1), TILED(DT, 0, 1, 256, 256, 64, 2, 2, 4),                             \
+        TILED(DT, 0, 1, 256, 128, 64, 2, 2, 8), TILED(DT, 0, 1, 128, 256, 64, 2, 2, 8),    \
         TILED(DT, 0, 1, 128, 128, 64, 2, 2, 8), TILED(DT, 0, 1, 64, 64, 64, 2, 2, 8),      \
         PINGPONG(DT, 0, 1, 256, 256, 64, 2, 4), PINGPONG(DT, 0, 1, 256, 256, 32, 5, 4)
 // A [K,M], either B
