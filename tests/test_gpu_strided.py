@@ -116,18 +116,19 @@ def test_strided_table_choice_any_alignment(dev, orc, dtype, a_layout, b_layout,
 
 @pytest.mark.parametrize("a_layout,b_layout", LAYOUTS)
 def test_strided_large_table_choice(dev, orc, a_layout, b_layout):
-    """A shape the large-tile kernels take (quad for A [M,K] with B [N,K], ping-pong for
-    the other storages), with padded rows, checked on sampled entries."""
+    """The large-tile kernels (quad for A [M,K] with B [N,K], ping-pong for the other
+    storages) on padded rows, checked on sampled entries."""
     from tests.gpu_util import sample_positions
     from tiled_dense_gemm_major_amd import tgemm
     dtype = BF16
     M, N, K = 3584, 4096, 1000
     quad = a_layout == A_MK and b_layout == B_NK
-    assert tgemm.query_config(dtype, M, N, K, b_layout, True, a_layout).kernel == \
-        (tgemm.KERNEL_QUAD if quad else tgemm.KERNEL_PINGPONG)
+    kind = tgemm.KERNEL_QUAD if quad else tgemm.KERNEL_PINGPONG
+    cfgs = [c for c in tgemm.list_configs(dtype, b_layout, a_layout) if c.kernel == kind]
+    assert cfgs, kind
     A, Bn = _inputs(dtype, M, N, K, 900 + a_layout + 2 * b_layout)
-    say(f"strided large A{a_layout} B{b_layout} {M}x{N}x{K}")
-    got = run_strided(dtype, A, Bn, a_layout, b_layout, pads=(64, 8, 256))
+    say(f"strided large A{a_layout} B{b_layout} {M}x{N}x{K} {cfgs[0].as_dict()}")
+    got = run_strided(dtype, A, Bn, a_layout, b_layout, pads=(64, 8, 256), config=cfgs[0])
     rows, cols = sample_positions(M, N, 2000, 5)
     want, _ = orc.gemm_entries(dtype, A, Bn, B_NK, rows, cols)
     assert_parity(orc, dtype, K, got[rows, cols], want, "large")

@@ -44,7 +44,9 @@ extern "C" int attn_fwd_f16(int64_t batch, int64_t seq, int64_t heads, int64_t d
         return TGEMM_ERR_ALIASING;
     const int nqb = (int)((seq + 127) / 128);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)dim));
-    const dim3 grid((unsigned)nqb, (unsigned)heads, (unsigned)batch);
+    // one workgroup per (query block, batch, head); batch * seq * heads <= 2^24 (the
+    // size check above), so the count stays below 2^25
+    const dim3 grid((unsigned)(nqb * heads * batch));
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     const tgemm::u16* q = static_cast<const tgemm::u16*>(Q);

@@ -37,6 +37,39 @@ namespace tgemm {
 //            c ^ 2(row mod 4) (the 4 x 16 blocks of the transposing reads hit distinct
 //            banks).  Rows past seq read as zeros (buffer range check).
 //   The whole (b, h) slice spans at most 2^31 bytes (checked by the host).
+// Lane l and lane l ^ 32 combined, in every lane: v_permlane32_swap exchanges the upper
+// half of its first operand with the lower half of its second, so with both operands v
+// the two results hold v of lanes 0-31 and v of lanes 32-63, each in all 64 lanes.
+__device__ __forceinline__ float half_swap_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One transposing LDS read (ds_read_b64_tr_b16) at a byte address plus a constant offset
+// (the instruction's offset field; the compiler's own form of this read does not fold
+// constants into it).  Its result may be used only after lds_reads_done: the compiler does
+// not count this read among the LDS operations it waits for.
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16_b64(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "16-bit offset");
+    u32x2 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+// Wait for every LDS read issued so far; the values pass through the wait, so no use of
+// them is scheduled before it.
+__device__ __forceinline__ void lds_reads_done(u32x2 (&v)[2][2][2]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(v[0][0][0]), "+v"(v[0][0][1]), "+v"(v[0][1][0]), "+v"(v[0][1][1]),
+                   "+v"(v[1][0][0]), "+v"(v[1][0][1]), "+v"(v[1][1][0]), "+v"(v[1][1][1]));
+}
+
 template <int D, bool CAUSAL>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
                                amdgpu_waves_per_eu(3, 3)))
@@ -56,9 +89,14 @@ attn_fwd(const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __rest
 
     const int tid = (int)threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // the blocks with the most keys first (causal: the last queries)
-    const int qb = CAUSAL ? nqb - 1 - (int)blockIdx.x : (int)blockIdx.x;
-    const int h = (int)blockIdx.y, b = (int)blockIdx.z;
+    // One-dimensional grid, the (batch, head) index varying fastest and the query block
+    // slowest, so that workgroups start in order of decreasing work (causal: the last
+    // query blocks, which visit the most key tiles, first) and the short ones fill the
+    // tail of the launch.
+    const int nbh = (int)gridDim.x / nqb;
+    const int qi = (int)blockIdx.x / nbh, bh = (int)blockIdx.x - qi * nbh;
+    const int qb = CAUSAL ? nqb - 1 - qi : qi;
+    const int b = bh / H, h = bh - (bh / H) * H;
     const int q0 = qb * BM + 32 * wave;
     const int r = lane & 31, hh = lane >> 5;
     const uint32_t rs = (uint32_t)H * D;               // elements between sequence positions
@@ -122,17 +160,11 @@ attn_fwd(const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __rest
         const int col = 32 * db + vcol;
         vofs[db] = vrow * D + ((col >> 3) ^ (2 * (vrow & 3))) * 8 + (col & 7);
     }
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    typedef __attribute__((address_space(3))) u16 lds_u16;
-    auto read_vt = [&](const lds_u16* vt, int kb, int step, int db) {
-        const lds_u16* p = vt + vofs[db] + (32 * kb + 16 * step) * D;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * D));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-        return u32x4{l2[0], l2[1], h2[0], h2[1]};
-    };
+    // byte address of the lane's first V^T read in the V part of stage 0, per column block
+    uint32_t vaddr0[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+        vaddr0[db] = lds_addr(lds) + (uint32_t)(TILE + vofs[db]) * 2u;
     // K reads: lane's key row r of a 32-key block, chunk (2 s + l/32) swizzled by the row
     // (the swizzle of rows r and 32 + r agree)
     int kofs[NS];
@@ -169,7 +201,10 @@ attn_fwd(const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __rest
         if (kt + 2 < nkt)
             issue(kt + 2);
         const u16* kt_lds = lds + (kt % ST) * 2 * TILE;
-        const lds_u16* vt_lds = (const lds_u16*)(kt_lds + TILE);
+        uint32_t vb[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            vb[db] = vaddr0[db] + (uint32_t)((kt % ST) * 2 * TILE * 2);
 
         // S = Q K^T, two 32-key blocks
         f32x16 sacc[2];
@@ -204,14 +239,16 @@ attn_fwd(const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __rest
             for (int v = 0; v < 16; v += 2)
                 asm("v_max3_f32 %0, %1, %2, %3" : "=v"(mx) : "v"(mx), "v"(sacc[kb][v]),
                     "v"(sacc[kb][v + 1]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = half_swap_max(mx);
         // The exponentials are taken against a reference m_run that moves only when the
         // row maximum (scaled) has risen more than kSlack above it, so most tiles skip the
         // rescale of O: a weight is then at most 2^kSlack, which fp16 and the fp32 sums
         // hold exactly as well (the softmax does not depend on the reference).
         const float m_cand = fmaxf(m_run, mx * scale_log2);
         const bool move = m_cand > m_run + kSlack;         // also the first finite maximum
-        {
+        // (the rescale is skipped when no lane of the wave moves: it would multiply by 1,
+        // or, for a row with no key yet, multiply zeros by 0)
+        if (__builtin_amdgcn_ballot_w64(move)) {
             const float m_new = move ? m_cand : m_run;
             // a row with no key yet keeps an offset of 0 (its scores are all -infinity)
             const float m_use = m_new == -__builtin_huge_valf() ? 0.0f : m_new;
@@ -238,25 +275,42 @@ attn_fwd(const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __rest
         }
         l_run += psum;
 
-        // O += P V: four 16-key steps, the probabilities in fp16
+        // O += P V: four 16-key steps, the probabilities in fp16.  The V^T operands of a
+        // 32-key block are read first (8 transposing reads), then the weights packed, then
+        // the reads waited for and the four products issued.
+        static_for<0, 2>([&](auto kbc) {
+            constexpr int kb = decltype(kbc)::value;
+            u32x2 vf[2][NDB][2];
+            static_for<0, 2>([&](auto qqc) {
+                constexpr int qq = decltype(qqc)::value;
+                constexpr int off = (32 * kb + 16 * qq) * D * 2;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+                for (int db = 0; db < NDB; ++db) {
+                    vf[qq][db][0] = ds_read_tr16_b64<off>(vb[db]);
+                    vf[qq][db][1] = ds_read_tr16_b64<off + 8 * D * 2>(vb[db]);
+                }
+            });
+            u32x4 pf[2];
 #pragma unroll
-            for (int qq = 0; qq < 2; ++qq) {
-                u32x4 pf;
+            for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    pf[e] = pack_f16(sacc[kb][8 * qq + 2 * e], sacc[kb][8 * qq + 2 * e + 1]);
+                    pf[qq][e] = pack_f16(sacc[kb][8 * qq + 2 * e], sacc[kb][8 * qq + 2 * e + 1]);
+            lds_reads_done(vf);
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
-                    oacc[db] = mfma_32x32x16<DT_F16>(read_vt(vt_lds, kb, qq, db), pf, oacc[db]);
-            }
-        }
+                    oacc[db] = mfma_32x32x16<DT_F16>(
+                        u32x4{vf[qq][db][0][0], vf[qq][db][0][1], vf[qq][db][1][0],
+                              vf[qq][db][1][1]},
+                        pf[qq], oacc[db]);
+        });
     }
     wait_vm<0>();                               // no load left in flight
 
     // divide by the row sum once, cast, store: lane holds row q, columns 8g' + 4hh + 0..3
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = half_swap_sum(l_run);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     if (q < S) {
         u16* orow = O + base + (size_t)q * rs;

@@ -6,8 +6,9 @@
       --workload "bf16 8192x8192x8192, B [N,K]" --out profiles/traffic_....json
 
 `trace` reads the kernel trace (`--kernel-trace`) and prints the dispatch count and the
-average, median, min and max duration of the named kernel, over all dispatches and over
-the last `--timed` ones (the timed region of a benchmark run).
+average, median, min and max duration of the named kernel, over all dispatches (or those
+of `--range A:B`, in start order) and over the last `--timed` ones of them (the timed
+region of a benchmark run).
 
 `traffic` reads two counter runs of the kernel (`--pmc FETCH_SIZE`, `--pmc WRITE_SIZE`,
 KiB per dispatch) and the same two counters for a plain device copy of `--copy-bytes`
@@ -75,6 +76,11 @@ def cmd_trace(args):
     if not d:
         raise SystemExit(f"no dispatch of {args.kernel!r}")
     us = [x / 1e3 for x in d]
+    if args.range:
+        lo, hi = (int(x) for x in args.range.split(":"))
+        us = us[lo:hi]
+        if not us:
+            raise SystemExit(f"no dispatch in range {args.range}")
     timed = us[-args.timed:] if args.timed else us
     out = {
         "kernel": name,
@@ -130,6 +136,8 @@ def main(argv=None):
     t.add_argument("dir")
     t.add_argument("--kernel", required=True)
     t.add_argument("--timed", type=int, default=0)
+    t.add_argument("--range", default="",
+                   help="A:B, only dispatches A..B-1 of the kernel (in start order)")
     c = sub.add_parser("traffic")
     c.add_argument("--kernel", required=True)
     c.add_argument("--kernel-name", default="")
