@@ -1283,8 +1283,6 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
         const u16* bs1 = lds + (SA + jb1) * SLOT;
         const uint32_t a2_at = a_slot(ia2), b_at = b_slot(jb);
         const int k2 = k_base(t + 2);                 // this step loads tile t+2
-        if (tail && t + 2 == nfull)
-            mask_tail();
         static_for<0, KS>([&](auto subc) {
             constexpr int s = decltype(subc)::value;
             constexpr int cb = s & 1, nb = cb ^ 1;
@@ -1360,12 +1358,23 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
                    std::integral_constant<int, 0>{}, rc);
         });
         int ia = 0;                                // A slot of tile t (t % 3)
-        for (int t = 0; t < nk; ++t) {
-            const int ia1 = ia == SA - 1 ? 0 : ia + 1;
-            const int ia2 = ia1 == SA - 1 ? 0 : ia1 + 1;
-            const int jb = t & 1;
-            step(t, ia, ia1, ia2, jb, jb ^ 1);
-            ia = ia1;
+        auto steps = [&](int t0, int t1) __attribute__((always_inline)) {
+            for (int t = t0; t < t1; ++t) {
+                const int ia1 = ia == SA - 1 ? 0 : ia + 1;
+                const int ia2 = ia1 == SA - 1 ? 0 : ia1 + 1;
+                const int jb = t & 1;
+                step(t, ia, ia1, ia2, jb, jb ^ 1);
+                ia = ia1;
+            }
+        };
+        // Step t loads tile t+2, so the tail tile's loads go out in step nfull-2 (those
+        // of a tail tile 0 or 1 went out above): the walk runs in two loops with the
+        // masking between them, and no step carries the test.
+        const int tsplit = tail && nfull >= 2 ? nfull - 2 : nk;
+        steps(0, tsplit);
+        if (tsplit < nk) {
+            mask_tail();
+            steps(tsplit, nk);
         }
         wait_vm<0>();                              // the trailing zero loads
     }
