@@ -1095,6 +1095,44 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
     }
 }
 
+// Direct-to-LDS load into the 1 KiB block OFF bytes past M0.  The instruction offset is
+// added to the global address as well, so the caller's offset is OFF lower than the
+// element's.  NOP: an s_nop first (M0 was written by the instruction before).  STEP: M0
+// moves on by 4 KiB after the load (the instruction offset reaches 3 KiB at most).
+template <int POL, int OFF, bool NOP, bool STEP>
+__device__ __forceinline__ void dma16_off(rsrc4_t r, uint32_t voff, uint32_t soff) {
+    static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
+    const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+    static_assert(POL == 0 || POL == 2, "default or sc0 policy");
+    if constexpr (POL == 2) {
+        if constexpr (NOP && STEP)
+            asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen offset:%3 sc0 lds\n\ts_add_u32 m0, m0, 0x1000"
+                         ::"v"(voff), "s"(r), "s"(so), "i"(OFF) : "memory", "m0", "scc");
+        else if constexpr (NOP)
+            asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen offset:%3 sc0 lds"
+                         ::"v"(voff), "s"(r), "s"(so), "i"(OFF) : "memory");
+        else if constexpr (STEP)
+            asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 sc0 lds\n\ts_add_u32 m0, m0, 0x1000"
+                         ::"v"(voff), "s"(r), "s"(so), "i"(OFF) : "memory", "m0", "scc");
+        else
+            asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 sc0 lds"
+                         ::"v"(voff), "s"(r), "s"(so), "i"(OFF) : "memory");
+    } else {
+        if constexpr (NOP && STEP)
+            asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds\n\ts_add_u32 m0, m0, 0x1000"
+                         ::"v"(voff), "s"(r), "s"(so), "i"(OFF) : "memory", "m0", "scc");
+        else if constexpr (NOP)
+            asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds"
+                         ::"v"(voff), "s"(r), "s"(so), "i"(OFF) : "memory");
+        else if constexpr (STEP)
+            asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds\n\ts_add_u32 m0, m0, 0x1000"
+                         ::"v"(voff), "s"(r), "s"(so), "i"(OFF) : "memory", "m0", "scc");
+        else
+            asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds"
+                         ::"v"(voff), "s"(r), "s"(so), "i"(OFF) : "memory");
+    }
+}
+
 // ------------------------------------------------------------------------------------
 // Quadrant kernel (A [M,K], B [N,K]).
 //   One wave per SIMD: 4 waves in 2 x 2, each owning a 128 x 128 quadrant of the
@@ -1142,7 +1180,7 @@ constexpr int op_kind(int o) {
     return 0;
 }
 
-template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL>
+template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL, bool OFFS>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
                                amdgpu_waves_per_eu(1, 1)))
 gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
@@ -1164,6 +1202,9 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     static_assert(KS % 2 == 0, "every step starts from operand buffer 0");
     static_assert((SA + SB) * SLOT * 2 <= 160 * 1024, "LDS");
     static_assert(PRE >= 1 && PRE < NM && SPA >= 1 && SPB >= 1, "schedule");
+    // Two loads of one operand can be adjacent (no instruction between them) when the A
+    // loads outnumber their MFMA slots, or the B loads outnumber the reads dealt between.
+    constexpr bool TIGHT = NB > (SPA < (KS - 1) * NM ? SPA : (KS - 1) * NM) || NR < NB;
 
     __shared__ __attribute__((aligned(1024))) u16 lds[(SA + SB) * SLOT];
 
@@ -1189,12 +1230,18 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
 #pragma unroll
     for (int p = 0; p < 2; ++p)
         kcol[p] = (pch ^ swz<KC>(p * ROWS + prow)) * 8;
+    // With OFFS the 1 KiB LDS block of load b comes from the instruction offset
+    // (b % 4) KiB, M0 moving on by 4 KiB after the fourth load: one M0 update per four
+    // loads instead of one per load.  The offset adds to the global address as well, so
+    // the stored offsets are that much lower; rows b * ROWS >= 8 apart keep them
+    // non-negative when lda, ldb >= 64 (the launcher's condition for OFFS).
     uint32_t a_vo[NB], b_vo[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int ra = m0 + r0 + b * ROWS, rbn = n0 + r0 + b * ROWS;
-        a_vo[b] = ra < M ? (uint32_t)(ra * lda + kcol[b & 1]) * 2u : kOutOfRange;
-        b_vo[b] = rbn < N ? (uint32_t)(rbn * ldb + kcol[b & 1]) * 2u : kOutOfRange;
+        const uint32_t lo = OFFS ? (uint32_t)(b & 3) * 1024u : 0u;
+        a_vo[b] = ra < M ? (uint32_t)(ra * lda + kcol[b & 1]) * 2u - lo : kOutOfRange;
+        b_vo[b] = rbn < N ? (uint32_t)(rbn * ldb + kcol[b & 1]) * 2u - lo : kOutOfRange;
     }
     // The K walk: the whole tiles first, starting kofs tiles in (XCD x starts x/8 of the
     // way along) and wrapping, then the tail tile holding the last K % BK columns, if any.
@@ -1230,8 +1277,17 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     auto load_b = [&](int k0, auto isac, auto bc, auto nopc) {
         constexpr bool is_a = decltype(isac)::value;
         constexpr int b = decltype(bc)::value;
-        dma16_next<POL, decltype(nopc)::value>(is_a ? ra : rb, is_a ? a_vo[b] : b_vo[b],
-                                               (uint32_t)k0 * 2u);
+        constexpr bool back_to_back = decltype(nopc)::value;   // no instruction between loads
+        if constexpr (OFFS) {
+            // an s_nop after an M0 write: before block 0 of a back-to-back run (M0 was just
+            // set), and before block 4 when it may directly follow block 3's M0 step
+            constexpr bool nop = back_to_back ? (b & 3) == 0 : (b == 4 && TIGHT);
+            dma16_off<POL, (b & 3) * 1024, nop, (b & 3) == 3 && b + 1 < NB>(
+                is_a ? ra : rb, is_a ? a_vo[b] : b_vo[b], (uint32_t)k0 * 2u);
+        } else {
+            dma16_next<POL, back_to_back>(is_a ? ra : rb, is_a ? a_vo[b] : b_vo[b],
+                                          (uint32_t)k0 * 2u);
+        }
     };
     auto a_slot = [&](int i) { return lds0 + (uint32_t)(i * SLOT * 2); };
     auto b_slot = [&](int j) { return lds0 + (uint32_t)((SA + j) * SLOT * 2); };

@@ -97,8 +97,13 @@ template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL>
 hipError_t launch_quad(const void* A, const void* B, void* C, int M, int N, int K, int lda,
                        int ldb, int ldc, int group_m, hipStream_t s) {
     const int gm = cdiv(M, 256), gn = cdiv(N, 256);
-    hipLaunchKernelGGL((tgemm::gemm_quad<DT, MF, PRE, SPA, SPB, STAG, POL>),
-                       dim3((unsigned)(gm * gn)), dim3(256), 0, s, KARGS, gm, gn, group_m);
+    // the instruction-offset form of the loads needs rows of at least 64 elements
+    if (lda >= 64 && ldb >= 64)
+        hipLaunchKernelGGL((tgemm::gemm_quad<DT, MF, PRE, SPA, SPB, STAG, POL, true>),
+                           dim3((unsigned)(gm * gn)), dim3(256), 0, s, KARGS, gm, gn, group_m);
+    else
+        hipLaunchKernelGGL((tgemm::gemm_quad<DT, MF, PRE, SPA, SPB, STAG, POL, false>),
+                           dim3((unsigned)(gm * gn)), dim3(256), 0, s, KARGS, gm, gn, group_m);
     return hipGetLastError();
 }
 
