@@ -1236,31 +1236,30 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     // the stored offsets are that much lower; rows b * ROWS >= 8 apart keep them
     // non-negative when lda, ldb >= 64 (the launcher's condition for OFFS).
     uint32_t a_vo[NB], b_vo[NB];
+    auto set_offsets = [&]() {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        const int ra = m0 + r0 + b * ROWS, rbn = n0 + r0 + b * ROWS;
-        const uint32_t lo = OFFS ? (uint32_t)(b & 3) * 1024u : 0u;
-        a_vo[b] = ra < M ? (uint32_t)(ra * lda + kcol[b & 1]) * 2u - lo : kOutOfRange;
-        b_vo[b] = rbn < N ? (uint32_t)(rbn * ldb + kcol[b & 1]) * 2u - lo : kOutOfRange;
-    }
-    // The K walk: the whole tiles first, starting kofs tiles in (XCD x starts x/8 of the
-    // way along) and wrapping, then the tail tile holding the last K % BK columns, if any.
+        for (int b = 0; b < NB; ++b) {
+            const int ra = m0 + r0 + b * ROWS, rbn = n0 + r0 + b * ROWS;
+            const uint32_t lo = OFFS ? (uint32_t)(b & 3) * 1024u : 0u;
+            a_vo[b] = ra < M ? (uint32_t)(ra * lda + kcol[b & 1]) * 2u - lo : kOutOfRange;
+            b_vo[b] = rbn < N ? (uint32_t)(rbn * ldb + kcol[b & 1]) * 2u - lo : kOutOfRange;
+        }
+    };
+    set_offsets();
+    // The K walk: the tail tile holding the last K % BK columns first, if any (its loads
+    // go out before the loop, the only masked ones), then the whole tiles, starting kofs
+    // tiles in (XCD x starts x/8 of the way along) and wrapping.  Loads past the end of
+    // the walk are never read; they continue the wrap (any valid tile would do).
     const int nfull = K / BK;
     const bool tail = nfull < nk;
+    const int toff = tail ? 1 : 0;
     const int kofs = STAG ? (((int)blockIdx.x & 7) * nfull) >> 3 : 0;
     const uint32_t lds0 = lds_addr(lds);
     const uint32_t wave_at = (uint32_t)(64 * wave * BK * 2);
-    // K position of the tile loaded at walk step kt; a step past the end is never read,
-    // so its loads fetch tile 0 (any valid tile would do)
-    auto k_base = [&](int kt) {
-        if (kt >= nk)
-            return 0;
-        if (kt >= nfull)
-            return nfull * BK;
-        return (kt + kofs >= nfull ? kt + kofs - nfull : kt + kofs) * BK;
-    };
-    // Before the tail tile's loads (the last real loads of the walk): chunks past K get
-    // out-of-range offsets (zeros), in place, since every later load is never read.
+    // index among the whole tiles of walk step u >= toff
+    auto full_index = [&](int u) { return nfull > 0 ? (u - toff + kofs) % nfull : 0; };
+    // For the tail tile's loads: chunks past K get out-of-range offsets (zeros), in place
+    // (set_offsets restores them afterwards).
     auto mask_tail = [&]() {
         const int rem = K - nfull * BK;
         const bool ok0 = kcol[0] < rem, ok1 = kcol[1] < rem;
@@ -1331,14 +1330,19 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     };
 
     // One step: tile t from A slot ia and B slot jb; tile t+1 lies in A slot ia1 and
-    // B slot jb1 (= the other B slot); A slot ia2 takes tile t+2.
-    auto step = [&](int t, int ia, int ia1, int ia2, int jb, int jb1) {
+    // B slot jb1 (= the other B slot); A slot ia2 takes tile t+2, whose K position (in
+    // bytes) is k2.  The slots come as ints or as integral constants (then every LDS
+    // address of the step is a constant offset).  In a slot without memory operations the
+    // step advances the walk: kk, and k2n, the K position of the next step's loads.
+    int kk = 0;                                       // whole-tile index of k2n
+    auto step = [&](auto ia, auto ia1, auto ia2, auto jb, auto jb1, uint32_t k2,
+                    uint32_t& k2n) __attribute__((always_inline)) {
         const u16* as = lds + ia * SLOT;
         const u16* bs = lds + (SA + jb) * SLOT;
         const u16* as1 = lds + ia1 * SLOT;
         const u16* bs1 = lds + (SA + jb1) * SLOT;
         const uint32_t a2_at = a_slot(ia2), b_at = b_slot(jb);
-        const int k2 = k_base(t + 2);                 // this step loads tile t+2
+        const int k2i = (int)(k2 / 2u);               // load_b takes elements
         static_for<0, KS>([&](auto subc) {
             constexpr int s = decltype(subc)::value;
             constexpr int cb = s & 1, nb = cb ^ 1;
@@ -1369,15 +1373,23 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
                 if constexpr (!last) {
                     constexpr int G = s * NM + J;     // slot index over the pre-barrier sub-steps
                     static_for<deal<NB, SA_, G>::lo, deal<NB, SA_, G>::hi>([&](auto bc) {
-                        load_b(k2, std::true_type{}, bc, std::false_type{});
+                        load_b(k2i, std::true_type{}, bc, std::false_type{});
                         __builtin_amdgcn_sched_barrier(0);
                     });
+                }
+                if constexpr (s == 0 && J == NM - 4) {
+                    kk = kk + 1 >= nfull ? 0 : kk + 1;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if constexpr (s == 0 && J == NM - 3) {
+                    k2n = (uint32_t)kk * (uint32_t)(BK * 2);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 static_for<deal<NOPS, SS, J - J0>::lo, deal<NOPS, SS, J - J0>::hi>(
                     [&](auto oc) {
                         constexpr int kind = op_kind<NL, NR>(decltype(oc)::value);
                         if constexpr (kind >= 0)
-                            load_b(k2, std::false_type{}, std::integral_constant<int, kind>{},
+                            load_b(k2i, std::false_type{}, std::integral_constant<int, kind>{},
                                    std::false_type{});
                         else if constexpr (!last)
                             read_r(as, bs, std::integral_constant<int, s + 1>{},
@@ -1394,43 +1406,53 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     };
 
     if (nk > 0) {
+        // The steps run as nk % 6 single steps, then groups of six with constant slots
+        // (the A ring has 3 slots, the B ring 2): tile 0 goes into the slots that make
+        // the first group start at A slot 0 and B slot 0.
+        const int rem = nk % 6;
+        const int p0 = (6 - rem) % 6;              // ring phase of tile 0
         // tiles 0 and 1 (A then B each); step 0 issues the A loads of tile 2
         for (int u = 0; u < 2; ++u) {
-            if (tail && u == nfull)
+            const bool tail_tile = tail && u == 0;
+            if (tail_tile)
                 mask_tail();
-            const int ku = k_base(u);
-            set_m0(a_slot(u) + wave_at);
+            const int ku = tail_tile ? nfull * BK : full_index(u) * BK;
+            set_m0(a_slot((p0 + u) % SA) + wave_at);
             static_for<0, NB>([&](auto bc) {
                 load_b(ku, std::true_type{}, bc, std::true_type{});
             });
-            set_m0(b_slot(u) + wave_at);
+            set_m0(b_slot((p0 + u) % SB) + wave_at);
             static_for<0, NB>([&](auto bc) {
                 load_b(ku, std::false_type{}, bc, std::true_type{});
             });
+            if (tail_tile)
+                set_offsets();
         }
         wait_vm_then_sync<2 * NB>();              // tile 0 complete
         static_for<0, NR>([&](auto rc) {
-            read_r(lds, lds + SA * SLOT, std::integral_constant<int, 0>{},
-                   std::integral_constant<int, 0>{}, rc);
+            read_r(lds + (p0 % SA) * SLOT, lds + (SA + p0 % SB) * SLOT,
+                   std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, rc);
         });
-        int ia = 0;                                // A slot of tile t (t % 3)
-        auto steps = [&](int t0, int t1) __attribute__((always_inline)) {
-            for (int t = t0; t < t1; ++t) {
-                const int ia1 = ia == SA - 1 ? 0 : ia + 1;
-                const int ia2 = ia1 == SA - 1 ? 0 : ia1 + 1;
-                const int jb = t & 1;
-                step(t, ia, ia1, ia2, jb, jb ^ 1);
-                ia = ia1;
-            }
-        };
-        // Step t loads tile t+2, so the tail tile's loads go out in step nfull-2 (those
-        // of a tail tile 0 or 1 went out above): the walk runs in two loops with the
-        // masking between them, and no step carries the test.
-        const int tsplit = tail && nfull >= 2 ? nfull - 2 : nk;
-        steps(0, tsplit);
-        if (tsplit < nk) {
-            mask_tail();
-            steps(tsplit, nk);
+        kk = full_index(2);
+        uint32_t kx = (uint32_t)kk * (uint32_t)(BK * 2), ky = 0;
+        for (int t = 0; t < rem; ++t) {
+            const int p = p0 + t;                  // < 11
+            const int ia = p % SA, jb = p % SB;
+            const int ia1 = ia == SA - 1 ? 0 : ia + 1;
+            const int ia2 = ia1 == SA - 1 ? 0 : ia1 + 1;
+            step(ia, ia1, ia2, jb, jb ^ 1, kx, ky);
+            kx = ky;
+        }
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        for (int g = nk / 6; g > 0; --g) {
+            step(I0{}, I1{}, I2{}, I0{}, I1{}, kx, ky);
+            step(I1{}, I2{}, I0{}, I1{}, I0{}, ky, kx);
+            step(I2{}, I0{}, I1{}, I0{}, I1{}, kx, ky);
+            step(I0{}, I1{}, I2{}, I1{}, I0{}, ky, kx);
+            step(I1{}, I2{}, I0{}, I0{}, I1{}, kx, ky);
+            step(I2{}, I0{}, I1{}, I1{}, I0{}, ky, kx);
         }
         wait_vm<0>();                              // the trailing zero loads
     }
