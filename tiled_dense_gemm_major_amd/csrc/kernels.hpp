@@ -1288,8 +1288,10 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
                                           (uint32_t)k0 * 2u);
         }
     };
-    auto a_slot = [&](int i) { return lds0 + (uint32_t)(i * SLOT * 2); };
-    auto b_slot = [&](int j) { return lds0 + (uint32_t)((SA + j) * SLOT * 2); };
+    // M0 for the wave's first block of slot i (A slots 0..SA-1, then the B slots), from
+    // a base kept in a scalar register
+    const uint32_t m0_base = __builtin_amdgcn_readfirstlane(lds0 + wave_at);
+    auto m0_of = [&](auto i) { return m0_base + (uint32_t)(i * SLOT * 2); };
 
     // Operand reads: lane l takes row l % MF of an MFMA block, 16-byte chunk
     // s * CPS + l / MF of the sub-step (the swizzle of its row depends on l % 16 only).
@@ -1334,29 +1336,34 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     // bytes) is k2.  The slots come as ints or as integral constants (then every LDS
     // address of the step is a constant offset).  In a slot without memory operations the
     // step advances the walk: kk, and k2n, the K position of the next step's loads.
-    int kk = 0;                                       // whole-tile index of k2n
-    auto step = [&](auto ia, auto ia1, auto ia2, auto jb, auto jb1, uint32_t k2,
-                    uint32_t& k2n) __attribute__((always_inline)) {
+    uint32_t kwalk = 0;                // K position (bytes) of the next step's loads
+    const uint32_t kwrap = (uint32_t)nfull * (uint32_t)(BK * 2);
+    auto step = [&](auto ia, auto ia1, auto ia2, auto jb, auto jb1)
+                    __attribute__((always_inline)) {
         const u16* as = lds + ia * SLOT;
         const u16* bs = lds + (SA + jb) * SLOT;
         const u16* as1 = lds + ia1 * SLOT;
         const u16* bs1 = lds + (SA + jb1) * SLOT;
-        const uint32_t a2_at = a_slot(ia2), b_at = b_slot(jb);
-        const int k2i = (int)(k2 / 2u);               // load_b takes elements
+        const uint32_t k2b = kwalk;                   // this step loads tile t+2 from here
+        const int k2i = (int)(k2b / 2u);              // load_b takes elements
         static_for<0, KS>([&](auto subc) {
             constexpr int s = decltype(subc)::value;
             constexpr int cb = s & 1, nb = cb ^ 1;
             constexpr bool last = s + 1 == KS;
             constexpr int J0 = last ? PRE : 0;
+            // this sub-step's operands were read during the previous one: one wait for
+            // all of them (lgkmcnt(0), vmcnt and expcnt left at their maxima) instead of
+            // the compiler's wait before each first use
+            __builtin_amdgcn_s_waitcnt(0xC07F);
             if constexpr (s == 0) {
-                set_m0(a2_at + wave_at);               // the A loads of tile t+2
+                set_m0(m0_of(ia2));                 // the A loads of tile t+2
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (last) {
                 static_for<0, PRE>([&](auto jc) { mma(std::integral_constant<int, cb>{}, jc); });
                 wait_vm_then_sync<NB>();       // tile t+1 landed; the A loads of t+2 may fly
                 __builtin_amdgcn_sched_barrier(0);
-                set_m0(b_at + wave_at);                // the B loads of tile t+2
+                set_m0(m0_of(SA + jb));             // the B loads of tile t+2
                 __builtin_amdgcn_sched_barrier(0);
             }
             // the A loads of tile t+2 are dealt over the first SPA MFMA slots of the
@@ -1378,11 +1385,11 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
                     });
                 }
                 if constexpr (s == 0 && J == NM - 4) {
-                    kk = kk + 1 >= nfull ? 0 : kk + 1;
+                    kwalk += (uint32_t)(BK * 2);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if constexpr (s == 0 && J == NM - 3) {
-                    k2n = (uint32_t)kk * (uint32_t)(BK * 2);
+                    kwalk = kwalk >= kwrap ? 0u : kwalk;
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 static_for<deal<NOPS, SS, J - J0>::lo, deal<NOPS, SS, J - J0>::hi>(
@@ -1417,11 +1424,11 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
             if (tail_tile)
                 mask_tail();
             const int ku = tail_tile ? nfull * BK : full_index(u) * BK;
-            set_m0(a_slot((p0 + u) % SA) + wave_at);
+            set_m0(m0_of((p0 + u) % SA));
             static_for<0, NB>([&](auto bc) {
                 load_b(ku, std::true_type{}, bc, std::true_type{});
             });
-            set_m0(b_slot((p0 + u) % SB) + wave_at);
+            set_m0(m0_of(SA + (p0 + u) % SB));
             static_for<0, NB>([&](auto bc) {
                 load_b(ku, std::false_type{}, bc, std::true_type{});
             });
@@ -1433,26 +1440,24 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
             read_r(lds + (p0 % SA) * SLOT, lds + (SA + p0 % SB) * SLOT,
                    std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, rc);
         });
-        kk = full_index(2);
-        uint32_t kx = (uint32_t)kk * (uint32_t)(BK * 2), ky = 0;
+        kwalk = (uint32_t)full_index(2) * (uint32_t)(BK * 2);
         for (int t = 0; t < rem; ++t) {
             const int p = p0 + t;                  // < 11
             const int ia = p % SA, jb = p % SB;
             const int ia1 = ia == SA - 1 ? 0 : ia + 1;
             const int ia2 = ia1 == SA - 1 ? 0 : ia1 + 1;
-            step(ia, ia1, ia2, jb, jb ^ 1, kx, ky);
-            kx = ky;
+            step(ia, ia1, ia2, jb, jb ^ 1);
         }
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;
         using I2 = std::integral_constant<int, 2>;
         for (int g = nk / 6; g > 0; --g) {
-            step(I0{}, I1{}, I2{}, I0{}, I1{}, kx, ky);
-            step(I1{}, I2{}, I0{}, I1{}, I0{}, ky, kx);
-            step(I2{}, I0{}, I1{}, I0{}, I1{}, kx, ky);
-            step(I0{}, I1{}, I2{}, I1{}, I0{}, ky, kx);
-            step(I1{}, I2{}, I0{}, I0{}, I1{}, kx, ky);
-            step(I2{}, I0{}, I1{}, I1{}, I0{}, ky, kx);
+            step(I0{}, I1{}, I2{}, I0{}, I1{});
+            step(I1{}, I2{}, I0{}, I1{}, I0{});
+            step(I2{}, I0{}, I1{}, I0{}, I1{});
+            step(I0{}, I1{}, I2{}, I1{}, I0{});
+            step(I1{}, I2{}, I0{}, I0{}, I1{});
+            step(I2{}, I0{}, I1{}, I1{}, I0{});
         }
         wait_vm<0>();                              // the trailing zero loads
     }
