@@ -243,8 +243,19 @@ int nearest_point(const int64_t (&grid)[N], int64_t x) {
 const tgemm_config* table_lookup(int layout, int64_t m, int64_t n, int64_t k) {
     const int mi = nearest_point(kTableM, m), ni = nearest_point(kTableN, n),
               ki = nearest_point(kTableK, k);
+    constexpr int NM = sizeof(kTableM) / sizeof(kTableM[0]);
+    constexpr int NN = sizeof(kTableN) / sizeof(kTableN[0]);
+    constexpr int NK = sizeof(kTableK) / sizeof(kTableK[0]);
+    constexpr int NE = sizeof(kTable) / sizeof(kTable[0]);
+    auto match = [&](const TableEntry& e) {
+        return e.layout == layout && e.mi == mi && e.ni == ni && e.ki == ki;
+    };
+    // the generator writes every point in (layout, m, n, k) order: index it directly
+    const int idx = ((layout * NM + mi) * NN + ni) * NK + ki;
+    if (idx >= 0 && idx < NE && match(kTable[idx]))
+        return &kTable[idx].cfg;
     for (const TableEntry& e : kTable)
-        if (e.layout == layout && e.mi == mi && e.ni == ni && e.ki == ki)
+        if (match(e))
             return &e.cfg;
     return nullptr;
 }

@@ -61,9 +61,9 @@ def summary(t):
 
 
 # The table's grid (powers of two, plus the small M of decode-like products).
-TABLE_M = (16, 64, 128, 512, 1024, 2048, 4096, 8192)
-TABLE_N = (512, 2048, 8192)
-TABLE_K = (512, 2048, 8192)
+TABLE_M = (16, 64, 128, 256, 512, 1024, 2048, 4096, 8192)
+TABLE_N = (512, 1024, 2048, 4096, 8192)
+TABLE_K = (512, 1024, 2048, 4096, 8192)
 
 
 def emit_table(tgemm, torch, np, args, stream, path):
