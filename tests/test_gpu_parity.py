@@ -225,6 +225,26 @@ def test_every_config_short_k_exact(dev, orc, dtype, K):
         assert np.array_equal(run(dtype, A, B, B_NK, cfg), want), (K, _cfg_id(cfg))
 
 
+# K walks of the quadrant kernel, bit for bit on exact inputs: the steps run as
+# (K/64 mod 6) single steps and then groups of six with constant ring slots, a K tail is
+# walked first, and the XCD-staggered walk wraps at the last whole tile.  Each K below
+# picks one combination (whole tiles, tail, remainder steps, groups).
+@pytest.mark.parametrize("K", [136, 192, 384, 448, 456, 712, 776, 1000, 1536])
+def test_quad_k_walk_exact(dev, orc, K):
+    from tiled_dense_gemm_major_amd import tgemm
+    dtype = BF16
+    rng = np.random.default_rng(500 + K)
+    M, N = 512, 768          # 2 x 3 tiles, so the eight XCD staggers differ
+    A = _int_bits(dtype, rng.integers(-2, 3, (M, K)))
+    B = _int_bits(dtype, rng.integers(-2, 3, (N, K)))
+    want = orc.gemm(dtype, A, B, B_NK)
+    nk = -(-K // 64)
+    for cfg in [c for c in _configs(dtype, B_NK) if c.kernel == tgemm.KERNEL_QUAD]:
+        say(f"quad k walk K={K} (tiles {nk}, remainder {nk % 6}, tail {K % 64}) "
+            f"{_cfg_id(cfg)}")
+        assert np.array_equal(run(dtype, A, B, B_NK, cfg), want), (K, _cfg_id(cfg))
+
+
 def test_quad_repeat_launches_bitwise_identical(dev, orc):
     """Many workgroups per compute unit through the five-slot ring: a stage reused too
     early shows up as launch-to-launch differences."""
