@@ -1155,11 +1155,16 @@ __device__ __forceinline__ void dma16_off(rsrc4_t r, uint32_t voff, uint32_t sof
 //                        then in LDS and every wave has read all of tile t), then the
 //                        reads of tile t+1's first operands and the B loads of tile t+2
 //                        into the B slot tile t used.
-// An A load has a step and a half to land, a B load one step.  Loads past the last
-// tile fetch tile 0 into a slot no step reads, so every step has the same number of
-// loads in flight.  STAG starts the K walk of the workgroups of XCD x at
-// x/8 of K (wrapping), so that the eight XCDs do not stream the same addresses at once;
-// POL is the cache policy of the loads.
+// An A load has a step and a half to land, a B load one step.  The K walk takes the
+// tail tile (the last K % 64 columns, masked) first, then the whole tiles; loads past
+// the end of the walk continue it into a slot no step reads, so every step has the same
+// number of loads in flight.  STAG starts the whole-tile walk of the workgroups of XCD x
+// at x/8 of K (wrapping), so that the eight XCDs do not stream the same addresses at
+// once; POL is the cache policy of the loads; OFFS places each load's 1 KiB LDS block
+// by its instruction offset (one M0 update per four loads).  The steps run as
+// (tiles mod 6) single steps, then groups of six with constant ring slots (3 A slots,
+// 2 B slots), so a grouped step's LDS addresses are constant offsets and no scalar
+// bookkeeping sits between two steps' MFMAs.
 // ------------------------------------------------------------------------------------
 template <int NOPS, int SLOTS, int J>
 struct deal {   // ops [lo, hi) follow slot J when NOPS ops are dealt over SLOTS slots
