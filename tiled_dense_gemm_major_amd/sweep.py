@@ -176,6 +176,8 @@ def main(argv=None):
                     help="interleaved timing rounds of --repeat launches per configuration")
     ap.add_argument("--torch-ref", action="store_true",
                     help="also time torch.matmul (the vendor library) as context")
+    ap.add_argument("--table-only", action="store_true",
+                    help="time only the table's choices (without and with a workspace)")
     ap.add_argument("--kernels", default="",
                     help="comma-separated kernel ids to time (default: every compiled one)")
     args = ap.parse_args(argv)
@@ -232,11 +234,13 @@ def main(argv=None):
             else:
                 variants = [cfg]
             for c in variants:
-                nbytes = tgemm.workspace_size(w.M, w.N, c)
-                ws = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device="cuda")
-                def go(i, c=c, ws=ws, nbytes=nbytes):
+                if args.table_only and c.as_dict() not in (table, table_ws):
+                    continue
+                ws_bytes = tgemm.workspace_size(w.M, w.N, c)
+                ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device="cuda")
+                def go(i, c=c, ws=ws, ws_bytes=ws_bytes):
                     tgemm.gemm_ex_ws(w.dtype, w.M, w.N, w.K, As[i % copies],
-                                     Bs[i % copies], C, ws, nbytes, w.b_layout, c, stream)
+                                     Bs[i % copies], C, ws, ws_bytes, w.b_layout, c, stream)
                 runners.append((c, go))
         if args.torch_ref:
             # the [K, N] operand either way
