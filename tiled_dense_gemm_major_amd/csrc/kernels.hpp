@@ -1472,7 +1472,8 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     // stages its 128 x 128 block in LDS (the ring is free once every wave's loads have
     // landed and its reads are done; rows padded to 272 bytes so the 8-byte writes of 16
     // rows fall in distinct banks) and stores it back as 256-byte row segments, 16 bytes
-    // per lane.
+    // per lane, with the non-temporal hint (1-2 % faster than plain stores; storing
+    // straight from the accumulators instead was 3 % slower).
     constexpr int RSE = 128 + 8;                   // staged row stride in elements
     static_assert(4 * 128 * RSE <= (SA + SB) * SLOT, "C staging fits the LDS ring");
     wait_vm_then_sync<0>();
@@ -1500,8 +1501,8 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
         const int r = 4 * q + sr;
         const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * RSE + sc);
         const int m = m0 + wm * 128 + r;
-        if (m < M && n < N)
-            *reinterpret_cast<u32x4*>(C + (size_t)m * ldc + n) = v;
+        if (m < M && n < N)     // non-temporal: C is written once and not read back here
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + (size_t)m * ldc + n));
     }
 }
 
