@@ -181,6 +181,64 @@ __device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t voff, uint32_t soff) 
 // Steps past the last tile run with out-of-range loads (zeros), so the loop body has
 // no branches.
 // ------------------------------------------------------------------------------------
+// Epilogue through LDS for the 32x32x16 accumulator layout (a lane holds row lane % 32
+// of each 32-row block and columns 8g + 4 (lane / 32) .. +3, g = 0..3, of each 32-column
+// block: 16-byte pieces of 32 rows per store if written directly).  Each of the NW waves
+// stages its WTM x WTN block in LDS, WTM/NP rows per pass (rows padded by 16 bytes, so
+// the 8-byte writes of 16 rows fall in distinct banks), and stores it back as whole row
+// segments of WTN columns, 16 bytes per lane.  The caller has freed the first CAP
+// elements of LDS for all waves (a barrier after the last operand reads); a wave's LDS
+// accesses complete in order, so a pass's writes follow the previous pass's reads.
+template <int TM, int WTM, int SRS, int NW, int CAP>
+constexpr int staged_passes() {
+    for (int np = 1; np <= TM; ++np)
+        if (TM % np == 0 && (WTM / np) * SRS * NW <= CAP)
+            return np;
+    return -1;
+}
+template <int DT, int WTM, int WTN, int NW, int CAP>
+__device__ __forceinline__ void store_c_staged(const f32x16 (&acc)[WTM / 32][WTN / 32],
+                                               u16* lds, int wave, int lane, u16* C, int M,
+                                               int N, int ldc, int mrow0, int ncol0) {
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int SRS = WTN + 8;                   // staged row stride in elements
+    constexpr int NP = staged_passes<TM, WTM, SRS, NW, CAP>();
+    static_assert(NP > 0, "C staging fits the LDS ring");
+    constexpr int HR = WTM / NP;                   // rows staged per pass
+    constexpr int LPR = WTN / 8;                   // lanes per staged row
+    constexpr int RPR = 64 / LPR;                  // rows per 64-lane read
+    static_assert(64 % LPR == 0 && HR % RPR == 0, "staging split");
+    u16* stg = lds + wave * HR * SRS;
+    const int half = lane >> 5;
+    const int sr = lane / LPR, sc = (lane % LPR) * 8;
+    const int n = ncol0 + sc;
+#pragma unroll
+    for (int ps = 0; ps < NP; ++ps) {
+#pragma unroll
+        for (int i = ps * (TM / NP); i < (ps + 1) * (TM / NP); ++i) {
+            const int r = (i - ps * (TM / NP)) * 32 + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    u32x2 v;
+                    v[0] = pack2<DT>(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+                    v[1] = pack2<DT>(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                    *reinterpret_cast<u32x2*>(stg + r * SRS + j * 32 + 8 * g + 4 * half) = v;
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < HR / RPR; ++q) {
+            const int r = q * RPR + sr;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * SRS + sc);
+            const int m = mrow0 + ps * HR + r;
+            if (m < M && n < N)
+                *reinterpret_cast<u32x4*>(C + (size_t)m * ldc + n) = v;
+        }
+    }
+}
+
 template <int DT, int ALAYOUT, int LAYOUT, int BM, int BN, int BK, int WM, int WN>
 __global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64),
                                amdgpu_waves_per_eu(1, 1)))
@@ -419,23 +477,10 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
         }
     }
 
-    // ---- epilogue: cast once, store 4 consecutive columns (8 bytes) per group ----------
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int m = m0 + wm * WTM + i * 32 + (lane & 31);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * half;
-                u32x2 v;
-                v[0] = pack2<DT>(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-                v[1] = pack2<DT>(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-                if (m < M && n < N)
-                    *reinterpret_cast<u32x2*>(C + (size_t)m * ldc + n) = v;
-            }
-        }
-    }
+    // ---- epilogue: cast once, stage through LDS, store whole row segments ----------------
+    __syncthreads();
+    store_c_staged<DT, WTM, WTN, WM * WN, 2 * STAGE>(acc, lds, wave, lane, C, M, N, ldc,
+                                                     m0 + wm * WTM, n0 + wn * WTN);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1077,22 +1122,11 @@ gemm_pingpong(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restr
         wait_vm<0>();                              // the trailing zero loads
     }
 
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int m = m0 + grp * WTM + i * 32 + (lane & 31);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wc * WTN + j * 32 + 8 * g + 4 * half;
-                u32x2 v;
-                v[0] = pack2<DT>(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-                v[1] = pack2<DT>(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-                if (m < M && n < N)
-                    *reinterpret_cast<u32x2*>(C + (size_t)m * ldc + n) = v;
-            }
-        }
-    }
+    // Epilogue: one cast per value, staged through LDS into whole row segments (see
+    // store_c_staged); the ring is free once every wave has read its last operands.
+    __syncthreads();
+    store_c_staged<DT, WTM, WTN, 8, STAGES * STAGE>(acc, lds, wave, lane, C, M, N, ldc,
+                                                    m0 + grp * WTM, n0 + wc * WTN);
 }
 
 // Direct-to-LDS load into the 1 KiB block OFF bytes past M0.  The instruction offset is
