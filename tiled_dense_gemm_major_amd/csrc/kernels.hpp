@@ -1592,13 +1592,18 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
     auto wr_off = [&](int i) { return (8 * i + lrow) * CK + ((lpc ^ swz<KC>(8 * i + lrow)) * 8); };
 
     const int nch = (K + CK - 1) / CK;
-    const int c_lo = wave * nch / NW, c_hi = (wave + 1) * nch / NW;
+    const int c_lo = wave * nch / NW, len = (wave + 1) * nch / NW - c_lo;
+    // Every workgroup reads the same rows of A.  Each one starts its walk over the chunk
+    // range at a different chunk (workgroups on one XCD are 8 apart in blockIdx.x), so the
+    // workgroups of an XCD do not request the same A lines at the same moment.
+    const int rot = len > 0 ? (int)((blockIdx.x >> 3) % (unsigned)len) : 0;
 
     u32x4 buf[D][LD];
-    auto load_chunk = [&](int c, auto slot) {
+    auto load_chunk = [&](int t, auto slot) {     // t-th chunk of this wave's walk
         constexpr int S = decltype(slot)::value;
-        const bool live = c < c_hi;
-        const int k0 = live ? c * CK : 0;
+        const bool live = t < len;
+        const int p = t + rot < len ? t + rot : t + rot - len;
+        const int k0 = live ? (c_lo + p) * CK : 0;
         const bool ok = live && k0 + lpc * 8 < K;
 #pragma unroll
         for (int i = 0; i < LD; ++i)
@@ -1612,8 +1617,8 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
     for (int h = 0; h < MT; ++h)
         acc[h] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
-    static_for<0, D>([&](auto d) { load_chunk(c_lo + decltype(d)::value, d); });
-    for (int c = c_lo; c < c_hi; c += D) {
+    static_for<0, D>([&](auto d) { load_chunk(decltype(d)::value, d); });
+    for (int c = 0; c < len; c += D) {
         static_for<0, D>([&](auto dc) {
             constexpr int d = decltype(dc)::value;
 #pragma unroll
