@@ -245,6 +245,26 @@ def test_quad_k_walk_exact(dev, orc, K):
         assert np.array_equal(run(dtype, A, B, B_NK, cfg), want), (K, _cfg_id(cfg))
 
 
+# K walks of the skinny kernel, bit for bit on exact inputs: each of its 8 waves walks a
+# contiguous range of 64-wide chunks, starting at a chunk set by the workgroup's index
+# on its XCD, so with 33 column blocks and 2-6 chunks per wave the ragged last chunk is
+# reached first, last and in between.
+@pytest.mark.parametrize("K", [1000, 1544, 2568, 3080])
+@pytest.mark.parametrize("M", [16, 64, 100])
+def test_skinny_k_walk_exact(dev, orc, M, K):
+    from tiled_dense_gemm_major_amd import tgemm
+    dtype = BF16
+    rng = np.random.default_rng(700 + K + M)
+    N = 1056
+    A = _int_bits(dtype, rng.integers(-2, 3, (M, K)))
+    B = _int_bits(dtype, rng.integers(-2, 3, (N, K)))
+    want = orc.gemm(dtype, A, B, B_NK)
+    for cfg in [c for c in _configs(dtype, B_NK) if c.kernel == tgemm.KERNEL_SKINNY]:
+        say(f"skinny k walk M={M} K={K} (chunks {-(-K // 64)}, tail {K % 64}) "
+            f"{_cfg_id(cfg)}")
+        assert np.array_equal(run(dtype, A, B, B_NK, cfg), want), (M, K, _cfg_id(cfg))
+
+
 def test_quad_repeat_launches_bitwise_identical(dev, orc):
     """Many workgroups per compute unit through the five-slot ring: a stage reused too
     early shows up as launch-to-launch differences."""
