@@ -238,14 +238,15 @@ _MIN_NORMAL_EXP = {F16: -14, BF16: -126}
 
 def ulp_out(dtype: int, x) -> np.ndarray:
     """Spacing of the output format at |x|: 2^(floor(log2|x|) - p + 1) in the normal range,
-    the subnormal spacing below it (and at zero)."""
+    the subnormal spacing 2^(emin - p + 1) below it and at zero (2^-24 for fp16, 2^-133
+    for bf16).  A non-finite x has no spacing: NaN, so no comparison against it passes."""
     x = np.abs(np.asarray(x, dtype=np.float64))
     p = _PRECISION[dtype]
     emin = _MIN_NORMAL_EXP[dtype]
-    _, e = np.frexp(x)                      # x = f * 2^e, f in [0.5, 1)
-    floor_log2 = e.astype(np.int64) - 1
+    _, e = np.frexp(x)                      # x = f * 2^e, f in [0.5, 1); frexp(0) gives e = 0
+    floor_log2 = np.where(x == 0.0, emin, e.astype(np.int64) - 1)
     expo = np.maximum(floor_log2, emin) - (p - 1)
-    return np.ldexp(1.0, expo)
+    return np.where(np.isfinite(x), np.ldexp(1.0, expo), np.nan)
 
 
 def tolerance(dtype: int, K: int, orc_values) -> np.ndarray:
@@ -258,7 +259,8 @@ def compare(dtype: int, K: int, got_bits, want_bits) -> dict:
     got = decode(dtype, got_bits).ravel()
     want = decode(dtype, want_bits).ravel()
     tol = tolerance(dtype, K, want)
-    err = np.abs(got - want)
+    with np.errstate(invalid="ignore"):        # inf - inf is NaN: a failure below
+        err = np.abs(got - want)
     bad = ~np.isfinite(got) | ~(err <= tol)
     idx = np.flatnonzero(bad)
     ratio = np.where(np.isfinite(err), err / tol, np.inf)
