@@ -322,36 +322,56 @@ int oracle_gemm_f64(int64_t M, int64_t N, int64_t K, const double* A, const doub
 }
 
 /*
- * The tiled loop of "Tiling a matmul" (sections "The idea in one minute" and "Code"), on
- * square n x n fp64 matrices with B stored [K,N]: the output is cut into t x t tiles; each
- * tile walks k in steps of t, and every step brings one t x t tile of A and one of B from
- * memory (2*t*t element loads, counted in *loads) whose products are summed into a
- * partial that is then added to the output element.  n must be a multiple of t.
+ * The square tiled product of "Tiling a matmul" (sections "The idea in one minute" and
+ * "Code"), on n x n fp64 matrices with B stored [K,N], written as a staged computation:
+ * for each t x t block of C, the K range is walked t at a time; each step copies a t x t
+ * block of A and one of B into small staging buffers (the "loads": 2 t^2 elements per
+ * step, counted in *loads, so n^2/t^2 blocks x n/t steps give 2 n^3 / t in all) and adds,
+ * for every element of the block, the partial dot product of that step to the element's
+ * running sum.  n must be a multiple of t.  With t = 1 the running sums receive one
+ * product at a time in increasing k: the naive order.
  */
 int oracle_tiled_f64(int64_t n, int64_t t, const double* A, const double* B, double* C,
                      int64_t* loads) {
     if (n < 0 || t <= 0 || n % t != 0)
         return ORC_EINVAL;
-    int64_t count = 0;
-    for (int64_t i = 0; i < n * n; ++i)
-        C[i] = 0.0;
-    for (int64_t ti = 0; ti < n; ti += t) {
-        for (int64_t tj = 0; tj < n; tj += t) {
-            for (int64_t tk = 0; tk < n; tk += t) {
-                count += 2 * t * t; /* the A tile and the B tile of this step */
-                for (int64_t i = ti; i < ti + t; ++i) {
-                    for (int64_t j = tj; j < tj + t; ++j) {
-                        double part = 0.0;
-                        for (int64_t k = tk; k < tk + t; ++k)
-                            part += A[i * n + k] * B[k * n + j];
-                        C[i * n + j] += part;
-                    }
-                }
+    double* sa = (double*)malloc(sizeof(double) * (size_t)(t * t));   /* A block [t][t] */
+    double* sb = (double*)malloc(sizeof(double) * (size_t)(t * t));   /* B block [t][t] */
+    double* run = (double*)malloc(sizeof(double) * (size_t)(t * t));  /* running sums   */
+    if (!sa || !sb || !run) {
+        free(sa);
+        free(sb);
+        free(run);
+        return ORC_ENOMEM;
+    }
+    int64_t staged = 0;
+    const int64_t nb = n / t;
+    for (int64_t blk = 0; blk < nb * nb; ++blk) {
+        const int64_t row0 = (blk / nb) * t, col0 = (blk % nb) * t;
+        for (int64_t e = 0; e < t * t; ++e)
+            run[e] = 0.0;
+        for (int64_t k0 = 0; k0 < n; k0 += t) {
+            for (int64_t r = 0; r < t; ++r) {
+                memcpy(sa + r * t, A + (row0 + r) * n + k0, sizeof(double) * (size_t)t);
+                memcpy(sb + r * t, B + (k0 + r) * n + col0, sizeof(double) * (size_t)t);
+            }
+            staged += 2 * t * t;
+            for (int64_t e = 0; e < t * t; ++e) {
+                const int64_t r = e / t, c = e % t;
+                double dot = 0.0;
+                for (int64_t q = 0; q < t; ++q)
+                    dot += sa[r * t + q] * sb[q * t + c];
+                run[e] += dot;
             }
         }
+        for (int64_t e = 0; e < t * t; ++e)
+            C[(row0 + e / t) * n + col0 + e % t] = run[e];
     }
+    free(sa);
+    free(sb);
+    free(run);
     if (loads)
-        *loads = count;
+        *loads = staged;
     return ORC_OK;
 }
 

@@ -1,7 +1,6 @@
 """Pins for the CPU oracle against what the pages and the mathematics fix, independent of
 the oracle's own code: library routines (numpy, torch, Python fractions), exact integer
 arithmetic, closed forms, invariants and the values printed on the pages."""
-import random
 from fractions import Fraction
 
 import numpy as np
@@ -136,20 +135,23 @@ def test_encode_bf16_matches_round_to_odd(orc):
 # The experiment of "Tiling a matmul", section "Code": tiled vs naive on 32 x 32.
 # --------------------------------------------------------------------------------------
 def test_tiled_vs_naive_printed_loads(orc):
+    """The page's experiment: 32 x 32 operands of U[0,1) doubles, the tiled loop against
+    the naive one at tiles 1, 4 and 16.  The element loads it prints depend only on n and
+    t (2 n^3 / t); the errors it prints are a few 1e-15.  The operands here come from this
+    repository's seeded stream (the counts do not depend on the data)."""
     g = golden("tiling_a_matmul_code_output.json")["small_case"]
-    random.seed(g["seed"])
     n = g["n"]
-    a = [[random.random() for _ in range(n)] for _ in range(n)]
-    b = [[random.random() for _ in range(n)] for _ in range(n)]
-    A, B = np.array(a), np.array(b)
+    s = Stream(32)
+    A = s.unit(n * n).reshape(n, n)
+    B = s.unit(n * n).reshape(n, n)
     naive = orc.gemm_f64(A, B, B_KN)        # the page's product is A x B with B [K, N]
     assert np.allclose(naive, A @ B, rtol=0, atol=1e-13)
     for row in g["rows"]:
         C, loads = orc.tiled_f64(A, B, row["tile"])
         assert loads == row["loads"]
         err = np.max(np.abs(C - naive))
-        # the page prints errors of a few 1e-15 (a different summation order in the last
-        # bits); only the magnitude is fixed, the digits depend on Python's float sum
+        # only the magnitude of the printed errors is fixed: their digits depend on the
+        # data and on the summation of the page's reference product
         assert err <= 1e-14
     # With t = 1 every partial holds one product, so the tiled order is the naive order.
     C1, _ = orc.tiled_f64(A, B, 1)

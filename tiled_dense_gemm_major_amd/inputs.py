@@ -80,6 +80,10 @@ class Stream:
         self.pos += count
         return out
 
+    def unit(self, count: int) -> np.ndarray:
+        """U[0,1) doubles (53 random bits each)."""
+        return _unit(self._take(count))
+
     def uniform_pm1(self, count: int) -> np.ndarray:
         return 2.0 * _unit(self._take(count)) - 1.0
 

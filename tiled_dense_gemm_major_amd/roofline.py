@@ -33,11 +33,10 @@ def compulsory_bytes(M: int, N: int, K: int, elem: int = 2) -> int:
 
 
 def square_tile_traffic_bytes(n: int, t: int, elem: int = 2) -> int:
-    """No-cache traffic of an n x n product with t x t tiles: each input is read n // t
-    times, the output written once."""
-    reads = 2 * n * n * (n // t)
-    writes = n * n
-    return (reads + writes) * elem
+    """No-cache traffic of an n x n product with t x t tiles, in bytes: elem * (2 n^3 / t
+    + n^2) -- the n^2 / t^2 tiles each stream a t-row strip of A and a t-column strip of
+    B (2 t n elements), and C is written once."""
+    return elem * (2 * n ** 3 // t + n * n)
 
 
 def tile_traffic_bytes(M: int, N: int, K: int, bm: int, bn: int, elem: int = 2) -> int:
