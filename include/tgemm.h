@@ -184,19 +184,25 @@ int gemm_strided(int dtype, int64_t m, int64_t n, int64_t k, const void* A, int6
                  int a_layout, const void* B, int64_t ldb, int b_layout, void* C,
                  int64_t ldc, const tgemm_config* cfg, void* stream);
 
-/* The configuration the table picks for this problem (written to *out).  Host-only: it
- * touches no device.  Same argument checks as gemm_ex on the sizes, dtype and layout;
- * `aligned` says whether the operands will meet the fast-kernel alignment rules. */
+/* The configuration gemm_f16 / gemm_bf16 / gemm_ex(cfg = NULL) pick for this packed
+ * problem (A [M,K], B per b_layout, C [M,N], no padding) with operands at 16-byte-aligned
+ * addresses, written to *out; whether the fast kernels can take it follows from the sizes
+ * (K and N multiples of 8, A and B each at most 2^31 bytes).  Host-only: it touches no
+ * device.  Returns TGEMM_OK, TGEMM_ERR_NULL_POINTER (out NULL) or the size, dtype and
+ * layout errors of gemm_ex. */
 int tgemm_query_config(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
-                       int aligned, tgemm_config* out);
+                       tgemm_config* out);
 
 /* The configurations compiled into the library for (dtype, b_layout).  Writes up to
  * `capacity` entries to `out` (which may be NULL when capacity is 0) and returns the
  * total count, or a negative status.  Host-only. */
 int tgemm_list_configs(int dtype, int b_layout, tgemm_config* out, int capacity);
 
-/* tgemm_query_config and tgemm_list_configs for either storage of A (tgemm_a_layout);
- * the functions above answer for TGEMM_A_MK. */
+/* The choice for either storage of A (tgemm_a_layout) and a caller-stated alignment:
+ * `aligned` != 0 says the operands meet every fast-kernel rule (16-byte-aligned
+ * addresses, sizes and leading dimensions multiples of 8, spans within 2^31 bytes),
+ * 0 that they do not (the choice is then the any-alignment kernel).  The list for either
+ * storage of A; tgemm_list_configs answers for TGEMM_A_MK. */
 int tgemm_query_config_ex(int dtype, int64_t m, int64_t n, int64_t k, int a_layout,
                           int b_layout, int aligned, tgemm_config* out);
 int tgemm_list_configs_ex(int dtype, int a_layout, int b_layout, tgemm_config* out,
@@ -234,6 +240,24 @@ int tgemm_workspace_size(int64_t m, int64_t n, const tgemm_config* cfg, int64_t*
  */
 int attn_fwd_f16(int64_t batch, int64_t seq, int64_t heads, int64_t dim, const void* Q,
                  const void* K, const void* V, void* O, int causal, void* stream);
+
+/*
+ * Diagnostics for measurements: one lane on `stream` reads the device's shader-clock
+ * counter (it advances once per engine clock cycle, so its rate follows the clock the
+ * chip runs at) and its constant-rate wall clock, and writes them as two uint64 values
+ * to out[0] and out[1].
+ *   out    : device pointer to 16 bytes, 8-byte aligned; written when the stream reaches
+ *            the stamp
+ *   stream : hipStream_t (NULL = null stream)
+ * Two stamps around a stretch of work on one stream give its average engine clock:
+ * (out1[0] - out0[0]) / (out1[1] - out0[1]) * (tgemm_wall_clock_hz).  Returns TGEMM_OK,
+ * TGEMM_ERR_NULL_POINTER, TGEMM_ERR_ALIGNMENT or TGEMM_ERR_LAUNCH.  Nothing is allocated.
+ */
+int tgemm_clock_stamp(void* out, void* stream);
+
+/* The rate of the wall clock that tgemm_clock_stamp reads, in Hz, for the current
+ * device (written to *hz).  Returns TGEMM_OK, TGEMM_ERR_NULL_POINTER or TGEMM_ERR_DEVICE. */
+int tgemm_wall_clock_hz(int64_t* hz);
 
 /* A static, human-readable name for a status code. */
 const char* tgemm_status_string(int status);

@@ -260,3 +260,86 @@ def test_frozen_table_entries_are_compiled_and_chosen(lib):
         for dt in (tgemm.BF16, tgemm.F16):
             got = tgemm.query_config(dt, M, N, K, layout).as_dict()
             assert got == want, (layout, M, N, K, got, want)
+
+
+# The boundary's entry points as the header declares them: name -> parameter types.
+BOUNDARY = {
+    "gemm_f16": ["int64_t", "int64_t", "int64_t", "const void*", "const void*", "void*",
+                 "int", "void*"],
+    "gemm_bf16": ["int64_t", "int64_t", "int64_t", "const void*", "const void*", "void*",
+                  "int", "void*"],
+    "gemm_ex": ["int", "int64_t", "int64_t", "int64_t", "const void*", "const void*",
+                "void*", "int", "const tgemm_config*", "void*"],
+    "tgemm_query_config": ["int", "int64_t", "int64_t", "int64_t", "int", "tgemm_config*"],
+    "tgemm_status_string": ["int"],
+}
+
+
+def _prototype(name):
+    text = open(os.path.join(ROOT, "include", "tgemm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    m = re.search(r"\b%s\s*\(([^)]*)\)\s*;" % name, text)
+    assert m, name
+    params = [p.strip() for p in m.group(1).replace("\n", " ").split(",")]
+    # drop the parameter names, keep the types ("const void* A" -> "const void*")
+    return [re.sub(r"\s*\b\w+$", "", re.sub(r"\s+", " ", p)).replace(" *", "*")
+            for p in params]
+
+
+@pytest.mark.parametrize("name", sorted(BOUNDARY))
+def test_boundary_prototypes(name):
+    assert _prototype(name) == BOUNDARY[name]
+
+
+def test_boundary_calls_with_exact_arity(lib):
+    """Each entry point called through a fresh ctypes handle with exactly the header's
+    argument list (host-only calls: empty products, queries, status strings)."""
+    raw = ctypes.CDLL(tgemm.LIB_PATH)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    cfgp = ctypes.POINTER(tgemm.Config)
+    for name in ("gemm_f16", "gemm_bf16"):
+        f = getattr(raw, name)
+        f.argtypes, f.restype = [i64, i64, i64, vp, vp, vp, i32, vp], i32
+        assert f(0, 8, 8, None, None, None, 0, None) == 0
+        assert f(8, 8, 8, None, None, None, 0, None) == -2
+    raw.gemm_ex.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, cfgp, vp]
+    raw.gemm_ex.restype = i32
+    assert raw.gemm_ex(1, 8, 0, 8, None, None, None, 1, None, None) == 0
+    q = raw.tgemm_query_config
+    q.argtypes, q.restype = [i32, i64, i64, i64, i32, cfgp], i32
+    out = tgemm.Config()
+    assert q(1, 8192, 8192, 8192, 0, ctypes.byref(out)) == 0
+    assert out.kernel == tgemm.KERNEL_QUAD
+    # the packed choice follows from the sizes: K not a multiple of 8 -> any-alignment
+    assert q(0, 100, 100, 100, 0, ctypes.byref(out)) == 0
+    assert out.kernel == tgemm.KERNEL_GENERIC
+    # M need not be a multiple of 8; N must (C's rows, and B's rows when B is [K,N])
+    assert q(0, 100, 104, 104, 0, ctypes.byref(out)) == 0
+    assert out.kernel != tgemm.KERNEL_GENERIC
+    for layout in (0, 1):
+        assert q(0, 104, 100, 104, layout, ctypes.byref(out)) == 0
+        assert out.kernel == tgemm.KERNEL_GENERIC
+    assert q(1, 8, 8, 8, 0, None) == -2
+    assert q(1, -1, 8, 8, 0, ctypes.byref(out)) == -1
+    s = raw.tgemm_status_string
+    s.argtypes, s.restype = [i32], ctypes.c_char_p
+    assert s(0) == b"TGEMM_OK"
+
+
+def test_packed_query_agrees_with_the_explicit_one(lib):
+    for shape in [(512, 512, 512), (4096, 4096, 4096), (8192, 8192, 8192), (64, 8192, 8192),
+                  (4000, 3000, 1000)]:
+        for layout in (tgemm.B_NK, tgemm.B_KN):
+            for dt in (tgemm.F16, tgemm.BF16):
+                assert (tgemm.query_config_packed(dt, *shape, layout).as_dict()
+                        == tgemm.query_config(dt, *shape, layout, True).as_dict())
+
+
+def test_package_exports_every_binding_name():
+    import tiled_dense_gemm_major_amd as pkg
+    for name in tgemm.__all__:
+        assert getattr(pkg, name) is getattr(tgemm, name), name
+    # every C entry point has a wrapper or a constant in the binding's public names
+    assert "gemm_ex_ws" in tgemm.__all__ and "attn_fwd_f16" in tgemm.__all__
+    with pytest.raises(AttributeError):
+        getattr(pkg, "no_such_name")

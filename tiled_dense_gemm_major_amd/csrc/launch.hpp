@@ -1,0 +1,142 @@
+// libtgemm: the launchers of every kernel family and the macros that name one compiled
+// configuration of the registry.  Included by the variants_*.hip translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+#include "registry.hpp"
+
+namespace tgemm_reg {
+
+using tgemm::u16;
+
+inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+#define KARGS                                                                              \
+    static_cast<const u16*>(A), static_cast<const u16*>(B), static_cast<u16*>(C), M, N, K, \
+        lda, ldb, ldc
+
+template <int DT, int AL, int LAYOUT, int BM, int BN, int BK, int WM, int WN>
+hipError_t launch_tiled(const void* A, const void* B, void* C, int M, int N, int K, int lda,
+                        int ldb, int ldc, int group_m, hipStream_t s) {
+    const int gm = cdiv(M, BM), gn = cdiv(N, BN);
+    hipLaunchKernelGGL((tgemm::gemm_tiled<DT, AL, LAYOUT, BM, BN, BK, WM, WN>),
+                       dim3((unsigned)(gm * gn)), dim3(WM * WN * 64), 0, s, KARGS, gm, gn,
+                       group_m);
+    return hipGetLastError();
+}
+
+template <int DT, int BM, int BN, int BK, int WM, int WN, int STAGES>
+hipError_t launch_dma(const void* A, const void* B, void* C, int M, int N, int K, int lda,
+                      int ldb, int ldc, int group_m, hipStream_t s) {
+    const int gm = cdiv(M, BM), gn = cdiv(N, BN);
+    hipLaunchKernelGGL((tgemm::gemm_dma<DT, BM, BN, BK, WM, WN, STAGES, false>),
+                       dim3((unsigned)(gm * gn)), dim3(WM * WN * 64), 0, s, KARGS, gm, gn,
+                       group_m, static_cast<float*>(nullptr), 0);
+    return hipGetLastError();
+}
+
+// Split-K: splits workgroups per C tile, each over a whole number of K steps, write fp32
+// partial tiles to the workspace ([splits][M][N]); a second kernel sums them in split
+// order and writes C.
+template <int DT, int BM, int BN, int BK, int WM, int WN, int STAGES>
+hipError_t launch_splitk(const void* A, const void* B, void* C, int M, int N, int K, int lda,
+                         int ldb, int ldc, int group_m, int splits, void* ws, hipStream_t s) {
+    const int gm = cdiv(M, BM), gn = cdiv(N, BN);
+    const int kc = cdiv(cdiv(K, splits), BK) * BK;
+    float* W = static_cast<float*>(ws);
+    hipLaunchKernelGGL((tgemm::gemm_dma<DT, BM, BN, BK, WM, WN, STAGES, true>),
+                       dim3((unsigned)(gm * gn), (unsigned)splits), dim3(WM * WN * 64), 0, s,
+                       KARGS, gm, gn, group_m, W, kc);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((tgemm::splitk_reduce<DT>), dim3((unsigned)cdiv(M * (N / 8), 256)),
+                       dim3(256), 0, s, static_cast<const float*>(W), static_cast<u16*>(C), M,
+                       N, ldc, splits);
+    return hipGetLastError();
+}
+
+template <int DT, int AL, int LAYOUT, int BM, int BN, int BK, int S>
+hipError_t launch_pingpong(const void* A, const void* B, void* C, int M, int N, int K, int lda,
+                           int ldb, int ldc, int group_m, hipStream_t s) {
+    const int gm = cdiv(M, BM), gn = cdiv(N, BN);
+    hipLaunchKernelGGL((tgemm::gemm_pingpong<DT, AL, LAYOUT, BM, BN, BK, S>),
+                       dim3((unsigned)(gm * gn)), dim3(512), 0, s, KARGS, gm, gn, group_m);
+    return hipGetLastError();
+}
+
+template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL>
+hipError_t launch_quad(const void* A, const void* B, void* C, int M, int N, int K, int lda,
+                       int ldb, int ldc, int group_m, hipStream_t s) {
+    const int gm = cdiv(M, 256), gn = cdiv(N, 256);
+    // the instruction-offset form of the loads needs rows of at least 64 elements
+    if (lda >= 64 && ldb >= 64)
+        hipLaunchKernelGGL((tgemm::gemm_quad<DT, MF, PRE, SPA, SPB, STAG, POL, true>),
+                           dim3((unsigned)(gm * gn)), dim3(256), 0, s, KARGS, gm, gn, group_m);
+    else
+        hipLaunchKernelGGL((tgemm::gemm_quad<DT, MF, PRE, SPA, SPB, STAG, POL, false>),
+                           dim3((unsigned)(gm * gn)), dim3(256), 0, s, KARGS, gm, gn, group_m);
+    return hipGetLastError();
+}
+
+template <int DT, int MT, int D>
+hipError_t launch_skinny(const void* A, const void* B, void* C, int M, int N, int K, int lda,
+                         int ldb, int ldc, int, hipStream_t s) {
+    hipLaunchKernelGGL((tgemm::gemm_skinny<DT, MT, D>),
+                       dim3((unsigned)cdiv(N, 32), (unsigned)cdiv(M, MT * 32)), dim3(512), 0, s,
+                       KARGS);
+    return hipGetLastError();
+}
+
+template <int DT, int AL, int LAYOUT>
+hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, int K, int lda,
+                          int ldb, int ldc, int group_m, hipStream_t s) {
+    const int gm = cdiv(M, 64), gn = cdiv(N, 64);
+    hipLaunchKernelGGL((tgemm::gemm_generic<DT, AL, LAYOUT>), dim3((unsigned)(gm * gn)),
+                       dim3(256), 0, s, KARGS, gm, gn, group_m);
+    return hipGetLastError();
+}
+
+#define TILED(DT, AL, L, BM, BN, BK, WM, WN, G)                                           \
+    Variant {                                                                              \
+        DT, AL, L, tgemm_config{TGEMM_KERNEL_TILED, BM, BN, BK, WM, WN, 2, G, 1, 32},          \
+            &launch_tiled<DT, AL, L, BM, BN, BK, WM, WN>                                   \
+    }
+#define GENERIC(DT, AL, L)                                                                 \
+    Variant {                                                                              \
+        DT, AL, L, tgemm_config{TGEMM_KERNEL_GENERIC, 64, 64, 16, 2, 2, 1, 8, 1, 32},      \
+            &launch_generic<DT, AL, L>                                                     \
+    }
+#define DMA(DT, BM, BN, BK, WM, WN, ST, G)                                                 \
+    Variant {                                                                              \
+        DT, 0, 0, tgemm_config{TGEMM_KERNEL_DMA, BM, BN, BK, WM, WN, ST, G, 1, 32},            \
+            &launch_dma<DT, BM, BN, BK, WM, WN, ST>                                        \
+    }
+#define PINGPONG(DT, AL, L, BM, BN, BK, S, G)                                              \
+    Variant {                                                                              \
+        DT, AL, L, tgemm_config{TGEMM_KERNEL_PINGPONG, BM, BN, BK, 2, 4, S, G, 1, 32},         \
+            &launch_pingpong<DT, AL, L, BM, BN, BK, S>                                     \
+    }
+// Quad kernel schedules (pre-barrier MFMAs, A-load and read spreads), from the sweep;
+// K walks staggered per XCD, loads with the sc0 cache policy.
+#define QUAD(DT, MF, G)                                                                    \
+    Variant {                                                                              \
+        DT, 0, 0, tgemm_config{TGEMM_KERNEL_QUAD, 256, 256, 64, 2, 2, 5, G, 1, MF},        \
+            &launch_quad<DT, MF, (MF == 16 ? 2 : 1), (MF == 16 ? 56 : 40),                 \
+                         (MF == 16 ? 40 : 12), 1, 2>                                       \
+    }
+// Split-K over workgroups (registry entries carry split_k = 2; a call gives its own count).
+#define SPLITK(DT, BM, BN, BK, WM, WN, ST, G)                                              \
+    Variant {                                                                              \
+        DT, 0, 0, tgemm_config{TGEMM_KERNEL_SPLITK, BM, BN, BK, WM, WN, ST, G, 2, 32},         \
+            nullptr, &launch_splitk<DT, BM, BN, BK, WM, WN, ST>                            \
+    }
+#define SKINNY(DT, MT, D)                                                                  \
+    Variant {                                                                              \
+        DT, 0, 0, tgemm_config{TGEMM_KERNEL_SKINNY, MT * 32, 32, 64, 1, 8, D, 1, 8, 32},       \
+            &launch_skinny<DT, MT, D>                                                      \
+    }
+}  // namespace tgemm_reg

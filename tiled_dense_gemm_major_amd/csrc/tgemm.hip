@@ -8,190 +8,53 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "kernels.hpp"
+#include <algorithm>
+#include <vector>
+
+#include "registry.hpp"
 
 namespace {
 
-using tgemm::u16;
-
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
 
-// Leading dimensions are in elements: A[m*lda + k] ([M,K]) or A[k*lda + m] ([K,M]);
-// B[n*ldb + k] ([N,K]) or B[k*ldb + n] ([K,N]); C[m*ldc + n].
-typedef hipError_t (*launch_fn)(const void* A, const void* B, void* C, int M, int N, int K,
-                                int lda, int ldb, int ldc, int group_m, hipStream_t s);
-// Split-K launches also take the number of K splits and the caller's workspace.
-typedef hipError_t (*splitk_fn)(const void* A, const void* B, void* C, int M, int N, int K,
-                                int lda, int ldb, int ldc, int group_m, int splits, void* ws,
-                                hipStream_t s);
+using tgemm_reg::kMaxSplits;
+using tgemm_reg::Variant;
 
-struct Variant {
-    int dtype;
-    int a_layout;
-    int layout;
-    tgemm_config cfg;
-    launch_fn launch;              // every kernel but SPLITK
-    splitk_fn split_launch;        // SPLITK only
-};
-
-// Split-K bounds: at least 2 and at most kMaxSplits workgroups per C tile.
-constexpr int kMaxSplits = 64;
-
-int cdiv(int a, int b) { return (a + b - 1) / b; }
-
-#define KARGS                                                                              \
-    static_cast<const u16*>(A), static_cast<const u16*>(B), static_cast<u16*>(C), M, N, K, \
-        lda, ldb, ldc
-
-template <int DT, int AL, int LAYOUT, int BM, int BN, int BK, int WM, int WN>
-hipError_t launch_tiled(const void* A, const void* B, void* C, int M, int N, int K, int lda,
-                        int ldb, int ldc, int group_m, hipStream_t s) {
-    const int gm = cdiv(M, BM), gn = cdiv(N, BN);
-    hipLaunchKernelGGL((tgemm::gemm_tiled<DT, AL, LAYOUT, BM, BN, BK, WM, WN>),
-                       dim3((unsigned)(gm * gn)), dim3(WM * WN * 64), 0, s, KARGS, gm, gn,
-                       group_m);
-    return hipGetLastError();
+// Position of a kernel family in the listing order of one (A storage, B storage, dtype)
+// group: generic, tiled, direct-to-LDS ring, ping-pong, quad, skinny, split-K.
+int family_rank(int kernel) {
+    switch (kernel) {
+    case TGEMM_KERNEL_GENERIC: return 0;
+    case TGEMM_KERNEL_TILED: return 1;
+    case TGEMM_KERNEL_DMA: return 2;
+    case TGEMM_KERNEL_PINGPONG: return 3;
+    case TGEMM_KERNEL_QUAD: return 4;
+    case TGEMM_KERNEL_SKINNY: return 5;
+    default: return 6;
+    }
 }
 
-template <int DT, int BM, int BN, int BK, int WM, int WN, int STAGES>
-hipError_t launch_dma(const void* A, const void* B, void* C, int M, int N, int K, int lda,
-                      int ldb, int ldc, int group_m, hipStream_t s) {
-    const int gm = cdiv(M, BM), gn = cdiv(N, BN);
-    hipLaunchKernelGGL((tgemm::gemm_dma<DT, BM, BN, BK, WM, WN, STAGES, false>),
-                       dim3((unsigned)(gm * gn)), dim3(WM * WN * 64), 0, s, KARGS, gm, gn,
-                       group_m, static_cast<float*>(nullptr), 0);
-    return hipGetLastError();
+// Every compiled configuration, from the translation units' lists, in one fixed order:
+// grouped by A storage, B storage and dtype, then by family; a family's entries keep the
+// order its unit lists them in.
+const std::vector<const Variant*>& registry() {
+    static const std::vector<const Variant*> all = [] {
+        std::vector<const Variant*> v;
+        for (const tgemm_reg::VariantList& l :
+             {tgemm_reg::variants_tiled(), tgemm_reg::variants_small(),
+              tgemm_reg::variants_pingpong_nk(), tgemm_reg::variants_pingpong_other(),
+              tgemm_reg::variants_quad()})
+            for (int i = 0; i < l.n; ++i)
+                v.push_back(&l.v[i]);
+        const auto key = [](const Variant* x) {
+            return ((x->a_layout * 2 + x->layout) * 2 + x->dtype) * 8 + family_rank(x->cfg.kernel);
+        };
+        std::stable_sort(v.begin(), v.end(),
+                         [&](const Variant* a, const Variant* b) { return key(a) < key(b); });
+        return v;
+    }();
+    return all;
 }
-
-// Split-K: splits workgroups per C tile, each over a whole number of K steps, write fp32
-// partial tiles to the workspace ([splits][M][N]); a second kernel sums them in split
-// order and writes C.
-template <int DT, int BM, int BN, int BK, int WM, int WN, int STAGES>
-hipError_t launch_splitk(const void* A, const void* B, void* C, int M, int N, int K, int lda,
-                         int ldb, int ldc, int group_m, int splits, void* ws, hipStream_t s) {
-    const int gm = cdiv(M, BM), gn = cdiv(N, BN);
-    const int kc = cdiv(cdiv(K, splits), BK) * BK;
-    float* W = static_cast<float*>(ws);
-    hipLaunchKernelGGL((tgemm::gemm_dma<DT, BM, BN, BK, WM, WN, STAGES, true>),
-                       dim3((unsigned)(gm * gn), (unsigned)splits), dim3(WM * WN * 64), 0, s,
-                       KARGS, gm, gn, group_m, W, kc);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL((tgemm::splitk_reduce<DT>), dim3((unsigned)cdiv(M * (N / 8), 256)),
-                       dim3(256), 0, s, static_cast<const float*>(W), static_cast<u16*>(C), M,
-                       N, ldc, splits);
-    return hipGetLastError();
-}
-
-template <int DT, int AL, int LAYOUT, int BM, int BN, int BK, int S>
-hipError_t launch_pingpong(const void* A, const void* B, void* C, int M, int N, int K, int lda,
-                           int ldb, int ldc, int group_m, hipStream_t s) {
-    const int gm = cdiv(M, BM), gn = cdiv(N, BN);
-    hipLaunchKernelGGL((tgemm::gemm_pingpong<DT, AL, LAYOUT, BM, BN, BK, S>),
-                       dim3((unsigned)(gm * gn)), dim3(512), 0, s, KARGS, gm, gn, group_m);
-    return hipGetLastError();
-}
-
-template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL>
-hipError_t launch_quad(const void* A, const void* B, void* C, int M, int N, int K, int lda,
-                       int ldb, int ldc, int group_m, hipStream_t s) {
-    const int gm = cdiv(M, 256), gn = cdiv(N, 256);
-    // the instruction-offset form of the loads needs rows of at least 64 elements
-    if (lda >= 64 && ldb >= 64)
-        hipLaunchKernelGGL((tgemm::gemm_quad<DT, MF, PRE, SPA, SPB, STAG, POL, true>),
-                           dim3((unsigned)(gm * gn)), dim3(256), 0, s, KARGS, gm, gn, group_m);
-    else
-        hipLaunchKernelGGL((tgemm::gemm_quad<DT, MF, PRE, SPA, SPB, STAG, POL, false>),
-                           dim3((unsigned)(gm * gn)), dim3(256), 0, s, KARGS, gm, gn, group_m);
-    return hipGetLastError();
-}
-
-template <int DT, int MT, int D>
-hipError_t launch_skinny(const void* A, const void* B, void* C, int M, int N, int K, int lda,
-                         int ldb, int ldc, int, hipStream_t s) {
-    hipLaunchKernelGGL((tgemm::gemm_skinny<DT, MT, D>),
-                       dim3((unsigned)cdiv(N, 32), (unsigned)cdiv(M, MT * 32)), dim3(512), 0, s,
-                       KARGS);
-    return hipGetLastError();
-}
-
-template <int DT, int AL, int LAYOUT>
-hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, int K, int lda,
-                          int ldb, int ldc, int group_m, hipStream_t s) {
-    const int gm = cdiv(M, 64), gn = cdiv(N, 64);
-    hipLaunchKernelGGL((tgemm::gemm_generic<DT, AL, LAYOUT>), dim3((unsigned)(gm * gn)),
-                       dim3(256), 0, s, KARGS, gm, gn, group_m);
-    return hipGetLastError();
-}
-
-#define TILED(DT, AL, L, BM, BN, BK, WM, WN, G)                                           \
-    Variant {                                                                              \
-        DT, AL, L, tgemm_config{TGEMM_KERNEL_TILED, BM, BN, BK, WM, WN, 2, G, 1, 32},          \
-            &launch_tiled<DT, AL, L, BM, BN, BK, WM, WN>                                   \
-    }
-#define GENERIC(DT, AL, L)                                                                 \
-    Variant {                                                                              \
-        DT, AL, L, tgemm_config{TGEMM_KERNEL_GENERIC, 64, 64, 16, 2, 2, 1, 8, 1, 32},      \
-            &launch_generic<DT, AL, L>                                                     \
-    }
-#define DMA(DT, BM, BN, BK, WM, WN, ST, G)                                                 \
-    Variant {                                                                              \
-        DT, 0, 0, tgemm_config{TGEMM_KERNEL_DMA, BM, BN, BK, WM, WN, ST, G, 1, 32},            \
-            &launch_dma<DT, BM, BN, BK, WM, WN, ST>                                        \
-    }
-#define PINGPONG(DT, AL, L, BM, BN, BK, S, G)                                              \
-    Variant {                                                                              \
-        DT, AL, L, tgemm_config{TGEMM_KERNEL_PINGPONG, BM, BN, BK, 2, 4, S, G, 1, 32},         \
-            &launch_pingpong<DT, AL, L, BM, BN, BK, S>                                     \
-    }
-// Quad kernel schedules (pre-barrier MFMAs, A-load and read spreads), from the sweep;
-// K walks staggered per XCD, loads with the sc0 cache policy.
-#define QUAD(DT, MF, G)                                                                    \
-    Variant {                                                                              \
-        DT, 0, 0, tgemm_config{TGEMM_KERNEL_QUAD, 256, 256, 64, 2, 2, 5, G, 1, MF},        \
-            &launch_quad<DT, MF, (MF == 16 ? 2 : 1), (MF == 16 ? 56 : 40),                 \
-                         (MF == 16 ? 40 : 12), 1, 2>                                       \
-    }
-// Split-K over workgroups (registry entries carry split_k = 2; a call gives its own count).
-#define SPLITK(DT, BM, BN, BK, WM, WN, ST, G)                                              \
-    Variant {                                                                              \
-        DT, 0, 0, tgemm_config{TGEMM_KERNEL_SPLITK, BM, BN, BK, WM, WN, ST, G, 2, 32},         \
-            nullptr, &launch_splitk<DT, BM, BN, BK, WM, WN, ST>                            \
-    }
-#define SKINNY(DT, MT, D)                                                                  \
-    Variant {                                                                              \
-        DT, 0, 0, tgemm_config{TGEMM_KERNEL_SKINNY, MT * 32, 32, 64, 1, 8, D, 1, 8, 32},       \
-            &launch_skinny<DT, MT, D>                                                      \
-    }
-// A [M,K], B [N,K]: every kernel
-#define ALL_MK_NK(DT)                                                                      \
-    GENERIC(DT, 0, 0), TILED(DT, 0, 0, 256, 256, 64, 2, 2, 4),                             \
-        TILED(DT, 0, 0, 256, 128, 64, 2, 2, 8), TILED(DT, 0, 0, 128, 256, 64, 2, 2, 8),    \
-        TILED(DT, 0, 0, 128, 128, 64, 2, 2, 8), TILED(DT, 0, 0, 64, 64, 64, 2, 2, 8),      \
-        DMA(DT, 256, 256, 32, 2, 2, 4, 4), DMA(DT, 256, 256, 32, 2, 2, 5, 4),              \
-        PINGPONG(DT, 0, 0, 256, 256, 64, 2, 4), PINGPONG(DT, 0, 0, 256, 256, 32, 4, 4),    \
-        PINGPONG(DT, 0, 0, 256, 256, 32, 5, 4), QUAD(DT, 16, 4), QUAD(DT, 32, 4),          \
-        SKINNY(DT, 1, 4), SKINNY(DT, 2, 3), SKINNY(DT, 4, 1),                              \
-        SPLITK(DT, 64, 256, 32, 1, 4, 5, 1), SPLITK(DT, 64, 128, 32, 1, 4, 5, 1),          \
-        SPLITK(DT, 64, 256, 64, 1, 4, 4, 1), SPLITK(DT, 64, 128, 64, 1, 4, 4, 1),          \
-        SPLITK(DT, 64, 128, 64, 1, 4, 6, 1)
-// A [M,K], B [K,N]
-#define ALL_MK_KN(DT)                                                                      \
-    GENERIC(DT, 0, 1), TILED(DT, 0, 1, 256, 256, 64, 2, 2, 4),                             \
-        TILED(DT, 0, 1, 256, 128, 64, 2, 2, 8), TILED(DT, 0, 1, 128, 256, 64, 2, 2, 8),    \
-        TILED(DT, 0, 1, 128, 128, 64, 2, 2, 8), TILED(DT, 0, 1, 64, 64, 64, 2, 2, 8),      \
-        PINGPONG(DT, 0, 1, 256, 256, 64, 2, 4), PINGPONG(DT, 0, 1, 256, 256, 32, 5, 4)
-// A [K,M], either B
-#define ALL_KM(DT, L)                                                                      \
-    GENERIC(DT, 1, L), TILED(DT, 1, L, 128, 128, 64, 2, 2, 8),                             \
-        TILED(DT, 1, L, 64, 64, 64, 2, 2, 8), PINGPONG(DT, 1, L, 256, 256, 32, 4, 4)
-
-const Variant kVariants[] = {
-    ALL_MK_NK(0), ALL_MK_NK(1), ALL_MK_KN(0), ALL_MK_KN(1),
-    ALL_KM(0, 0), ALL_KM(1, 0), ALL_KM(0, 1), ALL_KM(1, 1),
-};
-constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
 bool same_shape(const tgemm_config& a, const tgemm_config& b) {
     // a split-K configuration's split count is a per-call choice
@@ -204,11 +67,10 @@ bool same_shape(const tgemm_config& a, const tgemm_config& b) {
 }
 
 const Variant* find_variant(int dtype, int a_layout, int layout, const tgemm_config& cfg) {
-    for (int i = 0; i < kNumVariants; ++i) {
-        const Variant& v = kVariants[i];
-        if (v.dtype == dtype && v.a_layout == a_layout && v.layout == layout &&
-            same_shape(v.cfg, cfg))
-            return &v;
+    for (const Variant* v : registry()) {
+        if (v->dtype == dtype && v->a_layout == a_layout && v->layout == layout &&
+            same_shape(v->cfg, cfg))
+            return v;
     }
     return nullptr;
 }
@@ -470,20 +332,53 @@ int list(int dtype, int a_layout, int b_layout, tgemm_config* out, int capacity)
     if (capacity < 0 || (capacity > 0 && !out))
         return TGEMM_ERR_INVALID_VALUE;
     int count = 0;
-    for (int i = 0; i < kNumVariants; ++i) {
-        const Variant& v = kVariants[i];
-        if (v.dtype != dtype || v.a_layout != a_layout || v.layout != b_layout)
+    for (const Variant* v : registry()) {
+        if (v->dtype != dtype || v->a_layout != a_layout || v->layout != b_layout)
             continue;
         if (count < capacity)
-            out[count] = v.cfg;
+            out[count] = v->cfg;
         ++count;
     }
     return count;
 }
 
+// One lane reads the engine-clock counter and the constant-rate wall clock.
+__global__ void __launch_bounds__(64) clock_stamp_kernel(unsigned long long* out) {
+    if (threadIdx.x == 0) {
+        const unsigned long long c = (unsigned long long)clock64();
+        const unsigned long long w = (unsigned long long)wall_clock64();
+        out[0] = c;
+        out[1] = w;
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+int tgemm_clock_stamp(void* out, void* stream) {
+    if (!out)
+        return TGEMM_ERR_NULL_POINTER;
+    if ((uintptr_t)out % 8 != 0)
+        return TGEMM_ERR_ALIGNMENT;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(clock_stamp_kernel, dim3(1), dim3(64), 0,
+                       static_cast<hipStream_t>(stream),
+                       static_cast<unsigned long long*>(out));
+    return hipGetLastError() == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+}
+
+int tgemm_wall_clock_hz(int64_t* hz) {
+    if (!hz)
+        return TGEMM_ERR_NULL_POINTER;
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+        khz <= 0)
+        return TGEMM_ERR_DEVICE;
+    *hz = (int64_t)khz * 1000;
+    return TGEMM_OK;
+}
 
 int gemm_f16(int64_t m, int64_t n, int64_t k, const void* A, const void* B, void* C,
              int b_layout, void* stream) {
@@ -516,9 +411,16 @@ int gemm_strided(int dtype, int64_t m, int64_t n, int64_t k, const void* A, int6
                nullptr, 0, stream);
 }
 
-int tgemm_query_config(int dtype, int64_t m, int64_t n, int64_t k, int b_layout, int aligned,
+int tgemm_query_config(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
                        tgemm_config* out) {
-    return query(dtype, m, n, k, TGEMM_A_MK, b_layout, aligned, out);
+    // the packed problem at 16-byte-aligned addresses: the sizes decide alignment
+    const int rc = check_sizes(dtype, m, n, k, TGEMM_A_MK, b_layout);
+    if (rc != TGEMM_OK)
+        return rc;
+    const Problem p = packed(dtype, m, n, k, reinterpret_cast<const void*>(uintptr_t(256)),
+                             reinterpret_cast<const void*>(uintptr_t(256)),
+                             reinterpret_cast<void*>(uintptr_t(256)), b_layout);
+    return query(dtype, m, n, k, TGEMM_A_MK, b_layout, fast_aligned(p) ? 1 : 0, out);
 }
 
 int tgemm_query_config_ex(int dtype, int64_t m, int64_t n, int64_t k, int a_layout,

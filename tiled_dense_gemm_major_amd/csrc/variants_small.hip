@@ -1,0 +1,20 @@
+// libtgemm registry: the any-alignment kernel (every storage), and for A [M,K] with
+// B [N,K] the deep direct-to-LDS ring, the skinny kernel and split-K over workgroups.
+#include "launch.hpp"
+
+namespace tgemm_reg {
+namespace {
+#define SMALL_MK_NK(DT)                                                                    \
+    GENERIC(DT, 0, 0), DMA(DT, 256, 256, 32, 2, 2, 4, 4), DMA(DT, 256, 256, 32, 2, 2, 5, 4), \
+        SKINNY(DT, 1, 4), SKINNY(DT, 2, 3), SKINNY(DT, 4, 1),                              \
+        SPLITK(DT, 64, 256, 32, 1, 4, 5, 1), SPLITK(DT, 64, 128, 32, 1, 4, 5, 1),          \
+        SPLITK(DT, 64, 256, 64, 1, 4, 4, 1), SPLITK(DT, 64, 128, 64, 1, 4, 4, 1),          \
+        SPLITK(DT, 64, 128, 64, 1, 4, 6, 1)
+const Variant kList[] = {
+    SMALL_MK_NK(0), SMALL_MK_NK(1),
+    GENERIC(0, 0, 1), GENERIC(1, 0, 1),
+    GENERIC(0, 1, 0), GENERIC(1, 1, 0), GENERIC(0, 1, 1), GENERIC(1, 1, 1),
+};
+}  // namespace
+VariantList variants_small() { return {kList, (int)(sizeof(kList) / sizeof(kList[0]))}; }
+}  // namespace tgemm_reg

@@ -21,7 +21,16 @@ LIB_PATH = os.path.join(_PKG, "libtgemm.so")
 EXPORTS = ("attn_fwd_f16", "gemm_f16", "gemm_bf16", "gemm_ex", "gemm_ex_ws", "gemm_strided",
            "tgemm_query_config", "tgemm_query_config_ex", "tgemm_query_config_ws",
            "tgemm_workspace_size", "tgemm_list_configs", "tgemm_list_configs_ex",
-           "tgemm_status_string", "tgemm_version")
+           "tgemm_status_string", "tgemm_version", "tgemm_clock_stamp",
+           "tgemm_wall_clock_hz")
+
+
+__all__ = ["F16", "BF16", "B_NK", "B_KN", "A_MK", "A_KM", "KERNEL_GENERIC", "KERNEL_TILED",
+           "KERNEL_SKINNY", "KERNEL_DMA", "KERNEL_PINGPONG", "KERNEL_QUAD", "KERNEL_SPLITK",
+           "LIB_PATH", "EXPORTS", "TGemmError", "Config", "load", "status_string", "gemm_f16",
+           "gemm_bf16", "gemm_ex", "gemm_ex_ws", "gemm_strided", "query_config",
+           "query_config_packed", "query_config_ws", "workspace_size", "list_configs",
+           "attn_fwd_f16", "version", "gemm", "clock_stamp", "wall_clock_hz"]
 
 
 class TGemmError(RuntimeError):
@@ -70,13 +79,15 @@ def load(path: str = LIB_PATH):
     lib.attn_fwd_f16.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, i32, vp]
     lib.gemm_strided.argtypes = [i32, i64, i64, i64, vp, i64, i32, vp, i64, i32, vp, i64,
                                  cfgp, vp]
-    lib.tgemm_query_config.argtypes = [i32, i64, i64, i64, i32, i32, cfgp]
+    lib.tgemm_query_config.argtypes = [i32, i64, i64, i64, i32, cfgp]
     lib.tgemm_query_config_ex.argtypes = [i32, i64, i64, i64, i32, i32, i32, cfgp]
     lib.tgemm_query_config_ws.argtypes = [i32, i64, i64, i64, i32, i32, cfgp,
                                           ctypes.POINTER(ctypes.c_int64)]
     lib.tgemm_workspace_size.argtypes = [i64, i64, cfgp, ctypes.POINTER(ctypes.c_int64)]
     lib.tgemm_list_configs.argtypes = [i32, i32, cfgp, i32]
     lib.tgemm_list_configs_ex.argtypes = [i32, i32, i32, cfgp, i32]
+    lib.tgemm_clock_stamp.argtypes = [vp, vp]
+    lib.tgemm_wall_clock_hz.argtypes = [ctypes.POINTER(ctypes.c_int64)]
     lib.tgemm_status_string.argtypes = [i32]
     lib.tgemm_status_string.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -181,6 +192,15 @@ def query_config(dtype, m, n, k, b_layout=B_NK, aligned=True, a_layout=A_MK) -> 
     return out
 
 
+def query_config_packed(dtype, m, n, k, b_layout=B_NK) -> Config:
+    """What gemm_f16 / gemm_bf16 pick for packed operands at 16-byte-aligned addresses
+    (tgemm_query_config: the sizes decide whether the fast kernels apply)."""
+    out = Config()
+    _check(load().tgemm_query_config(dtype, m, n, k, b_layout, ctypes.byref(out)),
+           "tgemm_query_config")
+    return out
+
+
 def list_configs(dtype, b_layout=B_NK, a_layout=A_MK) -> list:
     lib = load()
     count = lib.tgemm_list_configs_ex(dtype, a_layout, b_layout, None, 0)
@@ -197,6 +217,18 @@ def attn_fwd_f16(batch, seq, heads, dim, Q, K, V, O, causal=True, stream=None):
     addresses."""
     _check(load().attn_fwd_f16(batch, seq, heads, dim, _addr(Q), _addr(K), _addr(V), _addr(O),
                                int(bool(causal)), _stream(stream)), "attn_fwd_f16")
+
+
+def clock_stamp(out, stream=None):
+    """Enqueue a (engine-clock counter, wall clock) stamp into ``out`` (a device tensor of
+    at least two int64, or an address)."""
+    _check(load().tgemm_clock_stamp(_addr(out), _stream(stream)), "tgemm_clock_stamp")
+
+
+def wall_clock_hz() -> int:
+    hz = ctypes.c_int64(0)
+    _check(load().tgemm_wall_clock_hz(ctypes.byref(hz)), "tgemm_wall_clock_hz")
+    return int(hz.value)
 
 
 def version() -> int:
