@@ -88,3 +88,19 @@ def sample_positions(M, N, count, seed):
     rows += list(rng.integers(0, M, edge))
     cols += [N - 1] * edge
     return np.array(rows, dtype=np.int64), np.array(cols, dtype=np.int64)
+
+
+def assert_parity_full(orc, dtype, A_bits, B_bits, b_layout, got_bits, what="",
+                       chunk_rows=1024):
+    """Every element of C against the oracle, the oracle run over row blocks so host
+    memory stays bounded; returns the worst ratio of error to tolerance."""
+    M = A_bits.shape[0]
+    worst = 0.0
+    for lo in range(0, M, chunk_rows):
+        hi = min(M, lo + chunk_rows)
+        want = orc.gemm_rows(dtype, A_bits, B_bits, b_layout, lo, hi)
+        K = A_bits.shape[1]
+        res = orc.compare(dtype, K, got_bits[lo:hi], want)
+        assert res["n_fail"] == 0, f"{what} rows {lo}..{hi - 1}: {res}"
+        worst = max(worst, res["max_err_over_tol"])
+    return worst
