@@ -77,9 +77,14 @@ typedef enum {
                                      not compiled into the library                      */
     TGEMM_ERR_LAUNCH = -6,        /* the HIP launch was refused (no gfx950 device...)   */
     TGEMM_ERR_DEVICE = -7,        /* the current device could not be queried            */
-    TGEMM_ERR_WORKSPACE = -8      /* the configuration needs a workspace and none, or
+    TGEMM_ERR_WORKSPACE = -8,     /* the configuration needs a workspace and none, or
                                      too small a one, was given                         */
+    TGEMM_ERR_SCRATCH = -9        /* gemm_ex_noalloc: the configuration needs more than
+                                     the library's fixed scratch (TGEMM_SCRATCH_BYTES)  */
 } tgemm_status;
+
+/* Size of the fixed per-GPU scratch that gemm_ex_noalloc uses: 16 MiB. */
+#define TGEMM_SCRATCH_BYTES (16ll << 20)
 
 /* Kernel families in the library. */
 typedef enum {
@@ -167,6 +172,27 @@ int gemm_ex(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const voi
 int gemm_ex_ws(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const void* B,
                void* C, int b_layout, const tgemm_config* cfg, void* workspace,
                int64_t workspace_bytes, void* stream);
+
+/*
+ * gemm_ex_ws without a caller workspace and without any allocation, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split-K partial tiles go to a fixed scratch
+ * array inside the library: TGEMM_SCRATCH_BYTES of device memory per GPU, set aside when
+ * the library's code is loaded on that GPU and held until the process ends.  Nothing is
+ * allocated by the call (no hipMalloc, no hipFree); the first call on a device looks up
+ * that device's scratch address and keeps it.
+ *   arguments as for gemm_ex; cfg == NULL takes the table's choice given a workspace (as
+ *   gemm_ex_ws does), which for every shape needs at most TGEMM_SCRATCH_BYTES
+ * Errors as gemm_ex_ws, plus TGEMM_ERR_SCRATCH when an explicit configuration needs more
+ * than TGEMM_SCRATCH_BYTES (split_k * m * n * 4 bytes for SPLITK) and TGEMM_ERR_DEVICE
+ * when the scratch address cannot be found.  Results are bit for bit those of gemm_ex_ws
+ * with the same configuration.  Every call on one GPU uses that GPU's one scratch array:
+ * nothing in it needs to start at zero (each call overwrites what it reads), but two
+ * calls whose kernels overlap in time on one GPU (different streams, other host threads)
+ * race on it; calls in order on one stream do not.
+ */
+int gemm_ex_noalloc(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const void* B,
+                    void* C, int b_layout, const tgemm_config* cfg, void* stream);
 
 /*
  * The general product: either storage of A, either storage of B, leading dimensions.

@@ -35,7 +35,7 @@ def test_exports_every_declared_function(lib):
 
 def test_version_and_status_strings(lib):
     assert tgemm.version() >= 100
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         assert tgemm.status_string(code).startswith("TGEMM_")
     assert "unknown" in tgemm.status_string(-99)
 
@@ -343,3 +343,31 @@ def test_package_exports_every_binding_name():
     assert "gemm_ex_ws" in tgemm.__all__ and "attn_fwd_f16" in tgemm.__all__
     with pytest.raises(AttributeError):
         getattr(pkg, "no_such_name")
+
+
+def test_workspace_choice_fits_the_fixed_scratch(lib):
+    """The table's choice given a workspace never needs more than the fixed scratch that
+    gemm_ex_noalloc lends it (split count x tiles <= 256, each tile at most 64 x 256)."""
+    worst = 0
+    for M in (1, 16, 33, 64, 65, 100, 128):
+        for N in (8, 256, 264, 1032, 4096, 8192, 16384, 65536):
+            for K in (1024, 4096, 8192, 65536):
+                if N * K >= 2 ** 31:          # past the size limits
+                    continue
+                for dt in (tgemm.F16, tgemm.BF16):
+                    _, nbytes = tgemm.query_config_ws(dt, M, N, K)
+                    worst = max(worst, nbytes)
+    assert 0 < worst <= tgemm.SCRATCH_BYTES
+
+
+def test_no_alloc_argument_errors(lib):
+    f = lib.gemm_ex_noalloc
+    M, N, K = 128, 8192, 512
+    A, B, C = FAKE, FAKE + (1 << 24), FAKE + (1 << 26)
+    big = _splitk(64)                             # 64 * 128 * 8192 * 4 bytes: too many
+    assert f(1, M, N, K, A, B, C, 0, ctypes.byref(big), None) == -9
+    assert "scratch" in tgemm.status_string(-9)
+    assert f(1, -1, N, K, A, B, C, 0, None, None) == -1
+    assert f(1, M, N, K, None, B, C, 0, None, None) == -2
+    assert f(1, 0, N, K, None, None, None, 0, None, None) == 0
+    assert f(1, M, N, K, A, B, A + 64, 0, None, None) == -4

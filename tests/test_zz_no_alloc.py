@@ -1,0 +1,117 @@
+"""GPU test of gemm_ex_noalloc, the entry point that allocates nothing: its split-K
+partials live in the library's fixed per-GPU scratch.  Called through the C ABI, its
+results must equal gemm_ex_ws's with the same configuration bit for bit (the same
+kernels, the same split order) and meet the oracle's rule, on consecutive calls whose
+second is smaller than the first (the scratch keeps the first call's partials)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from tests.gpu_util import (assert_parity, from_dev, require_gpu, say, tdtype, to_dev,
+                            torch)
+from tiled_dense_gemm_major_amd.inputs import BF16, B_KN, B_NK, F16, WORKLOADS, Stream
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _with_ws(dtype, M, N, K, Ad, Bd, layout, cfg):
+    from tiled_dense_gemm_major_amd import tgemm
+    need = tgemm.workspace_size(M, N, cfg)
+    ws = torch.full((max(need, 16) // 4,), -1, dtype=torch.int32, device="cuda")
+    C = torch.empty((M, N), dtype=tdtype(dtype), device="cuda")
+    tgemm.gemm_ex_ws(dtype, M, N, K, Ad, Bd, C, ws, need, layout, cfg)
+    torch.cuda.synchronize()
+    return from_dev(C)
+
+
+def _no_alloc(dtype, M, N, K, Ad, Bd, layout, cfg=None):
+    """gemm_ex_noalloc through a fresh ctypes handle (the C ABI as declared)."""
+    from tiled_dense_gemm_major_amd import tgemm
+    raw = ctypes.CDLL(tgemm.LIB_PATH)
+    f = raw.gemm_ex_noalloc
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    f.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, ctypes.POINTER(tgemm.Config), vp]
+    f.restype = i32
+    C = torch.full((M, N), 0x7E00, dtype=torch.int16, device="cuda").view(tdtype(dtype))
+    rc = f(dtype, M, N, K, Ad.data_ptr(), Bd.data_ptr(), C.data_ptr(), layout,
+           ctypes.byref(cfg) if cfg is not None else None,
+           torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, tgemm.status_string(rc)
+    torch.cuda.synchronize()
+    return from_dev(C)
+
+
+def _case(dtype, M, N, K, layout, seed):
+    s = Stream(seed)
+    A = s.matrix((M, K), dtype, "uniform")
+    B = s.matrix((N, K) if layout == B_NK else (K, N), dtype, "uniform")
+    return A, B
+
+
+def test_no_alloc_matches_workspace_entry_point(dev, orc):
+    from tiled_dense_gemm_major_amd import tgemm
+    w = WORKLOADS["bf16_skinny_64x8192x8192"]
+    # first call: the skinny workload, whose split-K partials fill the whole scratch
+    cfg, need = tgemm.query_config_ws(w.dtype, w.M, w.N, w.K)
+    assert cfg.kernel == tgemm.KERNEL_SPLITK and need == tgemm.SCRATCH_BYTES
+    A, B = w.generate()
+    Ad, Bd = to_dev(A, w.dtype), to_dev(B, w.dtype)
+    say(f"no-alloc call 1: {w.describe()} splits {cfg.split_k} ({need} bytes)")
+    got1 = _no_alloc(w.dtype, w.M, w.N, w.K, Ad, Bd, w.b_layout)
+    assert np.array_equal(got1, _with_ws(w.dtype, w.M, w.N, w.K, Ad, Bd, w.b_layout, cfg))
+    assert_parity(orc, w.dtype, w.K, got1, orc.gemm(w.dtype, A, B, w.b_layout), "call 1")
+    # second call, smaller: fp16, 16 x 2056 x 4096 (a ragged column tile), more splits
+    M, N, K = 16, 2056, 4096
+    cfg2, need2 = tgemm.query_config_ws(F16, M, N, K)
+    assert cfg2.kernel == tgemm.KERNEL_SPLITK and 0 < need2 < need
+    A2, B2 = _case(F16, M, N, K, B_NK, 31)
+    Ad2, Bd2 = to_dev(A2, F16), to_dev(B2, F16)
+    say(f"no-alloc call 2: f16 {M}x{N}x{K} splits {cfg2.split_k} ({need2} bytes)")
+    got2 = _no_alloc(F16, M, N, K, Ad2, Bd2, B_NK)
+    assert np.array_equal(got2, _with_ws(F16, M, N, K, Ad2, Bd2, B_NK, cfg2))
+    assert_parity(orc, F16, K, got2, orc.gemm(F16, A2, B2, B_NK), "call 2")
+    # the first problem again, after the smaller one: same bits as before
+    say("no-alloc call 3: the first problem again")
+    assert np.array_equal(_no_alloc(w.dtype, w.M, w.N, w.K, Ad, Bd, w.b_layout), got1)
+
+
+def test_no_alloc_explicit_configs_and_no_workspace_shapes(dev, orc):
+    from tiled_dense_gemm_major_amd import tgemm
+    M, N, K = 100, 1032, 2056
+    A, B = _case(BF16, M, N, K, B_NK, 41)
+    Ad, Bd = to_dev(A, BF16), to_dev(B, BF16)
+    want = orc.gemm(BF16, A, B, B_NK)
+    for splits in (2, 7, 16):
+        cfg = tgemm.Config(kernel=tgemm.KERNEL_SPLITK, block_m=64, block_n=256, block_k=64,
+                           waves_m=1, waves_n=4, stages=4, group_m=1, split_k=splits, mfma=32)
+        say(f"no-alloc explicit split-K {M}x{N}x{K} splits {splits}")
+        got = _no_alloc(BF16, M, N, K, Ad, Bd, B_NK, cfg)
+        assert np.array_equal(got, _with_ws(BF16, M, N, K, Ad, Bd, B_NK, cfg)), splits
+        assert_parity(orc, BF16, K, got, want, f"splits {splits}")
+    # a configuration needing more than the scratch is refused before any launch
+    big = tgemm.Config(kernel=tgemm.KERNEL_SPLITK, block_m=64, block_n=256, block_k=64,
+                       waves_m=1, waves_n=4, stages=4, group_m=1, split_k=64, mfma=32)
+    assert tgemm.workspace_size(128, 8192, big) > tgemm.SCRATCH_BYTES
+    Ab = torch.zeros((128, 512), dtype=torch.bfloat16, device="cuda")
+    Bb = torch.zeros((8192, 512), dtype=torch.bfloat16, device="cuda")
+    Cb = torch.empty((128, 8192), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(tgemm.TGemmError) as e:
+        tgemm.gemm_ex_noalloc(BF16, 128, 8192, 512, Ab, Bb, Cb, B_NK, big)
+    assert e.value.status == -9
+    # shapes whose choice needs no workspace run their plain kernel, and B [K,N]
+    for (M, N, K, layout) in [(512, 512, 512, B_NK), (600, 520, 328, B_KN)]:
+        A, B = _case(F16, M, N, K, layout, 50 + M)
+        Ad, Bd = to_dev(A, F16), to_dev(B, F16)
+        say(f"no-alloc without workspace {M}x{N}x{K} layout {layout}")
+        got = _no_alloc(F16, M, N, K, Ad, Bd, layout)
+        C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        tgemm.gemm_ex(F16, M, N, K, Ad, Bd, C, layout)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, from_dev(C))
+        assert_parity(orc, F16, K, got, orc.gemm(F16, A, B, layout), "no workspace")

@@ -9,9 +9,17 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "registry.hpp"
+
+// The fixed scratch of gemm_ex_noalloc (split-K's fp32 partial tiles), for callers that
+// cannot allocate.  File-scope device memory: each GPU the library runs on holds its own
+// copy until the process ends.  Host code never passes this name to a kernel (on the
+// host it is only a stand-in); it uses the device address hipGetSymbolAddress returns.
+constexpr int64_t kScratchBytes = int64_t(16) << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / 4];
 
 namespace {
 
@@ -253,7 +261,31 @@ bool fast_aligned(const Problem& p) {
            2 * span_b(p) <= kMaxFastOperandBytes;
 }
 
-int run(const Problem& p, const tgemm_config* cfg, void* ws, int64_t ws_bytes, void* stream) {
+// The device address of `scratch` on the current device, looked up once per device (with
+// that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_at[kMaxDevices];
+
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return TGEMM_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_at[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return TGEMM_ERR_DEVICE;
+        g_scratch_at[dev] = p;
+    }
+    *out = g_scratch_at[dev];
+    return TGEMM_OK;
+}
+
+// One product.  ws / ws_bytes: the caller's workspace (NULL: none).  use_scratch: the
+// library's fixed scratch serves as the workspace instead (gemm_ex_noalloc).
+int run(const Problem& p, const tgemm_config* cfg, void* ws, int64_t ws_bytes, void* stream,
+        bool use_scratch = false) {
     int rc = check_problem(p);
     if (rc != TGEMM_OK)
         return rc;
@@ -269,14 +301,23 @@ int run(const Problem& p, const tgemm_config* cfg, void* ws, int64_t ws_bytes, v
     const bool aligned = fast_aligned(p);
     tgemm_config use =
         cfg ? *cfg
-            : (ws ? choose_ws(p.dtype, p.a_layout, p.b_layout, p.m, p.n, p.k, aligned)
-                  : choose(p.dtype, p.a_layout, p.b_layout, p.m, p.n, p.k, aligned));
+            : (ws || use_scratch
+                   ? choose_ws(p.dtype, p.a_layout, p.b_layout, p.m, p.n, p.k, aligned)
+                   : choose(p.dtype, p.a_layout, p.b_layout, p.m, p.n, p.k, aligned));
     const Variant* v = find_variant(p.dtype, p.a_layout, p.b_layout, use);
     if (!v)
         return TGEMM_ERR_UNSUPPORTED;
     if (use.kernel != TGEMM_KERNEL_GENERIC && !aligned)
         return TGEMM_ERR_ALIGNMENT;
     const int64_t need = workspace_bytes(use, p.m, p.n);
+    if (use_scratch && need > 0) {
+        if (need > kScratchBytes)
+            return TGEMM_ERR_SCRATCH;
+        rc = scratch_address(&ws);
+        if (rc != TGEMM_OK)
+            return rc;
+        ws_bytes = kScratchBytes;
+    }
     if (need > 0) {
         if (!ws || ws_bytes < need)
             return TGEMM_ERR_WORKSPACE;
@@ -404,6 +445,11 @@ int gemm_ex_ws(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const 
                stream);
 }
 
+int gemm_ex_noalloc(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const void* B,
+                    void* C, int b_layout, const tgemm_config* cfg, void* stream) {
+    return run(packed(dtype, m, n, k, A, B, C, b_layout), cfg, nullptr, 0, stream, true);
+}
+
 int gemm_strided(int dtype, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
                  int a_layout, const void* B, int64_t ldb, int b_layout, void* C, int64_t ldc,
                  const tgemm_config* cfg, void* stream) {
@@ -474,6 +520,9 @@ const char* tgemm_status_string(int status) {
     case TGEMM_ERR_DEVICE: return "TGEMM_ERR_DEVICE: device query failed";
     case TGEMM_ERR_WORKSPACE:
         return "TGEMM_ERR_WORKSPACE: the configuration needs a larger workspace";
+    case TGEMM_ERR_SCRATCH:
+        return "TGEMM_ERR_SCRATCH: the configuration needs more than the library's fixed "
+               "16 MiB scratch (gemm_ex_noalloc)";
     default: return "unknown tgemm status";
     }
 }

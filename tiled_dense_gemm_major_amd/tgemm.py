@@ -15,10 +15,13 @@ A_MK, A_KM = 0, 1
 (KERNEL_GENERIC, KERNEL_TILED, KERNEL_SKINNY, KERNEL_DMA, KERNEL_PINGPONG, KERNEL_QUAD,
  KERNEL_SPLITK) = range(7)
 
+SCRATCH_BYTES = 16 << 20    # the fixed per-GPU scratch of gemm_ex_noalloc
+
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtgemm.so")
 
-EXPORTS = ("attn_fwd_f16", "gemm_f16", "gemm_bf16", "gemm_ex", "gemm_ex_ws", "gemm_strided",
+EXPORTS = ("attn_fwd_f16", "gemm_f16", "gemm_bf16", "gemm_ex", "gemm_ex_ws", "gemm_ex_noalloc",
+           "gemm_strided",
            "tgemm_query_config", "tgemm_query_config_ex", "tgemm_query_config_ws",
            "tgemm_workspace_size", "tgemm_list_configs", "tgemm_list_configs_ex",
            "tgemm_status_string", "tgemm_version", "tgemm_clock_stamp",
@@ -28,7 +31,8 @@ EXPORTS = ("attn_fwd_f16", "gemm_f16", "gemm_bf16", "gemm_ex", "gemm_ex_ws", "ge
 __all__ = ["F16", "BF16", "B_NK", "B_KN", "A_MK", "A_KM", "KERNEL_GENERIC", "KERNEL_TILED",
            "KERNEL_SKINNY", "KERNEL_DMA", "KERNEL_PINGPONG", "KERNEL_QUAD", "KERNEL_SPLITK",
            "LIB_PATH", "EXPORTS", "TGemmError", "Config", "load", "status_string", "gemm_f16",
-           "gemm_bf16", "gemm_ex", "gemm_ex_ws", "gemm_strided", "query_config",
+           "gemm_bf16", "gemm_ex", "gemm_ex_ws", "gemm_ex_noalloc", "gemm_strided",
+           "query_config", "SCRATCH_BYTES",
            "query_config_packed", "query_config_ws", "workspace_size", "list_configs",
            "attn_fwd_f16", "version", "gemm", "clock_stamp", "wall_clock_hz"]
 
@@ -76,6 +80,7 @@ def load(path: str = LIB_PATH):
     lib.gemm_bf16.argtypes = [i64, i64, i64, vp, vp, vp, i32, vp]
     lib.gemm_ex.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, cfgp, vp]
     lib.gemm_ex_ws.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, cfgp, vp, i64, vp]
+    lib.gemm_ex_noalloc.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, cfgp, vp]
     lib.attn_fwd_f16.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, i32, vp]
     lib.gemm_strided.argtypes = [i32, i64, i64, i64, vp, i64, i32, vp, i64, i32, vp, i64,
                                  cfgp, vp]
@@ -156,6 +161,14 @@ def gemm_ex_ws(dtype, m, n, k, A, B, C, workspace, workspace_bytes, b_layout=B_N
     _check(load().gemm_ex_ws(dtype, m, n, k, _addr(A), _addr(B), _addr(C), b_layout, cfg,
                              _addr(workspace) if workspace is not None else None,
                              int(workspace_bytes), _stream(stream)), "gemm_ex_ws")
+
+
+def gemm_ex_noalloc(dtype, m, n, k, A, B, C, b_layout=B_NK, config: Config | None = None,
+                    stream=None):
+    """gemm_ex_ws with the library's fixed scratch as the workspace: allocates nothing."""
+    cfg = ctypes.byref(config) if config is not None else None
+    _check(load().gemm_ex_noalloc(dtype, m, n, k, _addr(A), _addr(B), _addr(C), b_layout, cfg,
+                                  _stream(stream)), "gemm_ex_noalloc")
 
 
 def query_config_ws(dtype, m, n, k, b_layout=B_NK, aligned=True):
