@@ -22,13 +22,14 @@ three fresh processes):
     run as the CPU baseline; a mismatch ends the benchmark with an error;
   * ``value`` is the median process's whole-region rate; ``roofline.achieved`` is the
     algorithmic FLOP of one launch over that process's mean per-launch event time.
+With --procs 1 the measurement runs in the bench process itself (the form to run under a
+profiler).
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
-import statistics
 import subprocess
 import sys
 import tempfile
@@ -109,8 +110,8 @@ def parity_and_cpu_baseline(A, B, C_gpu, w, budget_s: float):
     return baseline, parity
 
 
-def child(args):
-    """One fresh process: upload, verify (first process), time."""
+def measure(args, A_bits, B_bits, verify: bool) -> dict:
+    """Upload, verify (when asked), time; in the calling process."""
     import numpy as np
     import torch
     from tiled_dense_gemm_major_amd import tgemm
@@ -120,8 +121,6 @@ def child(args):
         sys.exit(1)
     tgemm.load()
     w = WORKLOADS[args.workload]
-    A_bits = np.load(os.path.join(args.inputs, "A.npy"))
-    B_bits = np.load(os.path.join(args.inputs, "B.npy"))
     tdt = torch.bfloat16 if w.dtype == BF16 else torch.float16
     A = torch.from_numpy(A_bits.view(np.int16)).cuda().view(tdt)
     B = torch.from_numpy(B_bits.view(np.int16)).cuda().view(tdt)
@@ -135,7 +134,7 @@ def child(args):
     step()
     torch.cuda.synchronize()
     out = {}
-    if args.verify:
+    if verify:
         C_host = C.view(torch.int16).cpu().numpy().view(np.uint16)
         out["cpu_baseline"], out["parity"] = parity_and_cpu_baseline(
             A_bits, B_bits, C_host, w, args.cpu_budget_s)
@@ -174,6 +173,15 @@ def child(args):
         "tile_config": tgemm.query_config(w.dtype, w.M, w.N, w.K, w.b_layout).as_dict(),
         "device": torch.cuda.get_device_name(0),
     })
+    return out
+
+
+def child(args):
+    """One fresh process started by the parent: the inputs come from its files."""
+    import numpy as np
+    A_bits = np.load(os.path.join(args.inputs, "A.npy"))
+    B_bits = np.load(os.path.join(args.inputs, "B.npy"))
+    out = measure(args, A_bits, B_bits, args.verify)
     print(CHILD_TAG + json.dumps(out), flush=True)
 
 
@@ -208,7 +216,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--procs", type=int, default=3,
-                    help="fresh processes to time; the reported figure is their median")
+                    help="fresh processes to time; the reported figure is their median "
+                         "(1: measure in this process)")
     ap.add_argument("--workload", default=HEADLINE, choices=list(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (and with it the parity check)")
@@ -234,6 +243,12 @@ def main():
     w = WORKLOADS[args.workload]
     log(f"workload {w.describe()}")
     A_bits, B_bits = w.generate()
+    if args.procs == 1:
+        # one process: measure here (no child process; also the form to run under a
+        # profiler, which starts the GPU before the program runs)
+        results = [measure(args, A_bits, B_bits, not args.no_cpu_baseline)]
+        report(args, w, results)
+        return
     tmp = tempfile.mkdtemp(prefix="tgemm_bench_", dir="/dev/shm" if os.path.isdir("/dev/shm")
                            else None)
     try:
@@ -248,7 +263,11 @@ def main():
             except OSError:
                 pass
         os.rmdir(tmp)
+    report(args, w, results)
 
+
+def report(args, w, results):
+    """The JSON line from the processes' measurements (the first one verified)."""
     first = results[0]
     if "parity" in first and first["parity"]["n_fail"]:
         log(f"parity failure: {first['parity']}")

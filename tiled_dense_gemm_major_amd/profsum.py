@@ -52,9 +52,28 @@ def _csv(directory: str, suffix: str):
     return rows
 
 
+def _db_kernel_rows(directory: str):
+    """Kernel dispatches from rocprofv3's SQLite output (*_results.db): name, start, end."""
+    import sqlite3
+    paths = sorted(glob.glob(os.path.join(directory, "**", "*_results.db"), recursive=True))
+    rows = []
+    for p in paths:
+        db = sqlite3.connect(p)
+        try:
+            for name, start, end in db.execute("select name, start, end from kernels"):
+                rows.append({"Kernel_Name": name, "Start_Timestamp": start,
+                             "End_Timestamp": end})
+        finally:
+            db.close()
+    return rows
+
+
 def trace_durations_ns(directory: str, kernel: str):
-    """Durations of the dispatches of the kernel whose name contains `kernel`, in order."""
-    rows = [r for r in _csv(directory, "kernel_trace.csv") if kernel in r["Kernel_Name"]]
+    """Durations of the dispatches of the kernel whose name contains `kernel`, in order
+    (from the CSV kernel trace, or else from the SQLite output)."""
+    paths = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
+    rows = _csv(directory, "kernel_trace.csv") if paths else _db_kernel_rows(directory)
+    rows = [r for r in rows if kernel in r["Kernel_Name"]]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     return [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows], \
         (rows[0]["Kernel_Name"] if rows else "")
