@@ -229,20 +229,24 @@ def test_every_config_short_k_exact(dev, orc, dtype, K):
 # (K/64 mod 6) single steps and then groups of six with constant ring slots, a K tail is
 # walked first, and the XCD-staggered walk wraps at the last whole tile.  Each K below
 # picks one combination (whole tiles, tail, remainder steps, groups).
-@pytest.mark.parametrize("K", [136, 192, 384, 448, 456, 712, 776, 1000, 1536])
-def test_quad_k_walk_exact(dev, orc, K):
+@pytest.mark.parametrize("layout", [B_NK, B_KN])
+@pytest.mark.parametrize("K", [8, 136, 192, 384, 448, 456, 712, 776, 1000, 1536])
+def test_quad_k_walk_exact(dev, orc, K, layout):
     from tiled_dense_gemm_major_amd import tgemm
     dtype = BF16
     rng = np.random.default_rng(500 + K)
     M, N = 512, 768          # 2 x 3 tiles, so the eight XCD staggers differ
     A = _int_bits(dtype, rng.integers(-2, 3, (M, K)))
-    B = _int_bits(dtype, rng.integers(-2, 3, (N, K)))
-    want = orc.gemm(dtype, A, B, B_NK)
+    Bn = _int_bits(dtype, rng.integers(-2, 3, (N, K)))
+    B = Bn if layout == B_NK else np.ascontiguousarray(Bn.T)
+    want = orc.gemm(dtype, A, B, layout)
     nk = -(-K // 64)
-    for cfg in [c for c in _configs(dtype, B_NK) if c.kernel == tgemm.KERNEL_QUAD]:
-        say(f"quad k walk K={K} (tiles {nk}, remainder {nk % 6}, tail {K % 64}) "
-            f"{_cfg_id(cfg)}")
-        assert np.array_equal(run(dtype, A, B, B_NK, cfg), want), (K, _cfg_id(cfg))
+    cfgs = [c for c in _configs(dtype, layout) if c.kernel == tgemm.KERNEL_QUAD]
+    assert cfgs
+    for cfg in cfgs:
+        say(f"quad k walk K={K} layout {layout} (tiles {nk}, remainder {nk % 6}, "
+            f"tail {K % 64}) {_cfg_id(cfg)}")
+        assert np.array_equal(run(dtype, A, B, layout, cfg), want), (K, _cfg_id(cfg))
 
 
 # K walks of the skinny kernel, bit for bit on exact inputs: each of its 8 waves walks a
@@ -265,22 +269,79 @@ def test_skinny_k_walk_exact(dev, orc, M, K):
         assert np.array_equal(run(dtype, A, B, B_NK, cfg), want), (M, K, _cfg_id(cfg))
 
 
-def test_quad_repeat_launches_bitwise_identical(dev, orc):
+@pytest.mark.parametrize("layout", [B_NK, B_KN])
+def test_quad_repeat_launches_bitwise_identical(dev, orc, layout):
     """Many workgroups per compute unit through the five-slot ring: a stage reused too
     early shows up as launch-to-launch differences."""
     from tiled_dense_gemm_major_amd import tgemm
     M, N, K = 2048, 2304, 1536
-    A, B = _inputs(BF16, M, N, K, B_NK, 91)
+    A, B = _inputs(BF16, M, N, K, layout, 91)
     Ad, Bd = to_dev(A, BF16), to_dev(B, BF16)
-    for cfg in [c for c in _configs(BF16, B_NK) if c.kernel == tgemm.KERNEL_QUAD]:
-        say(f"quad repeat launches {_cfg_id(cfg)} mfma {cfg.mfma}")
+    for cfg in [c for c in _configs(BF16, layout) if c.kernel == tgemm.KERNEL_QUAD]:
+        say(f"quad repeat launches layout {layout} {_cfg_id(cfg)} mfma {cfg.mfma}")
         C0 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-        tgemm.gemm_ex(BF16, M, N, K, Ad, Bd, C0, B_NK, cfg)
+        tgemm.gemm_ex(BF16, M, N, K, Ad, Bd, C0, layout, cfg)
         torch.cuda.synchronize()
         ref = from_dev(C0)
-        assert_parity_full(orc, BF16, A, B, B_NK, ref, "quad")
+        assert_parity_full(orc, BF16, A, B, layout, ref, "quad")
         C = torch.empty_like(C0)
         for _ in range(20):
-            tgemm.gemm_ex(BF16, M, N, K, Ad, Bd, C, B_NK, cfg)
+            tgemm.gemm_ex(BF16, M, N, K, Ad, Bd, C, layout, cfg)
             torch.cuda.synchronize()
             assert np.array_equal(from_dev(C), ref)
+
+
+# ---------------------------------------------------------------------------------------
+# B [K,N] through the quad kernel: column- and row-coded exact inputs (every element of C
+# names the column or row it came from, so a wrong swizzle or transposing-read lane shows
+# as a wrong value), padded leading dimensions below and above the 256 the instruction-
+# offset loads need, and the ragged workload and a 4096^3 product at full size.
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_quad_kn_coded_exact(dev, orc, dtype):
+    from tiled_dense_gemm_major_amd import tgemm
+    M, N, K = 520, 776, 200
+    cfgs = [c for c in _configs(dtype, B_KN) if c.kernel == tgemm.KERNEL_QUAD]
+    assert cfgs
+    # column-coded: B[k, n] = (n % 128) / 8 + 1 at k = K - 1 (else 0), A[:, K - 1] = 1
+    A = np.zeros((M, K)); A[:, K - 1] = 1.0
+    B = np.zeros((K, N)); B[K - 1, :] = (np.arange(N) % 128) / 8.0 + 1.0
+    A, B = _int_bits(dtype, A), _int_bits(dtype, B)
+    want = orc.gemm(dtype, A, B, B_KN)
+    for cfg in cfgs:
+        say(f"quad [K,N] column-coded {_cfg_id(cfg)}")
+        assert np.array_equal(run(dtype, A, B, B_KN, cfg), want), _cfg_id(cfg)
+    # k-coded: B[k, n] = (k % 64) / 8 for one column block, A = 1: C[m, n] = the sum
+    # over k, exact; every k row of every slot contributes its own value
+    A = np.ones((M, K))
+    B = np.zeros((K, N)); B[:, :] = ((np.arange(K) % 64) / 8.0)[:, None]
+    B[:, 300:] = ((np.arange(K) % 16) / 4.0)[:, None] * ((np.arange(N - 300) % 3) - 1)
+    A, B = _int_bits(dtype, A), _int_bits(dtype, B)
+    want = orc.gemm(dtype, A, B, B_KN)
+    for cfg in cfgs:
+        say(f"quad [K,N] k-coded {_cfg_id(cfg)}")
+        assert np.array_equal(run(dtype, A, B, B_KN, cfg), want), _cfg_id(cfg)
+
+
+@pytest.mark.parametrize("name", ["f16_4000x3000x1000_kn"])
+def test_quad_kn_ragged_workload_full(dev, orc, name):
+    """The ragged [K,N] workload (edge tiles, K tail of 40) through each quad
+    configuration, every element against the oracle."""
+    from tiled_dense_gemm_major_amd import tgemm
+    w = WORKLOADS[name]
+    A, B = w.generate()
+    want = orc.gemm(w.dtype, A, B, w.b_layout)
+    for cfg in [c for c in _configs(w.dtype, B_KN) if c.kernel == tgemm.KERNEL_QUAD]:
+        say(f"quad [K,N] {w.describe()} {_cfg_id(cfg)}")
+        got = run(w.dtype, A, B, w.b_layout, cfg)
+        assert_parity(orc, w.dtype, w.K, got, want, _cfg_id(cfg))
+
+
+def test_quad_kn_4096_full(dev, orc):
+    from tiled_dense_gemm_major_amd import tgemm
+    M = N = K = 4096
+    A, B = _inputs(BF16, M, N, K, B_KN, 4096)
+    want = orc.gemm(BF16, A, B, B_KN)
+    for cfg in [c for c in _configs(BF16, B_KN) if c.kernel == tgemm.KERNEL_QUAD]:
+        say(f"quad [K,N] 4096^3 {_cfg_id(cfg)}")
+        assert_parity(orc, BF16, K, run(BF16, A, B, B_KN, cfg), want, _cfg_id(cfg))

@@ -139,3 +139,17 @@ def test_strided_packed_matches_gemm_ex(dev, orc):
     got = run_strided(BF16, A, Bn, A_MK, B_NK, pads=(0, 0, 0))
     assert_parity(orc, BF16, 200, got, orc.gemm(BF16, A, Bn, B_NK), "strided packed")
     assert np.array_equal(got, run(BF16, A, Bn, B_NK))
+
+
+@pytest.mark.parametrize("pads", [(8, 8, 0), (0, 64, 8), (64, 0, 0)])
+def test_strided_quad_kn_leading_dims(dev, orc, pads):
+    """The quad kernel for B [K,N] with padded rows: N = 200 gives ldb 208-264, below and
+    above the 256 that its instruction-offset loads need."""
+    from tiled_dense_gemm_major_amd import tgemm
+    M, N, K = 300, 200, 328
+    A, Bn = _inputs(BF16, M, N, K, 1200 + sum(pads))
+    for cfg in [c for c in tgemm.list_configs(BF16, B_KN, A_MK)
+                if c.kernel == tgemm.KERNEL_QUAD]:
+        say(f"strided quad [K,N] pads {pads} {cfg.as_dict()}")
+        got = run_strided(BF16, A, Bn, A_MK, B_KN, pads=pads, config=cfg)
+        assert_parity(orc, BF16, K, got, orc.gemm(BF16, A, Bn, B_NK), str(pads))

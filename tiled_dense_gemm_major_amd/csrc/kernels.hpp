@@ -1168,7 +1168,7 @@ __device__ __forceinline__ void dma16_off(rsrc4_t r, uint32_t voff, uint32_t sof
 }
 
 // ------------------------------------------------------------------------------------
-// Quadrant kernel (A [M,K], B [N,K]).
+// Quadrant kernel (A [M,K]; B [N,K], or B [K,N] with LAYOUT_KN).
 //   One wave per SIMD: 4 waves in 2 x 2, each owning a 128 x 128 quadrant of the
 //   256 x 256 tile with all of its accumulators in registers.  Per MFMA this reads a
 //   third fewer operand bytes from LDS than 8 waves of 128 x 64 (4 x 256 instead of
@@ -1199,6 +1199,18 @@ __device__ __forceinline__ void dma16_off(rsrc4_t r, uint32_t voff, uint32_t sof
 // (tiles mod 6) single steps, then groups of six with constant ring slots (3 A slots,
 // 2 B slots), so a grouped step's LDS addresses are constant offsets and no scalar
 // bookkeeping sits between two steps' MFMAs.
+// B [K,N] ("TileLang: a tile language one level below Triton", section "The first kernel:
+// GEMM": B given as a (K, N) tensor): a B slot holds the tile's 64 k rows of 256 columns
+// (512 bytes each), filled by the same 1 KiB direct-to-LDS loads (two k rows per load,
+// wave w the rows [16w, 16w + 16)).  The 16-byte chunk holding column n of row k sits at
+// chunk (n / 8) ^ kn_swz(k) (below).  The MFMA operand of a lane (8
+// consecutive k of one column) comes from two transposing reads (ds_read_b64_tr_b16): in
+// each 16-lane group, lane s points at 4 columns of k row s / 4 of a 4 x 16 block and
+// receives its column's 4 values.  A wave's read covers the rows k0 + 8g + (0..3) of lane
+// group g for 16 columns (32x32x16: rows k0 + 8(g/2) + (0..3), 16 columns per group):
+// with the swizzle the 8 row pieces that lanes 0-31 read together land in 8 different
+// 32-byte bank slots, as do those of lanes 32-63.  With B [K,N] the two B slots come
+// first in LDS.
 // ------------------------------------------------------------------------------------
 template <int NOPS, int SLOTS, int J>
 struct deal {   // ops [lo, hi) follow slot J when NOPS ops are dealt over SLOTS slots
@@ -1219,7 +1231,16 @@ constexpr int op_kind(int o) {
     return 0;
 }
 
-template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL, bool OFFS>
+// Chunk swizzle of row k of a B [K,N] slot (see above): for 16x16x32 operands the rows
+// read together are k0 + (0..3) and k0 + 8 + (0..3) at the same 16 columns; for
+// 32x32x16 operands k0 + (0..3) at 32 columns.
+template <int MF>
+__device__ __forceinline__ int kn_swz(int k) {
+    return MF == 16 ? 2 * ((k & 3) + 4 * ((k >> 3) & 1)) : 4 * (k & 3);
+}
+
+template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL, bool OFFS,
+          int LAYOUT = LAYOUT_NK>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
                                amdgpu_waves_per_eu(1, 1)))
 gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
@@ -1241,6 +1262,7 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     static_assert(KS % 2 == 0, "every step starts from operand buffer 0");
     static_assert((SA + SB) * SLOT * 2 <= 160 * 1024, "LDS");
     static_assert(PRE >= 1 && PRE < NM && SPA >= 1 && SPB >= 1, "schedule");
+    constexpr bool KN = LAYOUT == LAYOUT_KN;
     // Two loads of one operand can be adjacent (no instruction between them) when the A
     // loads outnumber their MFMA slots, or the B loads outnumber the reads dealt between.
     constexpr bool TIGHT = NB > (SPA < (KS - 1) * NM ? SPA : (KS - 1) * NM) || NR < NB;
@@ -1256,13 +1278,15 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     const int nk = (K + BK - 1) / BK;
 
     const rsrc4_t ra = make_rsrc4(A, span_bytes(M, K, lda));
-    const rsrc4_t rb = make_rsrc4(B, span_bytes(N, K, ldb));
+    const rsrc4_t rb = KN ? make_rsrc4(B, span_bytes(K, N, ldb))
+                          : make_rsrc4(B, span_bytes(N, K, ldb));
 
     // Lane l lands in row r0 + b*ROWS (r0 = 64w + l/KC) of block b at physical chunk
     // l % KC and fetches the logical chunk that the row's swizzle puts there (the swizzle
     // repeats every 16 rows, i.e. every two blocks).  The byte offset of each block's row
     // and chunk is computed once, out-of-range for rows past M (A) or N (B); a load adds
-    // the K position of its tile as the scalar offset.
+    // the K position of its tile as the scalar offset.  B [K,N]: lane l of load b lands in
+    // k row 16w + 2b + l/32 at physical chunk l % 32, out-of-range for columns past N.
     const int prow = lane / KC, pch = lane % KC;
     const int r0 = 64 * wave + prow;
     int kcol[2];
@@ -1273,15 +1297,23 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     // (b % 4) KiB, M0 moving on by 4 KiB after the fourth load: one M0 update per four
     // loads instead of one per load.  The offset adds to the global address as well, so
     // the stored offsets are that much lower; rows b * ROWS >= 8 apart keep them
-    // non-negative when lda, ldb >= 64 (the launcher's condition for OFFS).
+    // non-negative when lda, ldb >= 64 (the launcher's condition for OFFS); with B [K,N],
+    // whose rows of load b are 2b apart, when ldb >= 256.
     uint32_t a_vo[NB], b_vo[NB];
+    auto kn_row = [&](int b) { return 16 * wave + 2 * b + (lane >> 5); };
     auto set_offsets = [&]() {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const int ra = m0 + r0 + b * ROWS, rbn = n0 + r0 + b * ROWS;
             const uint32_t lo = OFFS ? (uint32_t)(b & 3) * 1024u : 0u;
             a_vo[b] = ra < M ? (uint32_t)(ra * lda + kcol[b & 1]) * 2u - lo : kOutOfRange;
-            b_vo[b] = rbn < N ? (uint32_t)(rbn * ldb + kcol[b & 1]) * 2u - lo : kOutOfRange;
+            if constexpr (KN) {
+                const int kr = kn_row(b);
+                const int n = n0 + 8 * ((lane & 31) ^ kn_swz<MF>(kr));
+                b_vo[b] = n < N ? (uint32_t)(kr * ldb + n) * 2u - lo : kOutOfRange;
+            } else {
+                b_vo[b] = rbn < N ? (uint32_t)(rbn * ldb + kcol[b & 1]) * 2u - lo : kOutOfRange;
+            }
         }
     };
     set_offsets();
@@ -1297,8 +1329,8 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     const uint32_t wave_at = (uint32_t)(64 * wave * BK * 2);
     // index among the whole tiles of walk step u >= toff
     auto full_index = [&](int u) { return nfull > 0 ? (u - toff + kofs) % nfull : 0; };
-    // For the tail tile's loads: chunks past K get out-of-range offsets (zeros), in place
-    // (set_offsets restores them afterwards).
+    // For the tail tile's loads: chunks past K (B [K,N]: k rows past K) get out-of-range
+    // offsets (zeros), in place (set_offsets restores them afterwards).
     auto mask_tail = [&]() {
         const int rem = K - nfull * BK;
         const bool ok0 = kcol[0] < rem, ok1 = kcol[1] < rem;
@@ -1306,31 +1338,41 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
         for (int b = 0; b < NB; ++b) {
             const bool ok = (b & 1) ? ok1 : ok0;
             a_vo[b] = ok ? a_vo[b] : kOutOfRange;
-            b_vo[b] = ok ? b_vo[b] : kOutOfRange;
+            if constexpr (KN)
+                b_vo[b] = kn_row(b) < rem ? b_vo[b] : kOutOfRange;
+            else
+                b_vo[b] = ok ? b_vo[b] : kOutOfRange;
         }
     };
     // Load b (< NB) of operand A (is_a) or B of the tile at K position k0, into the 1 KiB
     // block M0 points at (the loads of one operand's tile go out in block order, M0 set to
-    // the wave's first block beforehand).
+    // the wave's first block beforehand).  The K position goes in the scalar offset: k0
+    // elements along a row ([M,K] and [N,K] operands) or k0 rows of ldb elements (B [K,N]).
     auto load_b = [&](int k0, auto isac, auto bc, auto nopc) {
         constexpr bool is_a = decltype(isac)::value;
         constexpr int b = decltype(bc)::value;
         constexpr bool back_to_back = decltype(nopc)::value;   // no instruction between loads
+        const uint32_t soff = (!is_a && KN) ? (uint32_t)k0 * (uint32_t)ldb * 2u
+                                            : (uint32_t)k0 * 2u;
         if constexpr (OFFS) {
             // an s_nop after an M0 write: before block 0 of a back-to-back run (M0 was just
             // set), and before block 4 when it may directly follow block 3's M0 step
             constexpr bool nop = back_to_back ? (b & 3) == 0 : (b == 4 && TIGHT);
             dma16_off<POL, (b & 3) * 1024, nop, (b & 3) == 3 && b + 1 < NB>(
-                is_a ? ra : rb, is_a ? a_vo[b] : b_vo[b], (uint32_t)k0 * 2u);
+                is_a ? ra : rb, is_a ? a_vo[b] : b_vo[b], soff);
         } else {
-            dma16_next<POL, back_to_back>(is_a ? ra : rb, is_a ? a_vo[b] : b_vo[b],
-                                          (uint32_t)k0 * 2u);
+            dma16_next<POL, back_to_back>(is_a ? ra : rb, is_a ? a_vo[b] : b_vo[b], soff);
         }
     };
     // M0 for the wave's first block of slot i (A slots 0..SA-1, then the B slots), from
     // a base kept in a scalar register
     const uint32_t m0_base = __builtin_amdgcn_readfirstlane(lds0 + wave_at);
     auto m0_of = [&](auto i) { return m0_base + (uint32_t)(i * SLOT * 2); };
+    // Slot order in LDS: A slots then B slots; with B [K,N] the B slots come first, so
+    // that a transposing read's slot, sub-step and second-read offsets fit the 16-bit
+    // offset field on one base register per column block.
+    auto a_slot = [&](auto i) { return KN ? SB + i : i; };
+    auto b_slot = [&](auto j) { return KN ? j : SA + j; };
 
     // Operand reads: lane l takes row l % MF of an MFMA block, 16-byte chunk
     // s * CPS + l / MF of the sub-step (the swizzle of its row depends on l % 16 only).
@@ -1338,17 +1380,53 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     const int xr = swz<KC>(lr);
     const int a_row0 = (wm * 128 + lr) * BK;
     const int b_row0 = (wn * 128 + lr) * BK;
+    // B [K,N]: lane s of 16-lane group g reads 4 columns of one k row of the sub-step
+    // (and, in the second read, the row 4 on).  16x16x32: row 8g + s/4, columns
+    // 16j + 4(s%4) of the wave's 128; 32x32x16: row 8(g/2) + s/4, columns
+    // 32j + 16(g%2) + 4(s%4).  The row's swizzle is the lane's own, so block j sits at a
+    // lane-dependent place: one element offset per block; the slot, the sub-step and the
+    // second read add constants.
+    int kn_off[KN ? TN : 1];
+    if constexpr (KN) {
+        const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            if constexpr (MF == 16) {
+                const int p = (sl >> 2) + 4 * (g & 1);
+                kn_off[j] = (8 * g + (sl >> 2)) * BN +
+                            (16 * wn + 2 * (j ^ p) + ((sl & 3) >> 1)) * 8 + 4 * (sl & 1);
+            } else {
+                const int q = sl >> 2;
+                kn_off[j] = (8 * (g >> 1) + q) * BN +
+                            (16 * wn + 4 * (j ^ q) + 2 * (g & 1) + ((sl & 3) >> 1)) * 8 +
+                            4 * (sl & 1);
+            }
+        }
+    }
     u32x4 fa[2][TM], fb[2][TN];
     auto read_r = [&](const u16* as, const u16* bs, auto sc, auto bufc, auto rc) {
         constexpr int s = decltype(sc)::value;
         constexpr int bf = decltype(bufc)::value;
         constexpr int r = decltype(rc)::value;
         const int koff = ((s * CPS + kq) ^ xr) * 8;
-        if constexpr (r < TN)
-            fb[bf][r] = *reinterpret_cast<const u32x4*>(bs + b_row0 + r * MF * BK + koff);
-        else
+        if constexpr (r < TN) {
+            if constexpr (KN) {
+                typedef short s16x4 __attribute__((ext_vector_type(4)));
+                typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+                const u16* p0 = bs + kn_off[r] + s * KM * BN;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+                const s16x4 hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * BN));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+                const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+                fb[bf][r] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+            } else {
+                fb[bf][r] = *reinterpret_cast<const u32x4*>(bs + b_row0 + r * MF * BK + koff);
+            }
+        } else {
             fa[bf][r - TN] =
                 *reinterpret_cast<const u32x4*>(as + a_row0 + (r - TN) * MF * BK + koff);
+        }
     };
 
     acc_t acc[TM][TN];
@@ -1379,10 +1457,10 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     const uint32_t kwrap = (uint32_t)nfull * (uint32_t)(BK * 2);
     auto step = [&](auto ia, auto ia1, auto ia2, auto jb, auto jb1)
                     __attribute__((always_inline)) {
-        const u16* as = lds + ia * SLOT;
-        const u16* bs = lds + (SA + jb) * SLOT;
-        const u16* as1 = lds + ia1 * SLOT;
-        const u16* bs1 = lds + (SA + jb1) * SLOT;
+        const u16* as = lds + a_slot(ia) * SLOT;
+        const u16* bs = lds + b_slot(jb) * SLOT;
+        const u16* as1 = lds + a_slot(ia1) * SLOT;
+        const u16* bs1 = lds + b_slot(jb1) * SLOT;
         const uint32_t k2b = kwalk;                   // this step loads tile t+2 from here
         const int k2i = (int)(k2b / 2u);              // load_b takes elements
         static_for<0, KS>([&](auto subc) {
@@ -1395,14 +1473,14 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
             // the compiler's wait before each first use
             __builtin_amdgcn_s_waitcnt(0xC07F);
             if constexpr (s == 0) {
-                set_m0(m0_of(ia2));                 // the A loads of tile t+2
+                set_m0(m0_of(a_slot(ia2)));         // the A loads of tile t+2
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (last) {
                 static_for<0, PRE>([&](auto jc) { mma(std::integral_constant<int, cb>{}, jc); });
                 wait_vm_then_sync<NB>();       // tile t+1 landed; the A loads of t+2 may fly
                 __builtin_amdgcn_sched_barrier(0);
-                set_m0(m0_of(SA + jb));             // the B loads of tile t+2
+                set_m0(m0_of(b_slot(jb)));          // the B loads of tile t+2
                 __builtin_amdgcn_sched_barrier(0);
             }
             // the A loads of tile t+2 are dealt over the first SPA MFMA slots of the
@@ -1463,20 +1541,22 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
             if (tail_tile)
                 mask_tail();
             const int ku = tail_tile ? nfull * BK : full_index(u) * BK;
-            set_m0(m0_of((p0 + u) % SA));
+            set_m0(m0_of(a_slot((p0 + u) % SA)));
             static_for<0, NB>([&](auto bc) {
                 load_b(ku, std::true_type{}, bc, std::true_type{});
             });
-            set_m0(m0_of(SA + (p0 + u) % SB));
+            set_m0(m0_of(b_slot((p0 + u) % SB)));
             static_for<0, NB>([&](auto bc) {
                 load_b(ku, std::false_type{}, bc, std::true_type{});
             });
-            if (tail_tile)
+            // with no whole tile the later loads keep the mask: they then never reach
+            // past K, whatever the instruction offset adds
+            if (tail_tile && nfull > 0)
                 set_offsets();
         }
         wait_vm_then_sync<2 * NB>();              // tile 0 complete
         static_for<0, NR>([&](auto rc) {
-            read_r(lds + (p0 % SA) * SLOT, lds + (SA + p0 % SB) * SLOT,
+            read_r(lds + a_slot(p0 % SA) * SLOT, lds + b_slot(p0 % SB) * SLOT,
                    std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, rc);
         });
         kwalk = (uint32_t)full_index(2) * (uint32_t)(BK * 2);

@@ -38,6 +38,7 @@ struct VariantList {
 
 // One list per translation unit.
 VariantList variants_quad();
+VariantList variants_quad_kn();
 VariantList variants_pingpong_nk();
 VariantList variants_pingpong_other();
 VariantList variants_tiled();

@@ -51,7 +51,7 @@ const std::vector<const Variant*>& registry() {
         for (const tgemm_reg::VariantList& l :
              {tgemm_reg::variants_tiled(), tgemm_reg::variants_small(),
               tgemm_reg::variants_pingpong_nk(), tgemm_reg::variants_pingpong_other(),
-              tgemm_reg::variants_quad()})
+              tgemm_reg::variants_quad(), tgemm_reg::variants_quad_kn()})
             for (int i = 0; i < l.n; ++i)
                 v.push_back(&l.v[i]);
         const auto key = [](const Variant* x) {

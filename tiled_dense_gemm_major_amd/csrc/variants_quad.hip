@@ -1,4 +1,4 @@
-// libtgemm registry: the quadrant kernel's compiled configurations (A [M,K], B [N,K]).
+// libtgemm registry: the quadrant kernel's compiled configurations for A [M,K], B [N,K].
 #include "launch.hpp"
 
 namespace tgemm_reg {

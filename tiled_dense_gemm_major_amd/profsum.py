@@ -29,6 +29,7 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_dense_gemm_major_amd", "csrc", f)
                   for f in ("kernels.hpp", "launch.hpp", "registry.hpp", "variants_quad.hip",
+                            "variants_quad_kn.hip",
                             "tgemm.hip", "tile_table.inc")]
 
 

@@ -26,6 +26,7 @@ refreshes the library's frozen per-device table: every fast configuration is tim
 grid of shapes (A [M,K], B [N,K] and [K,N]; bf16, whose kernels are fp16's too), and the
 fastest per grid point is written as a C++ table that `choose` consults (the nearest grid
 point in log2 of M, N and K) before its fallback rules.  Rebuild the library afterwards.
+With --layouts kn (or nk) only that half is re-timed and the rest kept from the file.
 
   python -m tiled_dense_gemm_major_amd.sweep --attention [--repeat 20]
 
@@ -40,7 +41,7 @@ import json
 import sys
 
 from . import roofline
-from .inputs import BF16, WORKLOADS
+from .inputs import B_KN, B_NK, BF16, F16, WORKLOADS, Workload
 
 
 def time_launches(torch, fn, n, stream):
@@ -66,23 +67,49 @@ TABLE_N = (512, 1024, 2048, 4096, 8192)
 TABLE_K = (512, 1024, 2048, 4096, 8192)
 
 
+def read_table(path):
+    """Entries of an existing table file: (layout, mi, ni, ki) -> (config dict, us)."""
+    import re
+    names = ["kernel", "block_m", "block_n", "block_k", "waves_m", "waves_n", "stages",
+             "group_m", "split_k", "mfma"]
+    out = {}
+    with open(path) as f:
+        for m in re.finditer(r"\{(\d+), (\d+), (\d+), (\d+), \{([-\d, ]+)\}\},\s*//\s*([\d.]+)",
+                             f.read()):
+            key = tuple(int(m.group(i)) for i in range(1, 5))
+            out[key] = (dict(zip(names, (int(v) for v in m.group(5).split(",")))),
+                        float(m.group(6)))
+    return out
+
+
 def emit_table(tgemm, torch, np, args, stream, path):
-    """Time every fast configuration on the grid and write the fastest per point."""
+    """Time every fast configuration on the grid and write the fastest per point.  With
+    --layouts, only those B storages are timed; the other rows are kept from the file."""
     import datetime
-    from .inputs import B_KN, B_NK, Stream
+    from .inputs import B_KN, B_NK
+    layouts = [B_NK, B_KN] if not args.layouts else \
+        [B_KN if x == "kn" else B_NK for x in args.layouts.split(",")]
+    kept = read_table(path) if args.layouts else {}
     rows = []
     for layout in (B_NK, B_KN):
+        if layout not in layouts:
+            for mi in range(len(TABLE_M)):
+                for ni in range(len(TABLE_N)):
+                    for ki in range(len(TABLE_K)):
+                        d, us = kept[(layout, mi, ni, ki)]
+                        rows.append((layout, mi, ni, ki, tgemm.Config.from_dict(d), us))
+            continue
         cfgs = [c for c in tgemm.list_configs(BF16, layout)
                 if c.kernel not in (tgemm.KERNEL_GENERIC, tgemm.KERNEL_SPLITK)]
         for mi, M in enumerate(TABLE_M):
             for ni, N in enumerate(TABLE_N):
                 for ki, K in enumerate(TABLE_K):
-                    st = Stream(1000 + M + N + K)
-                    A = torch.from_numpy(st.matrix((M, K), BF16, "uniform").view(np.int16)
-                                         ).cuda().view(torch.bfloat16)
+                    # uniform[-1,1) operands drawn on the device (timing only)
+                    A = torch.empty((M, K), dtype=torch.bfloat16,
+                                    device="cuda").uniform_(-1.0, 1.0)
                     shape_b = (N, K) if layout == B_NK else (K, N)
-                    B = torch.from_numpy(st.matrix(shape_b, BF16, "uniform").view(np.int16)
-                                         ).cuda().view(torch.bfloat16)
+                    B = torch.empty(shape_b, dtype=torch.bfloat16,
+                                    device="cuda").uniform_(-1.0, 1.0)
                     C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
                     runs = []
                     for c in cfgs:
@@ -110,7 +137,9 @@ def emit_table(tgemm, torch, np, args, stream, path):
         "// Frozen per-device configuration table (generated; do not edit by hand).",
         f"// Device: {dev.name} ({getattr(dev, 'gcnArchName', 'gfx950')}), "
         f"{datetime.date.today().isoformat()}; bf16, warmup {args.warmup}, "
-        f"{max(1, args.rounds)} x {args.repeat} launches per configuration, medians.",
+        f"{max(1, args.rounds)} x {args.repeat} launches per configuration, medians"
+        + (f"; re-timed: {args.layouts} rows, the others kept from the previous table."
+           if args.layouts else "."),
         "// Regenerate: python -m tiled_dense_gemm_major_amd.sweep --emit-table <this file>",
         "static const int64_t kTableM[] = {" + ", ".join(map(str, TABLE_M)) + "};",
         "static const int64_t kTableN[] = {" + ", ".join(map(str, TABLE_N)) + "};",
@@ -170,6 +199,9 @@ def main(argv=None):
                     help="rotate over this many copies of A and B (HBM-resident operands)")
     ap.add_argument("--emit-table", default="",
                     help="time the grid and write the frozen configuration table here")
+    ap.add_argument("--layouts", default="",
+                    help="with --emit-table: re-time only these B storages (nk, kn), "
+                         "keeping the file's other rows")
     ap.add_argument("--attention", action="store_true",
                     help="time the attention forward pass on its workloads instead")
     ap.add_argument("--rounds", type=int, default=1,
@@ -180,6 +212,9 @@ def main(argv=None):
                     help="time only the table's choices (without and with a workspace)")
     ap.add_argument("--kernels", default="",
                     help="comma-separated kernel ids to time (default: every compiled one)")
+    ap.add_argument("--shapes", default="",
+                    help="extra products to time, comma-separated DTYPE:MxNxK:LAYOUT "
+                         "(e.g. bf16:8192x8192x8192:kn), inputs U[-1,1] from seed 0")
     args = ap.parse_args(argv)
 
     import numpy as np
@@ -204,8 +239,13 @@ def main(argv=None):
         emit_table(tgemm, torch, np, args, stream, args.emit_table)
         return
     best = {}
-    for name in args.workloads.split(","):
-        w = WORKLOADS[name]
+    todo = [(name, WORKLOADS[name]) for name in args.workloads.split(",") if name]
+    for spec in [x for x in args.shapes.split(",") if x]:
+        dt, mnk, lay = spec.split(":")
+        M, N, K = (int(v) for v in mnk.split("x"))
+        todo.append((spec, Workload(spec, BF16 if dt == "bf16" else F16, M, N, K,
+                                    B_KN if lay == "kn" else B_NK, "uniform", 0)))
+    for name, w in todo:
         A_bits, B_bits = w.generate()
         tdt = torch.bfloat16 if w.dtype == BF16 else torch.float16
         copies = max(1, args.cold)
