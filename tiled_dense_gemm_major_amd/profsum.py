@@ -10,6 +10,9 @@ average, median, min and max duration of the named kernel, over all dispatches (
 of `--range A:B`, in start order) and over the last `--timed` ones of them (the timed
 region of a benchmark run).
 
+`counters` reads counter runs (with their kernel traces) of the kernel and reports GPU
+cycles per launch, the engine clock, MFMA utilisation and the LDS bank-conflict share.
+
 `traffic` reads two counter runs of the kernel (`--pmc FETCH_SIZE`, `--pmc WRITE_SIZE`,
 KiB per dispatch) and the same two counters for a plain device copy of `--copy-bytes`
 bytes, scales each counter so that the copy reads and writes exactly its size, and
@@ -92,6 +95,60 @@ def counter_per_dispatch(directory: str, kernel: str, counter: str):
     return [per[k] for k in sorted(per)]
 
 
+def counter_instances(directory: str, kernel: str, counter: str):
+    """Per dispatch of the matching kernel: (sum over the counter's instances, number of
+    instances), in dispatch order."""
+    per, n = {}, {}
+    for r in _csv(directory, "counter_collection.csv"):
+        if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            k = int(r["Dispatch_Id"])
+            per[k] = per.get(k, 0.0) + float(r["Counter_Value"])
+            n[k] = n.get(k, 0) + 1
+    return [(per[k], n[k]) for k in sorted(per)]
+
+
+def cmd_counters(args):
+    """Counter runs of one kernel, joined with the kernel trace of the same runs: GPU
+    cycles per launch (GRBM_GUI_ACTIVE over the XCDs it sums), the engine clock over the
+    launch, MFMA
+    utilisation (SQ_VALU_MFMA_BUSY_CYCLES over cycles x SIMDs) and the LDS bank-conflict
+    share of LDS cycles (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE), medians over the
+    dispatches."""
+    out = {"kernel": args.kernel}
+    vals = {}
+    for d in args.dirs:
+        for c in ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT",
+                  "SQ_LDS_IDX_ACTIVE", "SQ_BUSY_CYCLES", "SQ_INSTS_LDS"):
+            try:
+                got = counter_instances(d, args.kernel, c)
+            except SystemExit:
+                continue
+            if got:
+                vals[c] = got
+                out[c + "_median"] = statistics.median(v for v, _ in got)
+                out[c + "_instances"] = got[0][1]
+        if "GRBM_GUI_ACTIVE" in vals and "trace_us_median" not in out:
+            try:
+                dur, _ = trace_durations_ns(d, args.kernel)
+            except SystemExit:
+                dur = []
+            if dur:
+                out["trace_us_median"] = statistics.median(dur) / 1e3
+                out["trace_dispatches"] = len(dur)
+    if "GRBM_GUI_ACTIVE" in vals:
+        g = statistics.median(v for v, _ in vals["GRBM_GUI_ACTIVE"])
+        cycles = g / args.xcds                  # summed over the XCDs, each counting
+        out["cycles_per_launch"] = cycles
+        if "trace_us_median" in out:
+            out["clock_mhz"] = cycles / out["trace_us_median"]
+        if "SQ_VALU_MFMA_BUSY_CYCLES_median" in out:
+            out["mfma_util"] = out["SQ_VALU_MFMA_BUSY_CYCLES_median"] / (cycles * args.simds)
+    if "SQ_LDS_BANK_CONFLICT_median" in out and out.get("SQ_LDS_IDX_ACTIVE_median"):
+        out["lds_bank_conflict_share"] = (out["SQ_LDS_BANK_CONFLICT_median"] /
+                                          out["SQ_LDS_IDX_ACTIVE_median"])
+    print(json.dumps(out, indent=1))
+
+
 def cmd_trace(args):
     d, name = trace_durations_ns(args.dir, args.kernel)
     if not d:
@@ -159,6 +216,12 @@ def main(argv=None):
     t.add_argument("--timed", type=int, default=0)
     t.add_argument("--range", default="",
                    help="A:B, only dispatches A..B-1 of the kernel (in start order)")
+    k = sub.add_parser("counters")
+    k.add_argument("dirs", nargs="+")
+    k.add_argument("--kernel", required=True)
+    k.add_argument("--simds", type=int, default=1024, help="SIMDs on the chip (256 CUs x 4)")
+    k.add_argument("--xcds", type=int, default=8,
+                   help="XCDs whose GRBM_GUI_ACTIVE the reported value sums")
     c = sub.add_parser("traffic")
     c.add_argument("--kernel", required=True)
     c.add_argument("--kernel-name", default="")
@@ -171,7 +234,7 @@ def main(argv=None):
     c.add_argument("--workload", default="")
     c.add_argument("--out", default="")
     args = ap.parse_args(argv)
-    {"trace": cmd_trace, "traffic": cmd_traffic}[args.cmd](args)
+    {"trace": cmd_trace, "traffic": cmd_traffic, "counters": cmd_counters}[args.cmd](args)
 
 
 if __name__ == "__main__":
