@@ -101,10 +101,14 @@ typedef enum {
     TGEMM_KERNEL_QUAD = 5,    /* A [M,K], B [N,K] only: one wave per SIMD, each owning a
                                  128x128 quadrant of a 256x256 tile; direct-to-LDS loads
                                  into three A and two B slots, one barrier per K step  */
-    TGEMM_KERNEL_SPLITK = 6   /* A [M,K], B [N,K] only, with a workspace: the K range of
+    TGEMM_KERNEL_SPLITK = 6,  /* A [M,K], B [N,K] only, with a workspace: the K range of
                                  each C tile split over split_k workgroups (direct-to-LDS
                                  ring), fp32 partial tiles in the workspace, summed in
                                  split order and cast by a second kernel               */
+    TGEMM_KERNEL_DIRECT = 7   /* A [M,K], B [N,K] only, small products: 32x32 C tiles, the
+                                 K range split over the split_k = 4 waves of a workgroup,
+                                 MFMA operands loaded from global memory straight into
+                                 registers, partial tiles added in LDS                  */
 } tgemm_kernel;
 
 /* One tile configuration.  block_m x block_n is the C tile of one workgroup, block_k

@@ -249,6 +249,26 @@ def test_quad_k_walk_exact(dev, orc, K, layout):
         assert np.array_equal(run(dtype, A, B, layout, cfg), want), (K, _cfg_id(cfg))
 
 
+# K walks of the direct kernel, bit for bit on exact inputs: its four waves take a
+# quarter each of the 16-wide k blocks, in batches of eight, so these K give waves with no
+# block, one batch, a partial batch, two and three batches, and a final block with only
+# its first half inside K.
+@pytest.mark.parametrize("K", [8, 16, 40, 72, 136, 512, 520, 1000, 1032, 2056])
+def test_direct_k_walk_exact(dev, orc, K):
+    from tiled_dense_gemm_major_amd import tgemm
+    dtype = F16
+    rng = np.random.default_rng(900 + K)
+    M, N = 200, 264          # 7 x 9 tiles of 32, ragged in both
+    A = _int_bits(dtype, rng.integers(-2, 3, (M, K)))
+    B = _int_bits(dtype, rng.integers(-2, 3, (N, K)))
+    want = orc.gemm(dtype, A, B, B_NK)
+    cfgs = [c for c in _configs(dtype, B_NK) if c.kernel == tgemm.KERNEL_DIRECT]
+    assert cfgs
+    for cfg in cfgs:
+        say(f"direct k walk K={K} (blocks {-(-K // 16)}) {_cfg_id(cfg)}")
+        assert np.array_equal(run(dtype, A, B, B_NK, cfg), want), (K, _cfg_id(cfg))
+
+
 # K walks of the skinny kernel, bit for bit on exact inputs: each of its 8 waves walks a
 # contiguous range of 64-wide chunks, starting at a chunk set by the workgroup's index
 # on its XCD, so with 33 column blocks and 2-6 chunks per wave the ragged last chunk is

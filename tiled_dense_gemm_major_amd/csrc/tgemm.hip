@@ -29,7 +29,7 @@ using tgemm_reg::kMaxSplits;
 using tgemm_reg::Variant;
 
 // Position of a kernel family in the listing order of one (A storage, B storage, dtype)
-// group: generic, tiled, direct-to-LDS ring, ping-pong, quad, skinny, split-K.
+// group: generic, tiled, direct-to-LDS ring, ping-pong, quad, skinny, split-K, direct.
 int family_rank(int kernel) {
     switch (kernel) {
     case TGEMM_KERNEL_GENERIC: return 0;
@@ -38,7 +38,8 @@ int family_rank(int kernel) {
     case TGEMM_KERNEL_PINGPONG: return 3;
     case TGEMM_KERNEL_QUAD: return 4;
     case TGEMM_KERNEL_SKINNY: return 5;
-    default: return 6;
+    case TGEMM_KERNEL_SPLITK: return 6;
+    default: return 7;
     }
 }
 
@@ -51,7 +52,8 @@ const std::vector<const Variant*>& registry() {
         for (const tgemm_reg::VariantList& l :
              {tgemm_reg::variants_tiled(), tgemm_reg::variants_small(),
               tgemm_reg::variants_pingpong_nk(), tgemm_reg::variants_pingpong_other(),
-              tgemm_reg::variants_quad(), tgemm_reg::variants_quad_kn()})
+              tgemm_reg::variants_quad(), tgemm_reg::variants_quad_kn(),
+              tgemm_reg::variants_direct()})
             for (int i = 0; i < l.n; ++i)
                 v.push_back(&l.v[i]);
         const auto key = [](const Variant* x) {
