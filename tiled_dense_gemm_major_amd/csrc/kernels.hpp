@@ -1170,7 +1170,9 @@ __device__ __forceinline__ void dma16_off(rsrc4_t r, uint32_t voff, uint32_t sof
 // ------------------------------------------------------------------------------------
 // Quadrant kernel (A [M,K]; B [N,K], or B [K,N] with LAYOUT_KN).
 //   One wave per SIMD: 4 waves in 2 x 2, each owning a 128 x 128 quadrant of the
-//   256 x 256 tile with all of its accumulators in registers.  Per MFMA this reads a
+//   256 x 256 tile with all of its accumulators in registers (BMT = 192: a 192 x 256
+//   tile of 96 x 128 quadrants, for grids that 256-row tiles leave short of the compute
+//   units; its A slots hold 192 rows, each wave loading 48 of them in 6 loads).  Per MFMA this reads a
 //   third fewer operand bytes from LDS than 8 waves of 128 x 64 (4 x 256 instead of
 //   8 x 192 tile rows per K step).  MF picks the matrix instruction: 16 (16x16x32,
 //   8 x 8 blocks per wave) or 32 (32x32x16, 4 x 4 blocks per wave).
@@ -1240,34 +1242,39 @@ __device__ __forceinline__ int kn_swz(int k) {
 }
 
 template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL, bool OFFS,
-          int LAYOUT = LAYOUT_NK>
+          int LAYOUT = LAYOUT_NK, int BMT = 256>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
                                amdgpu_waves_per_eu(1, 1)))
 gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
           int N, int K, int lda, int ldb, int ldc, int grid_m, int grid_n, int group_m) {
-    constexpr int BM = 256, BN = 256, BK = 64;
+    constexpr int BM = BMT, BN = 256, BK = 64;
     constexpr int KC = BK / 8;                 // 16-byte chunks per tile row
     constexpr int ROWS = 64 / KC;              // tile rows per 1 KiB load (8)
-    constexpr int SLOT = BM * BK;              // elements of one operand slot (32 KiB)
+    constexpr int SLOTA = BM * BK;             // elements of one A slot (32 or 24 KiB)
+    constexpr int SLOTB = BN * BK;             // elements of one B slot (32 KiB)
     constexpr int SA = 3, SB = 2;              // A and B slots
-    constexpr int NB = 64 / ROWS;              // loads per wave per operand per tile (8)
+    constexpr int NBA = BM / 4 / ROWS;         // A loads per wave per tile (8 or 6)
+    constexpr int NBB = 64 / ROWS;             // B loads per wave per tile (8)
     constexpr int KM = MF == 16 ? 32 : 16;     // k per MFMA
     constexpr int KS = BK / KM;                // sub-steps per tile
     constexpr int CPS = KM / 8;                // 16-byte chunks per sub-step
-    constexpr int TM = 128 / MF, TN = 128 / MF;
+    constexpr int WTM = BM / 2;                // a wave's rows of C (128 or 96)
+    constexpr int TM = WTM / MF, TN = 128 / MF;
     constexpr int NR = TM + TN;                // operand reads per sub-step
     constexpr int NM = TM * TN;                // MFMAs per sub-step
     using acc_t = std::conditional_t<MF == 16, f32x4, f32x16>;
     static_assert(MF == 16 || MF == 32, "MFMA 16x16x32 or 32x32x16");
     static_assert(KS % 2 == 0, "every step starts from operand buffer 0");
-    static_assert((SA + SB) * SLOT * 2 <= 160 * 1024, "LDS");
+    static_assert(BM == 256 || BM == 192, "256 or 192 tile rows");
+    static_assert(WTM % MF == 0 && NBA % 2 == 0, "whole MFMA blocks, block pairs");
+    static_assert((SA * SLOTA + SB * SLOTB) * 2 <= 160 * 1024, "LDS");
     static_assert(PRE >= 1 && PRE < NM && SPA >= 1 && SPB >= 1, "schedule");
     constexpr bool KN = LAYOUT == LAYOUT_KN;
     // Two loads of one operand can be adjacent (no instruction between them) when the A
     // loads outnumber their MFMA slots, or the B loads outnumber the reads dealt between.
-    constexpr bool TIGHT = NB > (SPA < (KS - 1) * NM ? SPA : (KS - 1) * NM) || NR < NB;
+    constexpr bool TIGHT = NBA > (SPA < (KS - 1) * NM ? SPA : (KS - 1) * NM) || NR < NBB;
 
-    __shared__ __attribute__((aligned(1024))) u16 lds[(SA + SB) * SLOT];
+    __shared__ __attribute__((aligned(1024))) u16 lds[SA * SLOTA + SB * SLOTB];
 
     int tm, tn;
     tile_of((int)blockIdx.x, grid_m, grid_n, group_m, tm, tn);
@@ -1288,7 +1295,8 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     // the K position of its tile as the scalar offset.  B [K,N]: lane l of load b lands in
     // k row 16w + 2b + l/32 at physical chunk l % 32, out-of-range for columns past N.
     const int prow = lane / KC, pch = lane % KC;
-    const int r0 = 64 * wave + prow;
+    const int r0 = (BM / 4) * wave + prow;     // A rows of block 0 of this wave
+    const int rb0 = 64 * wave + prow;          // B [N,K] rows of block 0
     int kcol[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p)
@@ -1299,14 +1307,19 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     // the stored offsets are that much lower; rows b * ROWS >= 8 apart keep them
     // non-negative when lda, ldb >= 64 (the launcher's condition for OFFS); with B [K,N],
     // whose rows of load b are 2b apart, when ldb >= 256.
-    uint32_t a_vo[NB], b_vo[NB];
+    uint32_t a_vo[NBA], b_vo[NBB];
     auto kn_row = [&](int b) { return 16 * wave + 2 * b + (lane >> 5); };
     auto set_offsets = [&]() {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const int ra = m0 + r0 + b * ROWS, rbn = n0 + r0 + b * ROWS;
+        for (int b = 0; b < NBA; ++b) {
+            const int ra = m0 + r0 + b * ROWS;
             const uint32_t lo = OFFS ? (uint32_t)(b & 3) * 1024u : 0u;
             a_vo[b] = ra < M ? (uint32_t)(ra * lda + kcol[b & 1]) * 2u - lo : kOutOfRange;
+        }
+#pragma unroll
+        for (int b = 0; b < NBB; ++b) {
+            const int rbn = n0 + rb0 + b * ROWS;
+            const uint32_t lo = OFFS ? (uint32_t)(b & 3) * 1024u : 0u;
             if constexpr (KN) {
                 const int kr = kn_row(b);
                 const int n = n0 + 8 * ((lane & 31) ^ kn_swz<MF>(kr));
@@ -1326,7 +1339,9 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     const int toff = tail ? 1 : 0;
     const int kofs = STAG ? (((int)blockIdx.x & 7) * nfull) >> 3 : 0;
     const uint32_t lds0 = lds_addr(lds);
-    const uint32_t wave_at = (uint32_t)(64 * wave * BK * 2);
+    // the wave's first 1 KiB block in an A slot and in a B slot
+    const uint32_t wave_a_at = (uint32_t)((BM / 4) * wave * BK * 2);
+    const uint32_t wave_b_at = (uint32_t)(64 * wave * BK * 2);
     // index among the whole tiles of walk step u >= toff
     auto full_index = [&](int u) { return nfull > 0 ? (u - toff + kofs) % nfull : 0; };
     // For the tail tile's loads: chunks past K (B [K,N]: k rows past K) get out-of-range
@@ -1335,16 +1350,18 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
         const int rem = K - nfull * BK;
         const bool ok0 = kcol[0] < rem, ok1 = kcol[1] < rem;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
+        for (int b = 0; b < NBA; ++b)
+            a_vo[b] = ((b & 1) ? ok1 : ok0) ? a_vo[b] : kOutOfRange;
+#pragma unroll
+        for (int b = 0; b < NBB; ++b) {
             const bool ok = (b & 1) ? ok1 : ok0;
-            a_vo[b] = ok ? a_vo[b] : kOutOfRange;
             if constexpr (KN)
                 b_vo[b] = kn_row(b) < rem ? b_vo[b] : kOutOfRange;
             else
                 b_vo[b] = ok ? b_vo[b] : kOutOfRange;
         }
     };
-    // Load b (< NB) of operand A (is_a) or B of the tile at K position k0, into the 1 KiB
+    // Load b (< NBA or NBB) of operand A (is_a) or B of the tile at K position k0, into the 1 KiB
     // block M0 points at (the loads of one operand's tile go out in block order, M0 set to
     // the wave's first block beforehand).  The K position goes in the scalar offset: k0
     // elements along a row ([M,K] and [N,K] operands) or k0 rows of ldb elements (B [K,N]).
@@ -1352,33 +1369,37 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
         constexpr bool is_a = decltype(isac)::value;
         constexpr int b = decltype(bc)::value;
         constexpr bool back_to_back = decltype(nopc)::value;   // no instruction between loads
+        constexpr int NBX = is_a ? NBA : NBB;
         const uint32_t soff = (!is_a && KN) ? (uint32_t)k0 * (uint32_t)ldb * 2u
                                             : (uint32_t)k0 * 2u;
         if constexpr (OFFS) {
             // an s_nop after an M0 write: before block 0 of a back-to-back run (M0 was just
             // set), and before block 4 when it may directly follow block 3's M0 step
             constexpr bool nop = back_to_back ? (b & 3) == 0 : (b == 4 && TIGHT);
-            dma16_off<POL, (b & 3) * 1024, nop, (b & 3) == 3 && b + 1 < NB>(
+            dma16_off<POL, (b & 3) * 1024, nop, (b & 3) == 3 && b + 1 < NBX>(
                 is_a ? ra : rb, is_a ? a_vo[b] : b_vo[b], soff);
         } else {
             dma16_next<POL, back_to_back>(is_a ? ra : rb, is_a ? a_vo[b] : b_vo[b], soff);
         }
     };
-    // M0 for the wave's first block of slot i (A slots 0..SA-1, then the B slots), from
-    // a base kept in a scalar register
-    const uint32_t m0_base = __builtin_amdgcn_readfirstlane(lds0 + wave_at);
-    auto m0_of = [&](auto i) { return m0_base + (uint32_t)(i * SLOT * 2); };
     // Slot order in LDS: A slots then B slots; with B [K,N] the B slots come first, so
     // that a transposing read's slot, sub-step and second-read offsets fit the 16-bit
-    // offset field on one base register per column block.
-    auto a_slot = [&](auto i) { return KN ? SB + i : i; };
-    auto b_slot = [&](auto j) { return KN ? j : SA + j; };
+    // offset field on one base register per column block.  a_at / b_at: a slot's first
+    // element.
+    auto a_at = [&](auto i) { return (KN ? SB * SLOTB : 0) + i * SLOTA; };
+    auto b_at = [&](auto j) { return (KN ? 0 : SA * SLOTA) + j * SLOTB; };
+    // M0 for the wave's first block of A slot i or B slot j, from bases kept in scalar
+    // registers
+    const uint32_t m0_a = __builtin_amdgcn_readfirstlane(lds0 + wave_a_at);
+    const uint32_t m0_b = __builtin_amdgcn_readfirstlane(lds0 + wave_b_at);
+    auto m0_of_a = [&](auto i) { return m0_a + (uint32_t)(a_at(i) * 2); };
+    auto m0_of_b = [&](auto j) { return m0_b + (uint32_t)(b_at(j) * 2); };
 
     // Operand reads: lane l takes row l % MF of an MFMA block, 16-byte chunk
     // s * CPS + l / MF of the sub-step (the swizzle of its row depends on l % 16 only).
     const int lr = lane % MF, kq = lane / MF;
     const int xr = swz<KC>(lr);
-    const int a_row0 = (wm * 128 + lr) * BK;
+    const int a_row0 = (wm * WTM + lr) * BK;
     const int b_row0 = (wn * 128 + lr) * BK;
     // B [K,N]: lane s of 16-lane group g reads 4 columns of one k row of the sub-step
     // (and, in the second read, the row 4 on).  16x16x32: row 8g + s/4, columns
@@ -1457,10 +1478,10 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     const uint32_t kwrap = (uint32_t)nfull * (uint32_t)(BK * 2);
     auto step = [&](auto ia, auto ia1, auto ia2, auto jb, auto jb1)
                     __attribute__((always_inline)) {
-        const u16* as = lds + a_slot(ia) * SLOT;
-        const u16* bs = lds + b_slot(jb) * SLOT;
-        const u16* as1 = lds + a_slot(ia1) * SLOT;
-        const u16* bs1 = lds + b_slot(jb1) * SLOT;
+        const u16* as = lds + a_at(ia);
+        const u16* bs = lds + b_at(jb);
+        const u16* as1 = lds + a_at(ia1);
+        const u16* bs1 = lds + b_at(jb1);
         const uint32_t k2b = kwalk;                   // this step loads tile t+2 from here
         const int k2i = (int)(k2b / 2u);              // load_b takes elements
         static_for<0, KS>([&](auto subc) {
@@ -1473,14 +1494,14 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
             // the compiler's wait before each first use
             __builtin_amdgcn_s_waitcnt(0xC07F);
             if constexpr (s == 0) {
-                set_m0(m0_of(a_slot(ia2)));         // the A loads of tile t+2
+                set_m0(m0_of_a(ia2));               // the A loads of tile t+2
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (last) {
                 static_for<0, PRE>([&](auto jc) { mma(std::integral_constant<int, cb>{}, jc); });
-                wait_vm_then_sync<NB>();       // tile t+1 landed; the A loads of t+2 may fly
+                wait_vm_then_sync<NBA>();      // tile t+1 landed; the A loads of t+2 may fly
                 __builtin_amdgcn_sched_barrier(0);
-                set_m0(m0_of(b_slot(jb)));          // the B loads of tile t+2
+                set_m0(m0_of_b(jb));                // the B loads of tile t+2
                 __builtin_amdgcn_sched_barrier(0);
             }
             // the A loads of tile t+2 are dealt over the first SPA MFMA slots of the
@@ -1488,7 +1509,7 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
             // loads of tile t+2) over the first SPB slots of each sub-step
             constexpr int PRE_SLOTS = (KS - 1) * NM;
             constexpr int SA_ = SPA < PRE_SLOTS ? SPA : PRE_SLOTS;
-            constexpr int NL = last ? NB : 0;
+            constexpr int NL = last ? NBB : 0;
             constexpr int NOPS = NR + NL;
             constexpr int SS = SPB < NM - J0 ? SPB : NM - J0;
             static_for<J0, NM>([&](auto jc) {
@@ -1496,7 +1517,7 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
                 mma(std::integral_constant<int, cb>{}, jc);
                 if constexpr (!last) {
                     constexpr int G = s * NM + J;     // slot index over the pre-barrier sub-steps
-                    static_for<deal<NB, SA_, G>::lo, deal<NB, SA_, G>::hi>([&](auto bc) {
+                    static_for<deal<NBA, SA_, G>::lo, deal<NBA, SA_, G>::hi>([&](auto bc) {
                         load_b(k2i, std::true_type{}, bc, std::false_type{});
                         __builtin_amdgcn_sched_barrier(0);
                     });
@@ -1541,12 +1562,12 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
             if (tail_tile)
                 mask_tail();
             const int ku = tail_tile ? nfull * BK : full_index(u) * BK;
-            set_m0(m0_of(a_slot((p0 + u) % SA)));
-            static_for<0, NB>([&](auto bc) {
+            set_m0(m0_of_a((p0 + u) % SA));
+            static_for<0, NBA>([&](auto bc) {
                 load_b(ku, std::true_type{}, bc, std::true_type{});
             });
-            set_m0(m0_of(b_slot((p0 + u) % SB)));
-            static_for<0, NB>([&](auto bc) {
+            set_m0(m0_of_b((p0 + u) % SB));
+            static_for<0, NBB>([&](auto bc) {
                 load_b(ku, std::false_type{}, bc, std::true_type{});
             });
             // with no whole tile the later loads keep the mask: they then never reach
@@ -1554,9 +1575,9 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
             if (tail_tile && nfull > 0)
                 set_offsets();
         }
-        wait_vm_then_sync<2 * NB>();              // tile 0 complete
+        wait_vm_then_sync<NBA + NBB>();           // tile 0 complete
         static_for<0, NR>([&](auto rc) {
-            read_r(lds + a_slot(p0 % SA) * SLOT, lds + b_slot(p0 % SB) * SLOT,
+            read_r(lds + a_at(p0 % SA), lds + b_at(p0 % SB),
                    std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, rc);
         });
         kwalk = (uint32_t)full_index(2) * (uint32_t)(BK * 2);
@@ -1589,9 +1610,9 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     // per lane, with the non-temporal hint (1-2 % faster than plain stores; storing
     // straight from the accumulators instead was 3 % slower).
     constexpr int RSE = 128 + 8;                   // staged row stride in elements
-    static_assert(4 * 128 * RSE <= (SA + SB) * SLOT, "C staging fits the LDS ring");
+    static_assert(4 * WTM * RSE <= SA * SLOTA + SB * SLOTB, "C staging fits the LDS ring");
     wait_vm_then_sync<0>();
-    u16* stage = lds + wave * 128 * RSE;
+    u16* stage = lds + wave * WTM * RSE;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -1611,10 +1632,10 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     const int sr = lane >> 4, sc = (lane & 15) * 8;
     const int n = n0 + wn * 128 + sc;
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
+    for (int q = 0; q < WTM / 4; ++q) {
         const int r = 4 * q + sr;
         const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * RSE + sc);
-        const int m = m0 + wm * 128 + r;
+        const int m = m0 + wm * WTM + r;
         if (m < M && n < N)     // non-temporal: C is written once and not read back here
             __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + (size_t)m * ldc + n));
     }

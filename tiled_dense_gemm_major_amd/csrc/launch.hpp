@@ -68,17 +68,18 @@ hipError_t launch_pingpong(const void* A, const void* B, void* C, int M, int N, 
     return hipGetLastError();
 }
 
-template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL, int L = 0>
+template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL, int L = 0,
+          int BM = 256>
 hipError_t launch_quad(const void* A, const void* B, void* C, int M, int N, int K, int lda,
                        int ldb, int ldc, int group_m, hipStream_t s) {
-    const int gm = cdiv(M, 256), gn = cdiv(N, 256);
+    const int gm = cdiv(M, BM), gn = cdiv(N, 256);
     // the instruction-offset form of the loads needs rows of at least 64 elements (B
     // [K,N]: 256, its loads' rows being only two apart)
     if (lda >= 64 && ldb >= (L == 0 ? 64 : 256))
-        hipLaunchKernelGGL((tgemm::gemm_quad<DT, MF, PRE, SPA, SPB, STAG, POL, true, L>),
+        hipLaunchKernelGGL((tgemm::gemm_quad<DT, MF, PRE, SPA, SPB, STAG, POL, true, L, BM>),
                            dim3((unsigned)(gm * gn)), dim3(256), 0, s, KARGS, gm, gn, group_m);
     else
-        hipLaunchKernelGGL((tgemm::gemm_quad<DT, MF, PRE, SPA, SPB, STAG, POL, false, L>),
+        hipLaunchKernelGGL((tgemm::gemm_quad<DT, MF, PRE, SPA, SPB, STAG, POL, false, L, BM>),
                            dim3((unsigned)(gm * gn)), dim3(256), 0, s, KARGS, gm, gn, group_m);
     return hipGetLastError();
 }
@@ -135,6 +136,14 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
         DT, 0, 1, tgemm_config{TGEMM_KERNEL_QUAD, 256, 256, 64, 2, 2, 5, G, 1, MF},        \
             &launch_quad<DT, MF, (MF == 16 ? 2 : 1), (MF == 16 ? 56 : 40),                 \
                          (MF == 16 ? 40 : 12), 1, 2, 1>                                    \
+    }
+// The quad kernel with 192-row tiles (waves of 96 x 128), either B storage L: for grids
+// that 256 x 256 tiles would leave short of the 256 compute units.
+#define QUAD192(DT, MF, L, G)                                                              \
+    Variant {                                                                              \
+        DT, 0, L, tgemm_config{TGEMM_KERNEL_QUAD, 192, 256, 64, 2, 2, 5, G, 1, MF},        \
+            &launch_quad<DT, MF, (MF == 16 ? 2 : 1), (MF == 16 ? 56 : 40),                 \
+                         (MF == 16 ? 40 : 12), 1, 2, L, 192>                               \
     }
 // Split-K over workgroups (registry entries carry split_k = 2; a call gives its own count).
 #define SPLITK(DT, BM, BN, BK, WM, WN, ST, G)                                              \
