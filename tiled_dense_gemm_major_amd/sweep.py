@@ -61,9 +61,11 @@ def summary(t):
     return t[len(t) // 2], t[len(t) // 10], t[(9 * len(t)) // 10]
 
 
-# The table's grid (powers of two, plus the small M of decode-like products).
-TABLE_M = (16, 64, 128, 256, 512, 1024, 2048, 4096, 8192)
-TABLE_N = (512, 1024, 2048, 4096, 8192)
+# The table's grid: powers of two and, for M and N, the points half-way between them in
+# log2 (x 1.5), where tiles of 192 rows or 128 columns can fill the chip better than
+# 256-wide ones; plus the small M of decode-like products.
+TABLE_M = (16, 64, 128, 256, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192)
+TABLE_N = (512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192)
 TABLE_K = (512, 1024, 2048, 4096, 8192)
 
 
