@@ -150,8 +150,7 @@ def test_strided_query_and_list(lib):
             kinds = {c.kernel for c in cfgs}
             assert {tgemm.KERNEL_GENERIC, tgemm.KERNEL_TILED, tgemm.KERNEL_PINGPONG} <= kinds
             big = tgemm.query_config(tgemm.BF16, 8192, 8192, 8192, b_layout, True, a_layout)
-            quad = a_layout == tgemm.A_MK
-            assert big.kernel == (tgemm.KERNEL_QUAD if quad else tgemm.KERNEL_PINGPONG)
+            assert big.kernel == tgemm.KERNEL_QUAD
             listed = {tuple(sorted(c.as_dict().items())) for c in cfgs}
             assert tuple(sorted(big.as_dict().items())) in listed
     # the skinny kernel reads A [M,K] and B [N,K] only

@@ -116,19 +116,22 @@ def test_strided_table_choice_any_alignment(dev, orc, dtype, a_layout, b_layout,
 
 @pytest.mark.parametrize("a_layout,b_layout", LAYOUTS)
 def test_strided_large_table_choice(dev, orc, a_layout, b_layout):
-    """The large-tile kernels (quad for A [M,K] with B [N,K], ping-pong for the other
-    storages) on padded rows, every element against the oracle."""
+    """The large-tile kernels (every quad configuration of the storage pair, and the
+    first ping-pong one) on padded rows, every element against the oracle."""
     from tiled_dense_gemm_major_amd import tgemm
     dtype = BF16
     M, N, K = 3584, 4096, 1000
-    quad = a_layout == A_MK and b_layout == B_NK
-    kind = tgemm.KERNEL_QUAD if quad else tgemm.KERNEL_PINGPONG
-    cfgs = [c for c in tgemm.list_configs(dtype, b_layout, a_layout) if c.kernel == kind]
-    assert cfgs, kind
+    listed = tgemm.list_configs(dtype, b_layout, a_layout)
+    cfgs = [c for c in listed if c.kernel == tgemm.KERNEL_QUAD]
+    cfgs += [c for c in listed if c.kernel == tgemm.KERNEL_PINGPONG][:1]
+    assert len(cfgs) >= 2
     A, Bn = _inputs(dtype, M, N, K, 900 + a_layout + 2 * b_layout)
-    say(f"strided large A{a_layout} B{b_layout} {M}x{N}x{K} {cfgs[0].as_dict()}")
-    got = run_strided(dtype, A, Bn, a_layout, b_layout, pads=(64, 8, 256), config=cfgs[0])
-    assert_parity(orc, dtype, K, got, orc.gemm(dtype, A, Bn, B_NK), "large")
+    want = orc.gemm(dtype, A, Bn, B_NK)
+    for cfg in cfgs + [None]:             # None: the library's own choice
+        say(f"strided large A{a_layout} B{b_layout} {M}x{N}x{K} "
+            f"{cfg.as_dict() if cfg is not None else 'table choice'}")
+        got = run_strided(dtype, A, Bn, a_layout, b_layout, pads=(64, 8, 256), config=cfg)
+        assert_parity(orc, dtype, K, got, want, "large")
 
 
 def test_strided_packed_matches_gemm_ex(dev, orc):
@@ -153,3 +156,26 @@ def test_strided_quad_kn_leading_dims(dev, orc, pads):
         say(f"strided quad [K,N] pads {pads} {cfg.as_dict()}")
         got = run_strided(BF16, A, Bn, A_MK, B_KN, pads=pads, config=cfg)
         assert_parity(orc, BF16, K, got, orc.gemm(BF16, A, Bn, B_NK), str(pads))
+
+
+@pytest.mark.parametrize("b_layout", [B_NK, B_KN])
+@pytest.mark.parametrize("K", [8, 200, 456, 1000])
+def test_strided_quad_km_k_walk_exact(dev, orc, b_layout, K):
+    """The quad kernel for A [K,M] on small-integer inputs (every partial sum exact): the
+    K tail (rows of the A slot past K), the six-step groups and row blocks past M, bit
+    for bit.  M = 200 with lda = 208 takes the M0-walk loads (lda < 256); M = 520 with
+    lda = 776 the instruction-offset ones."""
+    from tiled_dense_gemm_major_amd import tgemm
+    N = 776
+    cfgs = [c for c in tgemm.list_configs(BF16, b_layout, A_KM)
+            if c.kernel == tgemm.KERNEL_QUAD]
+    assert cfgs
+    for M, pads in [(200, (8, 0, 8)), (520, (256, 8, 0))]:
+        rng = np.random.default_rng(1300 + K + b_layout + M)
+        A = _int_bits(BF16, rng.integers(-2, 3, (M, K)))
+        Bn = _int_bits(BF16, rng.integers(-2, 3, (N, K)))
+        want = orc.gemm(BF16, A, Bn, B_NK)
+        for cfg in cfgs:
+            say(f"quad [K,M] M={M} K={K} B{b_layout} pads {pads} {cfg.as_dict()}")
+            got = run_strided(BF16, A, Bn, A_KM, b_layout, pads=pads, config=cfg)
+            assert np.array_equal(got, want), (M, K, pads)

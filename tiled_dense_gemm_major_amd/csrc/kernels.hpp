@@ -1172,7 +1172,10 @@ __device__ __forceinline__ void dma16_off(rsrc4_t r, uint32_t voff, uint32_t sof
 //   One wave per SIMD: 4 waves in 2 x 2, each owning a 128 x 128 quadrant of the
 //   256 x 256 tile with all of its accumulators in registers (BMT = 192: a 192 x 256
 //   tile of 96 x 128 quadrants, for grids that 256-row tiles leave short of the compute
-//   units; its A slots hold 192 rows, each wave loading 48 of them in 6 loads).  Per MFMA this reads a
+//   units; its A slots hold 192 rows, each wave loading 48 of them in 6 loads).  A
+//   stored [K,M] (ALAY = LAYOUT_KM, 256-row tiles): A slots of 64 k rows of 256 columns,
+//   loaded and read exactly as B [K,N] below (k rows, the same swizzle, transposing
+//   reads), the A operand of a lane being 8 consecutive k of one row m.  Per MFMA this reads a
 //   third fewer operand bytes from LDS than 8 waves of 128 x 64 (4 x 256 instead of
 //   8 x 192 tile rows per K step).  MF picks the matrix instruction: 16 (16x16x32,
 //   8 x 8 blocks per wave) or 32 (32x32x16, 4 x 4 blocks per wave).
@@ -1242,7 +1245,7 @@ __device__ __forceinline__ int kn_swz(int k) {
 }
 
 template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL, bool OFFS,
-          int LAYOUT = LAYOUT_NK, int BMT = 256>
+          int LAYOUT = LAYOUT_NK, int BMT = 256, int ALAY = LAYOUT_MK>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
                                amdgpu_waves_per_eu(1, 1)))
 gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
@@ -1270,6 +1273,8 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     static_assert((SA * SLOTA + SB * SLOTB) * 2 <= 160 * 1024, "LDS");
     static_assert(PRE >= 1 && PRE < NM && SPA >= 1 && SPB >= 1, "schedule");
     constexpr bool KN = LAYOUT == LAYOUT_KN;
+    constexpr bool AKM = ALAY == LAYOUT_KM;    // A stored [K,M]: A slots of k rows, like B [K,N]
+    static_assert(!AKM || BM == 256, "A [K,M]: 256-row tiles (512-byte k rows)");
     // Two loads of one operand can be adjacent (no instruction between them) when the A
     // loads outnumber their MFMA slots, or the B loads outnumber the reads dealt between.
     constexpr bool TIGHT = NBA > (SPA < (KS - 1) * NM ? SPA : (KS - 1) * NM) || NR < NBB;
@@ -1284,7 +1289,8 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     const int wm = wave >> 1, wn = wave & 1;
     const int nk = (K + BK - 1) / BK;
 
-    const rsrc4_t ra = make_rsrc4(A, span_bytes(M, K, lda));
+    const rsrc4_t ra = AKM ? make_rsrc4(A, span_bytes(K, M, lda))
+                           : make_rsrc4(A, span_bytes(M, K, lda));
     const rsrc4_t rb = KN ? make_rsrc4(B, span_bytes(K, N, ldb))
                           : make_rsrc4(B, span_bytes(N, K, ldb));
 
@@ -1314,7 +1320,13 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
         for (int b = 0; b < NBA; ++b) {
             const int ra = m0 + r0 + b * ROWS;
             const uint32_t lo = OFFS ? (uint32_t)(b & 3) * 1024u : 0u;
-            a_vo[b] = ra < M ? (uint32_t)(ra * lda + kcol[b & 1]) * 2u - lo : kOutOfRange;
+            if constexpr (AKM) {
+                const int kr = kn_row(b);
+                const int m = m0 + 8 * ((lane & 31) ^ kn_swz<MF>(kr));
+                a_vo[b] = m < M ? (uint32_t)(kr * lda + m) * 2u - lo : kOutOfRange;
+            } else {
+                a_vo[b] = ra < M ? (uint32_t)(ra * lda + kcol[b & 1]) * 2u - lo : kOutOfRange;
+            }
         }
 #pragma unroll
         for (int b = 0; b < NBB; ++b) {
@@ -1350,8 +1362,12 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
         const int rem = K - nfull * BK;
         const bool ok0 = kcol[0] < rem, ok1 = kcol[1] < rem;
 #pragma unroll
-        for (int b = 0; b < NBA; ++b)
-            a_vo[b] = ((b & 1) ? ok1 : ok0) ? a_vo[b] : kOutOfRange;
+        for (int b = 0; b < NBA; ++b) {
+            if constexpr (AKM)
+                a_vo[b] = kn_row(b) < rem ? a_vo[b] : kOutOfRange;
+            else
+                a_vo[b] = ((b & 1) ? ok1 : ok0) ? a_vo[b] : kOutOfRange;
+        }
 #pragma unroll
         for (int b = 0; b < NBB; ++b) {
             const bool ok = (b & 1) ? ok1 : ok0;
@@ -1371,7 +1387,8 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
         constexpr bool back_to_back = decltype(nopc)::value;   // no instruction between loads
         constexpr int NBX = is_a ? NBA : NBB;
         const uint32_t soff = (!is_a && KN) ? (uint32_t)k0 * (uint32_t)ldb * 2u
-                                            : (uint32_t)k0 * 2u;
+                              : (is_a && AKM) ? (uint32_t)k0 * (uint32_t)lda * 2u
+                                              : (uint32_t)k0 * 2u;
         if constexpr (OFFS) {
             // an s_nop after an M0 write: before block 0 of a back-to-back run (M0 was just
             // set), and before block 4 when it may directly follow block 3's M0 step
@@ -1407,23 +1424,40 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     // 32j + 16(g%2) + 4(s%4).  The row's swizzle is the lane's own, so block j sits at a
     // lane-dependent place: one element offset per block; the slot, the sub-step and the
     // second read add constants.
-    int kn_off[KN ? TN : 1];
-    if constexpr (KN) {
+    // The element offset of block j of a [K, 256] slot for the wave half h (wn or wm).
+    auto tr_off = [&](int j, int h) {
         const int g = lane >> 4, sl = lane & 15;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            if constexpr (MF == 16) {
-                const int p = (sl >> 2) + 4 * (g & 1);
-                kn_off[j] = (8 * g + (sl >> 2)) * BN +
-                            (16 * wn + 2 * (j ^ p) + ((sl & 3) >> 1)) * 8 + 4 * (sl & 1);
-            } else {
-                const int q = sl >> 2;
-                kn_off[j] = (8 * (g >> 1) + q) * BN +
-                            (16 * wn + 4 * (j ^ q) + 2 * (g & 1) + ((sl & 3) >> 1)) * 8 +
-                            4 * (sl & 1);
-            }
+        if constexpr (MF == 16) {
+            const int p = (sl >> 2) + 4 * (g & 1);
+            return (8 * g + (sl >> 2)) * 256 +
+                   (16 * h + 2 * (j ^ p) + ((sl & 3) >> 1)) * 8 + 4 * (sl & 1);
+        } else {
+            const int q = sl >> 2;
+            return (8 * (g >> 1) + q) * 256 +
+                   (16 * h + 4 * (j ^ q) + 2 * (g & 1) + ((sl & 3) >> 1)) * 8 + 4 * (sl & 1);
         }
+    };
+    int kn_off[KN ? TN : 1], km_off[AKM ? TM : 1];
+    if constexpr (KN) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            kn_off[j] = tr_off(j, wn);
     }
+    if constexpr (AKM) {               // A [K,M]: the same reads over the wave's rows
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            km_off[i] = tr_off(i, wm);
+    }
+    // two transposing reads (k rows and 4 rows on) of a [K, 256] slot, one MFMA operand
+    auto read_tr = [&](const u16* p0) {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * 256));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    };
     u32x4 fa[2][TM], fb[2][TN];
     auto read_r = [&](const u16* as, const u16* bs, auto sc, auto bufc, auto rc) {
         constexpr int s = decltype(sc)::value;
@@ -1431,22 +1465,16 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
         constexpr int r = decltype(rc)::value;
         const int koff = ((s * CPS + kq) ^ xr) * 8;
         if constexpr (r < TN) {
-            if constexpr (KN) {
-                typedef short s16x4 __attribute__((ext_vector_type(4)));
-                typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-                const u16* p0 = bs + kn_off[r] + s * KM * BN;
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-                const s16x4 hi =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * BN));
-                const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-                const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-                fb[bf][r] = u32x4{l2[0], l2[1], h2[0], h2[1]};
-            } else {
+            if constexpr (KN)
+                fb[bf][r] = read_tr(bs + kn_off[r] + s * KM * BN);
+            else
                 fb[bf][r] = *reinterpret_cast<const u32x4*>(bs + b_row0 + r * MF * BK + koff);
-            }
         } else {
-            fa[bf][r - TN] =
-                *reinterpret_cast<const u32x4*>(as + a_row0 + (r - TN) * MF * BK + koff);
+            if constexpr (AKM)
+                fa[bf][r - TN] = read_tr(as + km_off[r - TN] + s * KM * BM);
+            else
+                fa[bf][r - TN] =
+                    *reinterpret_cast<const u32x4*>(as + a_row0 + (r - TN) * MF * BK + koff);
         }
     };
 

@@ -69,18 +69,20 @@ hipError_t launch_pingpong(const void* A, const void* B, void* C, int M, int N, 
 }
 
 template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL, int L = 0,
-          int BM = 256>
+          int BM = 256, int AL = 0>
 hipError_t launch_quad(const void* A, const void* B, void* C, int M, int N, int K, int lda,
                        int ldb, int ldc, int group_m, hipStream_t s) {
     const int gm = cdiv(M, BM), gn = cdiv(N, 256);
-    // the instruction-offset form of the loads needs rows of at least 64 elements (B
-    // [K,N]: 256, its loads' rows being only two apart)
-    if (lda >= 64 && ldb >= (L == 0 ? 64 : 256))
-        hipLaunchKernelGGL((tgemm::gemm_quad<DT, MF, PRE, SPA, SPB, STAG, POL, true, L, BM>),
-                           dim3((unsigned)(gm * gn)), dim3(256), 0, s, KARGS, gm, gn, group_m);
+    // the instruction-offset form of the loads needs rows of at least 64 elements (an
+    // operand stored [K,*]: 256, its loads' rows being only two apart)
+    if (lda >= (AL == 0 ? 64 : 256) && ldb >= (L == 0 ? 64 : 256))
+        hipLaunchKernelGGL(
+            (tgemm::gemm_quad<DT, MF, PRE, SPA, SPB, STAG, POL, true, L, BM, AL>),
+            dim3((unsigned)(gm * gn)), dim3(256), 0, s, KARGS, gm, gn, group_m);
     else
-        hipLaunchKernelGGL((tgemm::gemm_quad<DT, MF, PRE, SPA, SPB, STAG, POL, false, L, BM>),
-                           dim3((unsigned)(gm * gn)), dim3(256), 0, s, KARGS, gm, gn, group_m);
+        hipLaunchKernelGGL(
+            (tgemm::gemm_quad<DT, MF, PRE, SPA, SPB, STAG, POL, false, L, BM, AL>),
+            dim3((unsigned)(gm * gn)), dim3(256), 0, s, KARGS, gm, gn, group_m);
     return hipGetLastError();
 }
 
@@ -144,6 +146,13 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
         DT, 0, L, tgemm_config{TGEMM_KERNEL_QUAD, 192, 256, 64, 2, 2, 5, G, 1, MF},        \
             &launch_quad<DT, MF, (MF == 16 ? 2 : 1), (MF == 16 ? 56 : 40),                 \
                          (MF == 16 ? 40 : 12), 1, 2, L, 192>                               \
+    }
+// The quad kernel for A stored [K,M] (transposing A reads), either B storage L.
+#define QUAD_KM(DT, MF, L, G)                                                              \
+    Variant {                                                                              \
+        DT, 1, L, tgemm_config{TGEMM_KERNEL_QUAD, 256, 256, 64, 2, 2, 5, G, 1, MF},        \
+            &launch_quad<DT, MF, (MF == 16 ? 2 : 1), (MF == 16 ? 56 : 40),                 \
+                         (MF == 16 ? 40 : 12), 1, 2, L, 256, 1>                            \
     }
 // Split-K over workgroups (registry entries carry split_k = 2; a call gives its own count).
 #define SPLITK(DT, BM, BN, BK, WM, WN, ST, G)                                              \

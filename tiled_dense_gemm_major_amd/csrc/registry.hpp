@@ -39,6 +39,7 @@ struct VariantList {
 // One list per translation unit.
 VariantList variants_quad();
 VariantList variants_quad_kn();
+VariantList variants_quad_km();
 VariantList variants_direct();
 VariantList variants_pingpong_nk();
 VariantList variants_pingpong_other();

@@ -215,8 +215,9 @@ def main(argv=None):
     ap.add_argument("--kernels", default="",
                     help="comma-separated kernel ids to time (default: every compiled one)")
     ap.add_argument("--shapes", default="",
-                    help="extra products to time, comma-separated DTYPE:MxNxK:LAYOUT "
-                         "(e.g. bf16:8192x8192x8192:kn), inputs U[-1,1] from seed 0")
+                    help="extra products to time, comma-separated DTYPE:MxNxK:LAYOUT[:km] "
+                         "(e.g. bf16:8192x8192x8192:kn; :km stores A as [K,M]), inputs "
+                         "U[-1,1] from seed 0")
     args = ap.parse_args(argv)
 
     import numpy as np
@@ -241,30 +242,46 @@ def main(argv=None):
         emit_table(tgemm, torch, np, args, stream, args.emit_table)
         return
     best = {}
-    todo = [(name, WORKLOADS[name]) for name in args.workloads.split(",") if name]
+    todo = [(name, WORKLOADS[name], 0) for name in args.workloads.split(",") if name]
     for spec in [x for x in args.shapes.split(",") if x]:
-        dt, mnk, lay = spec.split(":")
+        parts = spec.split(":")
+        dt, mnk, lay = parts[:3]
+        a_km = len(parts) > 3 and parts[3] == "km"      # A stored [K,M]
         M, N, K = (int(v) for v in mnk.split("x"))
         todo.append((spec, Workload(spec, BF16 if dt == "bf16" else F16, M, N, K,
-                                    B_KN if lay == "kn" else B_NK, "uniform", 0)))
-    for name, w in todo:
+                                    B_KN if lay == "kn" else B_NK, "uniform", 0),
+                     1 if a_km else 0))
+    for name, w, a_layout in todo:
         A_bits, B_bits = w.generate()
         tdt = torch.bfloat16 if w.dtype == BF16 else torch.float16
         copies = max(1, args.cold)
+        if a_layout:                                    # A stored [K,M]
+            A_bits = np.ascontiguousarray(A_bits.T)
         As = [torch.from_numpy(A_bits.view(np.int16)).cuda().view(tdt) for _ in range(copies)]
         Bs = [torch.from_numpy(B_bits.view(np.int16)).cuda().view(tdt) for _ in range(copies)]
         C = torch.empty((w.M, w.N), dtype=tdt, device="cuda")
         dname = "bf16" if w.dtype == BF16 else "f16"
         flops = roofline.gemm_flops(w.M, w.N, w.K)
         nbytes = roofline.compulsory_bytes(w.M, w.N, w.K)
-        table = tgemm.query_config(w.dtype, w.M, w.N, w.K, w.b_layout).as_dict()
+        table = tgemm.query_config(w.dtype, w.M, w.N, w.K, w.b_layout, True,
+                                   a_layout).as_dict()
         table_ws = tgemm.query_config_ws(w.dtype, w.M, w.N, w.K, w.b_layout)[0].as_dict()
         kernels = {int(x) for x in args.kernels.split(",") if x}
 
         runners = []
         ws_cfg, _ = tgemm.query_config_ws(w.dtype, w.M, w.N, w.K, w.b_layout)
-        for cfg in tgemm.list_configs(w.dtype, w.b_layout):
+        lda = w.M if a_layout else w.K
+        ldb = w.N if w.b_layout == B_KN else w.K
+        for cfg in tgemm.list_configs(w.dtype, w.b_layout, a_layout):
             if kernels and cfg.kernel not in kernels:
+                continue
+            if a_layout:                                # the general entry point
+                def go(i, c=cfg):
+                    tgemm.gemm_strided(w.dtype, w.M, w.N, w.K, As[i % copies], lda,
+                                       a_layout, Bs[i % copies], ldb, w.b_layout, C, w.N,
+                                       c, stream)
+                if not args.table_only or cfg.as_dict() == table:
+                    runners.append((cfg, go))
                 continue
             if cfg.kernel == tgemm.KERNEL_SPLITK:
                 # split counts: the table's (with a workspace) and its neighbours
