@@ -16,7 +16,7 @@ three fresh processes):
     exactly ``steps`` back-to-back launches after ``warmup`` untimed ones, with HIP events
     recorded on the launch stream (one pair around all of them, one pair around each)
     and device synchronisation on both sides; two clock stamps around the timed region
-    give the engine clock the chip held meanwhile;
+    give the engine clock each XCD held meanwhile (reported as their mean);
   * the first child also checks its first result against the CPU oracle on the leading
     rows of C (every column, the full K) before it times anything, and times that oracle
     run as the CPU baseline; a mismatch ends the benchmark with an error;
@@ -52,15 +52,16 @@ def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def measured_traffic():
+def measured_traffic(tile_config):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None when the
-    kernel sources changed since they were taken."""
+    kernel sources changed since they were taken or the table now picks another
+    configuration."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_digest") != kernel_digest():
+    if rec.get("kernel_digest") != kernel_digest() or rec.get("tile_config") != tile_config:
         return None
     return rec.get("bytes_per_launch")
 
@@ -145,31 +146,34 @@ def measure(args, A_bits, B_bits, verify: bool) -> dict:
 
     for _ in range(args.warmup):
         step()
-    stamps = torch.zeros(4, dtype=torch.int64, device="cuda")
+    stamps = torch.zeros((2, 16, 2), dtype=torch.int64, device="cuda")
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     per = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
-    tgemm.clock_stamp(stamps[0:2], stream)
+    tgemm.clock_stamp(stamps[0], stream)
     start.record(stream)
     for ev0, ev1 in per:
         ev0.record(stream)
         step()
         ev1.record(stream)
     stop.record(stream)
-    tgemm.clock_stamp(stamps[2:4], stream)
+    tgemm.clock_stamp(stamps[1], stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     per_ms = [a.elapsed_time(b) for a, b in per]
     st = stamps.cpu().tolist()
     wall_hz = tgemm.wall_clock_hz()
-    clock_mhz = ((st[2] - st[0]) / (st[3] - st[1]) * wall_hz / 1e6
-                 if st[3] > st[1] else None)
+    # per XCD: its engine cycles over the wall time between the two stamps
+    per_xcd = [(b[0] - a[0]) / (b[1] - a[1]) * wall_hz / 1e6
+               for a, b in zip(st[0], st[1]) if a[1] > 0 and b[1] > a[1]]
+    clock_mhz = sum(per_xcd) / len(per_xcd) if per_xcd else None
     out.update({
         "total_ms": total_ms,
         "per_launch_ms": per_ms,
         "clock_mhz": clock_mhz,
+        "clock_mhz_per_xcd": per_xcd,
         "tile_config": tgemm.query_config(w.dtype, w.M, w.N, w.K, w.b_layout).as_dict(),
         "device": torch.cuda.get_device_name(0),
     })
@@ -333,7 +337,8 @@ def report(args, w, results):
             "peak": peak,
             "unit": unit,
             "frac": achieved / peak,
-            "traffic": measured_traffic(),
+            "traffic": (measured_traffic(r["tile_config"])
+                        if args.workload == HEADLINE else None),
             "achieved_basis": "median process: 2MNK over the mean of per-launch HIP events",
         },
     }

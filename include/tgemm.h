@@ -272,16 +272,19 @@ int attn_fwd_f16(int64_t batch, int64_t seq, int64_t heads, int64_t dim, const v
                  const void* K, const void* V, void* O, int causal, void* stream);
 
 /*
- * Diagnostics for measurements: one lane on `stream` reads the device's shader-clock
- * counter (it advances once per engine clock cycle, so its rate follows the clock the
- * chip runs at) and its constant-rate wall clock, and writes them as two uint64 values
- * to out[0] and out[1].
- *   out    : device pointer to 16 bytes, 8-byte aligned; written when the stream reaches
- *            the stamp
+ * Diagnostics for measurements: a clock stamp on every XCD.  Each XCD (accelerator
+ * complex die) counts engine cycles on a counter of its own, which advances once per
+ * cycle of the clock that die runs at; the wall clock runs at a constant rate.  A small
+ * kernel on `stream` (64 one-wave workgroups, spread over the XCDs) writes, for XCD x,
+ * its engine-clock counter to out[2x] and the wall clock to out[2x + 1].
+ *   out    : device pointer to 16 x 2 uint64 (256 bytes), 8-byte aligned; a slot whose
+ *            XCD ran none of the workgroups keeps its previous contents, so clear it
+ *            first (slots of XCDs the device does not have are never written)
  *   stream : hipStream_t (NULL = null stream)
- * Two stamps around a stretch of work on one stream give its average engine clock:
- * (out1[0] - out0[0]) / (out1[1] - out0[1]) * (tgemm_wall_clock_hz).  Returns TGEMM_OK,
- * TGEMM_ERR_NULL_POINTER, TGEMM_ERR_ALIGNMENT or TGEMM_ERR_LAUNCH.  Nothing is allocated.
+ * Two stamps around a stretch of work on one stream give each XCD's average engine
+ * clock: (after[2x] - before[2x]) / (after[2x+1] - before[2x+1]) * tgemm_wall_clock_hz.
+ * Returns TGEMM_OK, TGEMM_ERR_NULL_POINTER, TGEMM_ERR_ALIGNMENT or TGEMM_ERR_LAUNCH.
+ * Nothing is allocated.
  */
 int tgemm_clock_stamp(void* out, void* stream);
 

@@ -388,13 +388,18 @@ int list(int dtype, int a_layout, int b_layout, tgemm_config* out, int capacity)
     return count;
 }
 
-// One lane reads the engine-clock counter and the constant-rate wall clock.
+// Each XCD counts engine cycles on its own counter, so a stamp is taken on every XCD:
+// 64 one-wave workgroups (workgroups go to the XCDs in turn), each of whose first lanes
+// writes its XCD's engine-clock counter and the chip's constant-rate wall clock to slot
+// (XCD id) of out[16][2].
 __global__ void __launch_bounds__(64) clock_stamp_kernel(unsigned long long* out) {
     if (threadIdx.x == 0) {
+        unsigned xcc;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
         const unsigned long long c = (unsigned long long)clock64();
         const unsigned long long w = (unsigned long long)wall_clock64();
-        out[0] = c;
-        out[1] = w;
+        out[2 * (xcc & 15)] = c;
+        out[2 * (xcc & 15) + 1] = w;
     }
 }
 
@@ -408,7 +413,7 @@ int tgemm_clock_stamp(void* out, void* stream) {
     if ((uintptr_t)out % 8 != 0)
         return TGEMM_ERR_ALIGNMENT;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(clock_stamp_kernel, dim3(1), dim3(64), 0,
+    hipLaunchKernelGGL(clock_stamp_kernel, dim3(64), dim3(64), 0,
                        static_cast<hipStream_t>(stream),
                        static_cast<unsigned long long*>(out));
     return hipGetLastError() == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;

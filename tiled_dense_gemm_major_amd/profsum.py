@@ -30,10 +30,13 @@ import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+# The sources that define the quad kernel for A [M,K], B [N,K], its compiled
+# configurations and the table that picks one: counter figures taken on other sources
+# are stale.  (The traffic record also stores the configuration it was taken on, which
+# the benchmark compares with the table's current choice.)
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_dense_gemm_major_amd", "csrc", f)
                   for f in ("kernels.hpp", "launch.hpp", "registry.hpp", "variants_quad.hip",
-                            "variants_quad_kn.hip",
-                            "tgemm.hip", "tile_table.inc")]
+                            "tile_table.inc")]
 
 
 def kernel_digest() -> str:
@@ -174,6 +177,13 @@ def cmd_trace(args):
     print(json.dumps(out, indent=1))
 
 
+def _table_choice(shape: str):
+    """The library's configuration for "dtype,M,N,K,b_layout" (host-only query)."""
+    from . import tgemm
+    dt, m, n, k, lay = (int(x) for x in shape.split(","))
+    return tgemm.query_config(dt, m, n, k, lay).as_dict()
+
+
 def cmd_traffic(args):
     fetch = counter_per_dispatch(args.fetch, args.kernel, "FETCH_SIZE")
     write = counter_per_dispatch(args.write, args.kernel, "WRITE_SIZE")
@@ -189,6 +199,7 @@ def cmd_traffic(args):
         "kernel": args.kernel_name or args.kernel,
         "workload": args.workload,
         "kernel_digest": kernel_digest(),
+        "tile_config": _table_choice(args.shape) if args.shape else None,
         "bytes_per_launch": fb + wb,
         "fetch_bytes_per_launch": fb,
         "write_bytes_per_launch": wb,
@@ -232,6 +243,8 @@ def main(argv=None):
     c.add_argument("--copy-kernel", default="copyBuffer")
     c.add_argument("--copy-bytes", type=int, required=True)
     c.add_argument("--workload", default="")
+    c.add_argument("--shape", default="",
+                   help="dtype,M,N,K,b_layout of the product: its configuration is recorded")
     c.add_argument("--out", default="")
     args = ap.parse_args(argv)
     {"trace": cmd_trace, "traffic": cmd_traffic, "counters": cmd_counters}[args.cmd](args)
