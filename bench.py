@@ -146,7 +146,7 @@ def measure(args, A_bits, B_bits, verify: bool) -> dict:
 
     for _ in range(args.warmup):
         step()
-    stamps = torch.zeros((2, 16, 2), dtype=torch.int64, device="cuda")
+    stamps = torch.zeros((2, tgemm.CLOCK_STAMP_SLOTS, 2), dtype=torch.int64, device="cuda")
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     per = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -165,15 +165,18 @@ def measure(args, A_bits, B_bits, verify: bool) -> dict:
     per_ms = [a.elapsed_time(b) for a, b in per]
     st = stamps.cpu().tolist()
     wall_hz = tgemm.wall_clock_hz()
-    # per XCD: its engine cycles over the wall time between the two stamps
-    per_xcd = [(b[0] - a[0]) / (b[1] - a[1]) * wall_hz / 1e6
-               for a, b in zip(st[0], st[1]) if a[1] > 0 and b[1] > a[1]]
-    clock_mhz = sum(per_xcd) / len(per_xcd) if per_xcd else None
+    # per compute unit stamped both times: its engine cycles over the wall time between
+    # the stamps; the chip's figure is their median
+    per_cu = sorted((b[0] - a[0]) / (b[1] - a[1]) * wall_hz / 1e6
+                    for a, b in zip(st[0], st[1]) if a[1] > 0 and b[1] > a[1])
+    clock_mhz = per_cu[len(per_cu) // 2] if per_cu else None
+    clock_spread = ([per_cu[0], per_cu[len(per_cu) // 10], per_cu[-1 - len(per_cu) // 10],
+                     per_cu[-1], len(per_cu)] if per_cu else None)
     out.update({
         "total_ms": total_ms,
         "per_launch_ms": per_ms,
         "clock_mhz": clock_mhz,
-        "clock_mhz_per_xcd": per_xcd,
+        "clock_spread": clock_spread,
         "tile_config": tgemm.query_config(w.dtype, w.M, w.N, w.K, w.b_layout).as_dict(),
         "device": torch.cuda.get_device_name(0),
     })
@@ -208,8 +211,11 @@ def run_children(args, inputs_dir: str):
             sys.exit(1)
         r = json.loads(lines[-1][len(CHILD_TAG):])
         ms = r["total_ms"] / args.steps
+        sp = r.get("clock_spread")
+        spread = (f" (compute units: min {sp[0]:.0f}, p10 {sp[1]:.0f}, p90 {sp[2]:.0f}, "
+                  f"max {sp[3]:.0f} MHz over {sp[4]})" if sp else "")
         log(f"process {i + 1}: {ms * 1e3:.1f} us/step, engine clock "
-            f"{r['clock_mhz'] or 0:.0f} MHz over the timed region")
+            f"{r['clock_mhz'] or 0:.0f} MHz over the timed region{spread}")
         results.append(r)
     return results
 
@@ -324,6 +330,11 @@ def report(args, w, results):
             "tflops_per_process": rates,
             "engine_clock_mhz_per_process": [x["clock_mhz"] for x in results],
             "engine_clock_mhz": r["clock_mhz"],
+            "engine_clock_basis": "median over the compute units stamped before and after "
+                                  "the timed region: engine cycles over wall time",
+            "engine_clock_spread_mhz": dict(zip(("min", "p10", "p90", "max", "units"),
+                                                r["clock_spread"])) if r.get("clock_spread")
+            else None,
             "median_launch_ms": per_sorted[len(per_sorted) // 2],
             "p10_launch_ms": per_sorted[len(per_sorted) // 10],
             "p90_launch_ms": per_sorted[min(len(per_sorted) - 1, (9 * len(per_sorted)) // 10)],

@@ -272,20 +272,23 @@ int attn_fwd_f16(int64_t batch, int64_t seq, int64_t heads, int64_t dim, const v
                  const void* K, const void* V, void* O, int causal, void* stream);
 
 /*
- * Diagnostics for measurements: a clock stamp on every XCD.  Each XCD (accelerator
- * complex die) counts engine cycles on a counter of its own, which advances once per
- * cycle of the clock that die runs at; the wall clock runs at a constant rate.  A small
- * kernel on `stream` (64 one-wave workgroups, spread over the XCDs) writes, for XCD x,
- * its engine-clock counter to out[2x] and the wall clock to out[2x + 1].
- *   out    : device pointer to 16 x 2 uint64 (256 bytes), 8-byte aligned; a slot whose
- *            XCD ran none of the workgroups keeps its previous contents, so clear it
- *            first (slots of XCDs the device does not have are never written)
+ * Diagnostics for measurements: clock stamps on every compute unit.  Engine cycles are
+ * counted per compute unit (counters of different units are not aligned with each
+ * other), at the clock of the die the unit sits on; the wall clock runs at a constant
+ * rate.  A small kernel on `stream` (4096 one-wave workgroups, about 16 per compute unit)
+ * writes, for the compute unit with slot s = 256 * XCD id + (hardware id bits 8..15),
+ * its engine-clock counter to out[2s] and the wall clock to out[2s + 1].
+ *   out    : device pointer to 4096 x 2 uint64 (64 KiB), 16-byte aligned; a slot whose
+ *            compute unit ran none of the workgroups keeps its previous contents, so
+ *            clear it first (slots no compute unit maps to are never written)
  *   stream : hipStream_t (NULL = null stream)
- * Two stamps around a stretch of work on one stream give each XCD's average engine
- * clock: (after[2x] - before[2x]) / (after[2x+1] - before[2x+1]) * tgemm_wall_clock_hz.
+ * Two stamps around a stretch of work on one stream give each compute unit's average
+ * engine clock: (after[2s] - before[2s]) / (after[2s+1] - before[2s+1]) *
+ * tgemm_wall_clock_hz, for the slots written by both.
  * Returns TGEMM_OK, TGEMM_ERR_NULL_POINTER, TGEMM_ERR_ALIGNMENT or TGEMM_ERR_LAUNCH.
  * Nothing is allocated.
  */
+#define TGEMM_CLOCK_STAMP_SLOTS 4096
 int tgemm_clock_stamp(void* out, void* stream);
 
 /* The rate of the wall clock that tgemm_clock_stamp reads, in Hz, for the current

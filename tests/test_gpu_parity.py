@@ -250,9 +250,9 @@ def test_quad_k_walk_exact(dev, orc, K, layout):
 
 
 # K walks of the direct kernel, bit for bit on exact inputs: its four waves take a
-# quarter each of the 16-wide k blocks, in batches of eight, so these K give waves with no
-# block, one batch, a partial batch, two and three batches, and a final block with only
-# its first half inside K.
+# quarter each of the 16-wide k blocks, in batches of eight (four for 128-row tiles), so
+# these K give waves with no block, one batch, a partial batch, odd and even numbers of
+# batches, and a final block with only its first half inside K.
 @pytest.mark.parametrize("K", [8, 16, 40, 72, 136, 512, 520, 1000, 1032, 2056])
 def test_direct_k_walk_exact(dev, orc, K):
     from tiled_dense_gemm_major_amd import tgemm

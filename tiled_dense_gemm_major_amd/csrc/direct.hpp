@@ -67,18 +67,19 @@ gemm_direct(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    if (batches > 0)
-        load(I0{}, 0);
-    for (int j = 0; j < batches; j += 2) {
-        if (j + 1 < batches)
-            load(I1{}, j + 1);
+    // Pairs of batches with no branch inside (a branch there makes the compiler copy the
+    // accumulators out of and back into their registers every pass); a batch past the
+    // wave's list loads zeros without touching memory.
+    load(I0{}, 0);
+    int j = 0;
+    for (; j + 2 <= batches; j += 2) {
+        load(I1{}, j + 1);
         mul(I0{});
-        if (j + 1 < batches) {
-            if (j + 2 < batches)
-                load(I0{}, j + 2);
-            mul(I1{});
-        }
+        load(I0{}, j + 2);
+        mul(I1{});
     }
+    if (j < batches)                           // an odd last batch, in buffer 0
+        mul(I0{});
 
     // lane l holds C row m0 + l % 32 and, for element v, column
     // n0 + 8 (v / 4) + 4 (l / 32) + v % 4: four runs of 4 consecutive columns, the g-th

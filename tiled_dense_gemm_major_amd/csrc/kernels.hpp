@@ -1228,7 +1228,7 @@ template <int NL, int NR>
 constexpr int op_kind(int o) {
     int loads = 0;
     for (int p = 0; p <= o; ++p) {
-        const bool is_load = loads < NL && p == loads * (NL + NR) / NL;
+        const bool is_load = loads < NL && p == loads * (NL + NR) / (NL > 0 ? NL : 1);
         if (p == o)
             return is_load ? loads : -1 - (o - loads);
         loads += is_load;
@@ -1389,14 +1389,20 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
         const uint32_t soff = (!is_a && KN) ? (uint32_t)k0 * (uint32_t)ldb * 2u
                               : (is_a && AKM) ? (uint32_t)k0 * (uint32_t)lda * 2u
                                               : (uint32_t)k0 * 2u;
+        static_assert(b < NBX, "block of the operand's tile");
+        uint32_t vo;
+        if constexpr (is_a)
+            vo = a_vo[b];
+        else
+            vo = b_vo[b];
         if constexpr (OFFS) {
             // an s_nop after an M0 write: before block 0 of a back-to-back run (M0 was just
             // set), and before block 4 when it may directly follow block 3's M0 step
             constexpr bool nop = back_to_back ? (b & 3) == 0 : (b == 4 && TIGHT);
             dma16_off<POL, (b & 3) * 1024, nop, (b & 3) == 3 && b + 1 < NBX>(
-                is_a ? ra : rb, is_a ? a_vo[b] : b_vo[b], soff);
+                is_a ? ra : rb, vo, soff);
         } else {
-            dma16_next<POL, back_to_back>(is_a ? ra : rb, is_a ? a_vo[b] : b_vo[b], soff);
+            dma16_next<POL, back_to_back>(is_a ? ra : rb, vo, soff);
         }
     };
     // Slot order in LDS: A slots then B slots; with B [K,N] the B slots come first, so

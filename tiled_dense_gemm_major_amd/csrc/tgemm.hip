@@ -388,18 +388,25 @@ int list(int dtype, int a_layout, int b_layout, tgemm_config* out, int capacity)
     return count;
 }
 
-// Each XCD counts engine cycles on its own counter, so a stamp is taken on every XCD:
-// 64 one-wave workgroups (workgroups go to the XCDs in turn), each of whose first lanes
-// writes its XCD's engine-clock counter and the chip's constant-rate wall clock to slot
-// (XCD id) of out[16][2].
+// The engine-cycle counter is not one counter per chip, nor even per XCD: stamps of the
+// same XCD taken on different compute units disagree.  So stamps are kept per compute
+// unit: 4096 one-wave workgroups (about 16 per compute unit), each of whose first lanes
+// writes its compute unit's engine-clock counter and the chip's constant-rate wall clock,
+// as one 16-byte store, to slot (XCD id, hardware id bits 8..15: CU, SH and SE) of
+// out[16 * 256][2].
+constexpr int kStampSlots = 16 * 256;
+constexpr int kStampBlocks = 4096;
+
 __global__ void __launch_bounds__(64) clock_stamp_kernel(unsigned long long* out) {
     if (threadIdx.x == 0) {
-        unsigned xcc;
+        unsigned xcc, hw;
         asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-        const unsigned long long c = (unsigned long long)clock64();
-        const unsigned long long w = (unsigned long long)wall_clock64();
-        out[2 * (xcc & 15)] = c;
-        out[2 * (xcc & 15) + 1] = w;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+        const unsigned slot = (xcc & 15) * 256 + ((hw >> 8) & 255);
+        ulonglong2 v;
+        v.x = (unsigned long long)clock64();
+        v.y = (unsigned long long)wall_clock64();
+        reinterpret_cast<ulonglong2*>(out)[slot] = v;
     }
 }
 
@@ -410,10 +417,10 @@ extern "C" {
 int tgemm_clock_stamp(void* out, void* stream) {
     if (!out)
         return TGEMM_ERR_NULL_POINTER;
-    if ((uintptr_t)out % 8 != 0)
+    if ((uintptr_t)out % 16 != 0)
         return TGEMM_ERR_ALIGNMENT;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(clock_stamp_kernel, dim3(64), dim3(64), 0,
+    hipLaunchKernelGGL(clock_stamp_kernel, dim3(kStampBlocks), dim3(64), 0,
                        static_cast<hipStream_t>(stream),
                        static_cast<unsigned long long*>(out));
     return hipGetLastError() == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;

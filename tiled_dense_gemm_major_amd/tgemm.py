@@ -16,6 +16,7 @@ A_MK, A_KM = 0, 1
  KERNEL_SPLITK, KERNEL_DIRECT) = range(8)
 
 SCRATCH_BYTES = 16 << 20    # the fixed per-GPU scratch of gemm_ex_noalloc
+CLOCK_STAMP_SLOTS = 4096    # compute-unit slots of one clock stamp (2 int64 each)
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtgemm.so")
@@ -33,7 +34,7 @@ __all__ = ["F16", "BF16", "B_NK", "B_KN", "A_MK", "A_KM", "KERNEL_GENERIC", "KER
            "KERNEL_DIRECT",
            "LIB_PATH", "EXPORTS", "TGemmError", "Config", "load", "status_string", "gemm_f16",
            "gemm_bf16", "gemm_ex", "gemm_ex_ws", "gemm_ex_noalloc", "gemm_strided",
-           "query_config", "SCRATCH_BYTES",
+           "query_config", "SCRATCH_BYTES", "CLOCK_STAMP_SLOTS",
            "query_config_packed", "query_config_ws", "workspace_size", "list_configs",
            "attn_fwd_f16", "version", "gemm", "clock_stamp", "wall_clock_hz"]
 
@@ -234,8 +235,11 @@ def attn_fwd_f16(batch, seq, heads, dim, Q, K, V, O, causal=True, stream=None):
 
 
 def clock_stamp(out, stream=None):
-    """Enqueue a (engine-clock counter, wall clock) stamp into ``out`` (a device tensor of
-    at least two int64, or an address)."""
+    """Enqueue per-compute-unit (engine-clock counter, wall clock) stamps into ``out`` (a
+    zeroed device tensor of CLOCK_STAMP_SLOTS x 2 int64, 16-byte aligned, or an
+    address)."""
+    if hasattr(out, "numel") and out.numel() < 2 * CLOCK_STAMP_SLOTS:
+        raise ValueError(f"clock_stamp needs {2 * CLOCK_STAMP_SLOTS} int64, got {out.numel()}")
     _check(load().tgemm_clock_stamp(_addr(out), _stream(stream)), "tgemm_clock_stamp")
 
 
