@@ -98,24 +98,30 @@ typedef enum {
     TGEMM_KERNEL_PINGPONG = 4,/* 8 waves, two per SIMD, alternating between operand fetch
                                  and back-to-back MFMAs half a period apart; direct-to-LDS
                                  loads; [K,N] B and [K,M] A through transposing reads    */
-    TGEMM_KERNEL_QUAD = 5,    /* A [M,K], B [N,K] only: one wave per SIMD, each owning a
-                                 128x128 quadrant of a 256x256 tile; direct-to-LDS loads
-                                 into three A and two B slots, one barrier per K step  */
+    TGEMM_KERNEL_QUAD = 5,    /* one wave per SIMD, each owning a 128x128 quadrant of a
+                                 256x256 tile (or 96x128 of 192x256); direct-to-LDS loads
+                                 into three A and two B slots, one barrier per K step;
+                                 [K,N] B and [K,M] A through transposing reads          */
     TGEMM_KERNEL_SPLITK = 6,  /* A [M,K], B [N,K] only, with a workspace: the K range of
                                  each C tile split over split_k workgroups (direct-to-LDS
                                  ring), fp32 partial tiles in the workspace, summed in
                                  split order and cast by a second kernel               */
-    TGEMM_KERNEL_DIRECT = 7   /* A [M,K], B [N,K] only, small products: 32x32 C tiles, the
+    TGEMM_KERNEL_DIRECT = 7,  /* A [M,K], B [N,K] only, small products: 32x32 C tiles, the
                                  K range split over the split_k = 4 waves of a workgroup,
                                  MFMA operands loaded from global memory straight into
                                  registers, partial tiles added in LDS                  */
+    TGEMM_KERNEL_QUAD_SPLITK = 8 /* A [M,K], with a workspace: the quad kernel's 256x256
+                                 tiles, the K range of each split over split_k
+                                 workgroups, fp32 partial tiles in the workspace, summed
+                                 in split order and cast by a second kernel            */
 } tgemm_kernel;
 
 /* One tile configuration.  block_m x block_n is the C tile of one workgroup, block_k
  * the K step, waves_m x waves_n the wavefront grid inside the workgroup (64 lanes each),
  * stages the LDS buffers (QUAD: operand slots of block_m x block_k elements, three for
  * A tiles and two for B tiles), group_m the tile rows of one launch-order group,
- * split_k the number of waves (SKINNY) or workgroups (SPLITK, 2..64, chosen per call)
+ * split_k the number of waves (SKINNY) or workgroups (SPLITK and QUAD_SPLITK, 2..64,
+ * chosen per call)
  * that share one C tile's K range (else 1), and mfma the matrix instruction's block
  * size: 32 (32x32x16) or 16 (16x16x32). */
 typedef struct {
@@ -157,7 +163,8 @@ int gemm_ex(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const voi
 
 /*
  * gemm_ex with a workspace lent by the caller, for configurations that need one
- * (TGEMM_KERNEL_SPLITK: split_k * m * n * 4 bytes of fp32 partial tiles).  Split-K over
+ * (TGEMM_KERNEL_SPLITK and TGEMM_KERNEL_QUAD_SPLITK: split_k * m * n * 4 bytes of fp32
+ * partial tiles).  Split-K over
  * workgroups follows "Tiling a matmul", section "Where it breaks": a product with few
  * output tiles (small or skinny) leaves compute units idle unless K is split.
  *   workspace       : device pointer, 16-byte aligned, not overlapping A, B or C; its
@@ -166,8 +173,8 @@ int gemm_ex(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const voi
  *                     this call (two calls in flight on one workspace race)
  *   workspace_bytes : its size in bytes (>= 0)
  *   cfg             : NULL = the table's choice given a workspace (see
- *                     tgemm_query_config_ws), else as for gemm_ex; a SPLITK configuration
- *                     names its split count in split_k
+ *                     tgemm_query_config_ws), else as for gemm_ex; a split-K configuration
+ *                     (SPLITK, QUAD_SPLITK) names its split count in split_k
  * Errors as gemm_ex, plus TGEMM_ERR_WORKSPACE (workspace NULL or smaller than the
  * configuration needs), TGEMM_ERR_ALIGNMENT (workspace not 16-byte aligned) and
  * TGEMM_ERR_ALIASING (workspace overlapping an operand).  A configuration that needs no
@@ -186,9 +193,11 @@ int gemm_ex_ws(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const 
  * allocated by the call (no hipMalloc, no hipFree); the first call on a device looks up
  * that device's scratch address and keeps it.
  *   arguments as for gemm_ex; cfg == NULL takes the table's choice given a workspace (as
- *   gemm_ex_ws does), which for every shape needs at most TGEMM_SCRATCH_BYTES
+ *   gemm_ex_ws does) when its partial tiles fit TGEMM_SCRATCH_BYTES, else the
+ *   choice without a workspace
  * Errors as gemm_ex_ws, plus TGEMM_ERR_SCRATCH when an explicit configuration needs more
- * than TGEMM_SCRATCH_BYTES (split_k * m * n * 4 bytes for SPLITK) and TGEMM_ERR_DEVICE
+ * than TGEMM_SCRATCH_BYTES (split_k * m * n * 4 bytes for the split-K kernels) and
+ * TGEMM_ERR_DEVICE
  * when the scratch address cannot be found.  Results are bit for bit those of gemm_ex_ws
  * with the same configuration.  Every call on one GPU uses that GPU's one scratch array:
  * nothing in it needs to start at zero (each call overwrites what it reads), but two
@@ -243,7 +252,8 @@ int tgemm_list_configs_ex(int dtype, int a_layout, int b_layout, tgemm_config* o
 int tgemm_query_config_ws(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
                           int aligned, tgemm_config* out, int64_t* workspace_bytes);
 
-/* Workspace bytes a configuration needs for an m x n product (0 for all but SPLITK).
+/* Workspace bytes a configuration needs for an m x n product (0 for all but SPLITK and
+ * QUAD_SPLITK).
  * Host-only. */
 int tgemm_workspace_size(int64_t m, int64_t n, const tgemm_config* cfg, int64_t* bytes);
 

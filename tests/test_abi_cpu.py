@@ -111,7 +111,7 @@ def test_list_configs(lib):
             kinds = {c.kernel for c in cfgs}
             assert tgemm.KERNEL_GENERIC in kinds and tgemm.KERNEL_TILED in kinds
             for c in cfgs:
-                if c.kernel == tgemm.KERNEL_QUAD:
+                if c.kernel in (tgemm.KERNEL_QUAD, tgemm.KERNEL_QUAD_SPLITK):
                     # operand slots of block_m x block_k (three A, two B)
                     assert c.stages * max(c.block_m, c.block_n) * c.block_k * 2 <= 160 * 1024
                 elif c.kernel != tgemm.KERNEL_GENERIC:
@@ -174,9 +174,28 @@ def test_query_config_ws_and_workspace_size(lib):
         cfg, nbytes = tgemm.query_config_ws(tgemm.BF16, *shape)
         assert cfg.as_dict() == tgemm.query_config(tgemm.BF16, *shape).as_dict()
         assert nbytes == 0
-    # B [K,N] is not split
+    # B [K,N] with few rows is not split
     cfg, nbytes = tgemm.query_config_ws(tgemm.BF16, 64, 8192, 8192, tgemm.B_KN)
     assert cfg.kernel != tgemm.KERNEL_SPLITK and nbytes == 0
+    # at most 64 tiles of 256 x 256 and a long K: the quad kernel in split-K mode, about
+    # one workgroup per compute unit, K ranges at least 1024 deep, either B storage
+    for shape, layout, splits, mfma in [((2048, 2048, 16384), tgemm.B_NK, 4, 16),
+                                        ((1024, 2048, 8192), tgemm.B_NK, 8, 16),
+                                        ((1536, 1536, 12288), tgemm.B_NK, 7, 16),
+                                        ((512, 4096, 8192), tgemm.B_NK, 8, 16),
+                                        ((2048, 2048, 8192), tgemm.B_KN, 4, 32),
+                                        ((1024, 2048, 4096), tgemm.B_NK, 4, 16),
+                                        ((1536, 2048, 8192), tgemm.B_NK, 5, 16),
+                                        ((1024, 1024, 8192), tgemm.B_NK, 8, 16)]:
+        cfg, nbytes = tgemm.query_config_ws(tgemm.BF16, *shape, layout)
+        assert (cfg.kernel, cfg.split_k, cfg.mfma) == (tgemm.KERNEL_QUAD_SPLITK, splits,
+                                                       mfma), shape
+        assert nbytes == splits * shape[0] * shape[1] * 4
+    # more tiles, too short a K, or too little work: the plain choice
+    for shape in [(2048, 4096, 8192), (1024, 1024, 2048), (1024, 1024, 4096), (768, 768, 8192),
+                  (256, 256, 1024), (2048, 2048, 4096)]:
+        cfg, nbytes = tgemm.query_config_ws(tgemm.BF16, *shape)
+        assert cfg.kernel != tgemm.KERNEL_QUAD_SPLITK and nbytes == 0, shape
     # splits between 2 and 64
     assert tgemm.workspace_size(10, 24, _splitk(64)) == 64 * 10 * 24 * 4
     for bad in (1, 65):

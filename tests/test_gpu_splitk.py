@@ -7,7 +7,7 @@ import pytest
 
 from tests.gpu_util import (assert_parity, from_dev, require_gpu, say,
                             tdtype, to_dev, torch)
-from tiled_dense_gemm_major_amd.inputs import BF16, B_NK, F16, WORKLOADS, Stream
+from tiled_dense_gemm_major_amd.inputs import BF16, B_KN, B_NK, F16, WORKLOADS, Stream
 
 pytestmark = pytest.mark.gpu
 
@@ -170,3 +170,96 @@ def test_splitk_one_workspace_many_shapes(dev, orc):
                              B_NK, _splitk(sk))
             torch.cuda.synchronize()
             assert_parity(orc, BF16, K, from_dev(C), want, f"{M}x{N}x{K} x{sk}")
+
+
+# ---------------------------------------------------------------------------------------
+# The quad kernel in split-K mode (TGEMM_KERNEL_QUAD_SPLITK): 256x256 tiles, each K range
+# of kc (a multiple of 64) walked by the unchanged quad K walk on shifted operands, fp32
+# partial tiles, the same fixed-order reduction.
+# ---------------------------------------------------------------------------------------
+def _quad_split(layout, splits):
+    from tiled_dense_gemm_major_amd import tgemm
+    return tgemm.Config(kernel=tgemm.KERNEL_QUAD_SPLITK, block_m=256, block_n=256, block_k=64,
+                        waves_m=2, waves_n=2, stages=5, group_m=4, split_k=splits,
+                        mfma=16 if layout == B_NK else 32)
+
+
+def _run_quad_split(dtype, A, B, layout, splits, guard=1024):
+    """C from gemm_ex_ws with the quad split-K kernel; the workspace is pre-filled with a
+    NaN pattern and has a guard band after the bytes the configuration needs."""
+    from tiled_dense_gemm_major_amd import tgemm
+    M, K = A.shape
+    N = B.shape[0] if layout == B_NK else B.shape[1]
+    cfg = _quad_split(layout, splits)
+    need = tgemm.workspace_size(M, N, cfg)
+    assert need == splits * M * N * 4
+    ws = torch.full(((need + guard) // 4,), -1, dtype=torch.int32, device="cuda")
+    C = torch.full((M, N), 0x7E00, dtype=torch.int16, device="cuda").view(tdtype(dtype))
+    tgemm.gemm_ex_ws(dtype, M, N, K, to_dev(A, dtype), to_dev(B, dtype), C, ws, need, layout,
+                     cfg)
+    torch.cuda.synchronize()
+    assert np.all(ws.cpu().numpy()[need // 4:] == -1), "workspace written past its size"
+    return from_dev(C)
+
+
+def _layout_inputs(dtype, M, N, K, layout, seed, ints=False):
+    if ints:
+        rng = np.random.default_rng(seed)
+        A = _int_bits(dtype, rng.integers(-2, 3, (M, K)))
+        B = _int_bits(dtype, rng.integers(-2, 3, (N, K) if layout == B_NK else (K, N)))
+        return A, B
+    s = Stream(seed)
+    return (s.matrix((M, K), dtype, "uniform"),
+            s.matrix((N, K) if layout == B_NK else (K, N), dtype, "uniform"))
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("layout", [B_NK, B_KN])
+@pytest.mark.parametrize("shape", [(600, 536, 1000), (300, 520, 4104), (257, 264, 328),
+                                   (64, 1024, 2048)])
+def test_quad_split_ragged(dev, orc, dtype, layout, shape):
+    """Ragged tiles, a K tail in the last range, and split counts that leave the last
+    range short or (for the short K) several ranges empty."""
+    M, N, K = shape
+    A, B = _layout_inputs(dtype, M, N, K, layout, 500 + M + N + K + layout)
+    want = orc.gemm(dtype, A, B, layout)
+    for splits in (2, 3, 5, 16):
+        say(f"quad split-K {dtype} layout {layout} {shape} splits {splits}")
+        got = _run_quad_split(dtype, A, B, layout, splits)
+        assert_parity(orc, dtype, K, got, want, f"quad split-K {shape} x{splits}")
+
+
+@pytest.mark.parametrize("layout", [B_NK, B_KN])
+@pytest.mark.parametrize("K", [8, 64, 200, 1000, 1032, 4104])
+def test_quad_split_exact_ints(dev, orc, layout, K):
+    """Small-integer inputs: every partial sum exact, so any split gives the oracle's
+    bits (ranges with no whole tile, only a tail, or nothing at all included)."""
+    dtype = BF16
+    M, N = 520, 392
+    A, B = _layout_inputs(dtype, M, N, K, layout, 77 + K + layout, ints=True)
+    want = orc.gemm(dtype, A, B, layout)
+    for splits in (2, 4, 7, 64):
+        say(f"quad split-K exact layout {layout} K={K} splits {splits}")
+        got = _run_quad_split(dtype, A, B, layout, splits)
+        assert np.array_equal(got, want), (K, splits)
+
+
+def test_quad_split_repeat_launches_bitwise_identical(dev, orc):
+    from tiled_dense_gemm_major_amd import tgemm
+    M, N, K = 1024, 768, 8192
+    A, B = _inputs(BF16, M, N, K, 29)
+    Ad, Bd = to_dev(A, BF16), to_dev(B, BF16)
+    cfg = _quad_split(B_NK, 4)
+    need = tgemm.workspace_size(M, N, cfg)
+    ws = torch.empty((need // 4,), dtype=torch.int32, device="cuda")
+    C0 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    tgemm.gemm_ex_ws(BF16, M, N, K, Ad, Bd, C0, ws, need, B_NK, cfg)
+    torch.cuda.synchronize()
+    ref = from_dev(C0)
+    assert_parity(orc, BF16, K, ref, orc.gemm(BF16, A, B, B_NK), "quad split-K")
+    say("quad split-K repeat launches")
+    C = torch.empty_like(C0)
+    for _ in range(10):
+        tgemm.gemm_ex_ws(BF16, M, N, K, Ad, Bd, C, ws, need, B_NK, cfg)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(C), ref)

@@ -1244,12 +1244,16 @@ __device__ __forceinline__ int kn_swz(int k) {
     return MF == 16 ? 2 * ((k & 3) + 4 * ((k >> 3) & 1)) : 4 * (k & 3);
 }
 
-template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL, bool OFFS,
-          int LAYOUT = LAYOUT_NK, int BMT = 256, int ALAY = LAYOUT_MK>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
-                               amdgpu_waves_per_eu(1, 1)))
-gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
-          int N, int K, int lda, int ldb, int ldc, int grid_m, int grid_n, int group_m) {
+// The body of the quad kernels.  SPLIT: split-K mode, the workgroups of grid row
+// z = blockIdx.y walking only K range [z kc, (z + 1) kc) (kc a multiple of 64) and
+// storing their fp32 partial tiles to plane z of W (W[z][m][n], rows of N floats)
+// instead of casting to C; W and kc are unused otherwise.
+template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL, bool OFFS, int LAYOUT,
+          int BMT, int ALAY, bool SPLIT>
+__device__ __attribute__((always_inline)) inline void
+quad_body(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
+          int N, int K, int lda, int ldb, int ldc, int grid_m, int grid_n, int group_m,
+          float* __restrict__ W, int kc) {
     constexpr int BM = BMT, BN = 256, BK = 64;
     constexpr int KC = BK / 8;                 // 16-byte chunks per tile row
     constexpr int ROWS = 64 / KC;              // tile rows per 1 KiB load (8)
@@ -1280,6 +1284,17 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     constexpr bool TIGHT = NBA > (SPA < (KS - 1) * NM ? SPA : (KS - 1) * NM) || NR < NBB;
 
     __shared__ __attribute__((aligned(1024))) u16 lds[SA * SLOTA + SB * SLOTB];
+
+    if constexpr (SPLIT) {
+        // this workgroup's K range as a product of its own: the operands start at its
+        // first k, and K is the range's length (the last range may hold a partial tile
+        // or, with more ranges than K needs, nothing)
+        const int k0 = (int)blockIdx.y * kc;
+        const int kend = K < k0 + kc ? K : k0 + kc;
+        K = kend > k0 ? kend - k0 : 0;
+        A += AKM ? (size_t)k0 * (size_t)lda : (size_t)k0;
+        B += KN ? (size_t)k0 * (size_t)ldb : (size_t)k0;
+    }
 
     int tm, tn;
     tile_of((int)blockIdx.x, grid_m, grid_n, group_m, tm, tn);
@@ -1636,6 +1651,29 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
         wait_vm<0>();                              // the trailing zero loads
     }
 
+    if constexpr (SPLIT) {
+        // The fp32 partial tile, straight from the accumulators: a lane's four
+        // consecutive columns of one row are one 16-byte store (16 rows of 64 bytes per
+        // instruction), into plane blockIdx.y of W.
+        float* plane = W + (size_t)blockIdx.y * (size_t)M * (size_t)N;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int m = m0 + wm * WTM + i * MF + lr;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                for (int g = 0; g < (MF == 16 ? 1 : 4); ++g) {
+                    const int n = n0 + wn * 128 + j * MF + (MF == 16 ? 4 * kq : 8 * g + 4 * kq);
+                    const f32x4 v = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1],
+                                     acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    if (m < M && n < N)
+                        *reinterpret_cast<f32x4*>(plane + (size_t)m * N + n) = v;
+                }
+            }
+        }
+        return;
+    }
+
     // Epilogue: one cast per value.  A lane holds groups of four consecutive columns of a
     // row, which would leave each store as 16 scattered 32-byte pieces; instead each wave
     // stages its 128 x 128 block in LDS (the ring is free once every wave's loads have
@@ -1673,6 +1711,31 @@ gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
         if (m < M && n < N)     // non-temporal: C is written once and not read back here
             __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + (size_t)m * ldc + n));
     }
+}
+
+template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL, bool OFFS,
+          int LAYOUT = LAYOUT_NK, int BMT = 256, int ALAY = LAYOUT_MK>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
+                               amdgpu_waves_per_eu(1, 1)))
+gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
+          int N, int K, int lda, int ldb, int ldc, int grid_m, int grid_n, int group_m) {
+    quad_body<DT, MF, PRE, SPA, SPB, STAG, POL, OFFS, LAYOUT, BMT, ALAY, false>(
+        A, B, C, M, N, K, lda, ldb, ldc, grid_m, grid_n, group_m, nullptr, 0);
+}
+
+// Split-K over workgroups with the quad kernel ("Tiling a matmul", section "Where it
+// breaks": a grid of few tiles with a long K leaves compute units idle; splitting K
+// gives them work): grid (tiles, splits), each workgroup one tile over one K range of
+// kc, its fp32 partial tile to W[z]; splitk_reduce adds the planes in split order.
+template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL, bool OFFS,
+          int LAYOUT = LAYOUT_NK>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
+                               amdgpu_waves_per_eu(1, 1)))
+gemm_quad_split(const u16* __restrict__ A, const u16* __restrict__ B, int M, int N, int K,
+                int lda, int ldb, int grid_m, int grid_n, int group_m, float* __restrict__ W,
+                int kc) {
+    quad_body<DT, MF, PRE, SPA, SPB, STAG, POL, OFFS, LAYOUT, 256, LAYOUT_MK, true>(
+        A, B, nullptr, M, N, K, lda, ldb, N, grid_m, grid_n, group_m, W, kc);
 }
 
 // ------------------------------------------------------------------------------------

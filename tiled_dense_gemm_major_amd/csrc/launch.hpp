@@ -86,6 +86,35 @@ hipError_t launch_quad(const void* A, const void* B, void* C, int M, int N, int 
     return hipGetLastError();
 }
 
+// The quad kernel in split-K mode: grid (tiles, splits), each split a whole number of
+// 64-wide K steps (the last one what remains), then the fixed-order reduction.
+template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL, int L = 0>
+hipError_t launch_quad_split(const void* A, const void* B, void* C, int M, int N, int K,
+                             int lda, int ldb, int ldc, int group_m, int splits, void* ws,
+                             hipStream_t s) {
+    const int gm = cdiv(M, 256), gn = cdiv(N, 256);
+    const int kc = cdiv(cdiv(K, splits), 64) * 64;
+    float* W = static_cast<float*>(ws);
+    const auto a = static_cast<const tgemm::u16*>(A);
+    const auto b = static_cast<const tgemm::u16*>(B);
+    const dim3 grid((unsigned)(gm * gn), (unsigned)splits);
+    if (lda >= 64 && ldb >= (L == 0 ? 64 : 256))
+        hipLaunchKernelGGL((tgemm::gemm_quad_split<DT, MF, PRE, SPA, SPB, STAG, POL, true, L>),
+                           grid, dim3(256), 0, s, a, b, M, N, K, lda, ldb, gm, gn, group_m, W,
+                           kc);
+    else
+        hipLaunchKernelGGL((tgemm::gemm_quad_split<DT, MF, PRE, SPA, SPB, STAG, POL, false, L>),
+                           grid, dim3(256), 0, s, a, b, M, N, K, lda, ldb, gm, gn, group_m, W,
+                           kc);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((tgemm::splitk_reduce<DT>), dim3((unsigned)cdiv(M * (N / 8), 256)),
+                       dim3(256), 0, s, static_cast<const float*>(W), static_cast<tgemm::u16*>(C),
+                       M, N, ldc, splits);
+    return hipGetLastError();
+}
+
 template <int DT, int MT, int D>
 hipError_t launch_skinny(const void* A, const void* B, void* C, int M, int N, int K, int lda,
                          int ldb, int ldc, int, hipStream_t s) {
@@ -159,6 +188,14 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
     Variant {                                                                              \
         DT, 0, 0, tgemm_config{TGEMM_KERNEL_SPLITK, BM, BN, BK, WM, WN, ST, G, 2, 32},         \
             nullptr, &launch_splitk<DT, BM, BN, BK, WM, WN, ST>                            \
+    }
+// The quad kernel in split-K mode, either B storage L, with the schedules of QUAD.
+#define QUAD_SPLIT(DT, MF, L, G)                                                           \
+    Variant {                                                                              \
+        DT, 0, L, tgemm_config{TGEMM_KERNEL_QUAD_SPLITK, 256, 256, 64, 2, 2, 5, G, 2, MF}, \
+            nullptr,                                                                       \
+            &launch_quad_split<DT, MF, (MF == 16 ? 2 : 1), (MF == 16 ? 56 : 40),           \
+                               (MF == 16 ? 40 : 12), 1, 2, L>                              \
     }
 #define SKINNY(DT, MT, D)                                                                  \
     Variant {                                                                              \

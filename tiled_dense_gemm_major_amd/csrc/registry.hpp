@@ -27,8 +27,8 @@ struct Variant {
     int a_layout;
     int layout;
     tgemm_config cfg;
-    launch_fn launch;              // every kernel but SPLITK
-    splitk_fn split_launch;        // SPLITK only
+    launch_fn launch;              // every kernel but the split-K ones
+    splitk_fn split_launch;        // SPLITK and QUAD_SPLITK only
 };
 
 struct VariantList {
@@ -41,6 +41,7 @@ VariantList variants_quad();
 VariantList variants_quad_kn();
 VariantList variants_quad_km();
 VariantList variants_direct();
+VariantList variants_quad_split();
 VariantList variants_pingpong_nk();
 VariantList variants_pingpong_other();
 VariantList variants_tiled();

@@ -28,8 +28,14 @@ constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
 using tgemm_reg::kMaxSplits;
 using tgemm_reg::Variant;
 
+// The kernels that split K over workgroups, with fp32 partials in a workspace.
+bool is_split(int kernel) {
+    return kernel == TGEMM_KERNEL_SPLITK || kernel == TGEMM_KERNEL_QUAD_SPLITK;
+}
+
 // Position of a kernel family in the listing order of one (A storage, B storage, dtype)
-// group: generic, tiled, direct-to-LDS ring, ping-pong, quad, skinny, split-K, direct.
+// group: generic, tiled, direct-to-LDS ring, ping-pong, quad, skinny, split-K, quad
+// split-K, direct.
 int family_rank(int kernel) {
     switch (kernel) {
     case TGEMM_KERNEL_GENERIC: return 0;
@@ -39,7 +45,8 @@ int family_rank(int kernel) {
     case TGEMM_KERNEL_QUAD: return 4;
     case TGEMM_KERNEL_SKINNY: return 5;
     case TGEMM_KERNEL_SPLITK: return 6;
-    default: return 7;
+    case TGEMM_KERNEL_QUAD_SPLITK: return 7;
+    default: return 8;
     }
 }
 
@@ -53,7 +60,8 @@ const std::vector<const Variant*>& registry() {
              {tgemm_reg::variants_tiled(), tgemm_reg::variants_small(),
               tgemm_reg::variants_pingpong_nk(), tgemm_reg::variants_pingpong_other(),
               tgemm_reg::variants_quad(), tgemm_reg::variants_quad_kn(),
-              tgemm_reg::variants_quad_km(), tgemm_reg::variants_direct()})
+              tgemm_reg::variants_quad_km(), tgemm_reg::variants_direct(),
+              tgemm_reg::variants_quad_split()})
             for (int i = 0; i < l.n; ++i)
                 v.push_back(&l.v[i]);
         const auto key = [](const Variant* x) {
@@ -68,9 +76,8 @@ const std::vector<const Variant*>& registry() {
 
 bool same_shape(const tgemm_config& a, const tgemm_config& b) {
     // a split-K configuration's split count is a per-call choice
-    const bool split_ok = a.kernel == TGEMM_KERNEL_SPLITK
-                              ? b.split_k >= 2 && b.split_k <= kMaxSplits
-                              : a.split_k == b.split_k;
+    const bool split_ok = is_split(a.kernel) ? b.split_k >= 2 && b.split_k <= kMaxSplits
+                                             : a.split_k == b.split_k;
     return a.kernel == b.kernel && a.block_m == b.block_m && a.block_n == b.block_n &&
            a.block_k == b.block_k && a.waves_m == b.waves_m && a.waves_n == b.waves_n &&
            a.stages == b.stages && split_ok && a.mfma == b.mfma;
@@ -169,6 +176,29 @@ tgemm_config choose(int dtype, int a_layout, int layout, int64_t m, int64_t n, i
 tgemm_config choose_ws(int dtype, int a_layout, int layout, int64_t m, int64_t n, int64_t k,
                        bool aligned) {
     const tgemm_config plain = choose(dtype, a_layout, layout, m, n, k, aligned);
+    if (aligned && a_layout == TGEMM_A_MK && m > 128) {
+        // At most 64 tiles of 256x256 with a long K: the quad kernel in split-K mode,
+        // about one workgroup per compute unit, each K range at least 1024 deep, when
+        // that gives half the chip or more work, and with ranges under 2048 only where
+        // 128x128 tiles would not fill the chip either.  Measured against the table's
+        // plain choice on 22 shapes: 1.2-1.7x faster from 16 to 64 tiles (e.g.
+        // 2048x2048x16384 110.7 against 150.4 us, 2048x2048x32768 207.8 against 356.2),
+        // a tie at 128 workgroups; slower at 128 tiles (the 192-row quad kernel) and at
+        // 64 tiles with 1024-deep ranges (2048x2048x4096: 51.2 against 46.9 us, where
+        // 256 tiles of 128x128 fill the chip in one wave).
+        const int64_t tiles = ((m + 255) / 256) * ((n + 255) / 256);
+        const int64_t tiles128 = ((m + 127) / 128) * ((n + 127) / 128);
+        int64_t splits = tiles > 0 ? 256 / tiles : 0;
+        if (splits > k / 1024)
+            splits = k / 1024;
+        if (splits > kMaxSplits)
+            splits = kMaxSplits;
+        if (tiles <= 64 && splits >= 2 && tiles * splits >= 128 &&
+            (k / splits >= 2048 || tiles128 < 256))
+            return tgemm_config{TGEMM_KERNEL_QUAD_SPLITK, 256, 256, 64, 2, 2, 5, 4,
+                                (int32_t)splits, layout == TGEMM_B_NK ? 16 : 32};
+        return plain;
+    }
     if (!aligned || a_layout != TGEMM_A_MK || layout != TGEMM_B_NK || m > 128 || k < 1024)
         return plain;
     const int64_t tiles = ((m + 63) / 64) * ((n + 255) / 256);
@@ -185,7 +215,7 @@ tgemm_config choose_ws(int dtype, int a_layout, int layout, int64_t m, int64_t n
 // Workspace bytes of a configuration for an m x n product: the fp32 partial tiles of a
 // split-K configuration, nothing for the others.
 int64_t workspace_bytes(const tgemm_config& cfg, int64_t m, int64_t n) {
-    return cfg.kernel == TGEMM_KERNEL_SPLITK ? (int64_t)cfg.split_k * m * n * 4 : 0;
+    return is_split(cfg.kernel) ? (int64_t)cfg.split_k * m * n * 4 : 0;
 }
 
 // One product as the caller described it.
@@ -309,6 +339,9 @@ int run(const Problem& p, const tgemm_config* cfg, void* ws, int64_t ws_bytes, v
             : (ws || use_scratch
                    ? choose_ws(p.dtype, p.a_layout, p.b_layout, p.m, p.n, p.k, aligned)
                    : choose(p.dtype, p.a_layout, p.b_layout, p.m, p.n, p.k, aligned));
+    // the fixed scratch holds the skinny products' partials; a larger split goes plain
+    if (!cfg && use_scratch && workspace_bytes(use, p.m, p.n) > kScratchBytes)
+        use = choose(p.dtype, p.a_layout, p.b_layout, p.m, p.n, p.k, aligned);
     const Variant* v = find_variant(p.dtype, p.a_layout, p.b_layout, use);
     if (!v)
         return TGEMM_ERR_UNSUPPORTED;
@@ -507,7 +540,7 @@ int tgemm_workspace_size(int64_t m, int64_t n, const tgemm_config* cfg, int64_t*
         return TGEMM_ERR_NULL_POINTER;
     if (m < 0 || n < 0)
         return TGEMM_ERR_INVALID_VALUE;
-    if (cfg->kernel == TGEMM_KERNEL_SPLITK && (cfg->split_k < 2 || cfg->split_k > kMaxSplits))
+    if (is_split(cfg->kernel) && (cfg->split_k < 2 || cfg->split_k > kMaxSplits))
         return TGEMM_ERR_UNSUPPORTED;
     if (m > kMaxElems || n > kMaxElems || (n > 0 && m > kMaxElems / n))
         return TGEMM_ERR_UNSUPPORTED;

@@ -102,7 +102,7 @@ def emit_table(tgemm, torch, np, args, stream, path):
                         rows.append((layout, mi, ni, ki, tgemm.Config.from_dict(d), us))
             continue
         cfgs = [c for c in tgemm.list_configs(BF16, layout)
-                if c.kernel not in (tgemm.KERNEL_GENERIC, tgemm.KERNEL_SPLITK)]
+                if c.kernel != tgemm.KERNEL_GENERIC and c.kernel not in tgemm.SPLIT_KERNELS]
         for mi, M in enumerate(TABLE_M):
             for ni, N in enumerate(TABLE_N):
                 for ki, K in enumerate(TABLE_K):
@@ -212,6 +212,9 @@ def main(argv=None):
                     help="also time torch.matmul (the vendor library) as context")
     ap.add_argument("--table-only", action="store_true",
                     help="time only the table's choices (without and with a workspace)")
+    ap.add_argument("--splits", default="",
+                    help="comma-separated split counts to time for the split-K kernels "
+                         "(default: the table's count with a workspace and its neighbours)")
     ap.add_argument("--kernels", default="",
                     help="comma-separated kernel ids to time (default: every compiled one)")
     ap.add_argument("--shapes", default="",
@@ -283,11 +286,13 @@ def main(argv=None):
                 if not args.table_only or cfg.as_dict() == table:
                     runners.append((cfg, go))
                 continue
-            if cfg.kernel == tgemm.KERNEL_SPLITK:
+            if cfg.kernel in tgemm.SPLIT_KERNELS:
                 # split counts: the table's (with a workspace) and its neighbours
-                base = ws_cfg.split_k if ws_cfg.kernel == tgemm.KERNEL_SPLITK else 8
+                base = ws_cfg.split_k if ws_cfg.kernel == cfg.kernel else 8
+                counts = ([int(x) for x in args.splits.split(",") if x] if args.splits
+                          else [max(2, base // 2), base, min(64, base * 2)])
                 variants = []
-                for sk in sorted({max(2, base // 2), base, min(64, base * 2)}):
+                for sk in sorted(set(counts)):
                     c = tgemm.Config.from_dict({**cfg.as_dict(), "split_k": sk})
                     variants.append(c)
             else:
