@@ -83,6 +83,10 @@ typedef enum {
                                      the library's fixed scratch (TGEMM_SCRATCH_BYTES)  */
 } tgemm_status;
 
+/* Workspace of a TGEMM_KERNEL_QUAD_STREAMK configuration: two 256x256 fp32 partial
+ * tiles for each of its 256 workgroups, 128 MiB, whatever the shape. */
+#define TGEMM_STREAMK_WORKSPACE_BYTES (128ll << 20)
+
 /* Size of the fixed per-GPU scratch that gemm_ex_noalloc uses: 16 MiB. */
 #define TGEMM_SCRATCH_BYTES (16ll << 20)
 
@@ -110,10 +114,16 @@ typedef enum {
                                  K range split over the split_k = 4 waves of a workgroup,
                                  MFMA operands loaded from global memory straight into
                                  registers, partial tiles added in LDS                  */
-    TGEMM_KERNEL_QUAD_SPLITK = 8 /* A [M,K], with a workspace: the quad kernel's 256x256
+    TGEMM_KERNEL_QUAD_SPLITK = 8,/* A [M,K], with a workspace: the quad kernel's 256x256
                                  tiles, the K range of each split over split_k
                                  workgroups, fp32 partial tiles in the workspace, summed
                                  in split order and cast by a second kernel            */
+    TGEMM_KERNEL_QUAD_STREAMK = 9 /* A [M,K], with a workspace: the tile rows that fill
+                                 whole waves of 256x256 tiles as a plain quad product,
+                                 the rest by stream-K (256 workgroups, equal contiguous
+                                 shares of the remaining tiles' K steps, at most two
+                                 tile segments each, fp32 partial tiles in the
+                                 workspace) and a reduction in workgroup order        */
 } tgemm_kernel;
 
 /* One tile configuration.  block_m x block_n is the C tile of one workgroup, block_k
@@ -164,7 +174,7 @@ int gemm_ex(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const voi
 /*
  * gemm_ex with a workspace lent by the caller, for configurations that need one
  * (TGEMM_KERNEL_SPLITK and TGEMM_KERNEL_QUAD_SPLITK: split_k * m * n * 4 bytes of fp32
- * partial tiles).  Split-K over
+ * partial tiles; TGEMM_KERNEL_QUAD_STREAMK: TGEMM_STREAMK_WORKSPACE_BYTES).  Split-K over
  * workgroups follows "Tiling a matmul", section "Where it breaks": a product with few
  * output tiles (small or skinny) leaves compute units idle unless K is split.
  *   workspace       : device pointer, 16-byte aligned, not overlapping A, B or C; its
@@ -252,8 +262,8 @@ int tgemm_list_configs_ex(int dtype, int a_layout, int b_layout, tgemm_config* o
 int tgemm_query_config_ws(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
                           int aligned, tgemm_config* out, int64_t* workspace_bytes);
 
-/* Workspace bytes a configuration needs for an m x n product (0 for all but SPLITK and
- * QUAD_SPLITK).
+/* Workspace bytes a configuration needs for an m x n product (0 for all but SPLITK,
+ * QUAD_SPLITK and QUAD_STREAMK).
  * Host-only. */
 int tgemm_workspace_size(int64_t m, int64_t n, const tgemm_config* cfg, int64_t* bytes);
 

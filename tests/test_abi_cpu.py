@@ -111,7 +111,8 @@ def test_list_configs(lib):
             kinds = {c.kernel for c in cfgs}
             assert tgemm.KERNEL_GENERIC in kinds and tgemm.KERNEL_TILED in kinds
             for c in cfgs:
-                if c.kernel in (tgemm.KERNEL_QUAD, tgemm.KERNEL_QUAD_SPLITK):
+                if c.kernel in (tgemm.KERNEL_QUAD, tgemm.KERNEL_QUAD_SPLITK,
+                                tgemm.KERNEL_QUAD_STREAMK):
                     # operand slots of block_m x block_k (three A, two B)
                     assert c.stages * max(c.block_m, c.block_n) * c.block_k * 2 <= 160 * 1024
                 elif c.kernel != tgemm.KERNEL_GENERIC:
@@ -342,6 +343,22 @@ def test_boundary_calls_with_exact_arity(lib):
     s = raw.tgemm_status_string
     s.argtypes, s.restype = [i32], ctypes.c_char_p
     assert s(0) == b"TGEMM_OK"
+
+
+def test_quad_tile_height_by_waves(lib):
+    """Off the table's grid the quad kernel's tile height (256 or 192 rows) is re-decided
+    by wave quantization on 256 compute units; on the grid the table's choice stands."""
+    cases = [((4000, 3000, 1000), tgemm.F16, tgemm.B_KN, 192),   # 252 tiles of 192: 1 wave
+             ((4608, 4608, 8192), tgemm.BF16, tgemm.B_NK, 192),  # 324 of 256: 2 waves
+             ((5120, 5120, 8192), tgemm.BF16, tgemm.B_NK, 256),  # 540 of 192: 3 waves
+             ((2560, 6144, 4096), tgemm.BF16, tgemm.B_KN, 256),
+             ((1280, 8192, 8192), tgemm.BF16, tgemm.B_NK, 192)]
+    for shape, dt, layout, rows in cases:
+        c = tgemm.query_config(dt, *shape, layout)
+        assert c.kernel == tgemm.KERNEL_QUAD and c.block_m == rows, (shape, c)
+    for shape in [(8192, 8192, 8192), (4096, 4096, 4096), (3072, 3072, 8192)]:
+        assert tgemm.query_config(tgemm.BF16, *shape).block_m == \
+            (192 if shape[0] == 3072 else 256), shape
 
 
 def test_packed_query_agrees_with_the_explicit_one(lib):

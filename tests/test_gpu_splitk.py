@@ -263,3 +263,80 @@ def test_quad_split_repeat_launches_bitwise_identical(dev, orc):
         tgemm.gemm_ex_ws(BF16, M, N, K, Ad, Bd, C, ws, need, B_NK, cfg)
         torch.cuda.synchronize()
         assert np.array_equal(from_dev(C), ref)
+
+
+# ---------------------------------------------------------------------------------------
+# Stream-K (TGEMM_KERNEL_QUAD_STREAMK): the tile rows filling whole waves as a plain quad
+# product, the rest dealt in equal K-step ranges to 256 workgroups (at most two tile
+# segments each), fp32 partials summed per tile in workgroup order.
+# ---------------------------------------------------------------------------------------
+def _quad_sk(layout):
+    from tiled_dense_gemm_major_amd import tgemm
+    return tgemm.Config(kernel=tgemm.KERNEL_QUAD_STREAMK, block_m=256, block_n=256,
+                        block_k=64, waves_m=2, waves_n=2, stages=5, group_m=4, split_k=1,
+                        mfma=16 if layout == B_NK else 32)
+
+
+def _run_quad_sk(dtype, A, B, layout, guard=1024):
+    from tiled_dense_gemm_major_amd import tgemm
+    M, K = A.shape
+    N = B.shape[0] if layout == B_NK else B.shape[1]
+    cfg = _quad_sk(layout)
+    need = tgemm.workspace_size(M, N, cfg)
+    assert need == tgemm.STREAMK_WORKSPACE_BYTES
+    ws = torch.full(((need + guard) // 4,), -1, dtype=torch.int32, device="cuda")
+    C = torch.full((M, N), 0x7E00, dtype=torch.int16, device="cuda").view(tdtype(dtype))
+    tgemm.gemm_ex_ws(dtype, M, N, K, to_dev(A, dtype), to_dev(B, dtype), C, ws, need, layout,
+                     cfg)
+    torch.cuda.synchronize()
+    assert np.all(ws[need // 4:].cpu().numpy() == -1), "workspace written past its size"
+    return from_dev(C)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("layout", [B_NK, B_KN])
+@pytest.mark.parametrize("shape", [
+    (4500, 4000, 200),      # 18 x 16 tiles: 16 rows of whole waves, 2 rows by stream-K
+    (600, 536, 1000),       # 9 tiles, fewer K steps than workgroups (empty ranges)
+    (1000, 3000, 4104),     # 48 tiles of 65 steps: ranges across tile ends, a K tail
+    (5000, 1512, 520)])     # 20 x 6 tiles
+def test_quad_streamk_ragged(dev, orc, dtype, layout, shape):
+    M, N, K = shape
+    A, B = _layout_inputs(dtype, M, N, K, layout, 900 + M + N + K + layout)
+    say(f"quad stream-K {dtype} layout {layout} {shape}")
+    got = _run_quad_sk(dtype, A, B, layout)
+    assert not np.any(got == 0x7E00)
+    assert_parity(orc, dtype, K, got, orc.gemm(dtype, A, B, layout), f"stream-K {shape}")
+
+
+@pytest.mark.parametrize("layout", [B_NK, B_KN])
+@pytest.mark.parametrize("shape", [(1300, 2600, 4104), (4400, 4200, 136), (256, 66048, 64)])
+def test_quad_streamk_exact_ints(dev, orc, layout, shape):
+    """Small-integer inputs: the segments' partial sums are exact, so the stream-K result
+    is the oracle's bit for bit (the last shape has more than 256 tiles in its one tile
+    row, which runs as a plain quad product)."""
+    M, N, K = shape
+    A, B = _layout_inputs(BF16, M, N, K, layout, 31 + M + K + layout, ints=True)
+    say(f"quad stream-K exact layout {layout} {shape}")
+    assert np.array_equal(_run_quad_sk(BF16, A, B, layout), orc.gemm(BF16, A, B, layout))
+
+
+def test_quad_streamk_repeat_launches_bitwise_identical(dev, orc):
+    from tiled_dense_gemm_major_amd import tgemm
+    M, N, K = 4608, 4352, 2056            # 18 x 17 tiles: 15 whole-wave rows, 3 by stream-K
+    A, B = _inputs(BF16, M, N, K, 37)
+    Ad, Bd = to_dev(A, BF16), to_dev(B, BF16)
+    cfg = _quad_sk(B_NK)
+    need = tgemm.workspace_size(M, N, cfg)
+    ws = torch.empty((need // 4,), dtype=torch.int32, device="cuda")
+    C0 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    tgemm.gemm_ex_ws(BF16, M, N, K, Ad, Bd, C0, ws, need, B_NK, cfg)
+    torch.cuda.synchronize()
+    ref = from_dev(C0)
+    assert_parity(orc, BF16, K, ref, orc.gemm(BF16, A, B, B_NK), "quad stream-K")
+    say("quad stream-K repeat launches")
+    C = torch.empty_like(C0)
+    for _ in range(5):
+        tgemm.gemm_ex_ws(BF16, M, N, K, Ad, Bd, C, ws, need, B_NK, cfg)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(C), ref)

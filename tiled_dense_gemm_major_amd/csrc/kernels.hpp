@@ -828,6 +828,43 @@ splitk_reduce(const float* __restrict__ W, u16* __restrict__ C, int M, int N, in
 }
 
 
+// The stream-K partials (gemm_quad_sk): each element of C, eight consecutive columns per
+// thread, is the sum of its tile's segments in workgroup order (their K ranges in
+// order), read from the slots the workgroups wrote, cast once.  Workgroups with an
+// empty range wrote nothing and are skipped.
+template <int DT>
+__global__ void __launch_bounds__(256)
+sk_reduce(const float* __restrict__ W, u16* __restrict__ C, int M, int N, int ldc, int grid_n,
+          int nk, int tiles, int G) {
+    const int per_row = N >> 3;
+    const int idx = (int)blockIdx.x * 256 + (int)threadIdx.x;
+    if (idx >= M * per_row)
+        return;
+    const int m = idx / per_row, n = (idx - m * per_row) * 8;
+    const int tm = m >> 8, tn = n >> 8;
+    const int64_t I = (int64_t)tiles * nk;
+    const int64_t i0 = (int64_t)(tm * grid_n + tn) * nk, i1 = i0 + nk - 1;
+    // the workgroup whose range holds iteration i: the last w with w I / G <= i
+    const int w_lo = (int)(((i0 + 1) * G - 1) / I), w_hi = (int)(((i1 + 1) * G - 1) / I);
+    const size_t off = (size_t)(m - tm * 256) * 256 + (size_t)(n - tn * 256);
+    f32x4 lo = {0.0f, 0.0f, 0.0f, 0.0f}, hi = lo;
+    for (int w = w_lo; w <= w_hi; ++w) {
+        const int64_t bw = (int64_t)w * I / G, bw1 = (int64_t)(w + 1) * I / G;
+        if (bw1 <= bw)
+            continue;
+        // the tile is the workgroup's first segment if its range starts inside the tile
+        const float* p = W + (size_t)(2 * w + (bw >= i0 ? 0 : 1)) * 65536 + off;
+        lo += *reinterpret_cast<const f32x4*>(p);
+        hi += *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    u32x4 v;
+    v[0] = pack2<DT>(lo[0], lo[1]);
+    v[1] = pack2<DT>(lo[2], lo[3]);
+    v[2] = pack2<DT>(hi[0], hi[1]);
+    v[3] = pack2<DT>(hi[2], hi[3]);
+    *reinterpret_cast<u32x4*>(C + (size_t)m * ldc + n) = v;
+}
+
 // ------------------------------------------------------------------------------------
 // Ping-pong kernel.
 //   8 waves, two per SIMD, in two groups: group 0 (waves 0-3) owns C rows [0, BM/2) of the
@@ -1244,16 +1281,17 @@ __device__ __forceinline__ int kn_swz(int k) {
     return MF == 16 ? 2 * ((k & 3) + 4 * ((k >> 3) & 1)) : 4 * (k & 3);
 }
 
-// The body of the quad kernels.  SPLIT: split-K mode, the workgroups of grid row
-// z = blockIdx.y walking only K range [z kc, (z + 1) kc) (kc a multiple of 64) and
-// storing their fp32 partial tiles to plane z of W (W[z][m][n], rows of N floats)
-// instead of casting to C; W and kc are unused otherwise.
+// The body of the quad kernels: C tile (tm, tn).  MODE 0: the whole K walk, cast to C.
+// MODE 1 (partial): the K range [k0, k0 + klen) only (k0 a multiple of 64) and the fp32
+// partial tile stored to P, element (m, n) at P[(m - pm0) * ldp + (n - pn0)], instead of
+// the cast to C.  MODE 2: MODE 1 where `partial` holds, else MODE 0 (one body, so one LDS
+// ring, for a kernel that does both).
 template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL, bool OFFS, int LAYOUT,
-          int BMT, int ALAY, bool SPLIT>
+          int BMT, int ALAY, int MODE>
 __device__ __attribute__((always_inline)) inline void
 quad_body(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
-          int N, int K, int lda, int ldb, int ldc, int grid_m, int grid_n, int group_m,
-          float* __restrict__ W, int kc) {
+          int N, int K, int lda, int ldb, int ldc, int tm, int tn, int k0, int klen,
+          float* __restrict__ P, int ldp, int pm0, int pn0, bool partial = false) {
     constexpr int BM = BMT, BN = 256, BK = 64;
     constexpr int KC = BK / 8;                 // 16-byte chunks per tile row
     constexpr int ROWS = 64 / KC;              // tile rows per 1 KiB load (8)
@@ -1285,19 +1323,16 @@ quad_body(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
 
     __shared__ __attribute__((aligned(1024))) u16 lds[SA * SLOTA + SB * SLOTB];
 
-    if constexpr (SPLIT) {
-        // this workgroup's K range as a product of its own: the operands start at its
-        // first k, and K is the range's length (the last range may hold a partial tile
-        // or, with more ranges than K needs, nothing)
-        const int k0 = (int)blockIdx.y * kc;
-        const int kend = K < k0 + kc ? K : k0 + kc;
-        K = kend > k0 ? kend - k0 : 0;
+    static_assert(MODE >= 0 && MODE <= 2, "mode");
+    const bool part = MODE == 1 || (MODE == 2 && partial);
+    if (MODE != 0 && part) {
+        // the K range as a product of its own: the operands start at its first k, and K
+        // is its length (a last range may hold a partial tile, or nothing)
+        K = klen > 0 ? klen : 0;
         A += AKM ? (size_t)k0 * (size_t)lda : (size_t)k0;
         B += KN ? (size_t)k0 * (size_t)ldb : (size_t)k0;
     }
 
-    int tm, tn;
-    tile_of((int)blockIdx.x, grid_m, grid_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int tid = (int)threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1651,11 +1686,10 @@ quad_body(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
         wait_vm<0>();                              // the trailing zero loads
     }
 
-    if constexpr (SPLIT) {
+    if (MODE != 0 && part) {
         // The fp32 partial tile, straight from the accumulators: a lane's four
         // consecutive columns of one row are one 16-byte store (16 rows of 64 bytes per
-        // instruction), into plane blockIdx.y of W.
-        float* plane = W + (size_t)blockIdx.y * (size_t)M * (size_t)N;
+        // instruction).
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int m = m0 + wm * WTM + i * MF + lr;
@@ -1667,7 +1701,7 @@ quad_body(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
                     const f32x4 v = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1],
                                      acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
                     if (m < M && n < N)
-                        *reinterpret_cast<f32x4*>(plane + (size_t)m * N + n) = v;
+                        *reinterpret_cast<f32x4*>(P + (size_t)(m - pm0) * ldp + (n - pn0)) = v;
                 }
             }
         }
@@ -1719,8 +1753,10 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
                                amdgpu_waves_per_eu(1, 1)))
 gemm_quad(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
           int N, int K, int lda, int ldb, int ldc, int grid_m, int grid_n, int group_m) {
-    quad_body<DT, MF, PRE, SPA, SPB, STAG, POL, OFFS, LAYOUT, BMT, ALAY, false>(
-        A, B, C, M, N, K, lda, ldb, ldc, grid_m, grid_n, group_m, nullptr, 0);
+    int tm, tn;
+    tile_of((int)blockIdx.x, grid_m, grid_n, group_m, tm, tn);
+    quad_body<DT, MF, PRE, SPA, SPB, STAG, POL, OFFS, LAYOUT, BMT, ALAY, 0>(
+        A, B, C, M, N, K, lda, ldb, ldc, tm, tn, 0, 0, nullptr, 0, 0, 0);
 }
 
 // Split-K over workgroups with the quad kernel ("Tiling a matmul", section "Where it
@@ -1734,8 +1770,58 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
 gemm_quad_split(const u16* __restrict__ A, const u16* __restrict__ B, int M, int N, int K,
                 int lda, int ldb, int grid_m, int grid_n, int group_m, float* __restrict__ W,
                 int kc) {
-    quad_body<DT, MF, PRE, SPA, SPB, STAG, POL, OFFS, LAYOUT, 256, LAYOUT_MK, true>(
-        A, B, nullptr, M, N, K, lda, ldb, N, grid_m, grid_n, group_m, W, kc);
+    int tm, tn;
+    tile_of((int)blockIdx.x, grid_m, grid_n, group_m, tm, tn);
+    const int z = (int)blockIdx.y, k0 = z * kc;
+    const int kend = K < k0 + kc ? K : k0 + kc;
+    quad_body<DT, MF, PRE, SPA, SPB, STAG, POL, OFFS, LAYOUT, 256, LAYOUT_MK, 1>(
+        A, B, nullptr, M, N, K, lda, ldb, N, tm, tn, k0, kend - k0,
+        W + (size_t)z * (size_t)M * (size_t)N, N, 0, 0);
+}
+
+// Stream-K for a product whose tiles do not fill whole waves ("Tiling a matmul", section
+// "Where it breaks": a last partial wave leaves compute units idle), in one launch of
+// G + dp_rows * grid_n workgroups.  The first G take the stream-K rows (tile rows
+// dp_rows .. grid_m - 1): their (tile, 64-wide K step) iterations, tile by tile in
+// row-major order, dealt in equal contiguous ranges, workgroup w taking iterations
+// [w I / G, (w + 1) I / G) of the I = sk_tiles * nk.  With at most G such tiles a range
+// spans at most two tiles: each segment runs the quad K walk over its K range and stores
+// its fp32 partial tile to slot 2w + (its segment index) of W (256 x 256 floats per
+// slot); sk_reduce, the next kernel, adds each tile's segments in workgroup order.  The
+// other workgroups, dispatched after them, each take one whole tile of the leading
+// dp_rows tile rows (grouped, XCD-aware order) and store it cast, as gemm_quad does.
+template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL, bool OFFS,
+          int LAYOUT = LAYOUT_NK>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
+                               amdgpu_waves_per_eu(1, 1)))
+gemm_quad_sk(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
+             int N, int K, int lda, int ldb, int ldc, int grid_n, int group_m, int dp_rows,
+             int nk, int sk_tiles, int G, float* __restrict__ W) {
+    const int wg = (int)blockIdx.x;
+    if (wg >= G) {                             // a whole tile of the leading rows
+        int tm, tn;
+        tile_of(wg - G, dp_rows, grid_n, group_m, tm, tn);
+        quad_body<DT, MF, PRE, SPA, SPB, STAG, POL, OFFS, LAYOUT, 256, LAYOUT_MK, 2>(
+            A, B, C, M, N, K, lda, ldb, ldc, tm, tn, 0, 0, nullptr, 0, 0, 0, false);
+        return;
+    }
+    const int64_t I = (int64_t)sk_tiles * nk;
+    const int64_t b0 = (int64_t)wg * I / G, b1 = (int64_t)(wg + 1) * I / G;
+    int64_t it = b0;
+#pragma unroll 1
+    for (int seg = 0; seg < 2 && it < b1; ++seg) {
+        const int t = (int)(it / nk);
+        const int s0 = (int)(it - (int64_t)t * nk);
+        const int s1 = (int)((int64_t)nk < s0 + (b1 - it) ? (int64_t)nk : s0 + (b1 - it));
+        const int tm = dp_rows + t / grid_n, tn = t % grid_n;
+        const int k0 = s0 * 64, kend = K < s1 * 64 ? K : s1 * 64;
+        if (seg > 0)
+            __syncthreads();                   // the first segment's LDS reads are done
+        quad_body<DT, MF, PRE, SPA, SPB, STAG, POL, OFFS, LAYOUT, 256, LAYOUT_MK, 2>(
+            A, B, nullptr, M, N, K, lda, ldb, N, tm, tn, k0, kend - k0,
+            W + (size_t)(2 * wg + seg) * 65536, 256, tm * 256, tn * 256, true);
+        it += s1 - s0;
+    }
 }
 
 // ------------------------------------------------------------------------------------

@@ -115,6 +115,45 @@ hipError_t launch_quad_split(const void* A, const void* B, void* C, int M, int N
     return hipGetLastError();
 }
 
+// Stream-K over the last partial wave, in one launch: the leading tile rows that fill
+// whole waves of the 256 compute units as whole tiles, the remaining rows dealt to 256
+// stream-K workgroups (dispatched first) in equal shares of their tiles' K steps, then
+// the reduction of their partial tiles.  Without a partial wave (or with K = 0, or more
+// than 256 remaining tiles) the product runs as the plain quad kernel.
+constexpr int kStreamKGroups = 256;
+template <int DT, int MF, int PRE, int SPA, int SPB, int STAG, int POL, int L = 0>
+hipError_t launch_quad_sk(const void* A, const void* B, void* C, int M, int N, int K, int lda,
+                          int ldb, int ldc, int group_m, int, void* ws, hipStream_t s) {
+    const int gm = cdiv(M, 256), gn = cdiv(N, 256), nk = cdiv(K, 64);
+    const int dp_rows = (gm * gn / kStreamKGroups) * kStreamKGroups / gn;
+    const int m_dp = dp_rows * 256 < M ? dp_rows * 256 : M;
+    const int rows_sk = M - m_dp;
+    const int tiles_sk = cdiv(rows_sk, 256) * gn;
+    if (nk == 0 || rows_sk == 0 || tiles_sk > kStreamKGroups)
+        return launch_quad<DT, MF, PRE, SPA, SPB, STAG, POL, L>(A, B, C, M, N, K, lda, ldb, ldc,
+                                                               group_m, s);
+    const auto a = static_cast<const tgemm::u16*>(A);
+    const auto b = static_cast<const tgemm::u16*>(B);
+    const auto c = static_cast<tgemm::u16*>(C);
+    float* W = static_cast<float*>(ws);
+    const dim3 grid((unsigned)(kStreamKGroups + dp_rows * gn));
+    if (lda >= 64 && ldb >= (L == 0 ? 64 : 256))
+        hipLaunchKernelGGL((tgemm::gemm_quad_sk<DT, MF, PRE, SPA, SPB, STAG, POL, true, L>),
+                           grid, dim3(256), 0, s, a, b, c, M, N, K, lda, ldb, ldc, gn, group_m,
+                           dp_rows, nk, tiles_sk, kStreamKGroups, W);
+    else
+        hipLaunchKernelGGL((tgemm::gemm_quad_sk<DT, MF, PRE, SPA, SPB, STAG, POL, false, L>),
+                           grid, dim3(256), 0, s, a, b, c, M, N, K, lda, ldb, ldc, gn, group_m,
+                           dp_rows, nk, tiles_sk, kStreamKGroups, W);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((tgemm::sk_reduce<DT>), dim3((unsigned)cdiv(rows_sk * (N / 8), 256)),
+                       dim3(256), 0, s, static_cast<const float*>(W), c + (size_t)m_dp * ldc,
+                       rows_sk, N, ldc, gn, nk, tiles_sk, kStreamKGroups);
+    return hipGetLastError();
+}
+
 template <int DT, int MT, int D>
 hipError_t launch_skinny(const void* A, const void* B, void* C, int M, int N, int K, int lda,
                          int ldb, int ldc, int, hipStream_t s) {
@@ -196,6 +235,14 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
             nullptr,                                                                       \
             &launch_quad_split<DT, MF, (MF == 16 ? 2 : 1), (MF == 16 ? 56 : 40),           \
                                (MF == 16 ? 40 : 12), 1, 2, L>                              \
+    }
+// Stream-K over the last partial wave with the quad kernel, either B storage L.
+#define QUAD_SK(DT, MF, L, G)                                                              \
+    Variant {                                                                              \
+        DT, 0, L, tgemm_config{TGEMM_KERNEL_QUAD_STREAMK, 256, 256, 64, 2, 2, 5, G, 1, MF},\
+            nullptr,                                                                       \
+            &launch_quad_sk<DT, MF, (MF == 16 ? 2 : 1), (MF == 16 ? 56 : 40),              \
+                            (MF == 16 ? 40 : 12), 1, 2, L>                                 \
     }
 #define SKINNY(DT, MT, D)                                                                  \
     Variant {                                                                              \

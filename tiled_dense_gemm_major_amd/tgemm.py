@@ -13,8 +13,9 @@ F16, BF16 = 0, 1
 B_NK, B_KN = 0, 1
 A_MK, A_KM = 0, 1
 (KERNEL_GENERIC, KERNEL_TILED, KERNEL_SKINNY, KERNEL_DMA, KERNEL_PINGPONG, KERNEL_QUAD,
- KERNEL_SPLITK, KERNEL_DIRECT, KERNEL_QUAD_SPLITK) = range(9)
+ KERNEL_SPLITK, KERNEL_DIRECT, KERNEL_QUAD_SPLITK, KERNEL_QUAD_STREAMK) = range(10)
 SPLIT_KERNELS = (KERNEL_SPLITK, KERNEL_QUAD_SPLITK)   # split K over workgroups (workspace)
+STREAMK_WORKSPACE_BYTES = 128 << 20                   # a QUAD_STREAMK configuration's
 
 SCRATCH_BYTES = 16 << 20    # the fixed per-GPU scratch of gemm_ex_noalloc
 CLOCK_STAMP_SLOTS = 4096    # compute-unit slots of one clock stamp (2 int64 each)
@@ -32,7 +33,8 @@ EXPORTS = ("attn_fwd_f16", "gemm_f16", "gemm_bf16", "gemm_ex", "gemm_ex_ws", "ge
 
 __all__ = ["F16", "BF16", "B_NK", "B_KN", "A_MK", "A_KM", "KERNEL_GENERIC", "KERNEL_TILED",
            "KERNEL_SKINNY", "KERNEL_DMA", "KERNEL_PINGPONG", "KERNEL_QUAD", "KERNEL_SPLITK",
-           "KERNEL_QUAD_SPLITK", "SPLIT_KERNELS",
+           "KERNEL_QUAD_SPLITK", "KERNEL_QUAD_STREAMK", "SPLIT_KERNELS",
+           "STREAMK_WORKSPACE_BYTES",
            "KERNEL_DIRECT",
            "LIB_PATH", "EXPORTS", "TGemmError", "Config", "load", "status_string", "gemm_f16",
            "gemm_bf16", "gemm_ex", "gemm_ex_ws", "gemm_ex_noalloc", "gemm_strided",
