@@ -104,8 +104,14 @@ def test_no_alloc_explicit_configs_and_no_workspace_shapes(dev, orc):
     with pytest.raises(tgemm.TGemmError) as e:
         tgemm.gemm_ex_noalloc(BF16, 128, 8192, 512, Ab, Bb, Cb, B_NK, big)
     assert e.value.status == -9
-    # shapes whose choice needs no workspace run their plain kernel, and B [K,N]
-    for (M, N, K, layout) in [(512, 512, 512, B_NK), (600, 520, 328, B_KN)]:
+    # shapes whose choice needs no workspace run their plain kernel, and B [K,N]; the
+    # last one's choice given a workspace is the quad kernel's split-K, whose partials
+    # (8 planes of 1024 x 2048 fp32, 64 MiB) would not fit the scratch, so it runs the
+    # plain choice too
+    q, qneed = tgemm.query_config_ws(F16, 1024, 2048, 8192)
+    assert q.kernel == tgemm.KERNEL_QUAD_SPLITK and qneed > tgemm.SCRATCH_BYTES
+    for (M, N, K, layout) in [(512, 512, 512, B_NK), (600, 520, 328, B_KN),
+                              (1024, 2048, 8192, B_NK)]:
         A, B = _case(F16, M, N, K, layout, 50 + M)
         Ad, Bd = to_dev(A, F16), to_dev(B, F16)
         say(f"no-alloc without workspace {M}x{N}x{K} layout {layout}")
