@@ -1711,14 +1711,21 @@ quad_body(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     // Epilogue: one cast per value.  A lane holds groups of four consecutive columns of a
     // row, which would leave each store as 16 scattered 32-byte pieces; instead each wave
     // stages its 128 x 128 block in LDS (the ring is free once every wave's loads have
-    // landed and its reads are done; rows padded to 272 bytes so the 8-byte writes of 16
-    // rows fall in distinct banks) and stores it back as 256-byte row segments, 16 bytes
-    // per lane, with the non-temporal hint (1-2 % faster than plain stores; storing
-    // straight from the accumulators instead was 3 % slower).
+    // landed and its reads are done) and stores it back as 256-byte row segments, 16
+    // bytes per lane, with the non-temporal hint (1-2 % faster than plain stores; storing
+    // straight from the accumulators instead was 3 % slower).  Rows are padded to 272
+    // bytes, and in rows with bit 3 set the two 8-byte halves of each 16-byte chunk trade
+    // places: the 8-byte writes of a lane's 16 rows then use 16 distinct bank pairs when
+    // the LDS serves them 16 lanes at a time over 32 banks (rows r and r + 8 would share
+    // them otherwise), and stay distinct when it serves 32 lanes over 64 banks.  The
+    // reads swap the halves back in registers (the row's bit 3 is known at compile time).
     constexpr int RSE = 128 + 8;                   // staged row stride in elements
     static_assert(4 * WTM * RSE <= SA * SLOTA + SB * SLOTB, "C staging fits the LDS ring");
     wait_vm_then_sync<0>();
     u16* stage = lds + wave * WTM * RSE;
+    // the lane's column within an 8-column run, halves traded in rows with bit 3 set
+    // (bit 3 of a staged row i * MF + lr is bit 3 of lr); the rest is a constant offset
+    const int cx = (4 * kq) ^ (4 * ((lr >> 3) & 1));
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -1726,7 +1733,7 @@ quad_body(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
 #pragma unroll
             for (int g = 0; g < (MF == 16 ? 1 : 4); ++g) {
                 const int r = i * MF + lr;
-                const int c = j * MF + (MF == 16 ? 4 * kq : 8 * g + 4 * kq);
+                const int c = j * MF + (MF == 16 ? 0 : 8 * g) + cx;
                 u32x2 v;
                 v[0] = pack2<DT>(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
                 v[1] = pack2<DT>(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
@@ -1739,8 +1746,9 @@ quad_body(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
     const int n = n0 + wn * 128 + sc;
 #pragma unroll
     for (int q = 0; q < WTM / 4; ++q) {
-        const int r = 4 * q + sr;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * RSE + sc);
+        const int r = 4 * q + sr;                  // bit 3 of r is bit 1 of q (sr < 4)
+        const u32x4 h = *reinterpret_cast<const u32x4*>(stage + r * RSE + sc);
+        const u32x4 v = (q & 2) ? u32x4{h[2], h[3], h[0], h[1]} : h;
         const int m = m0 + wm * WTM + r;
         if (m < M && n < N)     // non-temporal: C is written once and not read back here
             __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + (size_t)m * ldc + n));
