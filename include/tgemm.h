@@ -258,7 +258,10 @@ int tgemm_list_configs_ex(int dtype, int a_layout, int b_layout, tgemm_config* o
                           int capacity);
 
 /* The configuration the table picks when the caller can lend a workspace (A [M,K]), and
- * the workspace bytes it needs (0 when it needs none).  Host-only. */
+ * the workspace bytes it needs (0 when it needs none): split-K over workgroups for
+ * products of at most 128 rows with K >= 1024 (B [N,K]), the quad kernel's split-K for
+ * products of more rows with at most 64 tiles of 256x256 and a long K (either B
+ * storage), else the choice without a workspace.  Host-only. */
 int tgemm_query_config_ws(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
                           int aligned, tgemm_config* out, int64_t* workspace_bytes);
 
