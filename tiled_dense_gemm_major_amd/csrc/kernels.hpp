@@ -1541,11 +1541,15 @@ quad_body(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict_
         for (int j = 0; j < TN; ++j)
             acc[i][j] = acc_t{};
     // MFMA J of a sub-step from operand buffer bf.  S0 = B rows (n), S1 = A rows (m): a
-    // lane then holds one C row and groups of four consecutive columns.
+    // lane then holds one C row and groups of four consecutive columns.  The blocks go
+    // row by row, every other row backwards, so that two consecutive MFMAs always share
+    // an operand (the A block along a row, the B block at a turn): fewer operand
+    // transitions cost less energy on this power-limited chip (measured 0.7-0.8 % faster
+    // at 4096^3 and 8192^3, both B storages; columns outermost was 1.8 % slower).
     auto mma = [&](auto bufc, auto jc) {
         constexpr int bf = decltype(bufc)::value;
         constexpr int J = decltype(jc)::value;
-        constexpr int i = J / TN, j = J % TN;
+        constexpr int i = J / TN, j = (i & 1) ? TN - 1 - J % TN : J % TN;
         if constexpr (MF == 16)
             acc[i][j] = mfma_16x16x32<DT>(fb[bf][j], fa[bf][i], acc[i][j]);
         else
