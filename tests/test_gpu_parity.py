@@ -365,3 +365,64 @@ def test_quad_kn_4096_full(dev, orc):
     for cfg in [c for c in _configs(BF16, B_KN) if c.kernel == tgemm.KERNEL_QUAD]:
         say(f"quad [K,N] 4096^3 {_cfg_id(cfg)}")
         assert_parity(orc, BF16, K, run(BF16, A, B, B_KN, cfg), want, _cfg_id(cfg))
+
+
+# ---------------------------------------------------------------------------------------
+# Non-finite results: NaN and infinite inputs, and sums past the output format's range.
+# The acceptance rule fails every non-finite GPU value, so these are checked by class:
+# where the oracle's result is NaN the GPU's must be NaN, where it is +-inf the GPU's must
+# be the same infinity, and every other element meets the rule.  Finite magnitudes stay
+# small enough that no fp32 partial sum overflows where the fp64 sum would not.
+# ---------------------------------------------------------------------------------------
+def _special_inputs(dtype, M, N, K, layout, seed):
+    from tiled_dense_gemm_major_amd.inputs import round_to_bf16_bits, round_to_f16_bits
+    enc = round_to_f16_bits if dtype == F16 else round_to_bf16_bits
+    nan, pinf, ninf = (0x7E00, 0x7C00, 0xFC00) if dtype == F16 else (0x7FC0, 0x7F80, 0xFF80)
+    rng = np.random.default_rng(seed)
+    a = rng.uniform(-1, 1, (M, K))
+    b = rng.uniform(-1, 1, (N, K))
+    b[:, 9] = np.abs(b[:, 9]) + 0.5                    # for row 7's +inf at k = 9
+    b[11, 9] = 0.0                                     # ... inf x 0: NaN in column 11
+    a[:, 2] = np.abs(a[:, 2]) + 0.25                   # for column 17's -inf at k = 2
+    a[7, :] = 0.0
+    # rows 20-23 x columns 30-33 past the largest finite value, through one k only: a
+    # product of two large values there, every other term of those sums (and every term
+    # elsewhere) small, so no fp32 partial sum can overflow where the fp64 sum does not
+    big = 300.0 if dtype == F16 else 3.0e37
+    b[:, 40] = rng.uniform(-1e-3, 1e-3, N)
+    a[20:24, 40] = big
+    b[30:34, 40] = big
+    A = enc(a)
+    Bn = enc(b)
+    A[3, 5] = nan                                      # row 3 of C: NaN
+    A[7, 9] = pinf                                     # row 7: +inf, NaN at column 11
+    Bn[17, 2] = ninf                                   # column 17: -inf (row 7: 0 x -inf)
+    B = Bn if layout == B_NK else np.ascontiguousarray(Bn.T)
+    return A, B
+
+
+def _assert_same_class(orc, dtype, K, got, want, what):
+    g = orc.decode(dtype, got).ravel()
+    w = orc.decode(dtype, want).ravel()
+    assert np.array_equal(np.isnan(g), np.isnan(w)), f"{what}: NaN positions differ"
+    inf = np.isinf(w)
+    assert np.array_equal(np.isinf(g), inf), f"{what}: infinite positions differ"
+    assert np.array_equal(np.sign(g[inf]), np.sign(w[inf])), f"{what}: infinity signs differ"
+    fin = np.isfinite(w)
+    res = orc.compare(dtype, K, got.ravel()[fin], want.ravel()[fin])
+    assert res["n_fail"] == 0, f"{what}: {res}"
+    return int(np.isnan(w).sum()), int(inf.sum())
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("layout", [B_NK, B_KN])
+def test_every_config_non_finite(dev, orc, dtype, layout):
+    M, N, K = 200, 264, 72
+    A, B = _special_inputs(dtype, M, N, K, layout, 61 + dtype + 2 * layout)
+    want = orc.gemm(dtype, A, B, layout)
+    n_nan, n_inf = _assert_same_class(orc, dtype, K, want, want, "oracle")
+    assert n_nan > 0 and n_inf > 0
+    for cfg in _configs(dtype, layout):
+        say(f"non-finite {_cfg_id(cfg)} dtype {dtype} layout {layout}")
+        got = run(dtype, A, B, layout, cfg)
+        _assert_same_class(orc, dtype, K, got, want, _cfg_id(cfg))
