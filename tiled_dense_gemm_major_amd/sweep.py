@@ -266,18 +266,24 @@ def main(argv=None):
         dname = "bf16" if w.dtype == BF16 else "f16"
         flops = roofline.gemm_flops(w.M, w.N, w.K)
         nbytes = roofline.compulsory_bytes(w.M, w.N, w.K)
-        table = tgemm.query_config(w.dtype, w.M, w.N, w.K, w.b_layout, True,
+        # packed operands meet the fast kernels' rules when every row length is a
+        # multiple of 8 elements (the allocations themselves are aligned)
+        aligned = w.K % 8 == 0 and w.N % 8 == 0 and (not a_layout or w.M % 8 == 0)
+        table = tgemm.query_config(w.dtype, w.M, w.N, w.K, w.b_layout, aligned,
                                    a_layout).as_dict()
-        table_ws = tgemm.query_config_ws(w.dtype, w.M, w.N, w.K, w.b_layout)[0].as_dict()
+        table_ws = tgemm.query_config_ws(w.dtype, w.M, w.N, w.K, w.b_layout,
+                                         aligned)[0].as_dict()
         kernels = {int(x) for x in args.kernels.split(",") if x}
 
         runners = []
-        ws_cfg, _ = tgemm.query_config_ws(w.dtype, w.M, w.N, w.K, w.b_layout)
+        ws_cfg, _ = tgemm.query_config_ws(w.dtype, w.M, w.N, w.K, w.b_layout, aligned)
         lda = w.M if a_layout else w.K
         ldb = w.N if w.b_layout == B_KN else w.K
         for cfg in tgemm.list_configs(w.dtype, w.b_layout, a_layout):
             if kernels and cfg.kernel not in kernels:
                 continue
+            if not aligned and cfg.kernel != tgemm.KERNEL_GENERIC:
+                continue                                # the fast kernels refuse these
             if a_layout:                                # the general entry point
                 def go(i, c=cfg):
                     tgemm.gemm_strided(w.dtype, w.M, w.N, w.K, As[i % copies], lda,
