@@ -36,7 +36,9 @@
  *   - Alignment: any 2-byte-aligned pointers, sizes and leading dimensions are accepted.
  *     The fast kernels need A, B, C 16-byte aligned, K, N, lda, ldb and ldc multiples of
  *     8, M a multiple of 8 when A is [K,M], and A and B each spanning at most 2^31 bytes;
- *     other calls run a slower kernel with the same arithmetic.
+ *     other calls run the same tiles with element-wise loads and stores
+ *     (TGEMM_KERNEL_MASKED), or, when A or B spans more than 2^31 bytes, a slower
+ *     generic kernel; the arithmetic is the same.
  *   - Limits: M, N, K < 2^31, M*K, N*K, M*N < 2^31, and the element span of each operand
  *     ((rows - 1) * ld + row length) < 2^31 (TGEMM_ERR_UNSUPPORTED).
  *   - Aliasing: the span of C may not overlap the span of A or B (TGEMM_ERR_ALIASING).
@@ -118,12 +120,16 @@ typedef enum {
                                  tiles, the K range of each split over split_k
                                  workgroups, fp32 partial tiles in the workspace, summed
                                  in split order and cast by a second kernel            */
-    TGEMM_KERNEL_QUAD_STREAMK = 9 /* A [M,K], with a workspace: the tile rows that fill
+    TGEMM_KERNEL_QUAD_STREAMK = 9,/* A [M,K], with a workspace: the tile rows that fill
                                  whole waves of 256x256 tiles as a plain quad product,
                                  the rest by stream-K (256 workgroups, equal contiguous
                                  shares of the remaining tiles' K steps, at most two
                                  tile segments each, fp32 partial tiles in the
                                  workspace) and a reduction in workgroup order        */
+    TGEMM_KERNEL_MASKED = 10  /* the TILED kernel for operands of any 2-byte alignment
+                                 and any sizes (A and B each at most 2^31 bytes): each
+                                 16-byte piece of a tile read as eight 2-byte elements,
+                                 masked one by one, and C stored element by element    */
 } tgemm_kernel;
 
 /* One tile configuration.  block_m x block_n is the C tile of one workgroup, block_k
@@ -236,7 +242,8 @@ int gemm_strided(int dtype, int64_t m, int64_t n, int64_t k, const void* A, int6
 /* The configuration gemm_f16 / gemm_bf16 / gemm_ex(cfg = NULL) pick for this packed
  * problem (A [M,K], B per b_layout, C [M,N], no padding) with operands at 16-byte-aligned
  * addresses, written to *out; whether the fast kernels can take it follows from the sizes
- * (K and N multiples of 8, A and B each at most 2^31 bytes).  Host-only: it touches no
+ * (K and N multiples of 8, A and B each at most 2^31 bytes; else the masked kernel, or
+ * the generic one past 2^31 bytes).  Host-only: it touches no
  * device.  Returns TGEMM_OK, TGEMM_ERR_NULL_POINTER (out NULL) or the size, dtype and
  * layout errors of gemm_ex. */
 int tgemm_query_config(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
@@ -250,8 +257,10 @@ int tgemm_list_configs(int dtype, int b_layout, tgemm_config* out, int capacity)
 /* The choice for either storage of A (tgemm_a_layout) and a caller-stated alignment:
  * `aligned` != 0 says the operands meet every fast-kernel rule (16-byte-aligned
  * addresses, sizes and leading dimensions multiples of 8, spans within 2^31 bytes),
- * 0 that they do not (the choice is then the any-alignment kernel).  The list for either
- * storage of A; tgemm_list_configs answers for TGEMM_A_MK. */
+ * 0 that they do not (the choice is then a TGEMM_KERNEL_MASKED configuration; a call
+ * whose A or B spans more than 2^31 bytes runs the generic kernel instead, which this
+ * query cannot see).  The list for either storage of A; tgemm_list_configs answers for
+ * TGEMM_A_MK. */
 int tgemm_query_config_ex(int dtype, int64_t m, int64_t n, int64_t k, int a_layout,
                           int b_layout, int aligned, tgemm_config* out);
 int tgemm_list_configs_ex(int dtype, int a_layout, int b_layout, tgemm_config* out,

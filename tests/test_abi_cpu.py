@@ -94,7 +94,7 @@ def test_query_config_table(lib):
     big = tgemm.query_config(tgemm.BF16, 8192, 8192, 8192)
     assert big.kernel != tgemm.KERNEL_GENERIC and big.block_m * big.block_n >= 128 * 128
     odd = tgemm.query_config(tgemm.F16, 100, 100, 100, aligned=False)
-    assert odd.kernel == tgemm.KERNEL_GENERIC
+    assert odd.kernel == tgemm.KERNEL_MASKED
     listed = {tuple(sorted(c.as_dict().items())) for c in tgemm.list_configs(tgemm.BF16)}
     for shape in [(512, 512, 512), (4096, 4096, 4096), (8192, 8192, 8192), (64, 8192, 8192),
                   (4000, 3000, 1000)]:
@@ -109,7 +109,7 @@ def test_list_configs(lib):
         for lay in (tgemm.B_NK, tgemm.B_KN):
             cfgs = tgemm.list_configs(dt, lay)
             kinds = {c.kernel for c in cfgs}
-            assert tgemm.KERNEL_GENERIC in kinds and tgemm.KERNEL_TILED in kinds
+            assert {tgemm.KERNEL_GENERIC, tgemm.KERNEL_MASKED, tgemm.KERNEL_TILED} <= kinds
             for c in cfgs:
                 if c.kernel in (tgemm.KERNEL_QUAD, tgemm.KERNEL_QUAD_SPLITK,
                                 tgemm.KERNEL_QUAD_STREAMK):
@@ -149,7 +149,8 @@ def test_strided_query_and_list(lib):
         for b_layout in (tgemm.B_NK, tgemm.B_KN):
             cfgs = tgemm.list_configs(tgemm.BF16, b_layout, a_layout)
             kinds = {c.kernel for c in cfgs}
-            assert {tgemm.KERNEL_GENERIC, tgemm.KERNEL_TILED, tgemm.KERNEL_PINGPONG} <= kinds
+            assert {tgemm.KERNEL_GENERIC, tgemm.KERNEL_MASKED, tgemm.KERNEL_TILED,
+                    tgemm.KERNEL_PINGPONG} <= kinds
             big = tgemm.query_config(tgemm.BF16, 8192, 8192, 8192, b_layout, True, a_layout)
             assert big.kernel == tgemm.KERNEL_QUAD
             listed = {tuple(sorted(c.as_dict().items())) for c in cfgs}
@@ -329,15 +330,18 @@ def test_boundary_calls_with_exact_arity(lib):
     out = tgemm.Config()
     assert q(1, 8192, 8192, 8192, 0, ctypes.byref(out)) == 0
     assert out.kernel == tgemm.KERNEL_QUAD
-    # the packed choice follows from the sizes: K not a multiple of 8 -> any-alignment
+    # the packed choice follows from the sizes: K not a multiple of 8 -> the masked kernel
     assert q(0, 100, 100, 100, 0, ctypes.byref(out)) == 0
-    assert out.kernel == tgemm.KERNEL_GENERIC
+    assert out.kernel == tgemm.KERNEL_MASKED
     # M need not be a multiple of 8; N must (C's rows, and B's rows when B is [K,N])
     assert q(0, 100, 104, 104, 0, ctypes.byref(out)) == 0
-    assert out.kernel != tgemm.KERNEL_GENERIC
+    assert out.kernel not in tgemm.ANY_ALIGNMENT_KERNELS
     for layout in (0, 1):
         assert q(0, 104, 100, 104, layout, ctypes.byref(out)) == 0
-        assert out.kernel == tgemm.KERNEL_GENERIC
+        assert out.kernel == tgemm.KERNEL_MASKED
+    # an operand past 2^31 bytes: the generic kernel (A is 2^16 x (2^14 + 1) halves)
+    assert q(0, 1 << 16, 8, (1 << 14) + 1, 0, ctypes.byref(out)) == 0
+    assert out.kernel == tgemm.KERNEL_GENERIC
     assert q(1, 8, 8, 8, 0, None) == -2
     assert q(1, -1, 8, 8, 0, ctypes.byref(out)) == -1
     s = raw.tgemm_status_string

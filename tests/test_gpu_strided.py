@@ -32,22 +32,36 @@ def _store(logical, transposed, pad):
     return st, K + pad
 
 
-def run_strided(dtype, A, Bn, a_layout, b_layout, pads=(8, 16, 24), config=None):
+def _shifted(st, off):
+    """A device copy of `st` starting `off` elements into its allocation (the elements
+    before it hold POISON): a base address off * 2 bytes past 16-byte alignment."""
+    flat = torch.full((off + st.size,), POISON, dtype=torch.int16, device="cuda")
+    flat[off:] = torch.from_numpy(st.reshape(-1).view(np.int16)).cuda()
+    return flat, flat[off:]
+
+
+def run_strided(dtype, A, Bn, a_layout, b_layout, pads=(8, 16, 24), config=None,
+                offsets=(0, 0, 0)):
     """C = A x Bn^T (logical A [M,K], Bn [N,K]) through gemm_strided with the given
-    storages; returns C's bits and checks that its padding was not written."""
+    storages, each base address `offsets` elements past an aligned allocation; returns
+    C's bits and checks that neither its padding nor the elements before it were
+    written."""
     from tiled_dense_gemm_major_amd import tgemm
     M, K = A.shape
     N = Bn.shape[0]
     a_st, lda = _store(A, a_layout == A_KM, pads[0])
     b_st, ldb = _store(Bn, b_layout == B_KN, pads[1])
     ldc = N + pads[2]
-    Ad = torch.from_numpy(a_st.view(np.int16)).cuda().view(tdtype(dtype))
-    Bd = torch.from_numpy(b_st.view(np.int16)).cuda().view(tdtype(dtype))
-    Cd = torch.full((max(M, 1), ldc), POISON, dtype=torch.int16, device="cuda")
-    tgemm.gemm_strided(dtype, M, N, K, Ad, lda, a_layout, Bd, ldb, b_layout,
-                       Cd.view(tdtype(dtype)), ldc, config)
+    _, Ad = _shifted(a_st, offsets[0])
+    _, Bd = _shifted(b_st, offsets[1])
+    c_all, Cd = _shifted(np.full((max(M, 1), ldc), POISON, dtype=np.uint16), offsets[2])
+    tgemm.gemm_strided(dtype, M, N, K, Ad.view(tdtype(dtype)), lda, a_layout,
+                       Bd.view(tdtype(dtype)), ldb, b_layout, Cd.view(tdtype(dtype)), ldc,
+                       config)
     torch.cuda.synchronize()
-    c = from_dev(Cd)
+    host = from_dev(c_all)
+    assert np.all(host[:offsets[2]] == POISON), "elements before C were written"
+    c = host[offsets[2]:].reshape(max(M, 1), ldc)
     assert np.all(c[:, N:] == POISON), "C padding was written"
     return c[:M, :N]
 
@@ -112,6 +126,56 @@ def test_strided_table_choice_any_alignment(dev, orc, dtype, a_layout, b_layout,
     say(f"strided table {dtype} A{a_layout} B{b_layout} {shape} pads {pads}")
     got = run_strided(dtype, A, Bn, a_layout, b_layout, pads=pads)
     assert_parity(orc, dtype, K, got, orc.gemm(dtype, A, Bn, B_NK), str((shape, pads)))
+
+
+# The masked tiled kernel (TGEMM_KERNEL_MASKED): every configuration of each storage pair
+# on operands with no alignment beyond 2 bytes -- odd sizes (K tails of 1-7 elements, M
+# and N not multiples of 8), odd leading dimensions and base addresses an odd number of
+# elements into their allocations.
+MASKED_CASES = [((77, 51, 37), (3, 5, 7), (0, 0, 0)),
+                ((613, 541, 203), (1, 3, 5), (1, 0, 3)),     # several tiles, K tail of 3
+                ((301, 262, 130), (0, 0, 0), (1, 1, 1)),     # packed rows, odd bases
+                ((130, 70, 7), (2, 1, 1), (3, 7, 1)),        # K shorter than one chunk
+                ((1, 1, 1), (0, 0, 0), (1, 1, 1))]
+
+
+def _masked_configs(dtype, a_layout, b_layout):
+    from tiled_dense_gemm_major_amd import tgemm
+    cfgs = [c for c in tgemm.list_configs(dtype, b_layout, a_layout)
+            if c.kernel == tgemm.KERNEL_MASKED]
+    assert len(cfgs) >= 2
+    return cfgs
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("a_layout,b_layout", LAYOUTS)
+def test_masked_every_config_unaligned(dev, orc, dtype, a_layout, b_layout):
+    for (M, N, K), pads, offs in MASKED_CASES:
+        A, Bn = _inputs(dtype, M, N, K, 1500 + M + K + 4 * a_layout + b_layout)
+        want = orc.gemm(dtype, A, Bn, B_NK)
+        for cfg in _masked_configs(dtype, a_layout, b_layout):
+            say(f"masked {dtype} A{a_layout} B{b_layout} {M}x{N}x{K} pads {pads} "
+                f"offsets {offs} {cfg.as_dict()}")
+            got = run_strided(dtype, A, Bn, a_layout, b_layout, pads=pads, config=cfg,
+                              offsets=offs)
+            assert_parity(orc, dtype, K, got, want, str(((M, N, K), pads, offs)))
+
+
+@pytest.mark.parametrize("a_layout,b_layout", LAYOUTS)
+def test_masked_exact_ints_bitwise(dev, orc, a_layout, b_layout):
+    """Small integers (every partial sum exact) through the masked kernel: the element
+    masks at the K tail and the M / N edges, bit for bit."""
+    for (M, N, K), pads, offs in [((523, 389, 267), (1, 1, 1), (1, 1, 1)),
+                                  ((200, 133, 64), (5, 0, 3), (0, 3, 0))]:
+        rng = np.random.default_rng(1700 + M + a_layout + 2 * b_layout)
+        A = _int_bits(BF16, rng.integers(-2, 3, (M, K)))
+        Bn = _int_bits(BF16, rng.integers(-2, 3, (N, K)))
+        want = orc.gemm(BF16, A, Bn, B_NK)
+        for cfg in _masked_configs(BF16, a_layout, b_layout):
+            say(f"masked exact A{a_layout} B{b_layout} {M}x{N}x{K} {cfg.as_dict()}")
+            got = run_strided(BF16, A, Bn, a_layout, b_layout, pads=pads, config=cfg,
+                              offsets=offs)
+            assert np.array_equal(got, want), ((M, N, K), pads, offs)
 
 
 @pytest.mark.parametrize("a_layout,b_layout", LAYOUTS)

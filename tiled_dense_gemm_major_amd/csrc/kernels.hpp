@@ -158,6 +158,13 @@ __device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t voff, uint32_t soff) 
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// One 2-byte element, for operands with no alignment beyond the element's own; an
+// offset of kOutOfRange reads zero.
+__device__ __forceinline__ u16 load2(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
 // ------------------------------------------------------------------------------------
 // The tiled kernel.
 //   Template: DT (fp16/bf16), LAYOUT (B as [N,K] or [K,N]), BM x BN x BK tile, WM x WN
@@ -167,6 +174,18 @@ __device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t voff, uint32_t soff) 
 //   Edges: a load that must not happen (a row of A past M, of B past N, a chunk with
 //   k >= K, a tile past the last) gets the offset kOutOfRange, which the buffer range
 //   check turns into zeros without a memory access; stores outside [M,N] are skipped.
+//   MASKED: the same tiles and pipeline for operands of any 2-byte alignment and any
+//   sizes (A and B still at most 2^31 bytes), read as 2-byte elements, each masked by
+//   its own k, m or n, and C stored one element at a time.  One load instruction reads
+//   64 consecutive elements of one memory row (128 contiguous bytes):
+//     K contiguous ([M,K] A, [N,K] B): a wave reads 8 whole tile rows per part (lanes
+//       0-31 the even k of the row, lanes 32-63 the odd ones) and writes each element
+//       to its place in LDS (the 32 lanes of a half-wave write 32 different words);
+//     K as the row index ([K,M] A, [K,N] B): lane l reads column 64h + l of 8
+//       consecutive k rows, which are the 8 k of one 16-byte LDS chunk of tile row
+//       64h + l, written whole (neighbouring lanes, neighbouring rows: no conflicts).
+//   The row and k positions common to the wave go into the scalar offset, the lane's
+//   own into the vector offset.
 //
 // Pipeline (two LDS stages, one register stage, double-buffered MFMA operands).  Step t
 // computes tile t from LDS stage t%2 in KS k-substeps of 16.  Alongside its MFMAs:
@@ -196,7 +215,9 @@ constexpr int staged_passes() {
             return np;
     return -1;
 }
-template <int DT, int WTM, int WTN, int NW, int CAP>
+// MASKED: C may have any 2-byte alignment and N any value, so each lane stores its eight
+// elements one by one, those at n < N only.
+template <int DT, int WTM, int WTN, int NW, int CAP, bool MASKED = false>
 __device__ __forceinline__ void store_c_staged(const f32x16 (&acc)[WTM / 32][WTN / 32],
                                                u16* lds, int wave, int lane, u16* C, int M,
                                                int N, int ldc, int mrow0, int ncol0) {
@@ -233,13 +254,24 @@ __device__ __forceinline__ void store_c_staged(const f32x16 (&acc)[WTM / 32][WTN
             const int r = q * RPR + sr;
             const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * SRS + sc);
             const int m = mrow0 + ps * HR + r;
-            if (m < M && n < N)
+            if constexpr (MASKED) {
+                if (m < M) {
+                    u16* row = C + (size_t)m * ldc + n;
+                    const u16x8 h = __builtin_bit_cast(u16x8, v);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < N)
+                            row[e] = h[e];
+                }
+            } else if (m < M && n < N) {
                 *reinterpret_cast<u32x4*>(C + (size_t)m * ldc + n) = v;
+            }
         }
     }
 }
 
-template <int DT, int ALAYOUT, int LAYOUT, int BM, int BN, int BK, int WM, int WN>
+template <int DT, int ALAYOUT, int LAYOUT, int BM, int BN, int BK, int WM, int WN,
+          bool MASKED = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64),
                                amdgpu_waves_per_eu(1, 1)))
 gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
@@ -265,6 +297,17 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
                   (LAYOUT == LAYOUT_KN || BN % RS == 0), "bad load split");
     static_assert(ALAYOUT == LAYOUT_MK || KM_BLK <= NT, "one 8x8 [K,M] block per thread");
     static_assert(LAYOUT == LAYOUT_NK || KN_BLK <= NT, "one 8x8 [K,N] block per thread");
+    // MASKED parts: 8 tile rows of a wave (K contiguous), or one 64-column x 8-k block of
+    // a wave (K as the row index); else the 16-byte loads above.
+    constexpr int NW = WM * WN;
+    constexpr int A_PARTS = !MASKED ? A_LD : (ALAYOUT == LAYOUT_MK ? BM / (8 * NW)
+                                                                     : BM / 64 * KC / NW);
+    constexpr int B_PARTS = !MASKED ? B_LD : (LAYOUT == LAYOUT_NK ? BN / (8 * NW)
+                                                                    : BN / 64 * KC / NW);
+    static_assert(!MASKED || (BK == 64 && BM % (8 * NW) == 0 && BN % (8 * NW) == 0 &&
+                              BM % 64 == 0 && BN % 64 == 0 && (BM / 64 * KC) % NW == 0 &&
+                              (BN / 64 * KC) % NW == 0),
+                  "masked parts: 64 k per tile row, whole parts per wave");
 
     __shared__ __attribute__((aligned(16))) u16 lds[2 * STAGE];
 
@@ -320,8 +363,74 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
         b_lds = A_ELEMS + (t_rb * 8) * BK;
     }
 
-    u32x4 a_reg[A_LD];
-    u32x4 b_reg[B_LD];
+    u32x4 a_reg[MASKED ? 1 : A_LD];
+    u32x4 b_reg[MASKED ? 1 : B_LD];
+    u16 a_el[MASKED ? A_PARTS : 1][8];
+    u16 b_el[MASKED ? B_PARTS : 1][8];
+    // MASKED: the wave index as a scalar (it feeds scalar offsets), this lane's k within
+    // a tile row (K contiguous), and each operand's per-lane byte offset
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int kk = 2 * (lane & 31) + (lane >> 5);
+    const uint32_t a_lane = ALAYOUT == LAYOUT_MK
+                                ? ((uint32_t)(m0 + wv * 8) * (uint32_t)lda + (uint32_t)kk) * 2u
+                                : (uint32_t)(m0 + lane) * 2u;
+    const uint32_t b_lane = LAYOUT == LAYOUT_NK
+                                ? ((uint32_t)(n0 + wv * 8) * (uint32_t)ldb + (uint32_t)kk) * 2u
+                                : (uint32_t)(n0 + lane) * 2u;
+
+    // MASKED part i of an operand (R rows of the tile, `rows` of them inside the operand,
+    // `cols` its extent along the contiguous index when K is the row index) of tile kt.
+    auto mload_part = [&](u16 (&el)[8], rsrc_t rs, uint32_t lane_off, bool kmajor, int r0,
+                          int rows, int ld, int kt, auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const bool live = kt < nk;
+        const int k0 = live ? kt * BK : 0;
+        if (kmajor) {
+            // tile rows 8 * (NW * i + wv) + j, j = 0..7; the lane's element k0 + kk
+            const bool kok = live && k0 + kk < K;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int rt = 8 * (NW * i + wv) + j;
+                const bool rok = r0 + rt < rows;
+                const uint32_t so =
+                    rok ? (uint32_t)k0 * 2u + (uint32_t)(8 * NW * i + j) * (uint32_t)ld * 2u
+                        : 0u;
+                el[j] = load2(rs, rok && kok ? lane_off : kOutOfRange, so);
+            }
+        } else {
+            // column 64h + lane of k rows 8 kb .. 8 kb + 7, (h, kb) = block NW * i + wv
+            const int q = NW * i + wv, h = q / KC, kb = q % KC;
+            const bool cok = r0 + 64 * h + lane < rows;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int kr = k0 + 8 * kb + j;
+                const bool kok = live && kr < K;
+                const uint32_t so =
+                    kok ? ((uint32_t)kr * (uint32_t)ld + (uint32_t)(64 * h)) * 2u : 0u;
+                el[j] = load2(rs, kok && cok ? lane_off : kOutOfRange, so);
+            }
+        }
+    };
+    auto mwrite_part = [&](u16* st, const u16 (&el)[8], bool kmajor, auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if (kmajor) {
+            const int kc = kk >> 3, ke = kk & 7;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int rt = 8 * (NW * i + wv) + j;
+                st[rt * BK + ((kc ^ swz<KC>(rt)) * 8) + ke] = el[j];
+            }
+        } else {
+            const int q = NW * i + wv, h = q / KC, kb = q % KC;
+            const int rt = 64 * h + lane;
+            u16x8 v;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                v[j] = el[j];
+            *reinterpret_cast<u32x4*>(st + rt * BK + ((kb ^ swz<KC>(rt)) * 8)) =
+                __builtin_bit_cast(u32x4, v);
+        }
+    };
 
     // One part of an operand's loads of tile kt: chunk i (K contiguous) or k row i of the
     // thread's 8x8 block (K as the row index).
@@ -340,16 +449,24 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
         }
     };
     auto gload_a_part = [&](int kt, auto ic) {
-        gload_part(a_reg, ra, a_off, ALAYOUT == LAYOUT_MK, km_live, lda, kt, ic);
+        if constexpr (MASKED)
+            mload_part(a_el[decltype(ic)::value], ra, a_lane, ALAYOUT == LAYOUT_MK, m0, M, lda,
+                       kt, ic);
+        else
+            gload_part(a_reg, ra, a_off, ALAYOUT == LAYOUT_MK, km_live, lda, kt, ic);
     };
     auto gload_b_part = [&](int kt, auto ic) {
-        gload_part(b_reg, rb, b_off, LAYOUT == LAYOUT_NK, kn_live, ldb, kt, ic);
+        if constexpr (MASKED)
+            mload_part(b_el[decltype(ic)::value], rb, b_lane, LAYOUT == LAYOUT_NK, n0, N, ldb,
+                       kt, ic);
+        else
+            gload_part(b_reg, rb, b_off, LAYOUT == LAYOUT_NK, kn_live, ldb, kt, ic);
     };
     auto gload_a = [&](int kt) {
-        static_for<0, A_LD>([&](auto i) { gload_a_part(kt, i); });
+        static_for<0, A_PARTS>([&](auto i) { gload_a_part(kt, i); });
     };
     auto gload_b = [&](int kt) {
-        static_for<0, B_LD>([&](auto i) { gload_b_part(kt, i); });
+        static_for<0, B_PARTS>([&](auto i) { gload_b_part(kt, i); });
     };
     // One part of an operand tile's LDS write: chunk i (K contiguous), or tile row
     // 8*rb + i of the transposed 8x8 block (reg[j] holds rows 0..7 at k = j; row i
@@ -372,16 +489,22 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
         }
     };
     auto swrite_a_part = [&](u16* st, auto ic) {
-        swrite_part(st, a_reg, a_lds, ALAYOUT == LAYOUT_MK, KM_BLK, ic);
+        if constexpr (MASKED)
+            mwrite_part(st, a_el[decltype(ic)::value], ALAYOUT == LAYOUT_MK, ic);
+        else
+            swrite_part(st, a_reg, a_lds, ALAYOUT == LAYOUT_MK, KM_BLK, ic);
     };
     auto swrite_b_part = [&](u16* st, auto ic) {
-        swrite_part(st, b_reg, b_lds, LAYOUT == LAYOUT_NK, KN_BLK, ic);
+        if constexpr (MASKED)
+            mwrite_part(st + A_ELEMS, b_el[decltype(ic)::value], LAYOUT == LAYOUT_NK, ic);
+        else
+            swrite_part(st, b_reg, b_lds, LAYOUT == LAYOUT_NK, KN_BLK, ic);
     };
     auto swrite_a = [&](u16* st) {
-        static_for<0, A_LD>([&](auto i) { swrite_a_part(st, i); });
+        static_for<0, A_PARTS>([&](auto i) { swrite_a_part(st, i); });
     };
     auto swrite_b = [&](u16* st) {
-        static_for<0, B_LD>([&](auto i) { swrite_b_part(st, i); });
+        static_for<0, B_PARTS>([&](auto i) { swrite_b_part(st, i); });
     };
 
     // ---- LDS -> MFMA operands ---------------------------------------------------------
@@ -430,8 +553,8 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
             const int kt2 = kt + 2;
             static_for<0, KS>([&](auto sc) {
                 constexpr int S = decltype(sc)::value;
-                constexpr int NWA = (S == 0) ? A_LD : 0;
-                constexpr int NWB = (S == WB) ? B_LD : 0;
+                constexpr int NWA = (S == 0) ? A_PARTS : 0;
+                constexpr int NWB = (S == WB) ? B_PARTS : 0;
                 constexpr int NOPS = NR + 2 * NWA + 2 * NWB;
                 constexpr int SLOTS = TM * TN;
                 auto mem_op = [&](auto oc) {
@@ -479,8 +602,9 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
 
     // ---- epilogue: cast once, stage through LDS, store whole row segments ----------------
     __syncthreads();
-    store_c_staged<DT, WTM, WTN, WM * WN, 2 * STAGE>(acc, lds, wave, lane, C, M, N, ldc,
-                                                     m0 + wm * WTM, n0 + wn * WTN);
+    store_c_staged<DT, WTM, WTN, WM * WN, 2 * STAGE, MASKED>(acc, lds, wave, lane, C, M, N,
+                                                             ldc, m0 + wm * WTM,
+                                                             n0 + wn * WTN);
 }
 
 // ------------------------------------------------------------------------------------

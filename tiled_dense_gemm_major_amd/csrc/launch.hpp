@@ -18,11 +18,12 @@ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
     static_cast<const u16*>(A), static_cast<const u16*>(B), static_cast<u16*>(C), M, N, K, \
         lda, ldb, ldc
 
-template <int DT, int AL, int LAYOUT, int BM, int BN, int BK, int WM, int WN>
+template <int DT, int AL, int LAYOUT, int BM, int BN, int BK, int WM, int WN,
+          bool MASKED = false>
 hipError_t launch_tiled(const void* A, const void* B, void* C, int M, int N, int K, int lda,
                         int ldb, int ldc, int group_m, hipStream_t s) {
     const int gm = cdiv(M, BM), gn = cdiv(N, BN);
-    hipLaunchKernelGGL((tgemm::gemm_tiled<DT, AL, LAYOUT, BM, BN, BK, WM, WN>),
+    hipLaunchKernelGGL((tgemm::gemm_tiled<DT, AL, LAYOUT, BM, BN, BK, WM, WN, MASKED>),
                        dim3((unsigned)(gm * gn)), dim3(WM * WN * 64), 0, s, KARGS, gm, gn,
                        group_m);
     return hipGetLastError();
@@ -176,6 +177,11 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
     Variant {                                                                              \
         DT, AL, L, tgemm_config{TGEMM_KERNEL_TILED, BM, BN, BK, WM, WN, 2, G, 1, 32},          \
             &launch_tiled<DT, AL, L, BM, BN, BK, WM, WN>                                   \
+    }
+#define MASKED_TILED(DT, AL, L, BM, BN, BK, WM, WN, G)                                    \
+    Variant {                                                                              \
+        DT, AL, L, tgemm_config{TGEMM_KERNEL_MASKED, BM, BN, BK, WM, WN, 2, G, 1, 32},         \
+            &launch_tiled<DT, AL, L, BM, BN, BK, WM, WN, true>                             \
     }
 #define GENERIC(DT, AL, L)                                                                 \
     Variant {                                                                              \

@@ -45,6 +45,7 @@ VariantList variants_quad_split();
 VariantList variants_pingpong_nk();
 VariantList variants_pingpong_other();
 VariantList variants_tiled();
+VariantList variants_masked();
 VariantList variants_small();
 
 }  // namespace tgemm_reg

@@ -34,20 +34,21 @@ bool is_split(int kernel) {
 }
 
 // Position of a kernel family in the listing order of one (A storage, B storage, dtype)
-// group: generic, tiled, direct-to-LDS ring, ping-pong, quad, skinny, split-K, quad
-// split-K, quad stream-K, direct.
+// group: generic, masked, tiled, direct-to-LDS ring, ping-pong, quad, skinny, split-K,
+// quad split-K, quad stream-K, direct.
 int family_rank(int kernel) {
     switch (kernel) {
     case TGEMM_KERNEL_GENERIC: return 0;
-    case TGEMM_KERNEL_TILED: return 1;
-    case TGEMM_KERNEL_DMA: return 2;
-    case TGEMM_KERNEL_PINGPONG: return 3;
-    case TGEMM_KERNEL_QUAD: return 4;
-    case TGEMM_KERNEL_SKINNY: return 5;
-    case TGEMM_KERNEL_SPLITK: return 6;
-    case TGEMM_KERNEL_QUAD_SPLITK: return 7;
-    case TGEMM_KERNEL_QUAD_STREAMK: return 8;
-    default: return 9;
+    case TGEMM_KERNEL_MASKED: return 1;
+    case TGEMM_KERNEL_TILED: return 2;
+    case TGEMM_KERNEL_DMA: return 3;
+    case TGEMM_KERNEL_PINGPONG: return 4;
+    case TGEMM_KERNEL_QUAD: return 5;
+    case TGEMM_KERNEL_SKINNY: return 6;
+    case TGEMM_KERNEL_SPLITK: return 7;
+    case TGEMM_KERNEL_QUAD_SPLITK: return 8;
+    case TGEMM_KERNEL_QUAD_STREAMK: return 9;
+    default: return 10;
     }
 }
 
@@ -58,7 +59,8 @@ const std::vector<const Variant*>& registry() {
     static const std::vector<const Variant*> all = [] {
         std::vector<const Variant*> v;
         for (const tgemm_reg::VariantList& l :
-             {tgemm_reg::variants_tiled(), tgemm_reg::variants_small(),
+             {tgemm_reg::variants_tiled(), tgemm_reg::variants_masked(),
+             tgemm_reg::variants_small(),
               tgemm_reg::variants_pingpong_nk(), tgemm_reg::variants_pingpong_other(),
               tgemm_reg::variants_quad(), tgemm_reg::variants_quad_kn(),
               tgemm_reg::variants_quad_km(), tgemm_reg::variants_direct(),
@@ -66,7 +68,8 @@ const std::vector<const Variant*>& registry() {
             for (int i = 0; i < l.n; ++i)
                 v.push_back(&l.v[i]);
         const auto key = [](const Variant* x) {
-            return ((x->a_layout * 2 + x->layout) * 2 + x->dtype) * 8 + family_rank(x->cfg.kernel);
+            return ((x->a_layout * 2 + x->layout) * 2 + x->dtype) * 16 +
+                   family_rank(x->cfg.kernel);
         };
         std::stable_sort(v.begin(), v.end(),
                          [&](const Variant* a, const Variant* b) { return key(a) < key(b); });
@@ -163,11 +166,23 @@ int quad_rows_by_waves(int64_t m, int64_t n) {
     return 0;
 }
 
+// Operands without the fast kernels' alignment: the masked tiled kernel, its tile by
+// how many workgroups it gives (as for the aligned tiled kernel).
+tgemm_config choose_masked(int64_t m, int64_t n) {
+    const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
+    if (t128 >= 128)
+        return tgemm_config{TGEMM_KERNEL_MASKED, 128, 128, 64, 2, 2, 2, 8, 1, 32};
+    return tgemm_config{TGEMM_KERNEL_MASKED, 64, 64, 64, 2, 2, 2, 8, 1, 32};
+}
+
+// The kernel for operands past what the masked kernel's buffer offsets reach.
+constexpr tgemm_config kGenericConfig{TGEMM_KERNEL_GENERIC, 64, 64, 16, 2, 2, 1, 8, 1, 32};
+
 tgemm_config choose(int dtype, int a_layout, int layout, int64_t m, int64_t n, int64_t k,
                     bool aligned) {
     (void)dtype;
     if (!aligned)
-        return tgemm_config{TGEMM_KERNEL_GENERIC, 64, 64, 16, 2, 2, 1, 8, 1, 32};
+        return choose_masked(m, n);
     if (a_layout == TGEMM_A_MK) {
         if (const tgemm_config* c = table_lookup(layout, m, n, k)) {
             tgemm_config cfg = *c;
@@ -325,15 +340,19 @@ bool overlaps(const void* p, int64_t pbytes, const void* q, int64_t qbytes) {
 // The fast kernels read A and B through buffer resources whose range check rejects any
 // offset with bit 31 set, which holds only for operands spanning at most 2^31 bytes; they
 // move 16-byte pieces, so every contiguous extent and leading dimension is a multiple of
-// 8 elements and every base address 16-byte aligned.
+// 8 elements and every base address 16-byte aligned.  The masked kernel reads through
+// the same resources, element by element: it needs the span limit only.
 constexpr int64_t kMaxFastOperandBytes = int64_t(1) << 31;
+
+bool buffer_reachable(const Problem& p) {
+    return 2 * span_a(p) <= kMaxFastOperandBytes && 2 * span_b(p) <= kMaxFastOperandBytes;
+}
 
 bool fast_aligned(const Problem& p) {
     const auto al16 = [](const void* q) { return ((uintptr_t)q % 16) == 0; };
     return p.k % 8 == 0 && p.n % 8 == 0 && (p.a_layout == TGEMM_A_MK || p.m % 8 == 0) &&
            p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % 8 == 0 && al16(p.A) && al16(p.B) &&
-           al16(p.C) && 2 * span_a(p) <= kMaxFastOperandBytes &&
-           2 * span_b(p) <= kMaxFastOperandBytes;
+           al16(p.C) && buffer_reachable(p);
 }
 
 // The device address of `scratch` on the current device, looked up once per device (with
@@ -382,10 +401,14 @@ int run(const Problem& p, const tgemm_config* cfg, void* ws, int64_t ws_bytes, v
     // the fixed scratch holds the skinny products' partials; a larger split goes plain
     if (!cfg && use_scratch && workspace_bytes(use, p.m, p.n) > kScratchBytes)
         use = choose(p.dtype, p.a_layout, p.b_layout, p.m, p.n, p.k, aligned);
+    const bool reachable = buffer_reachable(p);
+    if (!cfg && use.kernel == TGEMM_KERNEL_MASKED && !reachable)
+        use = kGenericConfig;
     const Variant* v = find_variant(p.dtype, p.a_layout, p.b_layout, use);
     if (!v)
         return TGEMM_ERR_UNSUPPORTED;
-    if (use.kernel != TGEMM_KERNEL_GENERIC && !aligned)
+    if (use.kernel == TGEMM_KERNEL_MASKED ? !reachable
+                                          : use.kernel != TGEMM_KERNEL_GENERIC && !aligned)
         return TGEMM_ERR_ALIGNMENT;
     const int64_t need = workspace_bytes(use, p.m, p.n);
     if (use_scratch && need > 0) {
@@ -556,6 +579,12 @@ int tgemm_query_config(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
     const Problem p = packed(dtype, m, n, k, reinterpret_cast<const void*>(uintptr_t(256)),
                              reinterpret_cast<const void*>(uintptr_t(256)),
                              reinterpret_cast<void*>(uintptr_t(256)), b_layout);
+    if (!buffer_reachable(p)) {
+        if (!out)
+            return TGEMM_ERR_NULL_POINTER;
+        *out = kGenericConfig;
+        return TGEMM_OK;
+    }
     return query(dtype, m, n, k, TGEMM_A_MK, b_layout, fast_aligned(p) ? 1 : 0, out);
 }
 

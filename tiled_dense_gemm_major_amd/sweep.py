@@ -102,7 +102,8 @@ def emit_table(tgemm, torch, np, args, stream, path):
                         rows.append((layout, mi, ni, ki, tgemm.Config.from_dict(d), us))
             continue
         cfgs = [c for c in tgemm.list_configs(BF16, layout)
-                if c.kernel != tgemm.KERNEL_GENERIC and c.kernel not in tgemm.SPLIT_KERNELS]
+                if c.kernel not in tgemm.ANY_ALIGNMENT_KERNELS
+                and c.kernel not in tgemm.SPLIT_KERNELS]
         for mi, M in enumerate(TABLE_M):
             for ni, N in enumerate(TABLE_N):
                 for ki, K in enumerate(TABLE_K):
@@ -282,7 +283,7 @@ def main(argv=None):
         for cfg in tgemm.list_configs(w.dtype, w.b_layout, a_layout):
             if kernels and cfg.kernel not in kernels:
                 continue
-            if not aligned and cfg.kernel != tgemm.KERNEL_GENERIC:
+            if not aligned and cfg.kernel not in tgemm.ANY_ALIGNMENT_KERNELS:
                 continue                                # the fast kernels refuse these
             if a_layout:                                # the general entry point
                 def go(i, c=cfg):

@@ -13,7 +13,10 @@ F16, BF16 = 0, 1
 B_NK, B_KN = 0, 1
 A_MK, A_KM = 0, 1
 (KERNEL_GENERIC, KERNEL_TILED, KERNEL_SKINNY, KERNEL_DMA, KERNEL_PINGPONG, KERNEL_QUAD,
- KERNEL_SPLITK, KERNEL_DIRECT, KERNEL_QUAD_SPLITK, KERNEL_QUAD_STREAMK) = range(10)
+ KERNEL_SPLITK, KERNEL_DIRECT, KERNEL_QUAD_SPLITK, KERNEL_QUAD_STREAMK,
+ KERNEL_MASKED) = range(11)
+# the kernels that take operands of any 2-byte alignment
+ANY_ALIGNMENT_KERNELS = (KERNEL_GENERIC, KERNEL_MASKED)
 SPLIT_KERNELS = (KERNEL_SPLITK, KERNEL_QUAD_SPLITK)   # split K over workgroups (workspace)
 STREAMK_WORKSPACE_BYTES = 128 << 20                   # a QUAD_STREAMK configuration's
 
@@ -33,7 +36,8 @@ EXPORTS = ("attn_fwd_f16", "gemm_f16", "gemm_bf16", "gemm_ex", "gemm_ex_ws", "ge
 
 __all__ = ["F16", "BF16", "B_NK", "B_KN", "A_MK", "A_KM", "KERNEL_GENERIC", "KERNEL_TILED",
            "KERNEL_SKINNY", "KERNEL_DMA", "KERNEL_PINGPONG", "KERNEL_QUAD", "KERNEL_SPLITK",
-           "KERNEL_QUAD_SPLITK", "KERNEL_QUAD_STREAMK", "SPLIT_KERNELS",
+           "KERNEL_QUAD_SPLITK", "KERNEL_QUAD_STREAMK", "KERNEL_MASKED", "SPLIT_KERNELS",
+           "ANY_ALIGNMENT_KERNELS",
            "STREAMK_WORKSPACE_BYTES",
            "KERNEL_DIRECT",
            "LIB_PATH", "EXPORTS", "TGemmError", "Config", "load", "status_string", "gemm_f16",
