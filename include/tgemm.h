@@ -36,8 +36,8 @@
  *   - Alignment: any 2-byte-aligned pointers, sizes and leading dimensions are accepted.
  *     The fast kernels need A, B, C 16-byte aligned, K, N, lda, ldb and ldc multiples of
  *     8, M a multiple of 8 when A is [K,M], and A and B each spanning at most 2^31 bytes;
- *     other calls run the same tiles with element-wise loads and stores
- *     (TGEMM_KERNEL_MASKED), or, when A or B spans more than 2^31 bytes, a slower
+ *     other calls run the same tiles with masked loads and element-wise stores
+ *     (TGEMM_KERNEL_MASKED), or, when A or B spans more than 2^31 - 32 bytes, a slower
  *     generic kernel; the arithmetic is the same.
  *   - Limits: M, N, K < 2^31, M*K, N*K, M*N < 2^31, and the element span of each operand
  *     ((rows - 1) * ld + row length) < 2^31 (TGEMM_ERR_UNSUPPORTED).
@@ -127,9 +127,12 @@ typedef enum {
                                  tile segments each, fp32 partial tiles in the
                                  workspace) and a reduction in workgroup order        */
     TGEMM_KERNEL_MASKED = 10  /* the TILED kernel for operands of any 2-byte alignment
-                                 and any sizes (A and B each at most 2^31 bytes): each
-                                 16-byte piece of a tile read as eight 2-byte elements,
-                                 masked one by one, and C stored element by element    */
+                                 and any sizes (A and B each at most 2^31 - 32 bytes):
+                                 K-contiguous tile rows read as the aligned 16-byte
+                                 blocks around each piece and realigned in registers,
+                                 [K,M] A and [K,N] B as 2-byte elements, every element
+                                 masked by its own position; C stored element by
+                                 element                                                */
 } tgemm_kernel;
 
 /* One tile configuration.  block_m x block_n is the C tile of one workgroup, block_k
@@ -243,7 +246,7 @@ int gemm_strided(int dtype, int64_t m, int64_t n, int64_t k, const void* A, int6
  * problem (A [M,K], B per b_layout, C [M,N], no padding) with operands at 16-byte-aligned
  * addresses, written to *out; whether the fast kernels can take it follows from the sizes
  * (K and N multiples of 8, A and B each at most 2^31 bytes; else the masked kernel, or
- * the generic one past 2^31 bytes).  Host-only: it touches no
+ * the generic one past 2^31 - 32 bytes).  Host-only: it touches no
  * device.  Returns TGEMM_OK, TGEMM_ERR_NULL_POINTER (out NULL) or the size, dtype and
  * layout errors of gemm_ex. */
 int tgemm_query_config(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
@@ -258,7 +261,7 @@ int tgemm_list_configs(int dtype, int b_layout, tgemm_config* out, int capacity)
  * `aligned` != 0 says the operands meet every fast-kernel rule (16-byte-aligned
  * addresses, sizes and leading dimensions multiples of 8, spans within 2^31 bytes),
  * 0 that they do not (the choice is then a TGEMM_KERNEL_MASKED configuration; a call
- * whose A or B spans more than 2^31 bytes runs the generic kernel instead, which this
+ * whose A or B spans more than 2^31 - 32 bytes runs the generic kernel instead, which this
  * query cannot see).  The list for either storage of A; tgemm_list_configs answers for
  * TGEMM_A_MK. */
 int tgemm_query_config_ex(int dtype, int64_t m, int64_t n, int64_t k, int a_layout,

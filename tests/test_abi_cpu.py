@@ -104,6 +104,29 @@ def test_query_config_table(lib):
         tgemm.query_config(tgemm.BF16, -1, 8, 8)
 
 
+def test_masked_tile_rule(lib):
+    # unaligned operands: the masked kernel, its tile by the tiles it gives; the larger
+    # tiles only where both operands are K-contiguous (read as realigned 16-byte blocks)
+    def q(m, n, k, b_layout=tgemm.B_NK, a_layout=tgemm.A_MK):
+        c = tgemm.query_config(tgemm.BF16, m, n, k, b_layout, False, a_layout)
+        assert c.kernel == tgemm.KERNEL_MASKED
+        return c.block_m, c.block_n
+    # (waves of 256 tiles) x (relative tile time 1, 0.646, 0.373, 0.180)
+    assert q(4096, 4096, 4094) == (256, 256)      # 1 x 1 against 2 x 0.646, 4 x 0.373
+    assert q(3000, 3000, 3001) == (256, 256)      # 144 tiles: 1 against 2 x 0.646
+    assert q(2000, 3000, 1001) == (128, 256)      # 192 tiles of 128x256; 384 of 128x128
+    assert q(6000, 1100, 999) == (128, 256)       # ties with 256x128 go to 128x256
+    assert q(2048, 2048, 2047) == (128, 128)      # 256 tiles of 128x128: one wave
+    assert q(1000, 1000, 999) == (64, 64)         # 256 tiles of 64x64: one wave
+    assert q(4096, 4096, 4094, tgemm.B_KN) == (128, 128)
+    assert q(4096, 4096, 4094, tgemm.B_NK, tgemm.A_KM) == (128, 128)
+    assert q(1000, 1000, 999, tgemm.B_KN) == (64, 64)
+    listed = {tuple(sorted(c.as_dict().items())) for c in tgemm.list_configs(tgemm.BF16)}
+    for shape in [(4096, 4096, 4094), (2000, 3000, 1001), (6000, 1100, 999)]:
+        c = tgemm.query_config(tgemm.BF16, *shape, tgemm.B_NK, False)
+        assert tuple(sorted(c.as_dict().items())) in listed
+
+
 def test_list_configs(lib):
     for dt in (tgemm.F16, tgemm.BF16):
         for lay in (tgemm.B_NK, tgemm.B_KN):
@@ -341,6 +364,11 @@ def test_boundary_calls_with_exact_arity(lib):
         assert out.kernel == tgemm.KERNEL_MASKED
     # an operand past 2^31 bytes: the generic kernel (A is 2^16 x (2^14 + 1) halves)
     assert q(0, 1 << 16, 8, (1 << 14) + 1, 0, ctypes.byref(out)) == 0
+    assert out.kernel == tgemm.KERNEL_GENERIC
+    # the masked kernel's buffers reach 30 bytes past an operand: up to 2^31 - 32 bytes
+    assert q(0, 1, 1, (1 << 30) - 16, 0, ctypes.byref(out)) == 0      # 2^31 - 32 bytes
+    assert out.kernel == tgemm.KERNEL_MASKED
+    assert q(0, 1, 1, (1 << 30) - 15, 0, ctypes.byref(out)) == 0      # 2^31 - 30 bytes
     assert out.kernel == tgemm.KERNEL_GENERIC
     assert q(1, 8, 8, 8, 0, None) == -2
     assert q(1, -1, 8, 8, 0, ctypes.byref(out)) == -1

@@ -165,6 +165,35 @@ __device__ __forceinline__ u16 load2(rsrc_t r, uint32_t voff, uint32_t soff) {
 }
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
+// Sixteen bytes starting `sh` bytes (even, 0..14) into the 32 bytes lo:hi (two aligned
+// 16-byte blocks loaded back to back): a two-stage select of the five words from
+// sh / 4 on, written as bit operations (a select between array elements could become a
+// dynamic index, which the compiler would place in memory), then a funnel shift by
+// (sh % 4) bytes.
+__device__ __forceinline__ u32x4 realign16(u32x4 lo, u32x4 hi, uint32_t sh) {
+    const uint32_t w0 = lo[0], w1 = lo[1], w2 = lo[2], w3 = lo[3];
+    const uint32_t w4 = hi[0], w5 = hi[1], w6 = hi[2], w7 = hi[3];
+    const uint32_t m8 = 0u - ((sh >> 3) & 1u), m4 = 0u - ((sh >> 2) & 1u);
+    const uint32_t bits = (sh & 2u) * 8u;
+    const auto pick = [](uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); };
+    const uint32_t s0 = pick(m8, w2, w0), s1 = pick(m8, w3, w1), s2 = pick(m8, w4, w2),
+                   s3 = pick(m8, w5, w3), s4 = pick(m8, w6, w4), s5 = pick(m8, w7, w5);
+    const uint32_t t0 = pick(m4, s1, s0), t1 = pick(m4, s2, s1), t2 = pick(m4, s3, s2),
+                   t3 = pick(m4, s4, s3), t4 = pick(m4, s5, s4);
+    return u32x4{__builtin_amdgcn_alignbit(t1, t0, bits), __builtin_amdgcn_alignbit(t2, t1, bits),
+                 __builtin_amdgcn_alignbit(t3, t2, bits), __builtin_amdgcn_alignbit(t4, t3, bits)};
+}
+
+// Word masks keeping the first `left` 2-byte elements of an 8-element chunk (left <= 0:
+// none, >= 8: all).
+__device__ __forceinline__ u32x4 first_elems_mask(int left) {
+    u32x4 m;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        m[j] = 2 * j + 1 < left ? 0xffffffffu : (2 * j < left ? 0x0000ffffu : 0u);
+    return m;
+}
+
 // ------------------------------------------------------------------------------------
 // The tiled kernel.
 //   Template: DT (fp16/bf16), LAYOUT (B as [N,K] or [K,N]), BM x BN x BK tile, WM x WN
@@ -175,17 +204,20 @@ typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 //   k >= K, a tile past the last) gets the offset kOutOfRange, which the buffer range
 //   check turns into zeros without a memory access; stores outside [M,N] are skipped.
 //   MASKED: the same tiles and pipeline for operands of any 2-byte alignment and any
-//   sizes (A and B still at most 2^31 bytes), read as 2-byte elements, each masked by
-//   its own k, m or n, and C stored one element at a time.  One load instruction reads
-//   64 consecutive elements of one memory row (128 contiguous bytes):
-//     K contiguous ([M,K] A, [N,K] B): a wave reads 8 whole tile rows per part (lanes
-//       0-31 the even k of the row, lanes 32-63 the odd ones) and writes each element
-//       to its place in LDS (the 32 lanes of a half-wave write 32 different words);
-//     K as the row index ([K,M] A, [K,N] B): lane l reads column 64h + l of 8
-//       consecutive k rows, which are the 8 k of one 16-byte LDS chunk of tile row
-//       64h + l, written whole (neighbouring lanes, neighbouring rows: no conflicts).
-//   The row and k positions common to the wave go into the scalar offset, the lane's
-//   own into the vector offset.
+//   sizes (A and B each at most 2^31 - 32 bytes), and C stored one element at a time.
+//     K contiguous ([M,K] A, [N,K] B): each 16-byte chunk of a tile row is read as the
+//       two aligned 16-byte blocks around it, through a buffer whose base is the
+//       operand's address rounded down to 16 bytes and whose size is rounded up to 16
+//       (so no block reaches past the operand's last 16-byte block), with the whole
+//       offset in the range-checked vector offset; the chunk's shift within the blocks
+//       is fixed per row (chunks start 16 bytes apart), and the chunk is realigned in
+//       registers and, in the last K tile, masked to the elements below K;
+//     K as the row index ([K,M] A, [K,N] B): 2-byte loads, each masked by its own k
+//       and column: lane l reads column 64h + l of 8 consecutive k rows (one load
+//       instruction reads 128 contiguous bytes), which are the 8 k of one 16-byte LDS
+//       chunk of tile row 64h + l, written whole (neighbouring lanes, neighbouring
+//       rows: no conflicts); the row and k positions common to the wave go into the
+//       scalar offset.
 //
 // Pipeline (two LDS stages, one register stage, double-buffered MFMA operands).  Step t
 // computes tile t from LDS stage t%2 in KS k-substeps of 16.  Alongside its MFMAs:
@@ -300,13 +332,10 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
     // MASKED parts: 8 tile rows of a wave (K contiguous), or one 64-column x 8-k block of
     // a wave (K as the row index); else the 16-byte loads above.
     constexpr int NW = WM * WN;
-    constexpr int A_PARTS = !MASKED ? A_LD : (ALAYOUT == LAYOUT_MK ? BM / (8 * NW)
-                                                                     : BM / 64 * KC / NW);
-    constexpr int B_PARTS = !MASKED ? B_LD : (LAYOUT == LAYOUT_NK ? BN / (8 * NW)
-                                                                    : BN / 64 * KC / NW);
-    static_assert(!MASKED || (BK == 64 && BM % (8 * NW) == 0 && BN % (8 * NW) == 0 &&
-                              BM % 64 == 0 && BN % 64 == 0 && (BM / 64 * KC) % NW == 0 &&
-                              (BN / 64 * KC) % NW == 0),
+    constexpr int A_PARTS = !MASKED || ALAYOUT == LAYOUT_MK ? A_LD : BM / 64 * KC / NW;
+    constexpr int B_PARTS = !MASKED || LAYOUT == LAYOUT_NK ? B_LD : BN / 64 * KC / NW;
+    static_assert(!MASKED || (BK == 64 && BM % 64 == 0 && BN % 64 == 0 &&
+                              (BM / 64 * KC) % NW == 0 && (BN / 64 * KC) % NW == 0),
                   "masked parts: 64 k per tile row, whole parts per wave");
 
     __shared__ __attribute__((aligned(16))) u16 lds[2 * STAGE];
@@ -318,10 +347,22 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
     const int wm = wave / WN, wn = wave % WN;
     const int nk = (K + BK - 1) / BK;
 
-    const rsrc_t ra = ALAYOUT == LAYOUT_MK ? make_rsrc(A, span_bytes(M, K, lda))
-                                           : make_rsrc(A, span_bytes(K, M, lda));
-    const rsrc_t rb = LAYOUT == LAYOUT_NK ? make_rsrc(B, span_bytes(N, K, ldb))
-                                          : make_rsrc(B, span_bytes(K, N, ldb));
+    // MASKED, K contiguous: a_d / b_d is the operand's byte offset past 16-byte alignment;
+    // its buffer starts that many bytes lower and ends at the next 16-byte boundary.
+    constexpr bool A_RA = MASKED && ALAYOUT == LAYOUT_MK, B_RA = MASKED && LAYOUT == LAYOUT_NK;
+    const uint32_t a_d = A_RA ? (uint32_t)((uintptr_t)A & 15u) : 0u;
+    const uint32_t b_d = B_RA ? (uint32_t)((uintptr_t)B & 15u) : 0u;
+    const auto round16 = [](uint32_t x) { return (x + 15u) & ~15u; };
+    const rsrc_t ra =
+        A_RA ? make_rsrc(reinterpret_cast<const char*>(A) - a_d,
+                         round16(a_d + span_bytes(M, K, lda)))
+             : (ALAYOUT == LAYOUT_MK ? make_rsrc(A, span_bytes(M, K, lda))
+                                     : make_rsrc(A, span_bytes(K, M, lda)));
+    const rsrc_t rb =
+        B_RA ? make_rsrc(reinterpret_cast<const char*>(B) - b_d,
+                         round16(b_d + span_bytes(N, K, ldb)))
+             : (LAYOUT == LAYOUT_NK ? make_rsrc(B, span_bytes(N, K, ldb))
+                                    : make_rsrc(B, span_bytes(K, N, ldb)));
 
     // ---- global -> register addressing (byte offsets; the K position goes in soffset) --
     const int lc = tid % KC;                 // this thread's chunk column (row-major loads)
@@ -334,11 +375,18 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
     uint32_t a_off[ALAYOUT == LAYOUT_MK ? A_LD : 1];
     int a_lds;
     bool km_live = true;
+    uint32_t a_sh[A_RA ? A_LD : 1];      // MASKED: each row's chunk shift in bytes
     if constexpr (ALAYOUT == LAYOUT_MK) {
 #pragma unroll
         for (int i = 0; i < A_LD; ++i) {
             const int r = m0 + lr + i * RS;
-            a_off[i] = r < M ? (uint32_t)(r * lda + lc * 8) * 2u : kOutOfRange;
+            if constexpr (A_RA) {
+                const uint32_t at = a_d + (uint32_t)(r * lda + lc * 8) * 2u;
+                a_off[i] = r < M ? at & ~15u : kOutOfRange;
+                a_sh[i] = at & 15u;
+            } else {
+                a_off[i] = r < M ? (uint32_t)(r * lda + lc * 8) * 2u : kOutOfRange;
+            }
         }
         a_lds = lr * BK + ((lc ^ swz<KC>(lr)) * 8);
     } else {
@@ -350,11 +398,18 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
     uint32_t b_off[LAYOUT == LAYOUT_NK ? B_LD : 1];
     int b_lds;
     bool kn_live = true;
+    uint32_t b_sh[B_RA ? B_LD : 1];
     if constexpr (LAYOUT == LAYOUT_NK) {
 #pragma unroll
         for (int i = 0; i < B_LD; ++i) {
             const int r = n0 + lr + i * RS;
-            b_off[i] = r < N ? (uint32_t)(r * ldb + lc * 8) * 2u : kOutOfRange;
+            if constexpr (B_RA) {
+                const uint32_t at = b_d + (uint32_t)(r * ldb + lc * 8) * 2u;
+                b_off[i] = r < N ? at & ~15u : kOutOfRange;
+                b_sh[i] = at & 15u;
+            } else {
+                b_off[i] = r < N ? (uint32_t)(r * ldb + lc * 8) * 2u : kOutOfRange;
+            }
         }
         b_lds = A_ELEMS + lr * BK + ((lc ^ swz<KC>(lr)) * 8);
     } else {
@@ -363,73 +418,49 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
         b_lds = A_ELEMS + (t_rb * 8) * BK;
     }
 
-    u32x4 a_reg[MASKED ? 1 : A_LD];
-    u32x4 b_reg[MASKED ? 1 : B_LD];
-    u16 a_el[MASKED ? A_PARTS : 1][8];
-    u16 b_el[MASKED ? B_PARTS : 1][8];
-    // MASKED: the wave index as a scalar (it feeds scalar offsets), this lane's k within
-    // a tile row (K contiguous), and each operand's per-lane byte offset
+    u32x4 a_reg[MASKED && !A_RA ? 1 : A_LD];
+    u32x4 b_reg[MASKED && !B_RA ? 1 : B_LD];
+    u32x4 a_hi[A_RA ? A_LD : 1];          // MASKED, K contiguous: the second block
+    u32x4 b_hi[B_RA ? B_LD : 1];
+    u16 a_el[MASKED && !A_RA ? A_PARTS : 1][8];
+    u16 b_el[MASKED && !B_RA ? B_PARTS : 1][8];
+    // MASKED, K as the row index: the wave index as a scalar (it feeds scalar offsets)
+    // and each operand's per-lane byte offset (column m0 + lane, n0 + lane).
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const int kk = 2 * (lane & 31) + (lane >> 5);
-    const uint32_t a_lane = ALAYOUT == LAYOUT_MK
-                                ? ((uint32_t)(m0 + wv * 8) * (uint32_t)lda + (uint32_t)kk) * 2u
-                                : (uint32_t)(m0 + lane) * 2u;
-    const uint32_t b_lane = LAYOUT == LAYOUT_NK
-                                ? ((uint32_t)(n0 + wv * 8) * (uint32_t)ldb + (uint32_t)kk) * 2u
-                                : (uint32_t)(n0 + lane) * 2u;
+    const uint32_t a_lane = (uint32_t)(m0 + lane) * 2u;
+    const uint32_t b_lane = (uint32_t)(n0 + lane) * 2u;
 
-    // MASKED part i of an operand (R rows of the tile, `rows` of them inside the operand,
-    // `cols` its extent along the contiguous index when K is the row index) of tile kt.
-    auto mload_part = [&](u16 (&el)[8], rsrc_t rs, uint32_t lane_off, bool kmajor, int r0,
-                          int rows, int ld, int kt, auto ic) {
+    // MASKED, K as the row index: part i of an operand (`rows` columns inside it from
+    // column r0 on) of tile kt: column 64h + lane of k rows 8 kb .. 8 kb + 7, with
+    // (h, kb) = block NW * i + wv; then its 16-byte LDS write into tile row 64h + lane.
+    auto mload_part = [&](u16 (&el)[8], rsrc_t rs, uint32_t lane_off, int r0, int rows,
+                          int ld, int kt, auto ic) {
         constexpr int i = decltype(ic)::value;
         const bool live = kt < nk;
         const int k0 = live ? kt * BK : 0;
-        if (kmajor) {
-            // tile rows 8 * (NW * i + wv) + j, j = 0..7; the lane's element k0 + kk
-            const bool kok = live && k0 + kk < K;
+        const int q = NW * i + wv, h = q / KC, kb = q % KC;
+        const bool cok = r0 + 64 * h + lane < rows;
+        // (the range check sees the vector offset only: an element out of range needs no
+        // particular scalar offset; & rather than && and an unconditional scalar offset
+        // keep these selects, not branches)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int rt = 8 * (NW * i + wv) + j;
-                const bool rok = r0 + rt < rows;
-                const uint32_t so =
-                    rok ? (uint32_t)k0 * 2u + (uint32_t)(8 * NW * i + j) * (uint32_t)ld * 2u
-                        : 0u;
-                el[j] = load2(rs, rok && kok ? lane_off : kOutOfRange, so);
-            }
-        } else {
-            // column 64h + lane of k rows 8 kb .. 8 kb + 7, (h, kb) = block NW * i + wv
-            const int q = NW * i + wv, h = q / KC, kb = q % KC;
-            const bool cok = r0 + 64 * h + lane < rows;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int kr = k0 + 8 * kb + j;
-                const bool kok = live && kr < K;
-                const uint32_t so =
-                    kok ? ((uint32_t)kr * (uint32_t)ld + (uint32_t)(64 * h)) * 2u : 0u;
-                el[j] = load2(rs, kok && cok ? lane_off : kOutOfRange, so);
-            }
+        for (int j = 0; j < 8; ++j) {
+            const int kr = k0 + 8 * kb + j;
+            const bool kok = live & (kr < K);
+            const uint32_t so = ((uint32_t)kr * (uint32_t)ld + (uint32_t)(64 * h)) * 2u;
+            el[j] = load2(rs, (kok & cok) ? lane_off : kOutOfRange, so);
         }
     };
-    auto mwrite_part = [&](u16* st, const u16 (&el)[8], bool kmajor, auto ic) {
+    auto mwrite_part = [&](u16* st, const u16 (&el)[8], auto ic) {
         constexpr int i = decltype(ic)::value;
-        if (kmajor) {
-            const int kc = kk >> 3, ke = kk & 7;
+        const int q = NW * i + wv, h = q / KC, kb = q % KC;
+        const int rt = 64 * h + lane;
+        u16x8 v;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int rt = 8 * (NW * i + wv) + j;
-                st[rt * BK + ((kc ^ swz<KC>(rt)) * 8) + ke] = el[j];
-            }
-        } else {
-            const int q = NW * i + wv, h = q / KC, kb = q % KC;
-            const int rt = 64 * h + lane;
-            u16x8 v;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                v[j] = el[j];
-            *reinterpret_cast<u32x4*>(st + rt * BK + ((kb ^ swz<KC>(rt)) * 8)) =
-                __builtin_bit_cast(u32x4, v);
-        }
+        for (int j = 0; j < 8; ++j)
+            v[j] = el[j];
+        *reinterpret_cast<u32x4*>(st + rt * BK + ((kb ^ swz<KC>(rt)) * 8)) =
+            __builtin_bit_cast(u32x4, v);
     };
 
     // One part of an operand's loads of tile kt: chunk i (K contiguous) or k row i of the
@@ -448,17 +479,33 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
                             (uint32_t)k0 * (uint32_t)ld * 2u);
         }
     };
+    // MASKED, K contiguous: chunk i's two aligned blocks of tile kt, the whole offset in
+    // the vector offset (range-checked), out of range for a chunk at or past K.
+    auto rload_part = [&](u32x4* lo, u32x4* hi, rsrc_t rs, const uint32_t* off, int kt,
+                          auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const bool live = kt < nk;
+        const int k0 = live ? kt * BK : 0;
+        // (a row past the edge has off[i] = kOutOfRange, which stays out of range with
+        // the K offset added; & rather than && keeps this a select, not a branch)
+        const uint32_t at = off[i] + (uint32_t)k0 * 2u;
+        const uint32_t vo = (live & (k0 + lc * 8 < K)) ? at : kOutOfRange;
+        lo[i] = load16(rs, vo, 0u);
+        hi[i] = load16(rs, vo + 16u, 0u);
+    };
     auto gload_a_part = [&](int kt, auto ic) {
-        if constexpr (MASKED)
-            mload_part(a_el[decltype(ic)::value], ra, a_lane, ALAYOUT == LAYOUT_MK, m0, M, lda,
-                       kt, ic);
+        if constexpr (A_RA)
+            rload_part(a_reg, a_hi, ra, a_off, kt, ic);
+        else if constexpr (MASKED)
+            mload_part(a_el[decltype(ic)::value], ra, a_lane, m0, M, lda, kt, ic);
         else
             gload_part(a_reg, ra, a_off, ALAYOUT == LAYOUT_MK, km_live, lda, kt, ic);
     };
     auto gload_b_part = [&](int kt, auto ic) {
-        if constexpr (MASKED)
-            mload_part(b_el[decltype(ic)::value], rb, b_lane, LAYOUT == LAYOUT_NK, n0, N, ldb,
-                       kt, ic);
+        if constexpr (B_RA)
+            rload_part(b_reg, b_hi, rb, b_off, kt, ic);
+        else if constexpr (MASKED)
+            mload_part(b_el[decltype(ic)::value], rb, b_lane, n0, N, ldb, kt, ic);
         else
             gload_part(b_reg, rb, b_off, LAYOUT == LAYOUT_NK, kn_live, ldb, kt, ic);
     };
@@ -488,23 +535,41 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
                                       ((t_kb ^ swz<KC>(t_rb * 8 + i)) * 8)) = o;
         }
     };
-    auto swrite_a_part = [&](u16* st, auto ic) {
-        if constexpr (MASKED)
-            mwrite_part(st, a_el[decltype(ic)::value], ALAYOUT == LAYOUT_MK, ic);
-        else
+    // MASKED, K contiguous: chunk i of tile kt realigned and, in the last K tile, cut to
+    // the elements below K (tail_keep: this lane's chunk mask there), in place, ready for
+    // the plain chunk write.  Branch-free: other tiles OR the mask with all ones.
+    const u32x4 tail_keep =
+        A_RA || B_RA ? first_elems_mask(K - ((nk > 0 ? nk - 1 : 0) * BK + lc * 8)) : u32x4{};
+    auto realign_part = [&](u32x4* lo, const u32x4* hi, const uint32_t* sh, int kt, auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const uint32_t keep_all = kt * BK + BK > K ? 0u : 0xffffffffu;
+        lo[i] = realign16(lo[i], hi[i], sh[i]) & (tail_keep | keep_all);
+    };
+    auto swrite_a_part = [&](u16* st, int kt, auto ic) {
+        if constexpr (A_RA) {
+            realign_part(a_reg, a_hi, a_sh, kt, ic);
+            swrite_part(st, a_reg, a_lds, true, KM_BLK, ic);
+        } else if constexpr (MASKED) {
+            mwrite_part(st, a_el[decltype(ic)::value], ic);
+        } else {
             swrite_part(st, a_reg, a_lds, ALAYOUT == LAYOUT_MK, KM_BLK, ic);
+        }
     };
-    auto swrite_b_part = [&](u16* st, auto ic) {
-        if constexpr (MASKED)
-            mwrite_part(st + A_ELEMS, b_el[decltype(ic)::value], LAYOUT == LAYOUT_NK, ic);
-        else
+    auto swrite_b_part = [&](u16* st, int kt, auto ic) {
+        if constexpr (B_RA) {
+            realign_part(b_reg, b_hi, b_sh, kt, ic);
+            swrite_part(st, b_reg, b_lds, true, KN_BLK, ic);
+        } else if constexpr (MASKED) {
+            mwrite_part(st + A_ELEMS, b_el[decltype(ic)::value], ic);
+        } else {
             swrite_part(st, b_reg, b_lds, LAYOUT == LAYOUT_NK, KN_BLK, ic);
+        }
     };
-    auto swrite_a = [&](u16* st) {
-        static_for<0, A_PARTS>([&](auto i) { swrite_a_part(st, i); });
+    auto swrite_a = [&](u16* st, int kt) {
+        static_for<0, A_PARTS>([&](auto i) { swrite_a_part(st, kt, i); });
     };
-    auto swrite_b = [&](u16* st) {
-        static_for<0, B_PARTS>([&](auto i) { swrite_b_part(st, i); });
+    auto swrite_b = [&](u16* st, int kt) {
+        static_for<0, B_PARTS>([&](auto i) { swrite_b_part(st, kt, i); });
     };
 
     // ---- LDS -> MFMA operands ---------------------------------------------------------
@@ -534,8 +599,8 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
     if (nk > 0) {
         gload_a(0);
         gload_b(0);
-        swrite_a(lds);
-        swrite_b(lds);
+        swrite_a(lds, 0);
+        swrite_b(lds, 0);
         gload_a(1);
         gload_b(1);
         block_sync_lds();
@@ -566,13 +631,13 @@ gemm_tiled(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict
                             read_frag(nxt, 0, 0, std::integral_constant<int, O>{});
                     } else if constexpr (O < NR + NWA) {
                         constexpr int i = O - NR;
-                        swrite_a_part(nxt, std::integral_constant<int, i>{});
+                        swrite_a_part(nxt, kt + 1, std::integral_constant<int, i>{});
                     } else if constexpr (O < NR + 2 * NWA) {
                         constexpr int i = O - NR - NWA;
                         gload_a_part(kt2, std::integral_constant<int, i>{});
                     } else if constexpr (O < NR + 2 * NWA + NWB) {
                         constexpr int i = O - NR - 2 * NWA;
-                        swrite_b_part(nxt, std::integral_constant<int, i>{});
+                        swrite_b_part(nxt, kt + 1, std::integral_constant<int, i>{});
                     } else {
                         constexpr int i = O - NR - 2 * NWA - NWB;
                         gload_b_part(kt2, std::integral_constant<int, i>{});

@@ -46,6 +46,7 @@ VariantList variants_pingpong_nk();
 VariantList variants_pingpong_other();
 VariantList variants_tiled();
 VariantList variants_masked();
+VariantList variants_masked_nk();
 VariantList variants_small();
 
 }  // namespace tgemm_reg

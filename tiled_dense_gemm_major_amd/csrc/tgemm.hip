@@ -59,8 +59,8 @@ const std::vector<const Variant*>& registry() {
     static const std::vector<const Variant*> all = [] {
         std::vector<const Variant*> v;
         for (const tgemm_reg::VariantList& l :
-             {tgemm_reg::variants_tiled(), tgemm_reg::variants_masked(),
-             tgemm_reg::variants_small(),
+             {tgemm_reg::variants_tiled(), tgemm_reg::variants_masked_nk(),
+             tgemm_reg::variants_masked(), tgemm_reg::variants_small(),
               tgemm_reg::variants_pingpong_nk(), tgemm_reg::variants_pingpong_other(),
               tgemm_reg::variants_quad(), tgemm_reg::variants_quad_kn(),
               tgemm_reg::variants_quad_km(), tgemm_reg::variants_direct(),
@@ -166,13 +166,38 @@ int quad_rows_by_waves(int64_t m, int64_t n) {
     return 0;
 }
 
-// Operands without the fast kernels' alignment: the masked tiled kernel, its tile by
-// how many workgroups it gives (as for the aligned tiled kernel).
-tgemm_config choose_masked(int64_t m, int64_t n) {
-    const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
-    if (t128 >= 128)
-        return tgemm_config{TGEMM_KERNEL_MASKED, 128, 128, 64, 2, 2, 2, 8, 1, 32};
-    return tgemm_config{TGEMM_KERNEL_MASKED, 64, 64, 64, 2, 2, 2, 8, 1, 32};
+// Operands without the fast kernels' alignment: the masked tiled kernel, with the tile
+// that minimises (waves of 256 workgroups) x (one tile's time).  The tile times relative
+// to 256x256 (1, 0.646, 0.373, 0.180 for 256x256, 128x256 or 256x128, 128x128, 64x64)
+// are the per-wave times of bf16 4096x4096x4094, which fills the chip with every tile;
+// the model picked the fastest tile on all 7 shapes timed against it (1024^2 to 4096^2,
+// square, wide and tall).  The tiles above 128x128 only where A [M,K] and B [N,K] are
+// both read as realigned 16-byte blocks; an operand read as 2-byte elements holds a
+// register per element, and larger tiles would spill.
+tgemm_config choose_masked(int a_layout, int layout, int64_t m, int64_t n) {
+    struct Option {
+        int bm, bn, group;
+        double tile_time;
+    };
+    static const Option kOptions[] = {{256, 256, 4, 1.0},
+                                      {128, 256, 8, 0.646},
+                                      {256, 128, 8, 0.646},
+                                      {128, 128, 8, 0.373},
+                                      {64, 64, 8, 0.180}};
+    const bool large = a_layout == TGEMM_A_MK && layout == TGEMM_B_NK;
+    const Option* best = nullptr;
+    double best_cost = 0;
+    for (const Option& o : kOptions) {
+        if (!large && (o.bm > 128 || o.bn > 128))
+            continue;
+        const int64_t tiles = ((m + o.bm - 1) / o.bm) * ((n + o.bn - 1) / o.bn);
+        const double cost = (double)((tiles + 255) / 256) * o.tile_time;
+        if (!best || cost < best_cost) {
+            best = &o;
+            best_cost = cost;
+        }
+    }
+    return tgemm_config{TGEMM_KERNEL_MASKED, best->bm, best->bn, 64, 2, 2, 2, best->group, 1, 32};
 }
 
 // The kernel for operands past what the masked kernel's buffer offsets reach.
@@ -182,7 +207,7 @@ tgemm_config choose(int dtype, int a_layout, int layout, int64_t m, int64_t n, i
                     bool aligned) {
     (void)dtype;
     if (!aligned)
-        return choose_masked(m, n);
+        return choose_masked(a_layout, layout, m, n);
     if (a_layout == TGEMM_A_MK) {
         if (const tgemm_config* c = table_lookup(layout, m, n, k)) {
             tgemm_config cfg = *c;
@@ -341,18 +366,21 @@ bool overlaps(const void* p, int64_t pbytes, const void* q, int64_t qbytes) {
 // offset with bit 31 set, which holds only for operands spanning at most 2^31 bytes; they
 // move 16-byte pieces, so every contiguous extent and leading dimension is a multiple of
 // 8 elements and every base address 16-byte aligned.  The masked kernel reads through
-// the same resources, element by element: it needs the span limit only.
+// the same resources, its buffers widened to the 16-byte blocks around each operand
+// (up to 30 bytes more): it needs the span limit only, 32 bytes lower.
 constexpr int64_t kMaxFastOperandBytes = int64_t(1) << 31;
 
 bool buffer_reachable(const Problem& p) {
-    return 2 * span_a(p) <= kMaxFastOperandBytes && 2 * span_b(p) <= kMaxFastOperandBytes;
+    return 2 * span_a(p) + 32 <= kMaxFastOperandBytes &&
+           2 * span_b(p) + 32 <= kMaxFastOperandBytes;
 }
 
 bool fast_aligned(const Problem& p) {
     const auto al16 = [](const void* q) { return ((uintptr_t)q % 16) == 0; };
     return p.k % 8 == 0 && p.n % 8 == 0 && (p.a_layout == TGEMM_A_MK || p.m % 8 == 0) &&
            p.lda % 8 == 0 && p.ldb % 8 == 0 && p.ldc % 8 == 0 && al16(p.A) && al16(p.B) &&
-           al16(p.C) && buffer_reachable(p);
+           al16(p.C) && 2 * span_a(p) <= kMaxFastOperandBytes &&
+           2 * span_b(p) <= kMaxFastOperandBytes;
 }
 
 // The device address of `scratch` on the current device, looked up once per device (with
@@ -491,6 +519,7 @@ int list(int dtype, int a_layout, int b_layout, tgemm_config* out, int capacity)
 // as one 16-byte store, to slot (XCD id, hardware id bits 8..15: CU, SH and SE) of
 // out[16 * 256][2].
 constexpr int kStampSlots = 16 * 256;
+static_assert(kStampSlots == TGEMM_CLOCK_STAMP_SLOTS, "stamp slots as documented");
 constexpr int kStampBlocks = 4096;
 
 __global__ void __launch_bounds__(64) clock_stamp_kernel(unsigned long long* out) {
