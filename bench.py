@@ -111,6 +111,19 @@ def parity_and_cpu_baseline(A, B, C_gpu, w, budget_s: float):
     return baseline, parity
 
 
+def engine_clock(before, after, wall_hz: float):
+    """The engine clock from two clock stamps ([slot] = (engine cycles, wall ticks), a
+    slot with no stamp holds zeros): for each compute unit stamped both times, its engine
+    cycles over the wall time between the stamps, in MHz.  Returns (the median over the
+    compute units, [min, p10, p90, max, count]), or (None, None) with no such unit."""
+    per_cu = sorted((b[0] - a[0]) / (b[1] - a[1]) * wall_hz / 1e6
+                    for a, b in zip(before, after) if a[1] > 0 and b[1] > a[1])
+    if not per_cu:
+        return None, None
+    n = len(per_cu)
+    return per_cu[n // 2], [per_cu[0], per_cu[n // 10], per_cu[-1 - n // 10], per_cu[-1], n]
+
+
 def measure(args, A_bits, B_bits, verify: bool) -> dict:
     """Upload, verify (when asked), time; in the calling process."""
     import numpy as np
@@ -164,14 +177,7 @@ def measure(args, A_bits, B_bits, verify: bool) -> dict:
     total_ms = start.elapsed_time(stop)
     per_ms = [a.elapsed_time(b) for a, b in per]
     st = stamps.cpu().tolist()
-    wall_hz = tgemm.wall_clock_hz()
-    # per compute unit stamped both times: its engine cycles over the wall time between
-    # the stamps; the chip's figure is their median
-    per_cu = sorted((b[0] - a[0]) / (b[1] - a[1]) * wall_hz / 1e6
-                    for a, b in zip(st[0], st[1]) if a[1] > 0 and b[1] > a[1])
-    clock_mhz = per_cu[len(per_cu) // 2] if per_cu else None
-    clock_spread = ([per_cu[0], per_cu[len(per_cu) // 10], per_cu[-1 - len(per_cu) // 10],
-                     per_cu[-1], len(per_cu)] if per_cu else None)
+    clock_mhz, clock_spread = engine_clock(st[0], st[1], tgemm.wall_clock_hz())
     out.update({
         "total_ms": total_ms,
         "per_launch_ms": per_ms,
