@@ -1,0 +1,112 @@
+"""GPU parity on seeded random problems: sizes from 1 to several thousand (log-uniform,
+half of them rounded to multiples of 8), either storage of A and B, both dtypes, padded
+rows and odd base addresses, through each entry point (packed, strided, with a lent
+workspace, without allocation), every configuration the library's own choice.  Inputs
+are small integers, so every fp32 partial sum is exact and C must equal the oracle bit
+for bit whatever kernel and summation order the choice brings; padding holds NaN
+patterns that would poison C if read, and C's own padding must come back untouched."""
+import numpy as np
+import pytest
+
+from tests.gpu_util import from_dev, require_gpu, say, tdtype, torch
+from tiled_dense_gemm_major_amd.inputs import BF16, B_KN, B_NK, F16
+
+pytestmark = pytest.mark.gpu
+
+A_MK, A_KM = 0, 1
+POISON = 0x7E00          # a NaN in both fp16 and bf16
+CASES = 96
+MAX_MACS = 6e8           # keeps the oracle's share of the test to seconds
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _int_bits(dtype, arr):
+    from tiled_dense_gemm_major_amd.inputs import round_to_bf16_bits, round_to_f16_bits
+    f = round_to_f16_bits if dtype == F16 else round_to_bf16_bits
+    return f(np.asarray(arr, dtype=np.float64))
+
+
+def _draw(rng):
+    """One problem: (dtype, M, N, K, a_layout, b_layout, entry, pads, offsets)."""
+    while True:
+        M, N = (int(np.exp(rng.uniform(0, np.log(4096)))) for _ in range(2))
+        K = int(np.exp(rng.uniform(0, np.log(8192))))
+        if rng.random() < 0.5:
+            M, N, K = (-(-x // 8) * 8 for x in (M, N, K))
+        if M * N * K <= MAX_MACS:
+            break
+    dtype = F16 if rng.random() < 0.5 else BF16
+    entry = rng.choice(["packed", "strided", "ws", "noalloc"])
+    a_layout = A_KM if entry == "strided" and rng.random() < 0.5 else A_MK
+    b_layout = B_KN if rng.random() < 0.5 else B_NK
+    pads = tuple(int(rng.choice([0, 0, 8, int(rng.integers(1, 10))])) for _ in range(3)) \
+        if entry == "strided" else (0, 0, 0)
+    offsets = tuple(int(rng.choice([0, 0, int(rng.integers(1, 8))])) for _ in range(3)) \
+        if entry == "strided" else (0, 0, 0)
+    return dtype, M, N, K, a_layout, b_layout, entry, pads, offsets
+
+
+def _device(storage, offset):
+    """A device copy of `storage` (uint16 bits) starting `offset` elements into its
+    allocation; returns (allocation, view)."""
+    flat = torch.full((offset + storage.size,), POISON, dtype=torch.int16, device="cuda")
+    flat[offset:] = torch.from_numpy(storage.reshape(-1).view(np.int16)).cuda()
+    return flat, flat[offset:]
+
+
+def _storage(logical, transposed, pad):
+    R, C = logical.shape
+    if transposed:
+        st = np.full((C, R + pad), POISON, dtype=np.uint16)
+        st[:, :R] = logical.T
+        return st, R + pad
+    st = np.full((R, C + pad), POISON, dtype=np.uint16)
+    st[:, :C] = logical
+    return st, C + pad
+
+
+@pytest.mark.parametrize("block", range(4))
+def test_random_problems(dev, orc, block):
+    from tiled_dense_gemm_major_amd import tgemm
+    rng = np.random.default_rng(20261202 + block)
+    for case in range(CASES // 4):
+        dtype, M, N, K, a_layout, b_layout, entry, pads, offsets = _draw(rng)
+        tag = (f"random case {block}.{case}: {'f16' if dtype == F16 else 'bf16'} "
+               f"{M}x{N}x{K} A{'KM' if a_layout else 'MK'} B{'KN' if b_layout else 'NK'} "
+               f"{entry} pads {pads} offsets {offsets}")
+        say(tag)
+        A = _int_bits(dtype, rng.integers(-2, 3, (M, K)))
+        Bn = _int_bits(dtype, rng.integers(-2, 3, (N, K)))
+        want = orc.gemm(dtype, A, Bn, B_NK)
+        a_st, lda = _storage(A, a_layout == A_KM, pads[0])
+        b_st, ldb = _storage(Bn, b_layout == B_KN, pads[1])
+        ldc = N + pads[2]
+        _, Ad = _device(a_st, offsets[0])
+        _, Bd = _device(b_st, offsets[1])
+        c_all, Cd = _device(np.full((M, ldc), POISON, dtype=np.uint16), offsets[2])
+        t = tdtype(dtype)
+        if entry == "strided":
+            tgemm.gemm_strided(dtype, M, N, K, Ad.view(t), lda, a_layout, Bd.view(t), ldb,
+                               b_layout, Cd.view(t), ldc)
+        elif entry == "packed":
+            tgemm.gemm_ex(dtype, M, N, K, Ad.view(t), Bd.view(t), Cd.view(t), b_layout)
+        elif entry == "ws":
+            aligned = K % 8 == 0 and N % 8 == 0
+            _, nbytes = tgemm.query_config_ws(dtype, M, N, K, b_layout, aligned)
+            ws = torch.full((max(nbytes, 16) // 4,), float("nan"), dtype=torch.float32,
+                            device="cuda")
+            tgemm.gemm_ex_ws(dtype, M, N, K, Ad.view(t), Bd.view(t), Cd.view(t), ws,
+                             ws.numel() * 4, b_layout)
+        else:
+            tgemm.gemm_ex_noalloc(dtype, M, N, K, Ad.view(t), Bd.view(t), Cd.view(t),
+                                  b_layout)
+        torch.cuda.synchronize()
+        host = from_dev(c_all)
+        assert np.all(host[:offsets[2]] == POISON), tag + ": wrote before C"
+        c = host[offsets[2]:].reshape(M, ldc)
+        assert np.all(c[:, N:] == POISON), tag + ": wrote C's padding"
+        assert np.array_equal(c[:, :N], want), tag
