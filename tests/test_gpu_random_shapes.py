@@ -110,3 +110,48 @@ def test_random_problems(dev, orc, block):
         c = host[offsets[2]:].reshape(M, ldc)
         assert np.all(c[:, N:] == POISON), tag + ": wrote C's padding"
         assert np.array_equal(c[:, :N], want), tag
+
+
+def _dev_ints(shape, g):
+    """A device int8 tensor of integers in [-2, 2] (exact in bf16 and fp16)."""
+    return torch.randint(-2, 3, shape, generator=g, device="cuda", dtype=torch.int8)
+
+
+def test_random_large_problems(dev, orc):
+    """16 large random problems (sides up to 6144, aligned or not, both B storages, both
+    dtypes, packed or with a workspace): the big tiles the table picks at random
+    raggedness, checked on sampled rows and columns of C (each covering the first and
+    last of its kind) bit for bit."""
+    from tiled_dense_gemm_major_amd import tgemm
+    rng = np.random.default_rng(77)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(78)
+    for case in range(16):
+        M, N = (int(rng.integers(1024, 6145)) for _ in range(2))
+        K = int(rng.integers(256, 6145))
+        if rng.random() < 0.5:
+            M, N, K = (-(-x // 8) * 8 for x in (M, N, K))
+        dtype = F16 if rng.random() < 0.5 else BF16
+        b_layout = B_KN if rng.random() < 0.5 else B_NK
+        entry = "ws" if rng.random() < 0.5 else "packed"
+        t = tdtype(dtype)
+        say(f"random large case {case}: {'f16' if dtype == F16 else 'bf16'} {M}x{N}x{K} "
+            f"B{'KN' if b_layout else 'NK'} {entry}")
+        A = _dev_ints((M, K), g).to(t)
+        B = _dev_ints((N, K) if b_layout == B_NK else (K, N), g).to(t)
+        C = torch.full((M, N), float("nan"), dtype=t, device="cuda")
+        if entry == "ws":
+            aligned = K % 8 == 0 and N % 8 == 0
+            _, nbytes = tgemm.query_config_ws(dtype, M, N, K, b_layout, aligned)
+            ws = torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device="cuda")
+            tgemm.gemm_ex_ws(dtype, M, N, K, A, B, C, ws, ws.numel() * 4, b_layout)
+        else:
+            tgemm.gemm_ex(dtype, M, N, K, A, B, C, b_layout)
+        torch.cuda.synchronize()
+        rows = sorted({0, M - 1} | set(rng.integers(0, M, 4).tolist()))
+        cols = sorted({0, N - 1} | set(rng.integers(0, N, 4).tolist()))
+        Bn = B if b_layout == B_NK else B.t()
+        A_h, Bn_h = from_dev(A), from_dev(Bn)
+        assert np.array_equal(from_dev(C[rows]), orc.gemm(dtype, A_h[rows], Bn_h, B_NK))
+        assert np.array_equal(from_dev(C[:, cols]), orc.gemm(dtype, A_h, Bn_h[cols], B_NK))
+        del A, B, C
