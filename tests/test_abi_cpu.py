@@ -292,17 +292,39 @@ def _frozen_table():
 
 def test_frozen_table_entries_are_compiled_and_chosen(lib):
     """Every entry of the frozen table names a compiled configuration of its layout, and
-    the table's own grid points get exactly that entry from the table lookup."""
+    the table's own grid points get exactly that entry from the table lookup, but for
+    one rule: with B [K,N] the quad kernel's 256-row tiles take the 32x32x16 form (the
+    16x16x32 form spills there)."""
     grid, entries = _frozen_table()
     names = [n for n, _ in tgemm.Config._fields_]
+    overridden = 0
     for layout, mi, ni, ki, cfg in entries:
         want = dict(zip(names, cfg))
         listed = [c.as_dict() for c in tgemm.list_configs(tgemm.BF16, layout)]
         assert want in listed, (layout, mi, ni, ki, want)
+        if (layout == tgemm.B_KN and want["kernel"] == tgemm.KERNEL_QUAD
+                and want["block_m"] == 256 and want["mfma"] == 16):
+            want = dict(want, mfma=32)
+            overridden += 1
         M, N, K = grid["M"][mi], grid["N"][ni], grid["K"][ki]
         for dt in (tgemm.BF16, tgemm.F16):
             got = tgemm.query_config(dt, M, N, K, layout).as_dict()
             assert got == want, (layout, M, N, K, got, want)
+    assert overridden == 3
+
+
+def test_kn_quad_mfma_form_rule(lib):
+    # off the grid, B [K,N]: 192-row tiles take 16x16x32 above one wave of tiles, else
+    # 32x32x16; 256-row tiles always 32x32x16 (tiles of 192 x 256 in the comments)
+    def form(m, n, k):
+        c = tgemm.query_config(tgemm.F16, m, n, k, tgemm.B_KN)
+        assert c.kernel == tgemm.KERNEL_QUAD
+        return c.block_m, c.mfma
+    assert form(4000, 5944, 2352) == (192, 16)     # 21 x 24 = 504 tiles
+    assert form(3616, 4784, 3792) == (192, 16)     # 19 x 19 = 361
+    assert form(4000, 3000, 1000) == (192, 32)     # 21 x 12 = 252: one wave
+    assert form(2808, 5688, 4816) == (256, 32)     # the nearest point says 16x16x32
+    assert form(8192, 8192, 8192) == (256, 32)
 
 
 # The boundary's entry points as the header declares them: name -> parameter types.
