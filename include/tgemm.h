@@ -270,10 +270,14 @@ int tgemm_list_configs_ex(int dtype, int a_layout, int b_layout, tgemm_config* o
                           int capacity);
 
 /* The configuration the table picks when the caller can lend a workspace (A [M,K]), and
- * the workspace bytes it needs (0 when it needs none): split-K over workgroups for
- * products of at most 128 rows with K >= 1024 (B [N,K]), the quad kernel's split-K for
- * products of more rows with at most 64 tiles of 256x256 and a long K (either B
- * storage), else the choice without a workspace.  Host-only. */
+ * the workspace bytes it needs (0 when it needs none).  Only for K >= 1024 and aligned
+ * operands: with B [N,K] and M <= 64 (or fewer than 16 tiles of 256x256), split-K over
+ * workgroups with 64x128 tiles when there are at most 128 of them, else 64x256 tiles
+ * when there are at most 128 of those; otherwise the quad
+ * kernel's split-K when there are at most 128 tiles of 256x256; in both cases the split
+ * count is the power of two at most 256 / tiles (at most 16, and K / split at least 192).
+ * Shallow splits where the choice without a workspace already fills the chip keep that
+ * choice, as do short-K skinny products (K <= 4096, N <= 2048).  Host-only. */
 int tgemm_query_config_ws(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
                           int aligned, tgemm_config* out, int64_t* workspace_bytes);
 

@@ -190,37 +190,51 @@ def _splitk(splits):
 
 
 def test_query_config_ws_and_workspace_size(lib):
-    # a skinny product with a long K: split over K, one workgroup per compute unit
-    cfg, nbytes = tgemm.query_config_ws(tgemm.BF16, 64, 8192, 8192)
-    assert cfg.kernel == tgemm.KERNEL_SPLITK and cfg.split_k == 8
-    assert nbytes == 8 * 64 * 8192 * 4 == tgemm.workspace_size(64, 8192, cfg)
+    def ws(shape, layout=tgemm.B_NK):
+        cfg, nbytes = tgemm.query_config_ws(tgemm.BF16, *shape, layout)
+        if cfg.kernel in tgemm.SPLIT_KERNELS:
+            assert nbytes == cfg.split_k * shape[0] * shape[1] * 4
+        return cfg, nbytes
+    # a skinny product with B [N,K] and a long K: the split-K kernel's 64x128 tiles, 64
+    # of them, 4 splits (one wave of workgroups)
+    cfg, nbytes = ws((64, 8192, 8192))
+    assert (cfg.kernel, cfg.block_m, cfg.block_n, cfg.split_k) == (tgemm.KERNEL_SPLITK, 64,
+                                                                   128, 4)
+    assert nbytes == 4 * 64 * 8192 * 4 == tgemm.workspace_size(64, 8192, cfg)
+    # 224 tiles of 64x128 would exceed one wave: 112 tiles of 64x256, 2 splits
+    cfg, nbytes = ws((64, 28672, 4096))
+    assert (cfg.kernel, cfg.block_n, cfg.split_k) == (tgemm.KERNEL_SPLITK, 256, 2)
+    assert nbytes <= tgemm.SCRATCH_BYTES
+    # the same with B [K,N]: the quad kernel's split-K (32 tiles, 8 splits)
+    cfg, _ = ws((64, 8192, 8192), tgemm.B_KN)
+    assert (cfg.kernel, cfg.split_k, cfg.mfma) == (tgemm.KERNEL_QUAD_SPLITK, 8, 32)
     # enough tiles already, or a short K: the workspace-free choice, no workspace
-    for shape in [(8192, 8192, 8192), (64, 8192, 512), (4000, 3000, 1000)]:
-        cfg, nbytes = tgemm.query_config_ws(tgemm.BF16, *shape)
+    for shape in [(8192, 8192, 8192), (64, 8192, 512), (4000, 3000, 1000), (16, 65536, 4096)]:
+        cfg, nbytes = ws(shape)
         assert cfg.as_dict() == tgemm.query_config(tgemm.BF16, *shape).as_dict()
         assert nbytes == 0
-    # B [K,N] with few rows is not split
-    cfg, nbytes = tgemm.query_config_ws(tgemm.BF16, 64, 8192, 8192, tgemm.B_KN)
-    assert cfg.kernel != tgemm.KERNEL_SPLITK and nbytes == 0
-    # at most 64 tiles of 256 x 256 and a long K: the quad kernel in split-K mode, about
-    # one workgroup per compute unit, K ranges at least 1024 deep, either B storage
+    # few tiles of 256 x 256 and a long K: the quad kernel in split-K mode, the split count
+    # the power of two within 256 / tiles (and 16), either B storage
     for shape, layout, splits, mfma in [((2048, 2048, 16384), tgemm.B_NK, 4, 16),
                                         ((1024, 2048, 8192), tgemm.B_NK, 8, 16),
-                                        ((1536, 1536, 12288), tgemm.B_NK, 7, 16),
+                                        ((1536, 1536, 12288), tgemm.B_NK, 4, 16),
                                         ((512, 4096, 8192), tgemm.B_NK, 8, 16),
                                         ((2048, 2048, 8192), tgemm.B_KN, 4, 32),
-                                        ((1024, 2048, 4096), tgemm.B_NK, 4, 16),
-                                        ((1536, 2048, 8192), tgemm.B_NK, 5, 16),
-                                        ((1024, 1024, 8192), tgemm.B_NK, 8, 16)]:
-        cfg, nbytes = tgemm.query_config_ws(tgemm.BF16, *shape, layout)
+                                        ((1536, 2048, 8192), tgemm.B_NK, 4, 16),
+                                        ((944, 672, 10936), tgemm.B_KN, 16, 32),
+                                        ((1232, 5152, 12848), tgemm.B_NK, 2, 16)]:
+        cfg, _ = ws(shape, layout)
         assert (cfg.kernel, cfg.split_k, cfg.mfma) == (tgemm.KERNEL_QUAD_SPLITK, splits,
                                                        mfma), shape
-        assert nbytes == splits * shape[0] * shape[1] * 4
-    # more tiles, too short a K, or too little work: the plain choice
-    for shape in [(2048, 4096, 8192), (1024, 1024, 2048), (1024, 1024, 4096), (768, 768, 8192),
-                  (256, 256, 1024), (2048, 2048, 4096)]:
-        cfg, nbytes = tgemm.query_config_ws(tgemm.BF16, *shape)
-        assert cfg.kernel != tgemm.KERNEL_QUAD_SPLITK and nbytes == 0, shape
+    # shallow splits where the workspace-free choice fills the chip, or too many tiles:
+    # the plain choice
+    for shape in [(1024, 1024, 2048), (2048, 2048, 4096), (1024, 2048, 4096),
+                  (2056, 3544, 4960), (4008, 2264, 3664)]:
+        cfg, nbytes = ws(shape)
+        assert cfg.kernel not in tgemm.SPLIT_KERNELS and nbytes == 0, shape
+    # fewer than 16 tiles of 256 x 256 with B [N,K]: the split-K kernel's 64x128 tiles
+    cfg, _ = ws((768, 768, 8192))
+    assert (cfg.kernel, cfg.block_n, cfg.split_k) == (tgemm.KERNEL_SPLITK, 128, 2)
     # splits between 2 and 64
     assert tgemm.workspace_size(10, 24, _splitk(64)) == 64 * 10 * 24 * 4
     for bad in (1, 65):
@@ -435,10 +449,12 @@ def test_package_exports_every_binding_name():
 
 
 def test_workspace_choice_fits_the_fixed_scratch(lib):
-    """The table's choice given a workspace never needs more than the fixed scratch that
-    gemm_ex_noalloc lends it (split count x tiles <= 256, each tile at most 64 x 256)."""
+    """For products of at most 64 rows the choice given a workspace never needs more than
+    the fixed scratch that gemm_ex_noalloc lends it (split count x tiles <= 256, each tile
+    at most 64 x 256 fp32).  Larger products may take the quad kernel's split-K,
+    whose partials can exceed it; gemm_ex_noalloc then runs the workspace-free choice."""
     worst = 0
-    for M in (1, 16, 33, 64, 65, 100, 128):
+    for M in (1, 16, 33, 64):
         for N in (8, 256, 264, 1032, 4096, 8192, 16384, 65536):
             for K in (1024, 4096, 8192, 65536):
                 if N * K >= 2 ** 31:          # past the size limits

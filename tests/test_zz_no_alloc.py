@@ -57,15 +57,19 @@ def _case(dtype, M, N, K, layout, seed):
 def test_no_alloc_matches_workspace_entry_point(dev, orc):
     from tiled_dense_gemm_major_amd import tgemm
     w = WORKLOADS["bf16_skinny_64x8192x8192"]
-    # first call: the skinny workload, whose split-K partials fill the whole scratch
-    cfg, need = tgemm.query_config_ws(w.dtype, w.M, w.N, w.K)
-    assert cfg.kernel == tgemm.KERNEL_SPLITK and need == tgemm.SCRATCH_BYTES
+    # first call: the skinny workload with 8 splits of 64x128 tiles, whose partials fill
+    # the whole scratch
+    full = tgemm.Config(kernel=tgemm.KERNEL_SPLITK, block_m=64, block_n=128, block_k=64,
+                        waves_m=1, waves_n=4, stages=4, group_m=1, split_k=8, mfma=32)
+    need = tgemm.workspace_size(w.M, w.N, full)
+    assert need == tgemm.SCRATCH_BYTES
     A, B = w.generate()
     Ad, Bd = to_dev(A, w.dtype), to_dev(B, w.dtype)
-    say(f"no-alloc call 1: {w.describe()} splits {cfg.split_k} ({need} bytes)")
-    got1 = _no_alloc(w.dtype, w.M, w.N, w.K, Ad, Bd, w.b_layout)
-    assert np.array_equal(got1, _with_ws(w.dtype, w.M, w.N, w.K, Ad, Bd, w.b_layout, cfg))
-    assert_parity(orc, w.dtype, w.K, got1, orc.gemm(w.dtype, A, B, w.b_layout), "call 1")
+    want = orc.gemm(w.dtype, A, B, w.b_layout)
+    say(f"no-alloc call 1: {w.describe()} splits 8 ({need} bytes)")
+    got1 = _no_alloc(w.dtype, w.M, w.N, w.K, Ad, Bd, w.b_layout, full)
+    assert np.array_equal(got1, _with_ws(w.dtype, w.M, w.N, w.K, Ad, Bd, w.b_layout, full))
+    assert_parity(orc, w.dtype, w.K, got1, want, "call 1")
     # second call, smaller: fp16, 16 x 2056 x 4096 (a ragged column tile), more splits
     M, N, K = 16, 2056, 4096
     cfg2, need2 = tgemm.query_config_ws(F16, M, N, K)
@@ -78,7 +82,14 @@ def test_no_alloc_matches_workspace_entry_point(dev, orc):
     assert_parity(orc, F16, K, got2, orc.gemm(F16, A2, B2, B_NK), "call 2")
     # the first problem again, after the smaller one: same bits as before
     say("no-alloc call 3: the first problem again")
-    assert np.array_equal(_no_alloc(w.dtype, w.M, w.N, w.K, Ad, Bd, w.b_layout), got1)
+    assert np.array_equal(_no_alloc(w.dtype, w.M, w.N, w.K, Ad, Bd, w.b_layout, full), got1)
+    # and with the table's choice given a workspace (fewer splits, within the scratch)
+    cfg, need3 = tgemm.query_config_ws(w.dtype, w.M, w.N, w.K)
+    assert cfg.kernel == tgemm.KERNEL_SPLITK and 0 < need3 <= tgemm.SCRATCH_BYTES
+    say(f"no-alloc call 4: {w.describe()} table choice, splits {cfg.split_k}")
+    got4 = _no_alloc(w.dtype, w.M, w.N, w.K, Ad, Bd, w.b_layout)
+    assert np.array_equal(got4, _with_ws(w.dtype, w.M, w.N, w.K, Ad, Bd, w.b_layout, cfg))
+    assert_parity(orc, w.dtype, w.K, got4, want, "call 4")
 
 
 def test_no_alloc_explicit_configs_and_no_workspace_shapes(dev, orc):

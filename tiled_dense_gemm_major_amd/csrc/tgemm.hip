@@ -265,47 +265,80 @@ tgemm_config choose(int dtype, int a_layout, int layout, int64_t m, int64_t n, i
     return tgemm_config{TGEMM_KERNEL_TILED, 64, 64, 64, 2, 2, 2, 8, 1, 32};
 }
 
-// The table when the caller lends a workspace: a grid of few output tiles with a long K
-// ("Tiling a matmul", section "Where it breaks": skinny products leave compute units
-// idle) is split over K so that about one workgroup per compute unit runs, each split
-// at least 256 deep; everything else as without a workspace.
+// The choice when the caller lends a workspace ("Tiling a matmul", section "Where it
+// breaks": a product with few output tiles leaves compute units idle unless its K range
+// is split).
+//   - With B [N,K], M <= 64 or fewer than 16 tiles of 256x256: the split-K kernel's
+//     64x128 tiles, up to 128 of them, else its 64x256 tiles, up to 128 of them (a 64-row
+//     tile reads B once per 64 rows, so larger M goes to the quad kernel's 256-row tiles).
+//     Streaming B from memory (operands past the last-level cache) at 64x28672x4096 the
+//     wider tiles took 56.6 us against 88.4 without a workspace.
+//   - Otherwise, up to 128 tiles of 256x256: the quad kernel in split-K mode, unless the
+//     workspace-free choice already fills the chip and the splits would be shallow: with
+//     more than 64 tiles each split must be at least 3072 deep; where that choice (a
+//     tiled, ping-pong or quad kernel) has 256 workgroups or more, 2048; with B [N,K]
+//     and 128 or more, 1024.
+//   - The split count is the largest power of two within 256 / tiles (about one wave of
+//     workgroups), 16, and K / 192 (three K steps per split): more splits add partial
+//     traffic and fixed costs faster than parallelism.
+//   - The skinny and direct kernels keep products with K <= 4096 and N <= 2048, where
+//     their single pass is as fast.
+// Fitted on 102 random shapes (few to 144 tiles, K 2048-16384; every configuration and
+// split counts 2-64 timed): the pick was within 5 % of the fastest on 88 and 1.5 %
+// slower on average (at most 17 %).  The rules before, which left small-M products with
+// B [K,N] and many mid-size ones unsplit, were 146 % slower on average on the 20 few-tile
+// shapes where their pick was timed.  On 36 shapes drawn after the rule was fixed the
+// pick was within 5 % of the fastest on 26, 3.8 % slower on average (at most 25 %).
+int64_t pow2_at_most(int64_t x) {
+    int64_t p = 1;
+    while (p * 2 <= x)
+        p *= 2;
+    return p;
+}
+
 tgemm_config choose_ws(int dtype, int a_layout, int layout, int64_t m, int64_t n, int64_t k,
                        bool aligned) {
     const tgemm_config plain = choose(dtype, a_layout, layout, m, n, k, aligned);
-    if (aligned && a_layout == TGEMM_A_MK && m > 128) {
-        // At most 64 tiles of 256x256 with a long K: the quad kernel in split-K mode,
-        // about one workgroup per compute unit, each K range at least 1024 deep, when
-        // that gives half the chip or more work, and with ranges under 2048 only where
-        // 128x128 tiles would not fill the chip either.  Measured against the table's
-        // plain choice on 22 shapes: 1.2-1.7x faster from 16 to 64 tiles (e.g.
-        // 2048x2048x16384 110.7 against 150.4 us, 2048x2048x32768 207.8 against 356.2),
-        // a tie at 128 workgroups; slower at 128 tiles (the 192-row quad kernel) and at
-        // 64 tiles with 1024-deep ranges (2048x2048x4096: 51.2 against 46.9 us, where
-        // 256 tiles of 128x128 fill the chip in one wave).
-        const int64_t tiles = ((m + 255) / 256) * ((n + 255) / 256);
-        const int64_t tiles128 = ((m + 127) / 128) * ((n + 127) / 128);
-        int64_t splits = tiles > 0 ? 256 / tiles : 0;
-        if (splits > k / 1024)
-            splits = k / 1024;
-        if (splits > kMaxSplits)
-            splits = kMaxSplits;
-        if (tiles <= 64 && splits >= 2 && tiles * splits >= 128 &&
-            (k / splits >= 2048 || tiles128 < 256))
-            return tgemm_config{TGEMM_KERNEL_QUAD_SPLITK, 256, 256, 64, 2, 2, 5, 4,
-                                (int32_t)splits, layout == TGEMM_B_NK ? 16 : 32};
+    if (!aligned || a_layout != TGEMM_A_MK || k < 1024)
         return plain;
+    if ((plain.kernel == TGEMM_KERNEL_SKINNY || plain.kernel == TGEMM_KERNEL_DIRECT) &&
+        k <= 4096 && n <= 2048)
+        return plain;
+    const auto tiles = [&](int64_t bm, int64_t bn) {
+        return ((m + bm - 1) / bm) * ((n + bn - 1) / bn);
+    };
+    const int64_t t256 = tiles(256, 256);
+    const int64_t deep = pow2_at_most(k / 192);       // splits of at least 3 K steps
+    if (layout == TGEMM_B_NK && (m <= 64 || t256 < 16)) {
+        // 64-column-deep tiles 128 wide, or 256 wide where the narrow ones would exceed
+        // 128; past that a wave of tiles needs no split
+        const int32_t bn = tiles(64, 128) <= 128 ? 128 : 256;
+        const int64_t t = tiles(64, bn);
+        if (t > 128)
+            return plain;
+        int64_t splits = pow2_at_most(256 / t);
+        splits = splits > 16 ? 16 : splits;
+        splits = splits > deep ? deep : splits;
+        splits = splits < 2 ? 2 : splits;
+        return tgemm_config{TGEMM_KERNEL_SPLITK, 64, bn, 64, 1, 4, 4, 1, (int32_t)splits, 32};
     }
-    if (!aligned || a_layout != TGEMM_A_MK || layout != TGEMM_B_NK || m > 128 || k < 1024)
+    if (t256 == 0 || t256 > 128)
         return plain;
-    const int64_t tiles = ((m + 63) / 64) * ((n + 255) / 256);
-    int64_t splits = 256 / (tiles > 0 ? tiles : 1);
-    if (splits > k / 256)
-        splits = k / 256;
-    if (splits > kMaxSplits)
-        splits = kMaxSplits;
+    int64_t splits = pow2_at_most(256 / t256);
+    splits = splits > 16 ? 16 : splits;
+    splits = splits > deep ? deep : splits;
     if (splits < 2)
         return plain;
-    return tgemm_config{TGEMM_KERNEL_SPLITK, 64, 256, 64, 1, 4, 4, 1, (int32_t)splits, 32};
+    const int64_t depth = k / splits;
+    const bool full_tiles = plain.kernel == TGEMM_KERNEL_TILED ||
+                            plain.kernel == TGEMM_KERNEL_PINGPONG ||
+                            plain.kernel == TGEMM_KERNEL_QUAD;
+    const int64_t plain_wgs = full_tiles ? tiles(plain.block_m, plain.block_n) : 0;
+    if ((t256 > 64 && depth < 3072) || (plain_wgs >= 256 && depth < 2048) ||
+        (layout == TGEMM_B_NK && plain_wgs >= 128 && depth < 1024))
+        return plain;
+    return tgemm_config{TGEMM_KERNEL_QUAD_SPLITK, 256, 256, 64, 2, 2, 5, 4, (int32_t)splits,
+                        layout == TGEMM_B_NK ? 16 : 32};
 }
 
 // Workspace bytes of a configuration for an m x n product: the fp32 partial tiles of a
