@@ -31,9 +31,14 @@ namespace tgemm {
 //            reads V^T in that same key order with two transposing LDS reads
 //            (ds_read_b64_tr_b16), keys base and base + 8.
 //   Loads:   K and V tiles (64 x D each) arrive by direct-to-LDS 16-byte loads into a
-//            3-stage ring; tile t+2's loads go out once every wave has met at the start of
-//            step t.  K rows are stored with 16-byte chunk c at c ^ ((row / 2) mod KC) (the
-//            row-wise reads of 32 rows hit distinct banks); V rows with chunk c at
+//            2-stage ring (32 KiB per workgroup, so four workgroups share a compute unit
+//            and each SIMD holds four waves); tile t+1's loads go out once every wave has
+//            met at the start of step t, into the stage tile t-1 left.  The step is
+//            compiled once per stage, so every LDS address is a fixed lane offset plus an
+//            immediate, and a tile's loads read through a descriptor based at its first
+//            key row: the lane offsets stay fixed and the advance is scalar.  K rows are
+//            stored with 16-byte chunk c at c ^ ((row / 2) mod KC) (the row-wise reads of
+//            32 rows hit distinct banks); V rows with chunk c at
 //            c ^ 2(row mod 4) (the 4 x 16 blocks of the transposing reads hit distinct
 //            banks).  Rows past seq read as zeros (buffer range check).
 //   The whole (b, h) slice spans at most 2^31 bytes (checked by the host).
@@ -72,10 +77,10 @@ __device__ __forceinline__ void lds_reads_done(u32x2 (&v)[2][2][2]) {
 
 template <int D, bool CAUSAL>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
-                               amdgpu_waves_per_eu(3, 3)))
+                               amdgpu_waves_per_eu(4, 4)))
 attn_fwd(const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
          u16* __restrict__ O, int S, int H, float scale_log2, int nqb) {
-    constexpr int BM = 128, BN = 64, ST = 3;
+    constexpr int BM = 128, BN = 64, ST = 2;
     constexpr int KC = D / 8;                  // 16-byte chunks per row
     constexpr int ROWS = 64 / KC;              // rows per 1 KiB load
     constexpr int TILE = BN * D;               // elements of one K or V tile
@@ -103,8 +108,6 @@ attn_fwd(const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __rest
     const size_t base = ((size_t)b * S * H + h) * D;   // (b, 0, h, 0)
     const uint32_t span = S > 0 ? ((uint32_t)(S - 1) * rs + D) * 2u : 0u;
     const rsrc_t rq = make_rsrc(Q + base, span);
-    const rsrc4_t rk = make_rsrc4(K + base, span);
-    const rsrc4_t rv = make_rsrc4(V + base, span);
 
     // key tiles this block visits: those holding a key at or before its last query
     const int ntile_all = (S + BN - 1) / BN;
@@ -134,16 +137,25 @@ attn_fwd(const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __rest
         vchunk[i] = pch ^ (2 * (trow[i] & 3));
     }
     const uint32_t lds0 = lds_addr(lds);
-    auto issue = [&](int kt) {
-        const int st = kt % ST;
+    // a tile's loads read through descriptors based at its first key row and ending where
+    // the (b, h) slice ends, so the lane offsets are fixed and rows past seq (whose offsets
+    // reach past the descriptor's end, the row stride being at least D) read as zeros
+    uint32_t kgo[LW], vgo[LW];
+#pragma unroll
+    for (int i = 0; i < LW; ++i) {
+        kgo[i] = ((uint32_t)trow[i] * rs + kchunk[i] * 8) * 2u;
+        vgo[i] = ((uint32_t)trow[i] * rs + vchunk[i] * 8) * 2u;
+    }
+    auto issue = [&](auto stc, int kt) {
+        constexpr int st = decltype(stc)::value;
+        const uint32_t skip = (uint32_t)kt * BN * rs * 2u;      // kt * BN < S: below span
+        const rsrc4_t rkt = make_rsrc4(K + base + (size_t)kt * BN * rs, span - skip);
+        const rsrc4_t rvt = make_rsrc4(V + base + (size_t)kt * BN * rs, span - skip);
 #pragma unroll
         for (int i = 0; i < LW; ++i) {
-            const int key = kt * BN + trow[i];
-            const uint32_t row = (uint32_t)key * rs;
             const uint32_t ldsb = lds0 + (uint32_t)((st * 2 * TILE + (BN / 4 * wave + ROWS * i) * D) * 2);
-            dma16_at(rk, ldsb, key < S ? (row + kchunk[i] * 8) * 2u : kOutOfRange, 0);
-            dma16_at(rv, ldsb + TILE * 2, key < S ? (row + vchunk[i] * 8) * 2u : kOutOfRange,
-                     0);
+            dma16_at(rkt, ldsb, kgo[i], 0);
+            dma16_at(rvt, ldsb + TILE * 2, vgo[i], 0);
         }
     };
 
@@ -187,24 +199,21 @@ attn_fwd(const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __rest
     float l_run = 0.0f;                        // this lane's half of the running row sum
     const int q = q0 + r;
 
-    if (nkt > 0) {
-        issue(0);
-        if (nkt > 1)
-            issue(1);
-    }
-    for (int kt = 0; kt < nkt; ++kt) {
-        // tile kt has landed (tile kt+1 may fly) and every wave is done with tile kt-1
+    if (nkt > 0)
+        issue(std::integral_constant<int, 0>{}, 0);
+    // one copy of the step per ring stage, the stage a compile-time constant in each
+    for (int kt0 = 0; kt0 < nkt; kt0 += ST) {
+      static_for<0, ST>([&](auto stc) {
+        constexpr int st = decltype(stc)::value;
+        const int kt = kt0 + st;
+        if (kt >= nkt)
+            return;
+        // tile kt has landed and every wave is done with tile kt-1, whose stage tile kt+1
+        // then fills
+        wait_vm_then_sync<0>();
         if (kt + 1 < nkt)
-            wait_vm_then_sync<2 * LW>();
-        else
-            wait_vm_then_sync<0>();
-        if (kt + 2 < nkt)
-            issue(kt + 2);
-        const u16* kt_lds = lds + (kt % ST) * 2 * TILE;
-        uint32_t vb[NDB];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-            vb[db] = vaddr0[db] + (uint32_t)((kt % ST) * 2 * TILE * 2);
+            issue(std::integral_constant<int, (st + 1) % ST>{}, kt + 1);
+        const u16* kt_lds = lds + st * 2 * TILE;
 
         // S = Q K^T, two 32-key blocks
         f32x16 sacc[2];
@@ -283,11 +292,11 @@ attn_fwd(const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __rest
             u32x2 vf[2][NDB][2];
             static_for<0, 2>([&](auto qqc) {
                 constexpr int qq = decltype(qqc)::value;
-                constexpr int off = (32 * kb + 16 * qq) * D * 2;
+                constexpr int off = (st * 2 * TILE + 32 * kb * D + 16 * qq * D) * 2;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    vf[qq][db][0] = ds_read_tr16_b64<off>(vb[db]);
-                    vf[qq][db][1] = ds_read_tr16_b64<off + 8 * D * 2>(vb[db]);
+                    vf[qq][db][0] = ds_read_tr16_b64<off>(vaddr0[db]);
+                    vf[qq][db][1] = ds_read_tr16_b64<off + 8 * D * 2>(vaddr0[db]);
                 }
             });
             u32x4 pf[2];
@@ -306,6 +315,7 @@ attn_fwd(const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __rest
                               vf[qq][db][1][1]},
                         pf[qq], oacc[db]);
         });
+      });
     }
     wait_vm<0>();                               // no load left in flight
 
