@@ -113,6 +113,22 @@ def test_splitk_table_choice_skinny_workload(dev, orc):
                   "skinny split-K")
 
 
+def test_splitk_table_choice_wide_skinny(dev, orc):
+    """A skinny product with more than 128 tiles of 64x128 (ragged N): the table's choice
+    with a workspace takes the split-K kernel's 64x256 tiles, every element against the
+    oracle."""
+    from tiled_dense_gemm_major_amd import tgemm
+    M, N, K = 48, 28680, 2056
+    cfg, need = tgemm.query_config_ws(BF16, M, N, K)
+    assert (cfg.kernel, cfg.block_n, cfg.split_k) == (tgemm.KERNEL_SPLITK, 256, 2)
+    assert need == 2 * M * N * 4
+    A, B, want = _case(orc, BF16, M, N, K)
+    say(f"split-K table choice bf16 {M}x{N}x{K}: 64x256 tiles, 2 splits")
+    got = _run_ws(BF16, A, B, None)
+    assert not np.any(got == 0x7E00)
+    assert_parity(orc, BF16, K, got, want, "wide skinny split-K")
+
+
 def test_splitk_repeat_launches_bitwise_identical(dev, orc):
     from tiled_dense_gemm_major_amd import tgemm
     M, N, K = 96, 4096, 8192
