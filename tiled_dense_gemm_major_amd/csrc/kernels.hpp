@@ -2075,6 +2075,16 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
     u16* wb = lds + wave * WBUF;
     // LDS slot of load i's piece: chunk row 8i + lrow, swizzled by that row
     auto wr_off = [&](int i) { return (8 * i + lrow) * CK + ((lpc ^ swz<KC>(8 * i + lrow)) * 8); };
+    // A loads whose 8 rows all lie past M carry nothing but still take a slot of the
+    // compute unit's load path (decode products have M of 1-16 in a 32-row block): they
+    // are not issued, and the LDS rows they would fill are zeroed once (a wave reads only
+    // its own buffer)
+    const int a_rows = M - m0;
+    auto dead = [&](int i) { return i * 8 < BM && 8 * i >= a_rows; };
+#pragma unroll
+    for (int i = 0; i < LD; ++i)
+        if (dead(i))
+            *reinterpret_cast<u32x4*>(wb + wr_off(i)) = u32x4{0u, 0u, 0u, 0u};
 
     const int nch = (K + CK - 1) / CK;
     const int c_lo = wave * nch / NW, len = (wave + 1) * nch / NW - c_lo;
@@ -2092,8 +2102,9 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
         const bool ok = live && k0 + lpc * 8 < K;
 #pragma unroll
         for (int i = 0; i < LD; ++i)
-            buf[S][i] = load16(i * 8 < BM ? ra : rb, ok ? off[i] : kOutOfRange,
-                               (uint32_t)k0 * 2u);
+            if (!dead(i))
+                buf[S][i] = load16(i * 8 < BM ? ra : rb, ok ? off[i] : kOutOfRange,
+                                   (uint32_t)k0 * 2u);
     };
 
     const int xr = swz<KC>(lane & 31);
@@ -2108,7 +2119,8 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
             constexpr int d = decltype(dc)::value;
 #pragma unroll
             for (int i = 0; i < LD; ++i)
-                *reinterpret_cast<u32x4*>(wb + wr_off(i)) = buf[d][i];
+                if (!dead(i))
+                    *reinterpret_cast<u32x4*>(wb + wr_off(i)) = buf[d][i];
             u32x4 fa[4][MT], fb[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {

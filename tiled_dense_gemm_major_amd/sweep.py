@@ -26,7 +26,8 @@ refreshes the library's frozen per-device table: every fast configuration is tim
 grid of shapes (A [M,K], B [N,K] and [K,N]; bf16, whose kernels are fp16's too), and the
 fastest per grid point is written as a C++ table that `choose` consults (the nearest grid
 point in log2 of M, N and K) before its fallback rules.  Rebuild the library afterwards.
-With --layouts kn (or nk) only that half is re-timed and the rest kept from the file.
+With --layouts kn (or nk) only that half is re-timed and the rest kept from the file;
+--table-ms 16,64 likewise limits the re-timing to those rows of M.
 
   python -m tiled_dense_gemm_major_amd.sweep --attention [--repeat 20]
 
@@ -86,25 +87,29 @@ def read_table(path):
 
 def emit_table(tgemm, torch, np, args, stream, path):
     """Time every fast configuration on the grid and write the fastest per point.  With
-    --layouts, only those B storages are timed; the other rows are kept from the file."""
+    --layouts (and --table-ms), only those B storages (and M rows) are timed; the other
+    rows are kept from the file."""
     import datetime
     from .inputs import B_KN, B_NK
     layouts = [B_NK, B_KN] if not args.layouts else \
         [B_KN if x == "kn" else B_NK for x in args.layouts.split(",")]
-    kept = read_table(path) if args.layouts else {}
+    ms = [int(x) for x in args.table_ms.split(",") if x]
+    if any(m not in TABLE_M for m in ms):
+        raise SystemExit(f"--table-ms: rows of the grid are {TABLE_M}")
+    partial = bool(args.layouts or ms)
+    kept = read_table(path) if partial else {}
     rows = []
     for layout in (B_NK, B_KN):
-        if layout not in layouts:
-            for mi in range(len(TABLE_M)):
+        cfgs = [c for c in tgemm.list_configs(BF16, layout)
+                if c.kernel not in tgemm.ANY_ALIGNMENT_KERNELS
+                and c.kernel not in tgemm.WORKSPACE_KERNELS]
+        for mi, M in enumerate(TABLE_M):
+            if layout not in layouts or (ms and M not in ms):
                 for ni in range(len(TABLE_N)):
                     for ki in range(len(TABLE_K)):
                         d, us = kept[(layout, mi, ni, ki)]
                         rows.append((layout, mi, ni, ki, tgemm.Config.from_dict(d), us))
-            continue
-        cfgs = [c for c in tgemm.list_configs(BF16, layout)
-                if c.kernel not in tgemm.ANY_ALIGNMENT_KERNELS
-                and c.kernel not in tgemm.SPLIT_KERNELS]
-        for mi, M in enumerate(TABLE_M):
+                continue
             for ni, N in enumerate(TABLE_N):
                 for ki, K in enumerate(TABLE_K):
                     # uniform[-1,1) operands drawn on the device (timing only)
@@ -141,8 +146,9 @@ def emit_table(tgemm, torch, np, args, stream, path):
         f"// Device: {dev.name} ({getattr(dev, 'gcnArchName', 'gfx950')}), "
         f"{datetime.date.today().isoformat()}; bf16, warmup {args.warmup}, "
         f"{max(1, args.rounds)} x {args.repeat} launches per configuration, medians"
-        + (f"; re-timed: {args.layouts} rows, the others kept from the previous table."
-           if args.layouts else "."),
+        + (f"; re-timed: {args.layouts or 'nk,kn'} rows"
+           + (f" at M {args.table_ms}" if ms else "")
+           + ", the others kept from the previous table." if partial else "."),
         "// Regenerate: python -m tiled_dense_gemm_major_amd.sweep --emit-table <this file>",
         "static const int64_t kTableM[] = {" + ", ".join(map(str, TABLE_M)) + "};",
         "static const int64_t kTableN[] = {" + ", ".join(map(str, TABLE_N)) + "};",
@@ -202,6 +208,9 @@ def main(argv=None):
                     help="rotate over this many copies of A and B (HBM-resident operands)")
     ap.add_argument("--emit-table", default="",
                     help="time the grid and write the frozen configuration table here")
+    ap.add_argument("--table-ms", default="",
+                    help="with --emit-table: re-time only these M rows of the grid "
+                         "(e.g. 16,64), keeping the others from the file")
     ap.add_argument("--layouts", default="",
                     help="with --emit-table: re-time only these B storages (nk, kn), "
                          "keeping the file's other rows")

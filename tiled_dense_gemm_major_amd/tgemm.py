@@ -18,6 +18,7 @@ A_MK, A_KM = 0, 1
 # the kernels that take operands of any 2-byte alignment
 ANY_ALIGNMENT_KERNELS = (KERNEL_GENERIC, KERNEL_MASKED)
 SPLIT_KERNELS = (KERNEL_SPLITK, KERNEL_QUAD_SPLITK)   # split K over workgroups (workspace)
+WORKSPACE_KERNELS = SPLIT_KERNELS + (KERNEL_QUAD_STREAMK,)   # need a lent workspace
 STREAMK_WORKSPACE_BYTES = 128 << 20                   # a QUAD_STREAMK configuration's
 
 SCRATCH_BYTES = 16 << 20    # the fixed per-GPU scratch of gemm_ex_noalloc
@@ -37,6 +38,7 @@ EXPORTS = ("attn_fwd_f16", "gemm_f16", "gemm_bf16", "gemm_ex", "gemm_ex_ws", "ge
 __all__ = ["F16", "BF16", "B_NK", "B_KN", "A_MK", "A_KM", "KERNEL_GENERIC", "KERNEL_TILED",
            "KERNEL_SKINNY", "KERNEL_DMA", "KERNEL_PINGPONG", "KERNEL_QUAD", "KERNEL_SPLITK",
            "KERNEL_QUAD_SPLITK", "KERNEL_QUAD_STREAMK", "KERNEL_MASKED", "SPLIT_KERNELS",
+           "WORKSPACE_KERNELS",
            "ANY_ALIGNMENT_KERNELS",
            "STREAMK_WORKSPACE_BYTES",
            "KERNEL_DIRECT",
