@@ -136,7 +136,7 @@ typedef enum {
 } tgemm_kernel;
 
 /* One tile configuration.  block_m x block_n is the C tile of one workgroup, block_k
- * the K step, waves_m x waves_n the wavefront grid inside the workgroup (64 lanes each),
+ * the K step (SKINNY: the k chunk a wave loads at once, 64 or 128), waves_m x waves_n the wavefront grid inside the workgroup (64 lanes each),
  * stages the LDS buffers (QUAD: operand slots of block_m x block_k elements, three for
  * A tiles and two for B tiles), group_m the tile rows of one launch-order group,
  * split_k the number of waves (SKINNY) or workgroups (SPLITK and QUAD_SPLITK, 2..64,
@@ -277,7 +277,8 @@ int tgemm_list_configs_ex(int dtype, int a_layout, int b_layout, tgemm_config* o
  * kernel's split-K when there are at most 128 tiles of 256x256; in both cases the split
  * count is the power of two at most 256 / tiles (at most 16, and K / split at least 192).
  * Shallow splits where the choice without a workspace already fills the chip keep that
- * choice, as do short-K skinny products (K <= 4096, N <= 2048).  Host-only. */
+ * choice, as do short-K skinny products (K <= 4096, N <= 2048) and products of at most 32
+ * rows whose skinny workgroups make one wave (192-256 of them).  Host-only. */
 int tgemm_query_config_ws(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
                           int aligned, tgemm_config* out, int64_t* workspace_bytes);
 

@@ -208,10 +208,12 @@ def test_query_config_ws_and_workspace_size(lib):
     # the same with B [K,N]: the quad kernel's split-K (32 tiles, 8 splits)
     cfg, _ = ws((64, 8192, 8192), tgemm.B_KN)
     assert (cfg.kernel, cfg.split_k, cfg.mfma) == (tgemm.KERNEL_QUAD_SPLITK, 8, 32)
-    # enough tiles already, or a short K: the workspace-free choice, no workspace
-    for shape in [(8192, 8192, 8192), (64, 8192, 512), (4000, 3000, 1000), (16, 65536, 4096)]:
+    # enough tiles already, or a short K, or a skinny product of at most 32 rows whose
+    # workgroups make one wave: the workspace-free choice, no workspace
+    for shape in [(8192, 8192, 8192), (64, 8192, 512), (4000, 3000, 1000), (16, 65536, 4096),
+                  (1, 8192, 8192), (8, 8192, 8192), (32, 8192, 8192), (16, 7112, 4192)]:
         cfg, nbytes = ws(shape)
-        assert cfg.as_dict() == tgemm.query_config(tgemm.BF16, *shape).as_dict()
+        assert cfg.as_dict() == tgemm.query_config(tgemm.BF16, *shape).as_dict(), shape
         assert nbytes == 0
     # few tiles of 256 x 256 and a long K: the quad kernel in split-K mode, the split count
     # the power of two within 256 / tiles (and 16), either B storage
@@ -232,6 +234,10 @@ def test_query_config_ws_and_workspace_size(lib):
                   (2056, 3544, 4960), (4008, 2264, 3664)]:
         cfg, nbytes = ws(shape)
         assert cfg.kernel not in tgemm.SPLIT_KERNELS and nbytes == 0, shape
+    # a 32-row skinny product with half a wave of workgroups, or more than a wave: split
+    for shape in [(8, 4096, 14336), (8, 14336, 4096)]:
+        cfg, _ = ws(shape)
+        assert cfg.kernel == tgemm.KERNEL_SPLITK, shape
     # fewer than 16 tiles of 256 x 256 with B [N,K]: the split-K kernel's 64x128 tiles
     cfg, _ = ws((768, 768, 8192))
     assert (cfg.kernel, cfg.block_n, cfg.split_k) == (tgemm.KERNEL_SPLITK, 128, 2)

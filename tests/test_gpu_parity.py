@@ -270,9 +270,9 @@ def test_direct_k_walk_exact(dev, orc, K):
 
 
 # K walks of the skinny kernel, bit for bit on exact inputs: each of its 8 waves walks a
-# contiguous range of 64-wide chunks, starting at a chunk set by the workgroup's index
-# on its XCD, so with 33 column blocks and 2-6 chunks per wave the ragged last chunk is
-# reached first, last and in between.  The row counts leave 1 to 7 of a row block's
+# contiguous range of 64- or 128-wide chunks, starting at a chunk set by the workgroup's
+# index on its XCD, so with 33 column blocks and 1-6 chunks per wave the ragged last
+# chunk is reached first, last and in between.  The row counts leave 1 to 7 of a row block's
 # 8-row A loads past M (not issued: their LDS rows are zeroed once), including a last
 # row block of 36 rows (M = 100).
 @pytest.mark.parametrize("K", [1000, 1544, 2568, 3080])

@@ -2031,26 +2031,30 @@ gemm_quad_sk(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restri
 // memory-bound whatever the tiling; split-K keeps all the compute units busy).
 //   One workgroup per 32 columns of C (all MT*32 rows of a row block); its 8 waves split
 //   the K range into 8 contiguous parts (split-K inside the workgroup), each wave
-//   accumulating a full (MT*32) x 32 partial product.  Per 64-wide k chunk a wave loads
-//   whole 128-byte row segments (8 lanes per row: full cache lines), D chunks ahead into
-//   registers, writes the chunk to its own swizzled LDS buffer and reads it back in MFMA
+//   accumulating a full (MT*32) x 32 partial product.  Per k chunk (64 wide: whole
+//   128-byte row segments, 8 lanes per row; or 128 wide: 256-byte segments, 16 lanes
+//   per row, longer runs per memory page) a wave loads the chunk D chunks ahead into
+//   registers, writes it to its own swizzled LDS buffer and reads it back in MFMA
 //   operand layout (a wave's LDS accesses complete in order, so no barrier is needed).
 //   At the end the 8 partial products are summed through LDS in a fixed order
 //   (deterministic), cast once and stored.  Requirements as for gemm_tiled; rows past
 //   M, columns past N and k past K read as zero through the buffer range check.
 // ------------------------------------------------------------------------------------
-template <int DT, int MT, int D>
+template <int DT, int MT, int D, int CKT = 64>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512),
                                amdgpu_waves_per_eu(2, 2)))
 gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
             int N, int K, int lda, int ldb, int ldc) {
-    constexpr int NW = 8, BN = 32, CK = 64, KC = CK / 8;
+    constexpr int NW = 8, BN = 32, CK = CKT, KC = CK / 8;
+    constexpr int RPL = 64 / KC;                   // chunk rows per 1 KiB load
     constexpr int BM = MT * 32;
     constexpr int ROWS = BM + BN;                  // rows of one chunk: A rows, then B rows
-    constexpr int LD = ROWS / 8;                   // 1 KiB loads per chunk per wave
+    constexpr int LD = ROWS / RPL;                 // 1 KiB loads per chunk per wave
     constexpr int WBUF = ROWS * CK;                // elements of one wave's LDS buffer
     constexpr int RED = NW * BN * BM;              // floats of the final reduction
     constexpr int LDS_ELEMS = (NW * WBUF * 2 > RED * 4) ? NW * WBUF : RED * 2;
+    static_assert(CK == 64 || CK == 128, "64- or 128-wide chunks");
+    static_assert(ROWS % RPL == 0 && LDS_ELEMS * 2 <= 160 * 1024, "chunk layout and LDS");
     __shared__ __attribute__((aligned(16))) u16 lds[LDS_ELEMS];
 
     const int n0 = (int)blockIdx.x * BN, m0 = (int)blockIdx.y * BM;
@@ -2060,12 +2064,13 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
 
     const rsrc_t ra = make_rsrc(A, span_bytes(M, K, lda));
     const rsrc_t rb = make_rsrc(B, span_bytes(N, K, ldb));
-    // load i covers chunk rows 8i .. 8i+7: lane l takes row 8i + l/8, 16-byte piece l%8
-    const int lrow = lane >> 3, lpc = lane & 7;
+    // load i covers chunk rows RPL*i .. RPL*(i+1)-1: lane l takes row RPL*i + l/KC, 16-byte
+    // piece l%KC (8 lanes per 128-byte row segment, or 16 per 256-byte one)
+    const int lrow = lane / KC, lpc = lane % KC;
     uint32_t off[LD];
 #pragma unroll
     for (int i = 0; i < LD; ++i) {
-        const int r = 8 * i + lrow;
+        const int r = RPL * i + lrow;
         if (r < BM)
             off[i] = m0 + r < M ? (uint32_t)((m0 + r) * lda + lpc * 8) * 2u : kOutOfRange;
         else
@@ -2073,14 +2078,16 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
                                      : kOutOfRange;
     }
     u16* wb = lds + wave * WBUF;
-    // LDS slot of load i's piece: chunk row 8i + lrow, swizzled by that row
-    auto wr_off = [&](int i) { return (8 * i + lrow) * CK + ((lpc ^ swz<KC>(8 * i + lrow)) * 8); };
-    // A loads whose 8 rows all lie past M carry nothing but still take a slot of the
+    // LDS slot of load i's piece: chunk row RPL*i + lrow, swizzled by that row
+    auto wr_off = [&](int i) {
+        return (RPL * i + lrow) * CK + ((lpc ^ swz<KC>(RPL * i + lrow)) * 8);
+    };
+    // A loads whose RPL rows all lie past M carry nothing but still take a slot of the
     // compute unit's load path (decode products have M of 1-16 in a 32-row block): they
     // are not issued, and the LDS rows they would fill are zeroed once (a wave reads only
     // its own buffer)
     const int a_rows = M - m0;
-    auto dead = [&](int i) { return i * 8 < BM && 8 * i >= a_rows; };
+    auto dead = [&](int i) { return i * RPL < BM && RPL * i >= a_rows; };
 #pragma unroll
     for (int i = 0; i < LD; ++i)
         if (dead(i))
@@ -2103,7 +2110,7 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
 #pragma unroll
         for (int i = 0; i < LD; ++i)
             if (!dead(i))
-                buf[S][i] = load16(i * 8 < BM ? ra : rb, ok ? off[i] : kOutOfRange,
+                buf[S][i] = load16(i * RPL < BM ? ra : rb, ok ? off[i] : kOutOfRange,
                                    (uint32_t)k0 * 2u);
     };
 
@@ -2121,9 +2128,9 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
             for (int i = 0; i < LD; ++i)
                 if (!dead(i))
                     *reinterpret_cast<u32x4*>(wb + wr_off(i)) = buf[d][i];
-            u32x4 fa[4][MT], fb[4];
+            u32x4 fa[CK / 16][MT], fb[CK / 16];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < CK / 16; ++j) {
                 const int koff = (((2 * j) | half) ^ xr) * 8;
 #pragma unroll
                 for (int h = 0; h < MT; ++h)
@@ -2133,7 +2140,7 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
             }
             load_chunk(c + d + D, dc);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < CK / 16; ++j)
 #pragma unroll
                 for (int h = 0; h < MT; ++h)
                     acc[h] = mfma_32x32x16<DT>(fb[j], fa[j][h], acc[h]);

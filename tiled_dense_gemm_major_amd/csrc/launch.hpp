@@ -155,10 +155,10 @@ hipError_t launch_quad_sk(const void* A, const void* B, void* C, int M, int N, i
     return hipGetLastError();
 }
 
-template <int DT, int MT, int D>
+template <int DT, int MT, int D, int CK = 64>
 hipError_t launch_skinny(const void* A, const void* B, void* C, int M, int N, int K, int lda,
                          int ldb, int ldc, int, hipStream_t s) {
-    hipLaunchKernelGGL((tgemm::gemm_skinny<DT, MT, D>),
+    hipLaunchKernelGGL((tgemm::gemm_skinny<DT, MT, D, CK>),
                        dim3((unsigned)cdiv(N, 32), (unsigned)cdiv(M, MT * 32)), dim3(512), 0, s,
                        KARGS);
     return hipGetLastError();
@@ -254,5 +254,11 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
     Variant {                                                                              \
         DT, 0, 0, tgemm_config{TGEMM_KERNEL_SKINNY, MT * 32, 32, 64, 1, 8, D, 1, 8, 32},       \
             &launch_skinny<DT, MT, D>                                                      \
+    }
+// The skinny kernel with 128-wide k chunks (block_k 128): 256-byte row segments per load.
+#define SKINNY_WIDE(DT, MT, D)                                                             \
+    Variant {                                                                              \
+        DT, 0, 0, tgemm_config{TGEMM_KERNEL_SKINNY, MT * 32, 32, 128, 1, 8, D, 1, 8, 32},      \
+            &launch_skinny<DT, MT, D, 128>                                                 \
     }
 }  // namespace tgemm_reg

@@ -246,7 +246,10 @@ tgemm_config choose(int dtype, int a_layout, int layout, int64_t m, int64_t n, i
     }
     if (a_layout == TGEMM_A_MK && layout == TGEMM_B_NK && m <= 128 && k >= 1024) {
         const int mt = m <= 32 ? 1 : (m <= 64 ? 2 : 4);
-        const int depth = mt == 1 ? 4 : (mt == 2 ? 3 : 1);
+        // 32-row blocks take 128-wide k chunks (256-byte row segments), one chunk ahead
+        if (mt == 1)
+            return tgemm_config{TGEMM_KERNEL_SKINNY, 32, 32, 128, 1, 8, 1, 1, 8, 32};
+        const int depth = mt == 2 ? 3 : 1;
         return tgemm_config{TGEMM_KERNEL_SKINNY, mt * 32, 32, 64, 1, 8, depth, 1, 8, 32};
     }
     const int64_t t256 = ((m + 255) / 256) * ((n + 255) / 256);
@@ -282,7 +285,8 @@ tgemm_config choose(int dtype, int a_layout, int layout, int64_t m, int64_t n, i
 //     workgroups), 16, and K / 192 (three K steps per split): more splits add partial
 //     traffic and fixed costs faster than parallelism.
 //   - The skinny and direct kernels keep products with K <= 4096 and N <= 2048, where
-//     their single pass is as fast.
+//     their single pass is as fast, and the skinny kernel's 32-row blocks those whose
+//     workgroups make one wave.
 // Fitted on 102 random shapes (few to 144 tiles, K 2048-16384; every configuration and
 // split counts 2-64 timed): the pick was within 5 % of the fastest on 88 and 1.5 %
 // slower on average (at most 17 %).  The rules before, which left small-M products with
@@ -304,6 +308,15 @@ tgemm_config choose_ws(int dtype, int a_layout, int layout, int64_t m, int64_t n
     if ((plain.kernel == TGEMM_KERNEL_SKINNY || plain.kernel == TGEMM_KERNEL_DIRECT) &&
         k <= 4096 && n <= 2048)
         return plain;
+    // A 32-row skinny product whose workgroups make one wave (192-256 of them) streams B
+    // at the chip's rate on its own; split-K would add only its partials' traffic
+    // (1-32 x 8192 x 8192: 23.4-24.8 against 25.4-26.7 us hot, 27.8-29.6 against
+    // 36.4-37.8 us with operands past the last-level cache)
+    if (plain.kernel == TGEMM_KERNEL_SKINNY && plain.block_m == 32) {
+        const int64_t wgs = ((n + 31) / 32) * ((m + 31) / 32);
+        if (wgs >= 192 && wgs <= 256)
+            return plain;
+    }
     const auto tiles = [&](int64_t bm, int64_t bn) {
         return ((m + bm - 1) / bm) * ((n + bn - 1) / bn);
     };
