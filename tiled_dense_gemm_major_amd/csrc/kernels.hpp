@@ -2029,23 +2029,25 @@ gemm_quad_sk(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restri
 // Skinny kernel (small M, B as [N,K]): the product is a stream of B with little reuse
 // ("Tiling a matmul", section "Where it breaks": small or skinny shapes stay
 // memory-bound whatever the tiling; split-K keeps all the compute units busy).
-//   One workgroup per 32 columns of C (all MT*32 rows of a row block); its 8 waves split
-//   the K range into 8 contiguous parts (split-K inside the workgroup), each wave
+//   One workgroup per 32 columns of C (all MT*32 rows of a row block); its 8 waves (4
+//   with 128-wide chunks of 64 rows, whose LDS buffers would not fit eight times) split
+//   the K range into as many contiguous parts (split-K inside the workgroup), each wave
 //   accumulating a full (MT*32) x 32 partial product.  Per k chunk (64 wide: whole
 //   128-byte row segments, 8 lanes per row; or 128 wide: 256-byte segments, 16 lanes
 //   per row, longer runs per memory page) a wave loads the chunk D chunks ahead into
 //   registers, writes it to its own swizzled LDS buffer and reads it back in MFMA
 //   operand layout (a wave's LDS accesses complete in order, so no barrier is needed).
-//   At the end the 8 partial products are summed through LDS in a fixed order
+//   At the end the partial products are summed through LDS in a fixed order
 //   (deterministic), cast once and stored.  Requirements as for gemm_tiled; rows past
 //   M, columns past N and k past K read as zero through the buffer range check.
 // ------------------------------------------------------------------------------------
-template <int DT, int MT, int D, int CKT = 64>
-__global__ void __attribute__((amdgpu_flat_work_group_size(512, 512),
-                               amdgpu_waves_per_eu(2, 2)))
+template <int DT, int MT, int D, int CKT = 64, int NWT = 8>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NWT * 64, NWT * 64),
+                               amdgpu_waves_per_eu(NWT / 4, NWT / 4)))
 gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
             int N, int K, int lda, int ldb, int ldc) {
-    constexpr int NW = 8, BN = 32, CK = CKT, KC = CK / 8;
+    constexpr int NW = NWT, BN = 32, CK = CKT, KC = CK / 8;
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
     constexpr int RPL = 64 / KC;                   // chunk rows per 1 KiB load
     constexpr int BM = MT * 32;
     constexpr int ROWS = BM + BN;                  // rows of one chunk: A rows, then B rows

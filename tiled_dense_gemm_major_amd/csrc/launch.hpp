@@ -155,11 +155,12 @@ hipError_t launch_quad_sk(const void* A, const void* B, void* C, int M, int N, i
     return hipGetLastError();
 }
 
-template <int DT, int MT, int D, int CK = 64>
+template <int DT, int MT, int D, int CK = 64, int NW = 8>
 hipError_t launch_skinny(const void* A, const void* B, void* C, int M, int N, int K, int lda,
                          int ldb, int ldc, int, hipStream_t s) {
-    hipLaunchKernelGGL((tgemm::gemm_skinny<DT, MT, D, CK>),
-                       dim3((unsigned)cdiv(N, 32), (unsigned)cdiv(M, MT * 32)), dim3(512), 0, s,
+    hipLaunchKernelGGL((tgemm::gemm_skinny<DT, MT, D, CK, NW>),
+                       dim3((unsigned)cdiv(N, 32), (unsigned)cdiv(M, MT * 32)), dim3(NW * 64),
+                       0, s,
                        KARGS);
     return hipGetLastError();
 }
@@ -255,10 +256,16 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
         DT, 0, 0, tgemm_config{TGEMM_KERNEL_SKINNY, MT * 32, 32, 64, 1, 8, D, 1, 8, 32},       \
             &launch_skinny<DT, MT, D>                                                      \
     }
-// The skinny kernel with 128-wide k chunks (block_k 128): 256-byte row segments per load.
+// The skinny kernel with 128-wide k chunks (block_k 128): 256-byte row segments per load;
+// 64-row blocks with four waves (waves_n and split_k 4).
 #define SKINNY_WIDE(DT, MT, D)                                                             \
     Variant {                                                                              \
         DT, 0, 0, tgemm_config{TGEMM_KERNEL_SKINNY, MT * 32, 32, 128, 1, 8, D, 1, 8, 32},      \
             &launch_skinny<DT, MT, D, 128>                                                 \
+    }
+#define SKINNY_WIDE4(DT, MT, D)                                                            \
+    Variant {                                                                              \
+        DT, 0, 0, tgemm_config{TGEMM_KERNEL_SKINNY, MT * 32, 32, 128, 1, 4, D, 1, 4, 32},      \
+            &launch_skinny<DT, MT, D, 128, 4>                                              \
     }
 }  // namespace tgemm_reg

@@ -246,11 +246,13 @@ tgemm_config choose(int dtype, int a_layout, int layout, int64_t m, int64_t n, i
     }
     if (a_layout == TGEMM_A_MK && layout == TGEMM_B_NK && m <= 128 && k >= 1024) {
         const int mt = m <= 32 ? 1 : (m <= 64 ? 2 : 4);
-        // 32-row blocks take 128-wide k chunks (256-byte row segments), one chunk ahead
+        // 32- and 64-row blocks take 128-wide k chunks (256-byte row segments), one chunk
+        // ahead (64-row blocks with four waves)
         if (mt == 1)
             return tgemm_config{TGEMM_KERNEL_SKINNY, 32, 32, 128, 1, 8, 1, 1, 8, 32};
-        const int depth = mt == 2 ? 3 : 1;
-        return tgemm_config{TGEMM_KERNEL_SKINNY, mt * 32, 32, 64, 1, 8, depth, 1, 8, 32};
+        if (mt == 2)
+            return tgemm_config{TGEMM_KERNEL_SKINNY, 64, 32, 128, 1, 4, 1, 1, 4, 32};
+        return tgemm_config{TGEMM_KERNEL_SKINNY, 128, 32, 64, 1, 8, 1, 1, 8, 32};
     }
     const int64_t t256 = ((m + 255) / 256) * ((n + 255) / 256);
     const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
