@@ -98,7 +98,7 @@ typedef enum {
     TGEMM_KERNEL_TILED = 1,   /* 128-bit loads, register prefetch, two swizzled LDS
                                  stages, MFMA 32x32x16, grouped XCD-aware tile order     */
     TGEMM_KERNEL_SKINNY = 2,  /* small M: the K range of a tile split over the waves of a
-                                 workgroup and summed in LDS                              */
+                                 workgroup and summed in LDS (either B storage)           */
     TGEMM_KERNEL_DMA = 3,     /* A [M,K], B [N,K] only: global loads written straight into
                                  a deep ring of swizzled LDS stages (no register staging) */
     TGEMM_KERNEL_PINGPONG = 4,/* 8 waves, two per SIMD, alternating between operand fetch

@@ -274,10 +274,12 @@ def test_direct_k_walk_exact(dev, orc, K):
 # index on its XCD, so with 33 column blocks and 1-6 chunks per wave the ragged last
 # chunk is reached first, last and in between.  The row counts leave 1 to 7 of a row block's
 # 8-row A loads past M (not issued: their LDS rows are zeroed once), including a last
-# row block of 36 rows (M = 100).
+# row block of 36 rows (M = 100).  With B [K,N] the 33 column blocks also leave a ragged
+# last group of the pairing of column blocks onto XCDs.
+@pytest.mark.parametrize("layout", [B_NK, B_KN])
 @pytest.mark.parametrize("K", [1000, 1544, 2568, 3080])
 @pytest.mark.parametrize("M", [1, 9, 16, 64, 100])
-def test_skinny_k_walk_exact(dev, orc, M, K):
+def test_skinny_k_walk_exact(dev, orc, M, K, layout):
     from tiled_dense_gemm_major_amd import tgemm
     dtype = BF16
     rng = np.random.default_rng(700 + K + M)
@@ -285,10 +287,13 @@ def test_skinny_k_walk_exact(dev, orc, M, K):
     A = _int_bits(dtype, rng.integers(-2, 3, (M, K)))
     B = _int_bits(dtype, rng.integers(-2, 3, (N, K)))
     want = orc.gemm(dtype, A, B, B_NK)
-    for cfg in [c for c in _configs(dtype, B_NK) if c.kernel == tgemm.KERNEL_SKINNY]:
-        say(f"skinny k walk M={M} K={K} (chunks {-(-K // 64)}, tail {K % 64}) "
-            f"{_cfg_id(cfg)}")
-        assert np.array_equal(run(dtype, A, B, B_NK, cfg), want), (M, K, _cfg_id(cfg))
+    Bl = B if layout == B_NK else np.ascontiguousarray(B.T)
+    cfgs = [c for c in _configs(dtype, layout) if c.kernel == tgemm.KERNEL_SKINNY]
+    assert cfgs
+    for cfg in cfgs:
+        say(f"skinny k walk M={M} K={K} layout {layout} (chunks {-(-K // cfg.block_k)}, "
+            f"tail {K % cfg.block_k}) {_cfg_id(cfg)}")
+        assert np.array_equal(run(dtype, A, Bl, layout, cfg), want), (M, K, _cfg_id(cfg))
 
 
 @pytest.mark.parametrize("layout", [B_NK, B_KN])

@@ -2041,6 +2041,57 @@ gemm_quad_sk(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restri
 //   (deterministic), cast once and stored.  Requirements as for gemm_tiled; rows past
 //   M, columns past N and k past K read as zero through the buffer range check.
 // ------------------------------------------------------------------------------------
+// The skinny kernels' end: the waves' partial products to LDS as red[wave][n][m] (m
+// contiguous), summed in wave order (deterministic), cast once and stored.
+template <int DT, int MT, int NW>
+__device__ __forceinline__ void skinny_epilogue(u16* lds, const f32x16 (&acc)[MT],
+                                                u16* __restrict__ C, int M, int N, int ldc,
+                                                int m0, int n0, int tid, int lane, int wave) {
+    constexpr int BN = 32, BM = MT * 32;
+    const int half = lane >> 5;
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int h = 0; h < MT; ++h)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int n = 8 * (v >> 2) + 4 * half + (v & 3);
+            red[(wave * BN + n) * BM + 32 * h + (lane & 31)] = acc[h][v];
+        }
+    __syncthreads();
+    constexpr int OUT_PER_T = BM * BN / (NW * 64);   // consecutive n per thread
+    static_assert(OUT_PER_T % 4 == 0 || OUT_PER_T == 2, "store groups");
+    const int m = tid % BM;
+    const int nb = (tid / BM) * OUT_PER_T;
+    float sum[OUT_PER_T];
+#pragma unroll
+    for (int q = 0; q < OUT_PER_T; ++q) {
+        float t = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            t += red[(w * BN + nb + q) * BM + m];
+        sum[q] = t;
+    }
+    const int gm = m0 + m;
+    if (gm < M) {
+        if constexpr (OUT_PER_T >= 4) {
+#pragma unroll
+            for (int q = 0; q < OUT_PER_T; q += 4) {
+                if (n0 + nb + q < N) {
+                    u32x2 v;
+                    v[0] = pack2<DT>(sum[q], sum[q + 1]);
+                    v[1] = pack2<DT>(sum[q + 2], sum[q + 3]);
+                    *reinterpret_cast<u32x2*>(C + (size_t)gm * ldc + n0 + nb + q) = v;
+                }
+            }
+        } else {
+            if (n0 + nb < N)
+                *reinterpret_cast<uint32_t*>(C + (size_t)gm * ldc + n0 + nb) =
+                    pack2<DT>(sum[0], sum[1]);
+        }
+    }
+}
+
 template <int DT, int MT, int D, int CKT = 64, int NWT = 8>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NWT * 64, NWT * 64),
                                amdgpu_waves_per_eu(NWT / 4, NWT / 4)))
@@ -2149,48 +2200,143 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
         });
     }
 
-    // partial products to LDS as red[wave][n][m] (m contiguous), then a fixed-order sum
-    __syncthreads();
-    float* red = reinterpret_cast<float*>(lds);
+    skinny_epilogue<DT, MT, NW>(lds, acc, C, M, N, ldc, m0, n0, tid, lane, wave);
+}
+
+// The skinny kernel for B stored [K,N] (N contiguous): the same workgroup, wave split,
+// A chunks and epilogue, with the B chunk taken as 64 k rows of the workgroup's 32
+// columns (64 bytes per row; 16 rows per 1 KiB load) and stored as it lies.  Its MFMA
+// operands come from two transposing LDS reads (ds_read_b64_tr_b16, as in the [K,N]
+// forms of the tiled and ping-pong kernels): lane group g covers columns 16(g%2)..+15
+// and k rows 8(g/2)..+3 (then +4), so each lane receives its column's 8 consecutive k in
+// operand order; the four rows of a group's read are 64 bytes apart, so lanes 0-31 reach
+// all 64 banks once.  A B row's 128-byte line holds two workgroups' columns: column
+// blocks 2p and 2p+1 go to workgroups 8 ids apart (one XCD, one L2).
+template <int DT, int MT, int D>
+__global__ void __attribute__((amdgpu_flat_work_group_size(512, 512),
+                               amdgpu_waves_per_eu(2, 2)))
+gemm_skinny_kn(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C,
+               int M, int N, int K, int lda, int ldb, int ldc) {
+    constexpr int NW = 8, BN = 32, CK = 64, KC = CK / 8;
+    constexpr int RPL = 64 / KC;                   // A rows per 1 KiB load (8)
+    constexpr int BM = MT * 32;
+    constexpr int LA = BM / RPL;                   // A loads per chunk per wave
+    constexpr int LB = CK / 16;                    // B loads per chunk: 16 k rows each
+    constexpr int ABUF = BM * CK, WBUF = ABUF + CK * BN;
+    constexpr int RED = NW * BN * BM;              // floats of the final reduction
+    constexpr int LDS_ELEMS = (NW * WBUF * 2 > RED * 4) ? NW * WBUF : RED * 2;
+    static_assert(LDS_ELEMS * 2 <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(16))) u16 lds[LDS_ELEMS];
+
+    // column blocks in pairs per XCD; a ragged last group of 16 ids keeps the identity
+    const int bid = (int)blockIdx.x, full = (int)gridDim.x & ~15;
+    const int nblk = bid < full ? 2 * ((bid >> 4) * 8 + (bid & 7)) + ((bid >> 3) & 1) : bid;
+    const int n0 = nblk * BN, m0 = (int)blockIdx.y * BM;
+    const int tid = (int)threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5;
+
+    const rsrc_t ra = make_rsrc(A, span_bytes(M, K, lda));
+    const rsrc_t rb = make_rsrc(B, span_bytes(K, N, ldb));
+    // A load i: chunk rows 8i + lane/8, 16-byte piece lane%8 (as in gemm_skinny)
+    const int lrow = lane / KC, lpc = lane % KC;
+    uint32_t aoff[LA];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        const int r = RPL * i + lrow;
+        aoff[i] = m0 + r < M ? (uint32_t)((m0 + r) * lda + lpc * 8) * 2u : kOutOfRange;
+    }
+    // B load i: k rows 16i + lane/4 of the chunk, columns n0 + 8(lane%4) .. +7; the chunk's
+    // first k row comes in as the scalar offset
+    const int bkr = lane >> 2, bpc = lane & 3;
+    const bool bcol = n0 + bpc * 8 < N;
+    uint32_t boff[LB];
+#pragma unroll
+    for (int i = 0; i < LB; ++i)
+        boff[i] = (uint32_t)((16 * i + bkr) * ldb + n0 + bpc * 8) * 2u;
+    u16* wb = lds + wave * WBUF;                   // A rows [BM][CK], swizzled
+    u16* wbb = wb + ABUF;                          // B rows [CK][BN], as they lie
+    auto wr_a = [&](int i) {
+        return (RPL * i + lrow) * CK + ((lpc ^ swz<KC>(RPL * i + lrow)) * 8);
+    };
+    // A loads whose 8 rows all lie past M are not issued; their LDS rows are zeroed once
+    const int a_rows = M - m0;
+    auto dead = [&](int i) { return RPL * i >= a_rows; };
+#pragma unroll
+    for (int i = 0; i < LA; ++i)
+        if (dead(i))
+            *reinterpret_cast<u32x4*>(wb + wr_a(i)) = u32x4{0u, 0u, 0u, 0u};
+
+    const int nch = (K + CK - 1) / CK;
+    const int c_lo = wave * nch / NW, len = (wave + 1) * nch / NW - c_lo;
+    const int rot = len > 0 ? (int)((blockIdx.x >> 3) % (unsigned)len) : 0;
+
+    u32x4 abuf[D][LA], bbuf[D][LB];
+    auto load_chunk = [&](int t, auto slot) {     // t-th chunk of this wave's walk
+        constexpr int S = decltype(slot)::value;
+        const bool live = t < len;
+        const int p = t + rot < len ? t + rot : t + rot - len;
+        const int k0 = live ? (c_lo + p) * CK : 0;
+        const bool ok = live && k0 + lpc * 8 < K;
+#pragma unroll
+        for (int i = 0; i < LA; ++i)
+            if (!dead(i))
+                abuf[S][i] = load16(ra, ok ? aoff[i] : kOutOfRange, (uint32_t)k0 * 2u);
+#pragma unroll
+        for (int i = 0; i < LB; ++i) {
+            const bool bok = live && bcol && k0 + 16 * i + bkr < K;
+            bbuf[S][i] = load16(rb, bok ? boff[i] : kOutOfRange, (uint32_t)k0 * (uint32_t)ldb * 2u);
+        }
+    };
+
+    const int g = lane >> 4, sl = lane & 15;
+    const int btr = (8 * (g >> 1) + (sl >> 2)) * BN + 16 * (g & 1) + 4 * (sl & 3);
+    auto read_tr = [&](const u16* p0) {            // k rows kl and kl + 4
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * BN));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    };
+
+    const int xr = swz<KC>(lane & 31);
+    f32x16 acc[MT];
 #pragma unroll
     for (int h = 0; h < MT; ++h)
+        acc[h] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+
+    static_for<0, D>([&](auto d) { load_chunk(decltype(d)::value, d); });
+    for (int c = 0; c < len; c += D) {
+        static_for<0, D>([&](auto dc) {
+            constexpr int d = decltype(dc)::value;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int n = 8 * (v >> 2) + 4 * half + (v & 3);
-            red[(wave * BN + n) * BM + 32 * h + (lane & 31)] = acc[h][v];
-        }
-    __syncthreads();
-    constexpr int OUT_PER_T = BM * BN / (NW * 64);   // consecutive n per thread
-    static_assert(OUT_PER_T % 4 == 0 || OUT_PER_T == 2, "store groups");
-    const int m = tid % BM;
-    const int nb = (tid / BM) * OUT_PER_T;
-    float sum[OUT_PER_T];
+            for (int i = 0; i < LA; ++i)
+                if (!dead(i))
+                    *reinterpret_cast<u32x4*>(wb + wr_a(i)) = abuf[d][i];
 #pragma unroll
-    for (int q = 0; q < OUT_PER_T; ++q) {
-        float t = 0.0f;
+            for (int i = 0; i < LB; ++i)
+                *reinterpret_cast<u32x4*>(wbb + (16 * i + bkr) * BN + bpc * 8) = bbuf[d][i];
+            u32x4 fa[CK / 16][MT], fb[CK / 16];
 #pragma unroll
-        for (int w = 0; w < NW; ++w)
-            t += red[(w * BN + nb + q) * BM + m];
-        sum[q] = t;
-    }
-    const int gm = m0 + m;
-    if (gm < M) {
-        if constexpr (OUT_PER_T >= 4) {
+            for (int j = 0; j < CK / 16; ++j) {
+                const int koff = (((2 * j) | half) ^ xr) * 8;
 #pragma unroll
-            for (int q = 0; q < OUT_PER_T; q += 4) {
-                if (n0 + nb + q < N) {
-                    u32x2 v;
-                    v[0] = pack2<DT>(sum[q], sum[q + 1]);
-                    v[1] = pack2<DT>(sum[q + 2], sum[q + 3]);
-                    *reinterpret_cast<u32x2*>(C + (size_t)gm * ldc + n0 + nb + q) = v;
-                }
+                for (int h = 0; h < MT; ++h)
+                    fa[j][h] = *reinterpret_cast<const u32x4*>(
+                        wb + (32 * h + (lane & 31)) * CK + koff);
+                fb[j] = read_tr(wbb + 16 * j * BN + btr);
             }
-        } else {
-            if (n0 + nb < N)
-                *reinterpret_cast<uint32_t*>(C + (size_t)gm * ldc + n0 + nb) =
-                    pack2<DT>(sum[0], sum[1]);
-        }
+            load_chunk(c + d + D, dc);
+#pragma unroll
+            for (int j = 0; j < CK / 16; ++j)
+#pragma unroll
+                for (int h = 0; h < MT; ++h)
+                    acc[h] = mfma_32x32x16<DT>(fb[j], fa[j][h], acc[h]);
+        });
     }
+    skinny_epilogue<DT, MT, NW>(lds, acc, C, M, N, ldc, m0, n0, tid, lane, wave);
 }
 
 // ------------------------------------------------------------------------------------

@@ -165,6 +165,15 @@ hipError_t launch_skinny(const void* A, const void* B, void* C, int M, int N, in
     return hipGetLastError();
 }
 
+template <int DT, int MT, int D>
+hipError_t launch_skinny_kn(const void* A, const void* B, void* C, int M, int N, int K, int lda,
+                            int ldb, int ldc, int, hipStream_t s) {
+    hipLaunchKernelGGL((tgemm::gemm_skinny_kn<DT, MT, D>),
+                       dim3((unsigned)cdiv(N, 32), (unsigned)cdiv(M, MT * 32)), dim3(512), 0, s,
+                       KARGS);
+    return hipGetLastError();
+}
+
 template <int DT, int AL, int LAYOUT>
 hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, int K, int lda,
                           int ldb, int ldc, int group_m, hipStream_t s) {
@@ -262,6 +271,12 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
     Variant {                                                                              \
         DT, 0, 0, tgemm_config{TGEMM_KERNEL_SKINNY, MT * 32, 32, 128, 1, 8, D, 1, 8, 32},      \
             &launch_skinny<DT, MT, D, 128>                                                 \
+    }
+// The skinny kernel for B [K,N] (64-wide k chunks, transposing B reads).
+#define SKINNY_KN(DT, MT, D)                                                               \
+    Variant {                                                                              \
+        DT, 0, 1, tgemm_config{TGEMM_KERNEL_SKINNY, MT * 32, 32, 64, 1, 8, D, 1, 8, 32},       \
+            &launch_skinny_kn<DT, MT, D>                                                   \
     }
 #define SKINNY_WIDE4(DT, MT, D)                                                            \
     Variant {                                                                              \

@@ -244,6 +244,11 @@ tgemm_config choose(int dtype, int a_layout, int layout, int64_t m, int64_t n, i
             return cfg;
         }
     }
+    if (a_layout == TGEMM_A_MK && layout == TGEMM_B_KN && m <= 128 && k >= 1024) {
+        const int mt = m <= 32 ? 1 : (m <= 64 ? 2 : 4);
+        return tgemm_config{TGEMM_KERNEL_SKINNY, mt * 32, 32, 64, 1, 8, mt == 1 ? 4 : (mt == 2 ? 3 : 1),
+                            1, 8, 32};
+    }
     if (a_layout == TGEMM_A_MK && layout == TGEMM_B_NK && m <= 128 && k >= 1024) {
         const int mt = m <= 32 ? 1 : (m <= 64 ? 2 : 4);
         // 32- and 64-row blocks take 128-wide k chunks (256-byte row segments), one chunk

@@ -1,5 +1,6 @@
-// libtgemm registry: the any-alignment kernel (every storage), and for A [M,K] with
-// B [N,K] the deep direct-to-LDS ring, the skinny kernel and split-K over workgroups.
+// libtgemm registry: the any-alignment kernel (every storage), for A [M,K] with B [N,K]
+// the deep direct-to-LDS ring, the skinny kernel and split-K over workgroups, and the
+// skinny kernel for B [K,N].
 #include "launch.hpp"
 
 namespace tgemm_reg {
@@ -13,6 +14,8 @@ namespace {
         SPLITK(DT, 64, 128, 64, 1, 4, 6, 1)
 const Variant kList[] = {
     SMALL_MK_NK(0), SMALL_MK_NK(1),
+    SKINNY_KN(0, 1, 4), SKINNY_KN(0, 2, 3), SKINNY_KN(0, 4, 1),
+    SKINNY_KN(1, 1, 4), SKINNY_KN(1, 2, 3), SKINNY_KN(1, 4, 1),
     GENERIC(0, 0, 1), GENERIC(1, 0, 1),
     GENERIC(0, 1, 0), GENERIC(1, 1, 0), GENERIC(0, 1, 1), GENERIC(1, 1, 1),
 };
