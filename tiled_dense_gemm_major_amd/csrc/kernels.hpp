@@ -2269,7 +2269,9 @@ gemm_skinny_kn(const u16* __restrict__ A, const u16* __restrict__ B, u16* __rest
 
     const int nch = (K + CK - 1) / CK;
     const int c_lo = wave * nch / NW, len = (wave + 1) * nch / NW - c_lo;
-    const int rot = len > 0 ? (int)((blockIdx.x >> 3) % (unsigned)len) : 0;
+    // the two workgroups of a column pair start their walks at the same chunk (so the
+    // second read of each shared B line finds it in L2), pairs at different chunks
+    const int rot = len > 0 ? (int)((unsigned)(nblk >> 1) % (unsigned)len) : 0;
 
     u32x4 abuf[D][LA], bbuf[D][LB];
     auto load_chunk = [&](int t, auto slot) {     // t-th chunk of this wave's walk
