@@ -36,9 +36,10 @@
  *   - Alignment: any 2-byte-aligned pointers, sizes and leading dimensions are accepted.
  *     The fast kernels need A, B, C 16-byte aligned, K, N, lda, ldb and ldc multiples of
  *     8, M a multiple of 8 when A is [K,M], and A and B each spanning at most 2^31 bytes;
- *     other calls run the same tiles with masked loads and element-wise stores
- *     (TGEMM_KERNEL_MASKED), or, when A or B spans more than 2^31 - 32 bytes, a slower
- *     generic kernel; the arithmetic is the same.
+ *     the skinny kernels (A [M,K], B [N,K]) need those rules of A and B only, and store C
+ *     element by element where C or N breaks them.  Other calls run the same tiles with
+ *     masked loads and element-wise stores (TGEMM_KERNEL_MASKED), or, when A or B spans
+ *     more than 2^31 - 32 bytes, a slower generic kernel; the arithmetic is the same.
  *   - Limits: M, N, K < 2^31, M*K, N*K, M*N < 2^31, and the element span of each operand
  *     ((rows - 1) * ld + row length) < 2^31 (TGEMM_ERR_UNSUPPORTED).
  *   - Aliasing: the span of C may not overlap the span of A or B (TGEMM_ERR_ALIASING).
@@ -174,7 +175,8 @@ int gemm_bf16(int64_t m, int64_t n, int64_t k, const void* A, const void* B, voi
  * The same product with an explicit dtype (tgemm_dtype) and, optionally, an explicit
  * configuration (cfg == NULL: the table's choice).  A configuration must be one that
  * tgemm_list_configs reports (else TGEMM_ERR_UNSUPPORTED); a fast-kernel configuration
- * given operands that break its alignment rules fails with TGEMM_ERR_ALIGNMENT.  This is
+ * given operands that break its alignment rules fails with TGEMM_ERR_ALIGNMENT (a
+ * TGEMM_KERNEL_SKINNY configuration with B [N,K] checks A and B only).  This is
  * the entry point of the tile-configuration sweep.
  */
 int gemm_ex(int dtype, int64_t m, int64_t n, int64_t k, const void* A, const void* B,
@@ -245,8 +247,9 @@ int gemm_strided(int dtype, int64_t m, int64_t n, int64_t k, const void* A, int6
 /* The configuration gemm_f16 / gemm_bf16 / gemm_ex(cfg = NULL) pick for this packed
  * problem (A [M,K], B per b_layout, C [M,N], no padding) with operands at 16-byte-aligned
  * addresses, written to *out; whether the fast kernels can take it follows from the sizes
- * (K and N multiples of 8, A and B each at most 2^31 bytes; else the masked kernel, or
- * the generic one past 2^31 - 32 bytes).  Host-only: it touches no
+ * (K and N multiples of 8, A and B each at most 2^31 bytes; with B [N,K] and only N off a
+ * multiple of 8, a skinny configuration where the aligned choice is one; else the masked
+ * kernel, or the generic one past 2^31 - 32 bytes).  Host-only: it touches no
  * device.  Returns TGEMM_OK, TGEMM_ERR_NULL_POINTER (out NULL) or the size, dtype and
  * layout errors of gemm_ex. */
 int tgemm_query_config(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
@@ -258,12 +261,15 @@ int tgemm_query_config(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
 int tgemm_list_configs(int dtype, int b_layout, tgemm_config* out, int capacity);
 
 /* The choice for either storage of A (tgemm_a_layout) and a caller-stated alignment:
- * `aligned` != 0 says the operands meet every fast-kernel rule (16-byte-aligned
- * addresses, sizes and leading dimensions multiples of 8, spans within 2^31 bytes),
- * 0 that they do not (the choice is then a TGEMM_KERNEL_MASKED configuration; a call
- * whose A or B spans more than 2^31 - 32 bytes runs the generic kernel instead, which this
- * query cannot see).  The list for either storage of A; tgemm_list_configs answers for
- * TGEMM_A_MK. */
+ * `aligned` 1 (or any value but 0 and 2) says the operands meet every fast-kernel rule
+ * (16-byte-aligned addresses, sizes and leading dimensions multiples of 8, spans within
+ * 2^31 bytes); 0 that they do not (the choice is then a TGEMM_KERNEL_MASKED
+ * configuration; a call whose A or B spans more than 2^31 - 32 bytes runs the generic
+ * kernel instead, which this query cannot see); 2 that A [M,K] and B [N,K] meet the rules
+ * but C or N does not (an odd N, say): then a call takes the aligned choice where that is
+ * a TGEMM_KERNEL_SKINNY configuration (the skinny kernels store C element by element
+ * where it is not aligned), else the masked one.  The list for either storage of A;
+ * tgemm_list_configs answers for TGEMM_A_MK. */
 int tgemm_query_config_ex(int dtype, int64_t m, int64_t n, int64_t k, int a_layout,
                           int b_layout, int aligned, tgemm_config* out);
 int tgemm_list_configs_ex(int dtype, int a_layout, int b_layout, tgemm_config* out,

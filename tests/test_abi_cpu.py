@@ -90,6 +90,43 @@ def test_fast_config_needs_alignment(lib):
     assert rc == -3
 
 
+def test_operands_aligned_class(lib):
+    """A [M,K] and B [N,K] meeting the fast rules while N (or C) does not: the skinny
+    kernels take the product (they store C element by element where it is unaligned);
+    any other shape, or B [K,N], stays on the masked kernel."""
+    A = tgemm.ALIGN_OPERANDS
+    for dt in (tgemm.F16, tgemm.BF16):
+        for m, rows in ((1, 32), (8, 32), (32, 32), (64, 64)):
+            c = tgemm.query_config(dt, m, 50257, 4096, tgemm.B_NK, A)
+            assert c.kernel == tgemm.KERNEL_SKINNY and c.block_m == rows, (m, c)
+            # what an all-aligned product of that size would take
+            assert c.as_dict() == tgemm.query_config(dt, m, 50264, 4096).as_dict()
+        assert tgemm.query_config(dt, 8, 50257, 4096, tgemm.B_KN, A).kernel == \
+            tgemm.KERNEL_MASKED
+        assert tgemm.query_config(dt, 4096, 50257, 4096, tgemm.B_NK, A).kernel == \
+            tgemm.KERNEL_MASKED
+        assert tgemm.query_config(dt, 8, 50257, 4096, tgemm.B_NK, False).kernel == \
+            tgemm.KERNEL_MASKED
+        # packed operands: the sizes decide the class (K odd breaks the operands' rules)
+        assert tgemm.query_config_packed(dt, 8, 50257, 4096).kernel == tgemm.KERNEL_SKINNY
+        assert tgemm.query_config_packed(dt, 8, 50257, 4095).kernel == tgemm.KERNEL_MASKED
+        assert tgemm.query_config_packed(dt, 8, 50257, 4096, tgemm.B_KN).kernel == \
+            tgemm.KERNEL_MASKED
+    skinny = tgemm.query_config(tgemm.BF16, 8, 8192, 4096)
+    assert skinny.kernel == tgemm.KERNEL_SKINNY
+    # an explicit skinny configuration: odd N is accepted with B [N,K] (the call is only
+    # rejected before any launch here, so it runs no kernel) and refused with B [K,N]
+    st = lib.gemm_strided
+    kn = tgemm.query_config(tgemm.BF16, 8, 8192, 4096, tgemm.B_KN)
+    assert kn.kernel == tgemm.KERNEL_SKINNY
+    # B [K,N] with an odd leading dimension breaks the rules for that B storage
+    assert st(1, 8, 8191, 4096, FAKE, 4096, tgemm.A_MK, FAKE + (1 << 30), 8191, tgemm.B_KN,
+              FAKE + (1 << 31), 8191, ctypes.byref(kn), None) == -3
+    # A's rows not a multiple of 8 elements apart: refused with B [N,K] too
+    assert st(1, 8, 8191, 4096, FAKE, 4100, tgemm.A_MK, FAKE + (1 << 30), 4096, tgemm.B_NK,
+              FAKE + (1 << 31), 8191, ctypes.byref(skinny), None) == -3
+
+
 def test_query_config_table(lib):
     big = tgemm.query_config(tgemm.BF16, 8192, 8192, 8192)
     assert big.kernel != tgemm.KERNEL_GENERIC and big.block_m * big.block_n >= 128 * 128
@@ -410,10 +447,16 @@ def test_boundary_calls_with_exact_arity(lib):
     assert q(0, 1 << 16, 8, (1 << 14) + 1, 0, ctypes.byref(out)) == 0
     assert out.kernel == tgemm.KERNEL_GENERIC
     # the masked kernel's buffers reach 30 bytes past an operand: up to 2^31 - 32 bytes
-    assert q(0, 1, 1, (1 << 30) - 16, 0, ctypes.byref(out)) == 0      # 2^31 - 32 bytes
+    # (K odd, so the operands break the fast rules: 16 x 67108863 halves = 2^31 - 32 bytes)
+    assert 16 * 67108863 == (1 << 30) - 16
+    assert q(0, 16, 1, 67108863, 0, ctypes.byref(out)) == 0          # 2^31 - 32 bytes
     assert out.kernel == tgemm.KERNEL_MASKED
     assert q(0, 1, 1, (1 << 30) - 15, 0, ctypes.byref(out)) == 0      # 2^31 - 30 bytes
     assert out.kernel == tgemm.KERNEL_GENERIC
+    # K a multiple of 8: A [1,K] and B [1,K] meet the fast rules while N = 1 does not, and
+    # the skinny kernel (which needs the operands' rules only) takes the product
+    assert q(0, 1, 1, (1 << 30) - 16, 0, ctypes.byref(out)) == 0
+    assert out.kernel == tgemm.KERNEL_SKINNY
     assert q(1, 8, 8, 8, 0, None) == -2
     assert q(1, -1, 8, 8, 0, ctypes.byref(out)) == -1
     s = raw.tgemm_status_string

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 from tests.gpu_util import (assert_parity, assert_parity_full, from_dev, require_gpu, run,
-                            sample_positions, say, to_dev, torch)
+                            sample_positions, say, tdtype, to_dev, torch)
 from tiled_dense_gemm_major_amd.inputs import (BF16, B_KN, B_NK, F16, WORKLOADS, Stream,
                                                Workload)
 
@@ -433,3 +433,70 @@ def test_every_config_non_finite(dev, orc, dtype, layout):
         say(f"non-finite {_cfg_id(cfg)} dtype {dtype} layout {layout}")
         got = run(dtype, A, B, layout, cfg)
         _assert_same_class(orc, dtype, K, got, want, _cfg_id(cfg))
+
+
+# ---------------------------------------------------------------------------------------
+# Skinny kernels with A [M,K] and B [N,K] meeting the fast rules while C does not (odd N,
+# an odd leading dimension, a C base off 16 bytes): C is stored element by element where
+# its rows are unaligned, and nothing outside C's rows may change.
+# ---------------------------------------------------------------------------------------
+def _run_strided_c(dtype, A_bits, B_bits, ldc, c_offset, config=None, guard=64,
+                   fill=0x7E00):
+    from tiled_dense_gemm_major_amd import tgemm
+    M, K = A_bits.shape
+    N = B_bits.shape[0]
+    A, B = to_dev(A_bits, dtype), to_dev(B_bits, dtype)
+    total = c_offset + (M - 1) * ldc + N + guard
+    buf = torch.full((total,), fill, dtype=torch.int16, device="cuda")
+    C = buf.view(tdtype(dtype))[c_offset:]
+    tgemm.gemm_strided(dtype, M, N, K, A, K, tgemm.A_MK, B, K, tgemm.B_NK, C, ldc, config)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy().view(np.uint16)
+    outside = np.ones(total, dtype=bool)
+    rows = []
+    for r in range(M):
+        lo = c_offset + r * ldc
+        rows.append(host[lo:lo + N].copy())
+        outside[lo:lo + N] = False
+    assert np.all(host[outside] == fill), "an element outside C's rows changed"
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("M", [1, 9, 32, 64])
+@pytest.mark.parametrize("N,ldc,c_offset", [(257, 257, 0), (1031, 1031, 1), (1056, 1059, 0),
+                                            (1056, 1056, 3), (1063, 1070, 2)])
+def test_skinny_unaligned_c_exact(dev, orc, dtype, M, N, ldc, c_offset):
+    from tiled_dense_gemm_major_amd import tgemm
+    K = 1032                              # a multiple of 8, with a chunk tail
+    rng = np.random.default_rng(900 + M + N + ldc + c_offset)
+    A = _int_bits(dtype, rng.integers(-2, 3, (M, K)))
+    B = _int_bits(dtype, rng.integers(-2, 3, (N, K)))
+    want = orc.gemm(dtype, A, B, B_NK)
+    assert tgemm.query_config(dtype, M, N, K, B_NK, tgemm.ALIGN_OPERANDS).kernel == \
+        tgemm.KERNEL_SKINNY
+    say(f"skinny unaligned C M={M} N={N} ldc={ldc} offset={c_offset} table choice")
+    assert np.array_equal(_run_strided_c(dtype, A, B, ldc, c_offset), want)
+    for cfg in [c for c in _configs(dtype, B_NK) if c.kernel == tgemm.KERNEL_SKINNY]:
+        say(f"skinny unaligned C M={M} N={N} ldc={ldc} offset={c_offset} {_cfg_id(cfg)}")
+        assert np.array_equal(_run_strided_c(dtype, A, B, ldc, c_offset, cfg), want), \
+            _cfg_id(cfg)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_skinny_odd_vocabulary_full(dev, orc, dtype):
+    """A decode step's output projection over an odd vocabulary (8 x 50257 x 4096, packed,
+    so every C row but the first is unaligned): the packed entry point takes the skinny
+    kernel, every element against the oracle."""
+    from tiled_dense_gemm_major_amd import tgemm
+    M, N, K = 8, 50257, 4096
+    assert tgemm.query_config_packed(dtype, M, N, K).kernel == tgemm.KERNEL_SKINNY
+    s = Stream(61)
+    A = s.matrix((M, K), dtype, "normal")
+    B = s.matrix((N, K), dtype, "normal")
+    say(f"odd vocabulary {M}x{N}x{K} dtype {dtype}")
+    Ad, Bd = to_dev(A, dtype), to_dev(B, dtype)
+    C = torch.full((M, N), 0x7E00, dtype=torch.int16, device="cuda").view(tdtype(dtype))
+    (tgemm.gemm_f16 if dtype == F16 else tgemm.gemm_bf16)(M, N, K, Ad, Bd, C)
+    torch.cuda.synchronize()
+    assert_parity_full(orc, dtype, A, B, B_NK, from_dev(C), "odd vocabulary")

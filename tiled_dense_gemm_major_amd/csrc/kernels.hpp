@@ -2072,22 +2072,37 @@ __device__ __forceinline__ void skinny_epilogue(u16* lds, const f32x16 (&acc)[MT
             t += red[(w * BN + nb + q) * BM + m];
         sum[q] = t;
     }
+    // groups of G consecutive columns go out as one store where C's base and row stride
+    // keep them G * 2-byte aligned and the group lies inside N, else one element at a
+    // time (C may have any 2-byte alignment and any N: the operands alone decide whether
+    // this kernel runs)
+    constexpr int G = OUT_PER_T >= 4 ? 4 : 2;
+    const bool cvec = ((uintptr_t)C % (2 * G)) == 0 && ldc % G == 0;
     const int gm = m0 + m;
     if (gm < M) {
-        if constexpr (OUT_PER_T >= 4) {
+        u16* crow = C + (size_t)gm * ldc + n0 + nb;
 #pragma unroll
-            for (int q = 0; q < OUT_PER_T; q += 4) {
-                if (n0 + nb + q < N) {
+        for (int q = 0; q < OUT_PER_T; q += G) {
+            const int n = n0 + nb + q;
+            if (cvec && n + G <= N) {
+                if constexpr (G == 4) {
                     u32x2 v;
                     v[0] = pack2<DT>(sum[q], sum[q + 1]);
                     v[1] = pack2<DT>(sum[q + 2], sum[q + 3]);
-                    *reinterpret_cast<u32x2*>(C + (size_t)gm * ldc + n0 + nb + q) = v;
+                    *reinterpret_cast<u32x2*>(crow + q) = v;
+                } else {
+                    *reinterpret_cast<uint32_t*>(crow + q) = pack2<DT>(sum[q], sum[q + 1]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < G; e += 2) {
+                    const uint32_t pr = pack2<DT>(sum[q + e], sum[q + e + 1]);
+                    if (n + e < N)
+                        crow[q + e] = (u16)(pr & 0xffffu);
+                    if (n + e + 1 < N)
+                        crow[q + e + 1] = (u16)(pr >> 16);
                 }
             }
-        } else {
-            if (n0 + nb < N)
-                *reinterpret_cast<uint32_t*>(C + (size_t)gm * ldc + n0 + nb) =
-                    pack2<DT>(sum[0], sum[1]);
         }
     }
 }

@@ -454,6 +454,36 @@ bool fast_aligned(const Problem& p) {
            2 * span_b(p) <= kMaxFastOperandBytes;
 }
 
+// A [M,K] and B [N,K] alone meet those rules (C or N may not): the skinny kernels read
+// only A and B through buffers and store C element by element where it is not aligned,
+// so they serve such products as well (an odd vocabulary size, say).
+bool operands_fast(const Problem& p) {
+    const auto al16 = [](const void* q) { return ((uintptr_t)q % 16) == 0; };
+    return p.a_layout == TGEMM_A_MK && p.b_layout == TGEMM_B_NK && p.k % 8 == 0 &&
+           p.lda % 8 == 0 && p.ldb % 8 == 0 && al16(p.A) && al16(p.B) &&
+           2 * span_a(p) <= kMaxFastOperandBytes && 2 * span_b(p) <= kMaxFastOperandBytes;
+}
+
+// Alignment classes of a call or a query: kAlignNone (the masked kernel's rules), kAlignAll
+// (every fast-kernel rule), kAlignOperands (A and B meet them, C or N does not).
+constexpr int kAlignNone = 0, kAlignAll = 1, kAlignOperands = 2;
+
+// The choice for an alignment class: kAlignOperands takes the choice for aligned operands
+// when that is a skinny kernel (A [M,K], B [N,K]), else the masked one.
+tgemm_config choose_for(int dtype, int a_layout, int layout, int64_t m, int64_t n, int64_t k,
+                        int align, bool with_ws) {
+    if (align == kAlignAll)
+        return with_ws ? choose_ws(dtype, a_layout, layout, m, n, k, true)
+                       : choose(dtype, a_layout, layout, m, n, k, true);
+    if (align == kAlignOperands && a_layout == TGEMM_A_MK && layout == TGEMM_B_NK) {
+        const tgemm_config c = choose(dtype, a_layout, layout, m, n, k, true);
+        if (c.kernel == TGEMM_KERNEL_SKINNY)
+            return c;
+    }
+    return with_ws ? choose_ws(dtype, a_layout, layout, m, n, k, false)
+                   : choose(dtype, a_layout, layout, m, n, k, false);
+}
+
 // The device address of `scratch` on the current device, looked up once per device (with
 // that device current) and kept.
 constexpr int kMaxDevices = 64;
@@ -492,22 +522,25 @@ int run(const Problem& p, const tgemm_config* cfg, void* ws, int64_t ws_bytes, v
         overlaps(p.C, 2 * span_c(p), p.B, 2 * span_b(p)))
         return TGEMM_ERR_ALIASING;
     const bool aligned = fast_aligned(p);
-    tgemm_config use =
-        cfg ? *cfg
-            : (ws || use_scratch
-                   ? choose_ws(p.dtype, p.a_layout, p.b_layout, p.m, p.n, p.k, aligned)
-                   : choose(p.dtype, p.a_layout, p.b_layout, p.m, p.n, p.k, aligned));
+    const int align = aligned ? kAlignAll : (operands_fast(p) ? kAlignOperands : kAlignNone);
+    tgemm_config use = cfg ? *cfg
+                           : choose_for(p.dtype, p.a_layout, p.b_layout, p.m, p.n, p.k, align,
+                                        ws || use_scratch);
     // the fixed scratch holds the skinny products' partials; a larger split goes plain
     if (!cfg && use_scratch && workspace_bytes(use, p.m, p.n) > kScratchBytes)
-        use = choose(p.dtype, p.a_layout, p.b_layout, p.m, p.n, p.k, aligned);
+        use = choose_for(p.dtype, p.a_layout, p.b_layout, p.m, p.n, p.k, align, false);
     const bool reachable = buffer_reachable(p);
     if (!cfg && use.kernel == TGEMM_KERNEL_MASKED && !reachable)
         use = kGenericConfig;
     const Variant* v = find_variant(p.dtype, p.a_layout, p.b_layout, use);
     if (!v)
         return TGEMM_ERR_UNSUPPORTED;
-    if (use.kernel == TGEMM_KERNEL_MASKED ? !reachable
-                                          : use.kernel != TGEMM_KERNEL_GENERIC && !aligned)
+    // the skinny kernels need A and B aligned only (B [N,K]); the other fast kernels need
+    // every rule
+    const bool operands_ok = use.kernel == TGEMM_KERNEL_SKINNY && align == kAlignOperands;
+    if (use.kernel == TGEMM_KERNEL_MASKED
+            ? !reachable
+            : use.kernel != TGEMM_KERNEL_GENERIC && !aligned && !operands_ok)
         return TGEMM_ERR_ALIGNMENT;
     const int64_t need = workspace_bytes(use, p.m, p.n);
     if (use_scratch && need > 0) {
@@ -555,8 +588,9 @@ int query(int dtype, int64_t m, int64_t n, int64_t k, int a_layout, int b_layout
         return rc;
     if (!out)
         return TGEMM_ERR_NULL_POINTER;
-    *out = with_ws ? choose_ws(dtype, a_layout, b_layout, m, n, k, aligned != 0)
-                   : choose(dtype, a_layout, b_layout, m, n, k, aligned != 0);
+    const int align = aligned == kAlignOperands ? kAlignOperands
+                                                : (aligned != 0 ? kAlignAll : kAlignNone);
+    *out = choose_for(dtype, a_layout, b_layout, m, n, k, align, with_ws);
     const Variant* v = find_variant(dtype, a_layout, b_layout, *out);
     if (v)
         out->group_m = v->cfg.group_m;
@@ -679,13 +713,13 @@ int tgemm_query_config(int dtype, int64_t m, int64_t n, int64_t k, int b_layout,
     const Problem p = packed(dtype, m, n, k, reinterpret_cast<const void*>(uintptr_t(256)),
                              reinterpret_cast<const void*>(uintptr_t(256)),
                              reinterpret_cast<void*>(uintptr_t(256)), b_layout);
-    if (!buffer_reachable(p)) {
-        if (!out)
-            return TGEMM_ERR_NULL_POINTER;
+    const int q = query(
+        dtype, m, n, k, TGEMM_A_MK, b_layout,
+        fast_aligned(p) ? kAlignAll : (operands_fast(p) ? kAlignOperands : kAlignNone), out);
+    // as a call does: the masked kernel gives way to the generic one past its span limit
+    if (q == TGEMM_OK && out->kernel == TGEMM_KERNEL_MASKED && !buffer_reachable(p))
         *out = kGenericConfig;
-        return TGEMM_OK;
-    }
-    return query(dtype, m, n, k, TGEMM_A_MK, b_layout, fast_aligned(p) ? 1 : 0, out);
+    return q;
 }
 
 int tgemm_query_config_ex(int dtype, int64_t m, int64_t n, int64_t k, int a_layout,

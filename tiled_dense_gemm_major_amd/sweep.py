@@ -279,6 +279,10 @@ def main(argv=None):
         # packed operands meet the fast kernels' rules when every row length is a
         # multiple of 8 elements (the allocations themselves are aligned)
         aligned = w.K % 8 == 0 and w.N % 8 == 0 and (not a_layout or w.M % 8 == 0)
+        if not aligned and w.K % 8 == 0 and w.b_layout == B_NK and not a_layout:
+            aligned = tgemm.ALIGN_OPERANDS              # A and B meet them, N does not
+        operands_only = aligned is not True and aligned == tgemm.ALIGN_OPERANDS
+        allowed = tgemm.ANY_ALIGNMENT_KERNELS + ((tgemm.KERNEL_SKINNY,) if operands_only else ())
         table = tgemm.query_config(w.dtype, w.M, w.N, w.K, w.b_layout, aligned,
                                    a_layout).as_dict()
         table_ws = tgemm.query_config_ws(w.dtype, w.M, w.N, w.K, w.b_layout,
@@ -292,7 +296,7 @@ def main(argv=None):
         for cfg in tgemm.list_configs(w.dtype, w.b_layout, a_layout):
             if kernels and cfg.kernel not in kernels:
                 continue
-            if not aligned and cfg.kernel not in tgemm.ANY_ALIGNMENT_KERNELS:
+            if aligned is not True and cfg.kernel not in allowed:
                 continue                                # the fast kernels refuse these
             if a_layout:                                # the general entry point
                 def go(i, c=cfg):

@@ -38,7 +38,7 @@ EXPORTS = ("attn_fwd_f16", "gemm_f16", "gemm_bf16", "gemm_ex", "gemm_ex_ws", "ge
 __all__ = ["F16", "BF16", "B_NK", "B_KN", "A_MK", "A_KM", "KERNEL_GENERIC", "KERNEL_TILED",
            "KERNEL_SKINNY", "KERNEL_DMA", "KERNEL_PINGPONG", "KERNEL_QUAD", "KERNEL_SPLITK",
            "KERNEL_QUAD_SPLITK", "KERNEL_QUAD_STREAMK", "KERNEL_MASKED", "SPLIT_KERNELS",
-           "WORKSPACE_KERNELS",
+           "WORKSPACE_KERNELS", "ALIGN_OPERANDS",
            "ANY_ALIGNMENT_KERNELS",
            "STREAMK_WORKSPACE_BYTES",
            "KERNEL_DIRECT",
@@ -183,11 +183,20 @@ def gemm_ex_noalloc(dtype, m, n, k, A, B, C, b_layout=B_NK, config: Config | Non
                                   _stream(stream)), "gemm_ex_noalloc")
 
 
+ALIGN_OPERANDS = 2   # `aligned` value: A and B meet the fast rules, C or N does not
+
+
+def _align_arg(aligned) -> int:
+    return ALIGN_OPERANDS if (not isinstance(aligned, bool) and aligned == ALIGN_OPERANDS) \
+        else int(bool(aligned))
+
+
 def query_config_ws(dtype, m, n, k, b_layout=B_NK, aligned=True):
-    """(configuration, workspace bytes) the table picks when a workspace can be lent."""
+    """(configuration, workspace bytes) the table picks when a workspace can be lent;
+    aligned: True (every fast-kernel rule), False (none) or ALIGN_OPERANDS."""
     out = Config()
     nbytes = ctypes.c_int64(0)
-    _check(load().tgemm_query_config_ws(dtype, m, n, k, b_layout, int(bool(aligned)),
+    _check(load().tgemm_query_config_ws(dtype, m, n, k, b_layout, _align_arg(aligned),
                                         ctypes.byref(out), ctypes.byref(nbytes)),
            "tgemm_query_config_ws")
     return out, int(nbytes.value)
@@ -210,9 +219,11 @@ def gemm_strided(dtype, m, n, k, A, lda, a_layout, B, ldb, b_layout, C, ldc,
 
 
 def query_config(dtype, m, n, k, b_layout=B_NK, aligned=True, a_layout=A_MK) -> Config:
+    """The choice for an alignment class: aligned True (every fast-kernel rule), False
+    (none: the masked kernel) or ALIGN_OPERANDS (A and B meet the rules, C or N does not)."""
     out = Config()
     _check(load().tgemm_query_config_ex(dtype, m, n, k, a_layout, b_layout,
-                                        int(bool(aligned)), ctypes.byref(out)),
+                                        _align_arg(aligned), ctypes.byref(out)),
            "tgemm_query_config_ex")
     return out
 
