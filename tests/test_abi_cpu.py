@@ -96,11 +96,22 @@ def test_operands_aligned_class(lib):
     any other shape, or B [K,N], stays on the masked kernel."""
     A = tgemm.ALIGN_OPERANDS
     for dt in (tgemm.F16, tgemm.BF16):
-        for m, rows in ((1, 32), (8, 32), (32, 32), (64, 64)):
+        for m, rows, cols in ((1, 32, 32), (8, 32, 32), (16, 32, 64), (32, 32, 64),
+                              (64, 64, 64)):
             c = tgemm.query_config(dt, m, 50257, 4096, tgemm.B_NK, A)
-            assert c.kernel == tgemm.KERNEL_SKINNY and c.block_m == rows, (m, c)
-            # what an all-aligned product of that size would take
-            assert c.as_dict() == tgemm.query_config(dt, m, 50264, 4096).as_dict()
+            assert (c.kernel, c.block_m, c.block_n) == (tgemm.KERNEL_SKINNY, rows, cols), \
+                (m, c)
+            # what an all-aligned product of that size takes where that is the skinny
+            # kernel; past 8 rows aligned operands take the quad kernel instead
+            aligned = tgemm.query_config(dt, m, 50264, 4096)
+            if m <= 8:
+                assert c.as_dict() == aligned.as_dict()
+            else:
+                assert aligned.kernel == tgemm.KERNEL_QUAD
+        assert tgemm.query_config(dt, 32, 8200, 4096, tgemm.B_NK, A).as_dict() == \
+            tgemm.query_config(dt, 32, 8208, 4096).as_dict()
+        assert tgemm.query_config(dt, 128, 50257, 4096, tgemm.B_NK, A).kernel == \
+            tgemm.KERNEL_MASKED
         assert tgemm.query_config(dt, 8, 50257, 4096, tgemm.B_KN, A).kernel == \
             tgemm.KERNEL_MASKED
         assert tgemm.query_config(dt, 4096, 50257, 4096, tgemm.B_NK, A).kernel == \
@@ -125,6 +136,29 @@ def test_operands_aligned_class(lib):
     # A's rows not a multiple of 8 elements apart: refused with B [N,K] too
     assert st(1, 8, 8191, 4096, FAKE, 4100, tgemm.A_MK, FAKE + (1 << 30), 4096, tgemm.B_NK,
               FAKE + (1 << 31), 8191, ctypes.byref(skinny), None) == -3
+
+
+def test_wide_n_rule(lib):
+    """Past the grid's widest N (8192), products whose nearest grid point takes the skinny
+    kernel are re-decided: the 64-column skinny form up to 64 rows, the tiled kernel's
+    128x128 tiles above, and the quad kernel's 192x256 tiles from N = 40960 (more than
+    8 rows); the grid's own choices are untouched."""
+    def q(m, n, k=4096, layout=tgemm.B_NK):
+        c = tgemm.query_config(tgemm.BF16, m, n, k, layout)
+        return c.kernel, c.block_m, c.block_n
+    S, T, Q = tgemm.KERNEL_SKINNY, tgemm.KERNEL_TILED, tgemm.KERNEL_QUAD
+    assert q(8, 8192) == (S, 32, 32) and q(64, 8192) == (S, 64, 32)
+    assert q(8, 14336) == (S, 32, 64) and q(32, 28672) == (S, 32, 64)
+    assert q(64, 14336) == (S, 64, 64) and q(33, 12288) == (S, 64, 64)
+    assert q(65, 14336) == (T, 128, 128) and q(128, 28672) == (T, 128, 128)
+    assert q(150, 28672) == (T, 128, 128)
+    assert q(8, 50264) == (S, 32, 32) and q(1, 65536) == (S, 32, 32)
+    for m in (9, 32, 64, 128, 150):
+        assert q(m, 50264) == (Q, 192, 256), m
+        assert q(m, 40960) == (Q, 192, 256), m
+    # B [K,N] and the grid's non-skinny choices are unchanged
+    assert q(64, 14336, 4096, tgemm.B_KN)[0] == S and q(64, 14336, 4096, tgemm.B_KN)[2] == 32
+    assert q(2048, 16384)[0] != S
 
 
 def test_query_config_table(lib):

@@ -2043,21 +2043,24 @@ gemm_quad_sk(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restri
 // ------------------------------------------------------------------------------------
 // The skinny kernels' end: the waves' partial products to LDS as red[wave][n][m] (m
 // contiguous), summed in wave order (deterministic), cast once and stored.
-template <int DT, int MT, int NW>
-__device__ __forceinline__ void skinny_epilogue(u16* lds, const f32x16 (&acc)[MT],
+// acc[h * NB + b]: rows 32h.., columns 32b.. of the workgroup's BM x (32 NB) block.
+template <int DT, int MT, int NW, int NB = 1>
+__device__ __forceinline__ void skinny_epilogue(u16* lds, const f32x16 (&acc)[MT * NB],
                                                 u16* __restrict__ C, int M, int N, int ldc,
                                                 int m0, int n0, int tid, int lane, int wave) {
-    constexpr int BN = 32, BM = MT * 32;
+    constexpr int BN = 32 * NB, BM = MT * 32;
     const int half = lane >> 5;
     __syncthreads();
     float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
     for (int h = 0; h < MT; ++h)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int n = 8 * (v >> 2) + 4 * half + (v & 3);
-            red[(wave * BN + n) * BM + 32 * h + (lane & 31)] = acc[h][v];
-        }
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int n = 32 * b + 8 * (v >> 2) + 4 * half + (v & 3);
+                red[(wave * BN + n) * BM + 32 * h + (lane & 31)] = acc[h * NB + b][v];
+            }
     __syncthreads();
     constexpr int OUT_PER_T = BM * BN / (NW * 64);   // consecutive n per thread
     static_assert(OUT_PER_T % 4 == 0 || OUT_PER_T == 2, "store groups");
@@ -2107,12 +2110,12 @@ __device__ __forceinline__ void skinny_epilogue(u16* lds, const f32x16 (&acc)[MT
     }
 }
 
-template <int DT, int MT, int D, int CKT = 64, int NWT = 8>
+template <int DT, int MT, int D, int CKT = 64, int NWT = 8, int NB = 1>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NWT * 64, NWT * 64),
                                amdgpu_waves_per_eu(NWT / 4, NWT / 4)))
 gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restrict__ C, int M,
             int N, int K, int lda, int ldb, int ldc) {
-    constexpr int NW = NWT, BN = 32, CK = CKT, KC = CK / 8;
+    constexpr int NW = NWT, BN = 32 * NB, CK = CKT, KC = CK / 8;
     static_assert(NW == 4 || NW == 8, "four or eight waves");
     constexpr int RPL = 64 / KC;                   // chunk rows per 1 KiB load
     constexpr int BM = MT * 32;
@@ -2183,9 +2186,9 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
     };
 
     const int xr = swz<KC>(lane & 31);
-    f32x16 acc[MT];
+    f32x16 acc[MT * NB];
 #pragma unroll
-    for (int h = 0; h < MT; ++h)
+    for (int h = 0; h < MT * NB; ++h)
         acc[h] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
     static_for<0, D>([&](auto d) { load_chunk(decltype(d)::value, d); });
@@ -2196,7 +2199,7 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
             for (int i = 0; i < LD; ++i)
                 if (!dead(i))
                     *reinterpret_cast<u32x4*>(wb + wr_off(i)) = buf[d][i];
-            u32x4 fa[CK / 16][MT], fb[CK / 16];
+            u32x4 fa[CK / 16][MT], fb[CK / 16][NB];
 #pragma unroll
             for (int j = 0; j < CK / 16; ++j) {
                 const int koff = (((2 * j) | half) ^ xr) * 8;
@@ -2204,18 +2207,24 @@ gemm_skinny(const u16* __restrict__ A, const u16* __restrict__ B, u16* __restric
                 for (int h = 0; h < MT; ++h)
                     fa[j][h] = *reinterpret_cast<const u32x4*>(
                         wb + (32 * h + (lane & 31)) * CK + koff);
-                fb[j] = *reinterpret_cast<const u32x4*>(wb + (BM + (lane & 31)) * CK + koff);
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    fb[j][b] = *reinterpret_cast<const u32x4*>(
+                        wb + (BM + 32 * b + (lane & 31)) * CK + koff);
             }
             load_chunk(c + d + D, dc);
 #pragma unroll
             for (int j = 0; j < CK / 16; ++j)
 #pragma unroll
                 for (int h = 0; h < MT; ++h)
-                    acc[h] = mfma_32x32x16<DT>(fb[j], fa[j][h], acc[h]);
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        acc[h * NB + b] =
+                            mfma_32x32x16<DT>(fb[j][b], fa[j][h], acc[h * NB + b]);
         });
     }
 
-    skinny_epilogue<DT, MT, NW>(lds, acc, C, M, N, ldc, m0, n0, tid, lane, wave);
+    skinny_epilogue<DT, MT, NW, NB>(lds, acc, C, M, N, ldc, m0, n0, tid, lane, wave);
 }
 
 // The skinny kernel for B stored [K,N] (N contiguous): the same workgroup, wave split,

@@ -155,11 +155,12 @@ hipError_t launch_quad_sk(const void* A, const void* B, void* C, int M, int N, i
     return hipGetLastError();
 }
 
-template <int DT, int MT, int D, int CK = 64, int NW = 8>
+template <int DT, int MT, int D, int CK = 64, int NW = 8, int NB = 1>
 hipError_t launch_skinny(const void* A, const void* B, void* C, int M, int N, int K, int lda,
                          int ldb, int ldc, int, hipStream_t s) {
-    hipLaunchKernelGGL((tgemm::gemm_skinny<DT, MT, D, CK, NW>),
-                       dim3((unsigned)cdiv(N, 32), (unsigned)cdiv(M, MT * 32)), dim3(NW * 64),
+    hipLaunchKernelGGL((tgemm::gemm_skinny<DT, MT, D, CK, NW, NB>),
+                       dim3((unsigned)cdiv(N, 32 * NB), (unsigned)cdiv(M, MT * 32)),
+                       dim3(NW * 64),
                        0, s,
                        KARGS);
     return hipGetLastError();
@@ -282,5 +283,12 @@ hipError_t launch_generic(const void* A, const void* B, void* C, int M, int N, i
     Variant {                                                                              \
         DT, 0, 0, tgemm_config{TGEMM_KERNEL_SKINNY, MT * 32, 32, 128, 1, 4, D, 1, 4, 32},      \
             &launch_skinny<DT, MT, D, 128, 4>                                              \
+    }
+// The skinny kernel with 64 columns per workgroup (two 32-column blocks): half the
+// workgroups of the 32-column form, each reading A once for twice the columns.
+#define SKINNY_N64(DT, MT, CK, NW, D)                                                      \
+    Variant {                                                                              \
+        DT, 0, 0, tgemm_config{TGEMM_KERNEL_SKINNY, MT * 32, 64, CK, 1, NW, D, 1, NW, 32},     \
+            &launch_skinny<DT, MT, D, CK, NW, 2>                                           \
     }
 }  // namespace tgemm_reg

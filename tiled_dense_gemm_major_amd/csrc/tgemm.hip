@@ -200,6 +200,35 @@ tgemm_config choose_masked(int a_layout, int layout, int64_t m, int64_t n) {
     return tgemm_config{TGEMM_KERNEL_MASKED, best->bm, best->bn, 64, 2, 2, 2, best->group, 1, 32};
 }
 
+// The skinny kernel's 64-column forms: 32 rows with 64-wide chunks two ahead, 64 rows
+// with 64-wide chunks one ahead, eight waves each.
+constexpr tgemm_config kSkinnyN64Rows32{TGEMM_KERNEL_SKINNY, 32, 64, 64, 1, 8, 2, 1, 8, 32};
+constexpr tgemm_config kSkinnyN64Rows64{TGEMM_KERNEL_SKINNY, 64, 64, 64, 1, 8, 1, 1, 8, 32};
+
+constexpr tgemm_config kTiled128{TGEMM_KERNEL_TILED, 128, 128, 64, 2, 2, 2, 8, 1, 32};
+constexpr tgemm_config kQuadRows192{TGEMM_KERNEL_QUAD, 192, 256, 64, 2, 2, 5, 4, 1, 32};
+
+// Products with B [N,K] past the grid's widest N whose nearest grid point takes the
+// skinny kernel (up to about 180 rows): they stream B, and that choice re-reads all of A
+// once per 32 columns and, at thousands of workgroups, leaves a ragged last wave.  Measured
+// hot, bf16, K = 4096, M 1-128, N 12288-50264 (us, the grid's choice -> this one):
+// - below N = 40960, at most 64 rows: the 64-column skinny form, half the A re-reads
+//   (8x12288 22.5 -> 19.0, 32x14336 27.5 -> 21.5, 64x14336 33.0 -> 23.2, 64x28672
+//   61.1 -> 42.9);
+// - below N = 40960, more than 64 rows: the tiled kernel's 128x128 tiles (128x16384
+//   43.6 -> 38.7, 128x28672 82.0 -> 42.0);
+// - from N = 40960 (one wave of 192x256 tiles), more than 8 rows: the quad kernel
+//   (16x50264 90.0 -> 81.4, 32x50264 92.9 -> 82.0, 64x50264 103.5 -> 83.9, 128x50264
+//   169.9 -> 84.9); up to 8 rows the two are level (78.5-84.5 against 80.5-82.8) and
+//   the skinny form stays.
+tgemm_config choose_wide_n(int64_t m, int64_t n, const tgemm_config& grid_choice) {
+    if (n >= 40960)
+        return m <= 8 ? grid_choice : kQuadRows192;
+    if (m <= 64)
+        return m <= 32 ? kSkinnyN64Rows32 : kSkinnyN64Rows64;
+    return kTiled128;
+}
+
 // The kernel for operands past what the masked kernel's buffer offsets reach.
 constexpr tgemm_config kGenericConfig{TGEMM_KERNEL_GENERIC, 64, 64, 16, 2, 2, 1, 8, 1, 32};
 
@@ -241,6 +270,9 @@ tgemm_config choose(int dtype, int a_layout, int layout, int64_t m, int64_t n, i
                         cfg.mfma = tiles > 256 ? 16 : 32;
                 }
             }
+            if (cfg.kernel == TGEMM_KERNEL_SKINNY && layout == TGEMM_B_NK && k >= 1024 &&
+                n > kTableN[NN - 1])
+                cfg = choose_wide_n(m, n, cfg);
             return cfg;
         }
     }
@@ -479,6 +511,12 @@ tgemm_config choose_for(int dtype, int a_layout, int layout, int64_t m, int64_t 
         const tgemm_config c = choose(dtype, a_layout, layout, m, n, k, true);
         if (c.kernel == TGEMM_KERNEL_SKINNY)
             return c;
+        // past the grid's widest N, where aligned operands would take the quad kernel,
+        // up to 64 rows keep the skinny kernel's 64-column form (8-64 x 50257 x 4096:
+        // 84-115 us against 134-143 for the best masked tiling)
+        constexpr int NN = sizeof(kTableN) / sizeof(kTableN[0]);
+        if (m <= 64 && k >= 1024 && n > kTableN[NN - 1])
+            return m <= 32 ? kSkinnyN64Rows32 : kSkinnyN64Rows64;
     }
     return with_ws ? choose_ws(dtype, a_layout, layout, m, n, k, false)
                    : choose(dtype, a_layout, layout, m, n, k, false);
