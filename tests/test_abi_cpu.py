@@ -156,9 +156,16 @@ def test_wide_n_rule(lib):
     for m in (9, 32, 64, 128, 150):
         assert q(m, 50264) == (Q, 192, 256), m
         assert q(m, 40960) == (Q, 192, 256), m
-    # B [K,N] and the grid's non-skinny choices are unchanged
-    assert q(64, 14336, 4096, tgemm.B_KN)[0] == S and q(64, 14336, 4096, tgemm.B_KN)[2] == 32
-    assert q(2048, 16384)[0] != S
+    # B [K,N]: the quad kernel from N = 26624 above 8 rows, from N = 40960, and above
+    # 128 rows; the skinny kernel below
+    kn = tgemm.B_KN
+    assert q(64, 14336, 4096, kn) == (S, 128, 32) and q(8, 28672, 4096, kn) == (S, 32, 32)
+    assert q(48, 24576, 4096, kn)[0] == S
+    for m, n in ((9, 26624), (32, 28672), (8, 50264), (1, 40960), (160, 14336),
+                 (128, 50264)):
+        assert q(m, n, 4096, kn) == (Q, 192, 256), (m, n)
+    # the grid's non-skinny choices are unchanged
+    assert q(2048, 16384)[0] != S and q(2048, 16384, 4096, kn)[0] != S
 
 
 def test_query_config_table(lib):

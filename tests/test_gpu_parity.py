@@ -500,3 +500,26 @@ def test_skinny_odd_vocabulary_full(dev, orc, dtype):
     (tgemm.gemm_f16 if dtype == F16 else tgemm.gemm_bf16)(M, N, K, Ad, Bd, C)
     torch.cuda.synchronize()
     assert_parity_full(orc, dtype, A, B, B_NK, from_dev(C), "odd vocabulary")
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("shape,layout,kernel", [
+    ((24, 12288, 1024), B_NK, "skinny64"), ((80, 12288, 1024), B_NK, "tiled"),
+    ((16, 40960, 1024), B_NK, "quad"), ((8, 40960, 1024), B_NK, "skinny"),
+    ((40, 28672, 1024), B_KN, "quad"), ((8, 28672, 1024), B_KN, "skinny"),
+    ((136, 12296, 1032), B_KN, "quad")])
+def test_wide_n_table_choices(dev, orc, dtype, shape, layout, kernel):
+    """Products past the table's widest N take the rule's choice through the default path;
+    every element against the oracle."""
+    from tiled_dense_gemm_major_amd import tgemm
+    M, N, K = shape
+    c = tgemm.query_config(dtype, M, N, K, layout)
+    want_kernel = {"skinny64": tgemm.KERNEL_SKINNY, "skinny": tgemm.KERNEL_SKINNY,
+                   "tiled": tgemm.KERNEL_TILED, "quad": tgemm.KERNEL_QUAD}[kernel]
+    assert c.kernel == want_kernel, c
+    if kernel == "skinny64":
+        assert c.block_n == 64
+    A, B = _inputs(dtype, M, N, K, layout, 800 + M)
+    say(f"wide N {shape} layout {layout} dtype {dtype} -> {_cfg_id(c)}")
+    got = run(dtype, A, B, layout)
+    assert_parity(orc, dtype, K, got, orc.gemm(dtype, A, B, layout), str(shape))

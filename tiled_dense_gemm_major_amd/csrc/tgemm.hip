@@ -273,6 +273,16 @@ tgemm_config choose(int dtype, int a_layout, int layout, int64_t m, int64_t n, i
             if (cfg.kernel == TGEMM_KERNEL_SKINNY && layout == TGEMM_B_NK && k >= 1024 &&
                 n > kTableN[NN - 1])
                 cfg = choose_wide_n(m, n, cfg);
+            // With B [K,N] the same past-the-grid choice goes to the quad kernel's
+            // 192-row form from N = 26624 above 8 rows, from N = 40960 at any height,
+            // and above 128 rows (hot, bf16, K = 4096: 8x50264 129.3 -> 93.4 us,
+            // 32x28672 57.6 -> 53.9, 64x28672 66.2 -> 54.2, 128x50264 205.9 -> 98.2,
+            // 160x14336 71.5 -> 55.0, 160x50264 326.0 -> 102.9); below, the skinny
+            // kernel stays (8x28672 49.7 against 54.0, 128x14336 46.8 against 54.6,
+            // 48x24576 48.1 against 54.6)
+            if (cfg.kernel == TGEMM_KERNEL_SKINNY && layout == TGEMM_B_KN && k >= 1024 &&
+                n > kTableN[NN - 1] && (m > 128 || n >= 40960 || (n >= 26624 && m > 8)))
+                cfg = kQuadRows192;
             return cfg;
         }
     }
