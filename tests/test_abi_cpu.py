@@ -142,7 +142,8 @@ def test_wide_n_rule(lib):
     """Past the grid's widest N (8192), products whose nearest grid point takes the skinny
     kernel are re-decided: the 64-column skinny form up to 64 rows, the tiled kernel's
     128x128 tiles above, and the quad kernel's 192x256 tiles from N = 40960 (more than
-    8 rows); the grid's own choices are untouched."""
+    8 rows; above 64 rows the first of 64x128, 128x128 and 192x256 tiles that makes one
+    wave); the grid's own choices are untouched."""
     def q(m, n, k=4096, layout=tgemm.B_NK):
         c = tgemm.query_config(tgemm.BF16, m, n, k, layout)
         return c.kernel, c.block_m, c.block_n
@@ -150,8 +151,13 @@ def test_wide_n_rule(lib):
     assert q(8, 8192) == (S, 32, 32) and q(64, 8192) == (S, 64, 32)
     assert q(8, 14336) == (S, 32, 64) and q(32, 28672) == (S, 32, 64)
     assert q(64, 14336) == (S, 64, 64) and q(33, 12288) == (S, 64, 64)
-    assert q(65, 14336) == (T, 128, 128) and q(128, 28672) == (T, 128, 128)
-    assert q(150, 28672) == (T, 128, 128)
+    D = tgemm.KERNEL_DMA
+    # more than 64 rows: 64x128 tiles if they make one wave, else 128x128, else the quad
+    assert q(65, 14336) == (D, 64, 128) and q(128, 16384) == (D, 64, 128)
+    assert q(128, 28672) == (T, 128, 128) and q(160, 16384) == (T, 128, 128)
+    assert q(72, 20480) == (T, 128, 128) and q(144, 24576) == (Q, 192, 256)
+    # 65-192 rows whose grid point takes small tiles follow the same rule
+    assert q(128, 20480, 2048) == (T, 128, 128) and q(192, 28672) == (Q, 192, 256)
     assert q(8, 50264) == (S, 32, 32) and q(1, 65536) == (S, 32, 32)
     for m in (9, 32, 64, 128, 150):
         assert q(m, 50264) == (Q, 192, 256), m

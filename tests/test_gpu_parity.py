@@ -504,7 +504,8 @@ def test_skinny_odd_vocabulary_full(dev, orc, dtype):
 
 @pytest.mark.parametrize("dtype", [F16, BF16])
 @pytest.mark.parametrize("shape,layout,kernel", [
-    ((24, 12288, 1024), B_NK, "skinny64"), ((80, 12288, 1024), B_NK, "tiled"),
+    ((24, 12288, 1024), B_NK, "skinny64"), ((80, 12288, 1024), B_NK, "dma"),
+    ((72, 20480, 1024), B_NK, "tiled"),
     ((16, 40960, 1024), B_NK, "quad"), ((8, 40960, 1024), B_NK, "skinny"),
     ((40, 28672, 1024), B_KN, "quad"), ((8, 28672, 1024), B_KN, "skinny"),
     ((136, 12296, 1032), B_KN, "quad")])
@@ -515,10 +516,13 @@ def test_wide_n_table_choices(dev, orc, dtype, shape, layout, kernel):
     M, N, K = shape
     c = tgemm.query_config(dtype, M, N, K, layout)
     want_kernel = {"skinny64": tgemm.KERNEL_SKINNY, "skinny": tgemm.KERNEL_SKINNY,
-                   "tiled": tgemm.KERNEL_TILED, "quad": tgemm.KERNEL_QUAD}[kernel]
+                   "tiled": tgemm.KERNEL_TILED, "quad": tgemm.KERNEL_QUAD,
+                   "dma": tgemm.KERNEL_DMA}[kernel]
     assert c.kernel == want_kernel, c
     if kernel == "skinny64":
         assert c.block_n == 64
+    if kernel == "tiled":
+        assert (c.block_m, c.block_n) == (128, 128)
     A, B = _inputs(dtype, M, N, K, layout, 800 + M)
     say(f"wide N {shape} layout {layout} dtype {dtype} -> {_cfg_id(c)}")
     got = run(dtype, A, B, layout)

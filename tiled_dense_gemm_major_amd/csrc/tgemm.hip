@@ -206,6 +206,7 @@ constexpr tgemm_config kSkinnyN64Rows32{TGEMM_KERNEL_SKINNY, 32, 64, 64, 1, 8, 2
 constexpr tgemm_config kSkinnyN64Rows64{TGEMM_KERNEL_SKINNY, 64, 64, 64, 1, 8, 1, 1, 8, 32};
 
 constexpr tgemm_config kTiled128{TGEMM_KERNEL_TILED, 128, 128, 64, 2, 2, 2, 8, 1, 32};
+constexpr tgemm_config kDma64x128{TGEMM_KERNEL_DMA, 64, 128, 64, 1, 4, 4, 2, 1, 32};
 constexpr tgemm_config kQuadRows192{TGEMM_KERNEL_QUAD, 192, 256, 64, 2, 2, 5, 4, 1, 32};
 
 // Products with B [N,K] past the grid's widest N whose nearest grid point takes the
@@ -215,8 +216,11 @@ constexpr tgemm_config kQuadRows192{TGEMM_KERNEL_QUAD, 192, 256, 64, 2, 2, 5, 4,
 // - below N = 40960, at most 64 rows: the 64-column skinny form, half the A re-reads
 //   (8x12288 22.5 -> 19.0, 32x14336 27.5 -> 21.5, 64x14336 33.0 -> 23.2, 64x28672
 //   61.1 -> 42.9);
-// - below N = 40960, more than 64 rows: the tiled kernel's 128x128 tiles (128x16384
-//   43.6 -> 38.7, 128x28672 82.0 -> 42.0);
+// - below N = 40960, more than 64 rows: the first of these whose tiles make one wave
+//   (at most 256): the direct-to-LDS kernel's 64x128 tiles (128x12288 42.4 -> 33.8,
+//   96x14336 37.6 -> 33.7, 80x16384 40.0 -> 35.3), the tiled kernel's 128x128 tiles
+//   (128x28672 82.0 -> 44.0, 160x16384 71.5 -> 43.2, 72x20480 -> 39.4), else the quad
+//   kernel's 192x256 tiles (144x24576 -> 55.0 against 75.1 for 128x128 tiles);
 // - from N = 40960 (one wave of 192x256 tiles), more than 8 rows: the quad kernel
 //   (16x50264 90.0 -> 81.4, 32x50264 92.9 -> 82.0, 64x50264 103.5 -> 83.9, 128x50264
 //   169.9 -> 84.9); up to 8 rows the two are level (78.5-84.5 against 80.5-82.8) and
@@ -226,7 +230,12 @@ tgemm_config choose_wide_n(int64_t m, int64_t n, const tgemm_config& grid_choice
         return m <= 8 ? grid_choice : kQuadRows192;
     if (m <= 64)
         return m <= 32 ? kSkinnyN64Rows32 : kSkinnyN64Rows64;
-    return kTiled128;
+    const auto tiles = [&](int64_t bm, int64_t bn) {
+        return ((m + bm - 1) / bm) * ((n + bn - 1) / bn);
+    };
+    if (tiles(64, 128) <= 256)
+        return kDma64x128;
+    return tiles(128, 128) <= 256 ? kTiled128 : kQuadRows192;
 }
 
 // The kernel for operands past what the masked kernel's buffer offsets reach.
@@ -270,8 +279,12 @@ tgemm_config choose(int dtype, int a_layout, int layout, int64_t m, int64_t n, i
                         cfg.mfma = tiles > 256 ? 16 : 32;
                 }
             }
-            if (cfg.kernel == TGEMM_KERNEL_SKINNY && layout == TGEMM_B_NK && k >= 1024 &&
-                n > kTableN[NN - 1])
+            // (65-192 rows whose grid point takes 64x64 to 128x128 tiles are re-decided
+            // the same way: 128x20480x2048 40.4 -> 23.9 us, 192x28672x4096 80.1 -> 56.8)
+            const bool small_tiles =
+                cfg.kernel == TGEMM_KERNEL_TILED || cfg.kernel == TGEMM_KERNEL_DMA;
+            if ((cfg.kernel == TGEMM_KERNEL_SKINNY || (small_tiles && m > 64 && m <= 192)) &&
+                layout == TGEMM_B_NK && k >= 1024 && n > kTableN[NN - 1])
                 cfg = choose_wide_n(m, n, cfg);
             // With B [K,N] the same past-the-grid choice goes to the quad kernel's
             // 192-row form from N = 26624 above 8 rows, from N = 40960 at any height,

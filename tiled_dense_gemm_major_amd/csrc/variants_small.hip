@@ -7,6 +7,7 @@ namespace tgemm_reg {
 namespace {
 #define SMALL_MK_NK(DT)                                                                    \
     GENERIC(DT, 0, 0), DMA(DT, 256, 256, 32, 2, 2, 4, 4), DMA(DT, 256, 256, 32, 2, 2, 5, 4), \
+        DMA(DT, 64, 128, 64, 1, 4, 4, 2), DMA(DT, 64, 256, 64, 1, 4, 4, 2),               \
         SKINNY(DT, 1, 4), SKINNY(DT, 2, 3), SKINNY(DT, 4, 1), SKINNY_WIDE(DT, 1, 1),       \
         SKINNY_WIDE4(DT, 2, 1), SKINNY_N64(DT, 1, 64, 8, 2), SKINNY_N64(DT, 2, 64, 8, 1),  \
         SPLITK(DT, 64, 256, 32, 1, 4, 5, 1), SPLITK(DT, 64, 128, 32, 1, 4, 5, 1),          \
