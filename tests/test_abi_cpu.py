@@ -285,10 +285,12 @@ def test_query_config_ws_and_workspace_size(lib):
     assert (cfg.kernel, cfg.block_m, cfg.block_n, cfg.split_k) == (tgemm.KERNEL_SPLITK, 64,
                                                                    128, 4)
     assert nbytes == 4 * 64 * 8192 * 4 == tgemm.workspace_size(64, 8192, cfg)
-    # 224 tiles of 64x128 would exceed one wave: 112 tiles of 64x256, 2 splits
-    cfg, nbytes = ws((64, 28672, 4096))
-    assert (cfg.kernel, cfg.block_n, cfg.split_k) == (tgemm.KERNEL_SPLITK, 256, 2)
-    assert nbytes <= tgemm.SCRATCH_BYTES
+    # past the grid's widest N the skinny kernel's 64-column form keeps its plain launch
+    for shape in [(64, 28672, 4096), (8, 14336, 4096), (8, 32000, 8192), (4, 10240, 4096),
+                  (64, 24576, 8192)]:
+        cfg, nbytes = ws(shape)
+        assert (cfg.kernel, cfg.block_n, nbytes) == (tgemm.KERNEL_SKINNY, 64, 0), shape
+        assert cfg.as_dict() == tgemm.query_config(tgemm.BF16, *shape).as_dict()
     # the same with B [K,N]: the quad kernel's split-K (32 tiles, 8 splits)
     cfg, _ = ws((64, 8192, 8192), tgemm.B_KN)
     assert (cfg.kernel, cfg.split_k, cfg.mfma) == (tgemm.KERNEL_QUAD_SPLITK, 8, 32)
@@ -318,8 +320,8 @@ def test_query_config_ws_and_workspace_size(lib):
                   (2056, 3544, 4960), (4008, 2264, 3664)]:
         cfg, nbytes = ws(shape)
         assert cfg.kernel not in tgemm.SPLIT_KERNELS and nbytes == 0, shape
-    # a 32-row skinny product with half a wave of workgroups, or more than a wave: split
-    for shape in [(8, 4096, 14336), (8, 14336, 4096)]:
+    # a 32-row skinny product with half a wave of workgroups: split
+    for shape in [(8, 4096, 14336)]:
         cfg, _ = ws(shape)
         assert cfg.kernel == tgemm.KERNEL_SPLITK, shape
     # fewer than 16 tiles of 256 x 256 with B [N,K]: the split-K kernel's 64x128 tiles

@@ -114,17 +114,19 @@ def test_splitk_table_choice_skinny_workload(dev, orc):
 
 
 def test_splitk_table_choice_wide_skinny(dev, orc):
-    """A skinny product with more than 128 tiles of 64x128 (ragged N): the table's choice
-    with a workspace takes the split-K kernel's 64x256 tiles, every element against the
-    oracle."""
+    """A skinny product with more than 128 tiles of 64x128 (ragged N) on the split-K
+    kernel's 64x256 tiles, 2 splits, every element against the oracle; with a workspace
+    the table itself keeps the skinny kernel's plain 64-column form here."""
     from tiled_dense_gemm_major_amd import tgemm
     M, N, K = 48, 28680, 2056
-    cfg, need = tgemm.query_config_ws(BF16, M, N, K)
-    assert (cfg.kernel, cfg.block_n, cfg.split_k) == (tgemm.KERNEL_SPLITK, 256, 2)
-    assert need == 2 * M * N * 4
+    table, need = tgemm.query_config_ws(BF16, M, N, K)
+    assert (table.kernel, table.block_n, need) == (tgemm.KERNEL_SKINNY, 64, 0)
+    cfg = tgemm.Config(kernel=tgemm.KERNEL_SPLITK, block_m=64, block_n=256, block_k=64,
+                       waves_m=1, waves_n=4, stages=4, group_m=1, split_k=2, mfma=32)
+    assert tgemm.workspace_size(M, N, cfg) == 2 * M * N * 4
     A, B, want = _case(orc, BF16, M, N, K)
-    say(f"split-K table choice bf16 {M}x{N}x{K}: 64x256 tiles, 2 splits")
-    got = _run_ws(BF16, A, B, None)
+    say(f"split-K bf16 {M}x{N}x{K}: 64x256 tiles, 2 splits")
+    got = _run_ws(BF16, A, B, cfg)
     assert not np.any(got == 0x7E00)
     assert_parity(orc, BF16, K, got, want, "wide skinny split-K")
 

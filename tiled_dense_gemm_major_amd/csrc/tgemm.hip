@@ -370,6 +370,13 @@ tgemm_config choose_ws(int dtype, int a_layout, int layout, int64_t m, int64_t n
     if ((plain.kernel == TGEMM_KERNEL_SKINNY || plain.kernel == TGEMM_KERNEL_DIRECT) &&
         k <= 4096 && n <= 2048)
         return plain;
+    // The skinny kernel's 64-column form (products past the grid's widest N) keeps its
+    // plain launch: split-K over workgroups was slower on 6 of 9 shapes measured
+    // (64x24576x8192 106.1 against 90.3 us, 8x32000x8192 109.9 against 95.1, 4x10240x4096
+    // 20.3 against 17.0) and at most 4.5 us faster on the others (32x16384x8192 45.4
+    // against 49.9, 48x20480x4096 34.1 against 37.7)
+    if (plain.kernel == TGEMM_KERNEL_SKINNY && plain.block_n == 64)
+        return plain;
     // A 32-row skinny product whose workgroups make one wave (192-256 of them) streams B
     // at the chip's rate on its own; split-K would add only its partials' traffic
     // (1-32 x 8192 x 8192: 23.4-24.8 against 25.4-26.7 us hot, 27.8-29.6 against
