@@ -167,6 +167,9 @@ def test_wide_n_rule(lib):
     kn = tgemm.B_KN
     assert q(64, 14336, 4096, kn) == (S, 128, 32) and q(8, 28672, 4096, kn) == (S, 32, 32)
     assert q(48, 24576, 4096, kn)[0] == S
+    # above 64 rows with K of at most 2048 the quad kernel, else the skinny kernel
+    assert q(100, 20480, 1024, kn) == (Q, 192, 256) and q(96, 24576, 2048, kn) == (Q, 192, 256)
+    assert q(72, 16384, 4096, kn)[0] == S and q(64, 20480, 1024, kn)[0] == S
     for m, n in ((9, 26624), (32, 28672), (8, 50264), (1, 40960), (160, 14336),
                  (128, 50264)):
         assert q(m, n, 4096, kn) == (Q, 192, 256), (m, n)

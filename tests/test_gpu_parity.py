@@ -508,7 +508,7 @@ def test_skinny_odd_vocabulary_full(dev, orc, dtype):
     ((72, 20480, 1024), B_NK, "tiled"),
     ((16, 40960, 1024), B_NK, "quad"), ((8, 40960, 1024), B_NK, "skinny"),
     ((40, 28672, 1024), B_KN, "quad"), ((8, 28672, 1024), B_KN, "skinny"),
-    ((136, 12296, 1032), B_KN, "quad")])
+    ((136, 12296, 1032), B_KN, "quad"), ((100, 12288, 1024), B_KN, "quad")])
 def test_wide_n_table_choices(dev, orc, dtype, shape, layout, kernel):
     """Products past the table's widest N take the rule's choice through the default path;
     every element against the oracle."""

@@ -292,9 +292,14 @@ tgemm_config choose(int dtype, int a_layout, int layout, int64_t m, int64_t n, i
             // 32x28672 57.6 -> 53.9, 64x28672 66.2 -> 54.2, 128x50264 205.9 -> 98.2,
             // 160x14336 71.5 -> 55.0, 160x50264 326.0 -> 102.9); below, the skinny
             // kernel stays (8x28672 49.7 against 54.0, 128x14336 46.8 against 54.6,
-            // 48x24576 48.1 against 54.6)
+            // 48x24576 48.1 against 54.6).  The quad kernel's time follows its K walk and
+            // the skinny kernel's B's bytes, so above 64 rows a K of at most 2048 also
+            // goes to the quad kernel (100x20480x1024 27.2 -> 21.2 us, 96x24576x2048
+            // 38.2 -> 32.6, 128x20480x2048 42.3 -> 32.3; at K = 4096 72x16384 37.0
+            // against 54.0 and 80x12288 39.0 against 54.3 keep the skinny kernel)
             if (cfg.kernel == TGEMM_KERNEL_SKINNY && layout == TGEMM_B_KN && k >= 1024 &&
-                n > kTableN[NN - 1] && (m > 128 || n >= 40960 || (n >= 26624 && m > 8)))
+                n > kTableN[NN - 1] &&
+                (m > 128 || n >= 40960 || (n >= 26624 && m > 8) || (m > 64 && k <= 2048)))
                 cfg = kQuadRows192;
             return cfg;
         }
